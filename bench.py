@@ -1,0 +1,273 @@
+"""Benchmark of mixed FP8/TQ3 paged decode on one MI355X.
+
+One step = one mkv_decode call over the whole batch of the workload (all
+partial kernels and the merge, schedule cached), with the cache already
+resident in HBM.  The default workload is the 131072-token long-context case
+(B=1, Hq=48, Hkv=8, d=128, 16-token pages, last 4096 tokens FP8, the rest
+TQ3).  The cache is held in R identical replicas, one pool each (like the
+per-layer caches of a model), at different seeded physical pages; consecutive
+steps decode different replicas, so the 256 MB last-level cache cannot serve
+a step from the previous one.  Workloads whose live KV already exceeds a few GB
+use one pool with their own slab sizes.
+
+Prints one JSON line:
+  value        KV GB/s = algorithmic bytes per step / step time
+  roofline     the dominant kernel (the TQ3 partial kernel): its algorithmic
+               bytes per launch / its mean launch time from HIP events recorded
+               on the decode stream during the timed region, against 8 TB/s
+  cpu_baseline the CPU oracle on the same workload (bounded repetitions)
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mixed FP8/TQ3 paged decode: µs/step and achieved KV HBM GB/s (% of peak)"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["kernels_partial_ref.hip", "kernels_merge.hip", "mkv_device.hpp",
+                  "mkv_kernels.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_mixed_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload(name):
+    from decode_attention_mixed_amd import workloads as W
+    if name.startswith("sweep"):
+        return W.sweep(int(name[5:]) / 100.0)
+    return getattr(W, name)()
+
+
+def describe(wl) -> str:
+    if wl.B == 1:
+        L = f"L={int(wl.lengths[0])}"
+    else:
+        L = f"L in [{int(wl.lengths.min())},{int(wl.lengths.max())}]"
+    fp8 = sum(len(a) for a in wl.anchors)
+    tot = sum(wl.n_pages(b) for b in range(wl.B))
+    return (f"{wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} d={wl.d} page={wl.P} {L}, "
+            f"{fp8}/{tot} pages FP8 (e4m3) and the rest TQ3")
+
+
+def kv_bytes(wl):
+    """Algorithmic bytes per decode step and per format (codes, TQ3 group
+    scales, FP8 page-head scales of every live token of the batch)."""
+    fp8 = tq3 = 0
+    for b in range(wl.B):
+        L = int(wl.lengths[b])
+        anchors = set(int(p) for p in wl.anchors[b])
+        for lp in range(wl.n_pages(b)):
+            n = min(wl.P, L - lp * wl.P)
+            if lp in anchors:
+                fp8 += n * 2 * wl.Hkv * wl.d + 8 * wl.Hkv
+            else:
+                tq3 += n * wl.Hkv * wl.d * 7 // 8
+    return fp8, tq3
+
+
+def cpu_baseline(wl, per_step_bytes, budget_s=20.0):
+    """Time the CPU oracle's decode step on the same workload (bounded)."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import pool_model as PM
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    models = []
+    for b in range(wl.B):
+        k, v = wl.kv(b)
+        m = PM.SeqModel(wl.Hkv, wl.d, wl.P)
+        m.append(k, v)
+        for lp in wl.demote_pages(b):
+            m.demote(int(lp))
+        models.append(m)
+        del k, v
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for b in range(wl.B):
+            A.decode_seq(models[b], wl.q_bits[b], wl.tau)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s or reps >= 50:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    model_name = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model_name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": per_step_bytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{reps} full decode step(s) of the same workload, {dt:.3f} s/step "
+                  f"({per_step_bytes / dt / 1e6:.1f} MB/s); numpy fp64 on '{model_name}', "
+                  f"BLAS threads {blas_threads}, host cpus {os.cpu_count()}",
+    }
+
+
+def load_traffic(kernel: str, wl_name: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{wl_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != kernel_src_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--replicas", type=int, default=0, help="0: 8, or 1 for multi-GB workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this library "
+              "has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_mixed_amd as mkv
+    from decode_attention_mixed_amd import harness as H
+
+    torch.cuda.set_device(0)
+    wl = workload(args.workload)
+    fp8_b, tq3_b = kv_bytes(wl)
+    step_bytes = fp8_b + tq3_b
+    R = args.replicas if args.replicas > 0 else (8 if step_bytes < 2**30 else 1)
+    log(f"workload {describe(wl)}; {step_bytes} KV bytes/step; {R} replicas")
+
+    # R pools, each holding one replica of the batch at its own (seeded, scattered)
+    # physical pages, like the per-layer caches of a model; step i decodes pool i % R.
+    n_anchor = sum(len(a) for a in wl.anchors)
+    n_tq3 = sum(wl.n_pages(b) for b in range(wl.B)) - n_anchor
+    max_pages = max(wl.n_pages(b) for b in range(wl.B))
+    pools = []
+    t0 = time.perf_counter()
+    kvs = [wl.kv(b) for b in range(wl.B)] if wl.B * max_pages * wl.P * wl.Hkv * wl.d <= 2**29 else None
+    for r in range(R):
+        if R == 1:
+            desc = H.pool_desc(wl)
+        else:
+            desc = H.pool_desc(wl, fp8_pages=n_anchor + max_pages + 16, tq3_pages=n_tq3 + 16,
+                               placement_seed=wl.placement_seed + r)
+        pools.append(H.DevicePool(desc))
+    for b in range(wl.B):
+        kv = kvs[b] if kvs is not None else wl.kv(b)
+        for r in range(R):
+            H.load_sequence(pools[r], wl, b, kv=kv)
+    del kvs
+    torch.cuda.synchronize()
+    log(f"cache built in {time.perf_counter() - t0:.1f} s: {mkv.pool_stats(pools[0].handle)}")
+
+    q = H.q_tensor(wl)
+    out = torch.empty(wl.B, wl.Hq, wl.d, device="cuda")
+    lse = torch.empty(wl.B, wl.Hq, device="cuda")
+    batch = list(range(wl.B))
+    tau = float(wl.tau)
+
+    for i in range(max(args.warmup, R)):
+        mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
+    torch.cuda.synchronize()
+    for p in pools:
+        mkv.profile_enable(p.handle, True)
+        mkv.profile_read(p.handle)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    prof = {}
+    for p in pools:
+        for k2, v2 in mkv.profile_read(p.handle).items():
+            prof[k2] = prof.get(k2, 0) + v2
+        mkv.profile_enable(p.handle, False)
+    log(f"step {ms * 1e3:.2f} us; kernel profile {prof}")
+
+    kernel_ms = {"partial_tq3": prof["ms_partial_tq3"] / max(1, prof["n_partial_tq3"]),
+                 "partial_fp8": prof["ms_partial_fp8"] / max(1, prof["n_partial_fp8"]),
+                 "merge": prof["ms_merge"] / max(1, prof["n_merge"])}
+    dom = "partial_tq3" if tq3_b >= fp8_b else "partial_fp8"
+    dom_bytes = tq3_b if dom == "partial_tq3" else fp8_b
+    achieved = dom_bytes / (kernel_ms[dom] * 1e-3) / 1e9 if kernel_ms[dom] > 0 else 0.0
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_step": round(ms * 1e3, 3),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+tq3 codes, f32 compute",
+        "data": "synthetic: seeded N(0,1) fp32 K/V (outlier channels x8), bf16 N(0,1) query",
+        "config": {
+            "workload": describe(wl),
+            "kv_bytes_per_step": step_bytes,
+            "kv_bytes_fp8": fp8_b,
+            "kv_bytes_tq3": tq3_b,
+            "replicas_rotated": R,
+            "kernel_us": {k: round(v * 1e3, 3) for k, v in kernel_ms.items()},
+        },
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(dom, wl.name),
+            "algorithmic_bytes_per_launch": dom_bytes,
+        },
+    }
+    for p in pools:
+        p.close()
+    del pools
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, step_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

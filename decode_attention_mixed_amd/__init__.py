@@ -1,0 +1,268 @@
+"""Python binding of libmkv: mixed FP8/TQ3 paged decode attention on MI355X.
+
+Argument marshalling only.  Every operation runs in the HIP library
+(libmkv.so, built in-tree by ``python -m decode_attention_mixed_amd.build``);
+there is no Python or CPU fallback, and loading fails loudly when the library
+is missing.  Tensors are torch tensors on the pool's device; streams default
+to torch's current stream.
+
+Function names match the C-ABI in include/mkv.h without the ``mkv_`` prefix:
+pool_bytes, record_bytes, pool_create, pool_destroy, seq_reset, append,
+demote, decode, seq_info, page_table, pool_stats, debug_gather,
+profile_enable, profile_read, status_string, last_error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmkv.so")
+
+FMT_FP8 = 0
+FMT_TQ3 = 1
+
+OK, EINVAL, ENOMEM, ESTATE, ERANGE, EHIP = 0, -1, -2, -3, -4, -5
+
+
+class MkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("max_batch", ctypes.c_int32),
+        ("max_q_heads", ctypes.c_int32),
+        ("max_chunks", ctypes.c_int32),
+        ("fp8_pages", ctypes.c_int64),
+        ("tq3_pages", ctypes.c_int64),
+        ("placement_seed", ctypes.c_uint64),
+    ]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [
+        ("live_tokens", ctypes.c_int64),
+        ("fp8_pages_live", ctypes.c_int64),
+        ("tq3_pages_live", ctypes.c_int64),
+        ("fp8_pages_free", ctypes.c_int64),
+        ("tq3_pages_free", ctypes.c_int64),
+        ("kv_bytes", ctypes.c_int64),
+        ("bytes_per_token", ctypes.c_double),
+        ("ratio_vs_bf16", ctypes.c_double),
+        ("ratio_vs_fp8", ctypes.c_double),
+        ("dense_shadow_bytes", ctypes.c_int64),
+        ("dense_fallbacks", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [
+        ("ms_partial_fp8", ctypes.c_double),
+        ("ms_partial_tq3", ctypes.c_double),
+        ("ms_merge", ctypes.c_double),
+        ("n_partial_fp8", ctypes.c_int64),
+        ("n_partial_tq3", ctypes.c_int64),
+        ("n_merge", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+EXPORTED = [
+    "mkv_pool_bytes", "mkv_record_bytes", "mkv_pool_create", "mkv_pool_destroy",
+    "mkv_seq_reset", "mkv_append", "mkv_demote", "mkv_decode", "mkv_seq_info",
+    "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_profile_enable",
+    "mkv_profile_read", "mkv_status_string", "mkv_last_error",
+]
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m decode_attention_mixed_amd.build` (no CPU fallback exists)")
+    import torch  # noqa: F401  -- load torch's HIP runtime first so libmkv shares it
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "mkv_pool_bytes": (SZ, [ctypes.POINTER(PoolDesc)]),
+        "mkv_record_bytes": (SZ, [ctypes.POINTER(PoolDesc), I32]),
+        "mkv_pool_create": (I32, [ctypes.POINTER(PoolDesc), P, SZ, ctypes.POINTER(P)]),
+        "mkv_pool_destroy": (I32, [P]),
+        "mkv_seq_reset": (I32, [P, I32, P]),
+        "mkv_append": (I32, [P, I32, I32, P, P, P]),
+        "mkv_demote": (I32, [P, I32, P, I32, P]),
+        "mkv_decode": (I32, [P, P, I32, P, I32, F32, P, P, P]),
+        "mkv_seq_info": (I32, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "mkv_page_table": (I32, [P, I32, P, I32]),
+        "mkv_pool_stats": (I32, [P, ctypes.POINTER(Stats)]),
+        "mkv_debug_gather": (I32, [P, I32, I32, I32, P, P]),
+        "mkv_profile_enable": (I32, [P, I32]),
+        "mkv_profile_read": (I32, [P, ctypes.POINTER(Profile)]),
+        "mkv_status_string": (ctypes.c_char_p, [I32]),
+        "mkv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != OK:
+        lib = _load()
+        raise MkvError(status, f"{lib.mkv_status_string(status).decode()}: "
+                               f"{lib.mkv_last_error().decode()}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev_ptr(t, dtype=None, shape=None, name="tensor"):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32_array(values):
+    vals = [int(x) for x in values]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals), len(vals)
+
+
+# ----------------------------------------------------------------- functions
+def make_desc(*, num_kv_heads, head_dim, page_size, max_seqs, max_pages_per_seq, max_batch,
+              max_q_heads, fp8_pages, tq3_pages, placement_seed=0, max_chunks=0) -> PoolDesc:
+    return PoolDesc(num_kv_heads, head_dim, page_size, max_seqs, max_pages_per_seq, max_batch,
+                    max_q_heads, max_chunks, fp8_pages, tq3_pages, placement_seed)
+
+
+def pool_bytes(desc: PoolDesc) -> int:
+    return int(_load().mkv_pool_bytes(ctypes.byref(desc)))
+
+
+def record_bytes(desc: PoolDesc, fmt: int) -> int:
+    return int(_load().mkv_record_bytes(ctypes.byref(desc), fmt))
+
+
+def pool_create(desc: PoolDesc, device_mem=None):
+    """Create a pool.  device_mem: None (library allocates) or a torch uint8
+    device tensor of at least pool_bytes(desc) bytes that outlives the pool."""
+    lib = _load()
+    out = ctypes.c_void_p()
+    if device_mem is None:
+        _check(lib.mkv_pool_create(ctypes.byref(desc), None, 0, ctypes.byref(out)))
+    else:
+        ptr = _dev_ptr(device_mem, name="device_mem")
+        nbytes = device_mem.numel() * device_mem.element_size()
+        _check(lib.mkv_pool_create(ctypes.byref(desc), ptr, nbytes, ctypes.byref(out)))
+    return out
+
+
+def pool_destroy(pool) -> None:
+    _check(_load().mkv_pool_destroy(pool))
+
+
+def seq_reset(pool, seq: int, stream=None) -> None:
+    _check(_load().mkv_seq_reset(pool, seq, _stream(stream)))
+
+
+def append(pool, seq: int, k, v, stream=None) -> None:
+    """Append fp32 rows k, v [n][Hkv][d] (device) to sequence seq as FP8."""
+    import torch
+    n = k.shape[0]
+    _check(_load().mkv_append(pool, seq, n, _dev_ptr(k, torch.float32, name="k"),
+                              _dev_ptr(v, torch.float32, tuple(k.shape), name="v"),
+                              _stream(stream)))
+
+
+def demote(pool, seq: int, logical_pages, stream=None) -> None:
+    arr, n = _i32_array(logical_pages)
+    _check(_load().mkv_demote(pool, seq, arr, n, _stream(stream)))
+
+
+def decode(pool, seq_ids, q, softmax_scale: float, out, lse, stream=None) -> None:
+    """q: bf16 [B][Hq][d]; out: fp32 [B][Hq][d]; lse: fp32 [B][Hq] (all device)."""
+    import torch
+    ids, B = _i32_array(seq_ids)
+    if q.dim() != 3 or q.shape[0] != B:
+        raise ValueError("q must be [B][Hq][d] with B = len(seq_ids)")
+    Hq = q.shape[1]
+    _check(_load().mkv_decode(pool, ids, B, _dev_ptr(q, torch.bfloat16, name="q"), Hq,
+                              ctypes.c_float(softmax_scale),
+                              _dev_ptr(out, torch.float32, tuple(q.shape), name="out"),
+                              _dev_ptr(lse, torch.float32, tuple(q.shape[:2]), name="lse"),
+                              _stream(stream)))
+
+
+def seq_info(pool, seq: int):
+    n = ctypes.c_int32()
+    p = ctypes.c_int32()
+    _check(_load().mkv_seq_info(pool, seq, ctypes.byref(n), ctypes.byref(p)))
+    return n.value, p.value
+
+
+def page_table(pool, seq: int):
+    import numpy as np
+    _, n_pages = seq_info(pool, seq)
+    buf = np.zeros(max(1, n_pages), dtype=np.int32)
+    _check(_load().mkv_page_table(pool, seq, buf.ctypes.data_as(ctypes.c_void_p), buf.size))
+    return buf[:n_pages]
+
+
+def pool_stats(pool) -> dict:
+    st = Stats()
+    _check(_load().mkv_pool_stats(pool, ctypes.byref(st)))
+    return st.as_dict()
+
+
+def debug_gather(pool, seq: int, first: int, n: int, dst, stream=None) -> None:
+    """dst: uint8 device tensor of n * max(record bytes) bytes."""
+    _check(_load().mkv_debug_gather(pool, seq, first, n, _dev_ptr(dst, name="dst"),
+                                    _stream(stream)))
+
+
+def profile_enable(pool, on: bool) -> None:
+    _check(_load().mkv_profile_enable(pool, 1 if on else 0))
+
+
+def profile_read(pool) -> dict:
+    pr = Profile()
+    _check(_load().mkv_profile_read(pool, ctypes.byref(pr)))
+    return pr.as_dict()
+
+
+def status_string(status: int) -> str:
+    return _load().mkv_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _load().mkv_last_error().decode()

@@ -1,0 +1,175 @@
+// Kernels that write the cache: FP8 append, FP8 -> TQ3 demote, and the record
+// gather used to check placement and packing.
+//
+// Every floating-point step here decides a stored code, so this file is built
+// with -ffp-contract=off and relies on IEEE fp32 division and round-to-nearest-
+// even fp16 conversion; the results are bit-identical to the CPU definitions.
+#include <hip/hip_runtime.h>
+
+#include "mkv_device.hpp"
+
+namespace mkv {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ float block_max(float v, float* red) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Append: one block per (touched page, kv-head, K-or-V).
+// Minima-KV summary (brainszone.ai), "Ancoras em FP8, arquivo em TQ3": recent
+// pages are FP8.  Scale sigma = amax / 448 per page-head; when new rows raise
+// the running amax the earlier rows of the page are re-encoded from their
+// dequantised values, so a page filled in one call equals one-shot encoding.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float* __restrict__ k,
+                  const float* __restrict__ v) {
+  __shared__ float red[kThreads / 64];
+  const int per_page = pv.Hkv * 2;
+  const AppendPage ap = plan[blockIdx.x / per_page];
+  const int h = (blockIdx.x / 2) % pv.Hkv;
+  const int kv = blockIdx.x % 2;
+  const int d = pv.d;
+  const float* src = kv ? v : k;
+  uint8_t* page = pv.fp8 + int64_t(ap.phys) * pv.fp8_stride;
+  uint8_t* codes = page + fp8_codes_off(pv, h, kv);
+  float* scale_p = reinterpret_cast<float*>(page + fp8_scale_off(pv, h, kv));
+  float* amax_p = reinterpret_cast<float*>(page + fp8_amax_off(pv, h, kv));
+
+  const int n_new = ap.nrows * d;
+  float local = 0.0f;
+  for (int i = threadIdx.x; i < n_new; i += kThreads) {
+    const int r = i / d, j = i % d;
+    local = fmaxf(local, fabsf(src[(int64_t(ap.src_row + r) * pv.Hkv + h) * d + j]));
+  }
+  const float new_amax = block_max(local, red);
+  const float old_amax = ap.row0 > 0 ? *amax_p : 0.0f;
+  const float old_sigma = ap.row0 > 0 ? *scale_p : 1.0f;
+  const bool grown = new_amax > old_amax;
+  const float amax = grown ? new_amax : old_amax;
+  const float sigma = amax == 0.0f ? 1.0f : amax / 448.0f;
+  __syncthreads();  // everyone has read the old scale and amax
+
+  if (grown && ap.row0 > 0) {
+    for (int i = threadIdx.x; i < ap.row0 * d; i += kThreads) {
+      const float x = e4m3_to_f32(codes[i]) * old_sigma;
+      codes[i] = uint8_t(f32_to_e4m3(x / sigma));
+    }
+  }
+  for (int i = threadIdx.x; i < n_new; i += kThreads) {
+    const int r = i / d, j = i % d;
+    const float x = src[(int64_t(ap.src_row + r) * pv.Hkv + h) * d + j];
+    codes[int64_t(ap.row0) * d + i] = uint8_t(f32_to_e4m3(x / sigma));
+  }
+  if (threadIdx.x == 0) {
+    *scale_p = sigma;
+    *amax_p = amax;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Demote: one block per (page, kv-head); each thread encodes 32-element groups.
+// Minima-KV summary, "Ancoras em FP8, arquivo em TQ3": older non-anchor pages
+// are converted to packed TQ3.  x = fp32(e4m3(c) * sigma); s = fp16(fp32(a/3.5))
+// clamped to 65504; c = #{b in -3..3 : x >= b*s} (4 when s == 0); the 32 codes
+// form a 96-bit little-endian stream, code j at bit 3j.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+demote_tq3_kernel(PoolView pv, const DemotePage* __restrict__ plan) {
+  const DemotePage dp = plan[blockIdx.x / pv.Hkv];
+  const int h = blockIdx.x % pv.Hkv;
+  const int d = pv.d, ng = d / 32, row_bytes = 3 * d / 8;
+  const uint8_t* src = pv.fp8 + int64_t(dp.src_phys) * pv.fp8_stride;
+  uint8_t* dst = pv.tq3 + int64_t(dp.dst_phys) * pv.tq3_stride;
+  const int tasks = 2 * dp.ntok * ng;
+  for (int task = threadIdx.x; task < tasks; task += kThreads) {
+    const int kv = task / (dp.ntok * ng);
+    const int rem = task % (dp.ntok * ng);
+    const int t = rem / ng, g = rem % ng;
+    const float sigma = *reinterpret_cast<const float*>(src + fp8_scale_off(pv, h, kv));
+    const uint8_t* c8 = src + fp8_codes_off(pv, h, kv) + int64_t(t) * d + 32 * g;
+    float x[32];
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      x[j] = e4m3_to_f32(c8[j]) * sigma;
+      a = fmaxf(a, fabsf(x[j]));
+    }
+    const float q = fminf(a / 3.5f, 65504.0f);
+    const _Float16 s16 = _Float16(q);          // round to nearest even
+    const float s = float(s16);
+    uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      uint32_t c = 4u;
+      if (s != 0.0f) {
+        c = 0u;
+#pragma unroll
+        for (int b = -3; b <= 3; ++b) c += (x[j] >= float(b) * s) ? 1u : 0u;
+      }
+      const int bit = 3 * j;
+      w[bit >> 5] |= c << (bit & 31);
+      if ((bit & 31) > 29) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+    }
+    uint32_t* out = reinterpret_cast<uint32_t*>(dst + tq3_codes_off(pv, h, kv) +
+                                                int64_t(t) * row_bytes + 12 * g);
+    out[0] = w[0];
+    out[1] = w[1];
+    out[2] = w[2];
+    reinterpret_cast<uint16_t*>(dst + tq3_scale_off(pv, h, kv))[t * ng + g] =
+        __builtin_bit_cast(uint16_t, s16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gather: copy page records in logical order through the device page table.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+gather_kernel(PoolView pv, int32_t seq, int32_t first, uint8_t* __restrict__ dst, int64_t slot) {
+  const int32_t entry = pv.pt[int64_t(seq) * pv.pt_stride + first + blockIdx.x];
+  const uint8_t* src = page_address(pv, entry);
+  const int64_t rec = entry < 0 ? int64_t(pv.Hkv) * pv.P * pv.d * 7 / 8
+                                : 2ll * pv.Hkv * pv.P * pv.d + 16ll * pv.Hkv;
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+  uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + int64_t(blockIdx.x) * slot);
+  for (int64_t i = threadIdx.x; i < slot / 4; i += kThreads) d32[i] = i < rec / 4 ? s32[i] : 0u;
+}
+
+}  // namespace
+
+hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
+                         const float* k, const float* v, hipStream_t s) {
+  if (n_pages <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_fp8_kernel, dim3(unsigned(n_pages * pv.Hkv * 2)), dim3(kThreads), 0,
+                     s, pv, plan, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_pages,
+                         hipStream_t s) {
+  if (n_pages <= 0) return hipSuccess;
+  hipLaunchKernelGGL(demote_tq3_kernel, dim3(unsigned(n_pages * pv.Hkv)), dim3(kThreads), 0, s,
+                     pv, plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
+                         uint8_t* dst, int64_t slot_bytes, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3(unsigned(n)), dim3(kThreads), 0, s, pv, seq, first, dst,
+                     slot_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace mkv

@@ -1,0 +1,510 @@
+// C-ABI of libmkv (declared in include/mkv.h): argument validation, device
+// memory layout, stream-ordered metadata uploads and kernel launches.
+#include "mkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mkv_kernels.hpp"
+#include "mkv_meta.hpp"
+
+static_assert(MKV_OK == MKV_S_OK && MKV_EINVAL == MKV_S_EINVAL && MKV_ENOMEM == MKV_S_ENOMEM &&
+                  MKV_ESTATE == MKV_S_ESTATE && MKV_ERANGE == MKV_S_ERANGE &&
+                  MKV_EHIP == MKV_S_EHIP,
+              "status codes must agree");
+static_assert(sizeof(mkv::WorkItem) == 32 && sizeof(mkv::AppendPage) == 32 &&
+                  sizeof(mkv::DemotePage) == 32,
+              "device plan records are 32 bytes");
+
+namespace {
+
+thread_local std::string g_err;
+
+mkv_status set_err(mkv_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define MKV_HIP(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return set_err(MKV_EHIP, std::string(#call) + ": " + hipGetErrorString(e_));     \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+mkv::Desc to_desc(const mkv_pool_desc& d) {
+  return mkv::Desc{d.num_kv_heads, d.head_dim, d.page_size, d.max_seqs, d.max_pages_per_seq,
+                   d.max_batch,    d.max_q_heads, d.max_chunks, d.fp8_pages, d.tq3_pages,
+                   d.placement_seed};
+}
+
+// Device memory layout of a pool (offsets from the base of its block).
+struct Layout {
+  size_t fp8, tq3, pt, sched, sched_bytes, plan, plan_bytes, pm, pl, pacc, total;
+  size_t items_cap;  // work items that fit the schedule region
+  size_t pages_off;  // page-list offset inside the schedule region
+  size_t base_off;   // chunk_base offset inside the schedule region
+};
+
+Layout make_layout(const mkv::Desc& d, const mkv::Geom& g) {
+  Layout L{};
+  size_t o = 0;
+  L.fp8 = o;
+  o = align256(o + size_t(d.fp8_pages) * size_t(g.fp8_stride));
+  L.tq3 = o;
+  o = align256(o + size_t(d.tq3_pages) * size_t(g.tq3_stride));
+  L.pt = o;
+  o = align256(o + size_t(d.max_seqs) * size_t(d.max_pages_per_seq) * 4);
+  L.items_cap = size_t(g.max_chunks);
+  L.pages_off = align256(L.items_cap * sizeof(mkv::WorkItem));
+  L.base_off = align256(L.pages_off + size_t(d.max_batch) * size_t(d.max_pages_per_seq) * 4);
+  L.sched_bytes = align256(L.base_off + (size_t(d.max_batch) + 1) * 4);
+  L.sched = o;
+  o += L.sched_bytes;
+  L.plan_bytes = align256(size_t(d.max_pages_per_seq) * 32);
+  L.plan = o;
+  o += L.plan_bytes;
+  const size_t slots = size_t(g.max_chunks) * size_t(d.max_q_heads);
+  L.pm = o;
+  o = align256(o + slots * 4);
+  L.pl = o;
+  o = align256(o + slots * 4);
+  L.pacc = o;
+  o = align256(o + slots * size_t(d.d) * 4);
+  L.total = o;
+  return L;
+}
+
+struct ProfEvent {
+  int kind;
+  hipEvent_t a, b;
+};
+
+// Keeps the caller's current device and switches to the pool's for the call.
+struct DeviceGuard {
+  int prev = -1;
+  bool switched = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev)
+      switched = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (switched) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct mkv_pool {
+  mkv::Meta meta;
+  mkv_pool_desc desc{};
+  Layout lay{};
+  int device = 0;
+  uint8_t* mem = nullptr;
+  bool owns_mem = false;
+  // pinned staging for host -> device metadata uploads
+  uint8_t* staging = nullptr;
+  size_t staging_bytes = 0;
+  hipEvent_t staging_ev = nullptr;
+  bool staging_pending = false;
+  // cached decode schedule
+  bool sched_valid = false;
+  uint64_t sched_version = 0;
+  int32_t sched_Hq = 0;
+  std::vector<int32_t> sched_ids;
+  mkv::Schedule sched;
+  // profiling
+  bool prof = false;
+  std::vector<ProfEvent> prof_events;
+  std::vector<ProfEvent> prof_free;
+  double prof_ms[3] = {0, 0, 0};
+  int64_t prof_n[3] = {0, 0, 0};
+
+  mkv::PoolView view() const {
+    const mkv::Geom& g = meta.geom();
+    return mkv::PoolView{mem + lay.fp8, mem + lay.tq3,
+                         reinterpret_cast<const int32_t*>(mem + lay.pt), g.fp8_stride,
+                         g.tq3_stride, g.Hkv, g.d, g.P, desc.max_pages_per_seq};
+  }
+
+  mkv_status wait_staging() {
+    if (staging_pending) {
+      MKV_HIP(hipEventSynchronize(staging_ev));
+      staging_pending = false;
+    }
+    return MKV_OK;
+  }
+};
+
+namespace {
+
+struct Upload {
+  size_t dst_off;  // offset in the pool's device block
+  size_t bytes;
+};
+
+// Copy the staged bytes (laid out back to back) to their device offsets.
+mkv_status flush_uploads(mkv_pool* p, const std::vector<Upload>& ups, hipStream_t s) {
+  size_t src = 0;
+  for (const Upload& u : ups) {
+    if (u.bytes)
+      MKV_HIP(hipMemcpyAsync(p->mem + u.dst_off, p->staging + src, u.bytes,
+                             hipMemcpyHostToDevice, s));
+    src += u.bytes;
+  }
+  MKV_HIP(hipEventRecord(p->staging_ev, s));
+  p->staging_pending = true;
+  return MKV_OK;
+}
+
+mkv_status upload_pt_row_and_plan(mkv_pool* p, int32_t seq, const void* plan, size_t plan_bytes,
+                                  hipStream_t s) {
+  mkv_status st = p->wait_staging();
+  if (st) return st;
+  const std::vector<int32_t>& pt = p->meta.seq(seq).pt;
+  const size_t pt_bytes = pt.size() * 4;
+  std::memcpy(p->staging, plan, plan_bytes);
+  if (pt_bytes) std::memcpy(p->staging + plan_bytes, pt.data(), pt_bytes);
+  std::vector<Upload> ups{{p->lay.plan, plan_bytes},
+                          {p->lay.pt + size_t(seq) * size_t(p->desc.max_pages_per_seq) * 4,
+                           pt_bytes}};
+  return flush_uploads(p, ups, s);
+}
+
+ProfEvent* prof_begin(mkv_pool* p, int kind, hipStream_t s) {
+  if (!p->prof) return nullptr;
+  ProfEvent e{kind, nullptr, nullptr};
+  if (!p->prof_free.empty()) {
+    e = p->prof_free.back();
+    p->prof_free.pop_back();
+    e.kind = kind;
+  } else if (hipEventCreate(&e.a) != hipSuccess || hipEventCreate(&e.b) != hipSuccess) {
+    return nullptr;
+  }
+  if (hipEventRecord(e.a, s) != hipSuccess) return nullptr;
+  p->prof_events.push_back(e);
+  return &p->prof_events.back();
+}
+
+void prof_end(mkv_pool* p, ProfEvent* e, hipStream_t s) {
+  if (e) (void)hipEventRecord(e->b, s);
+}
+
+mkv_status prof_collect(mkv_pool* p) {
+  for (ProfEvent& e : p->prof_events) {
+    MKV_HIP(hipEventSynchronize(e.b));
+    float ms = 0.0f;
+    MKV_HIP(hipEventElapsedTime(&ms, e.a, e.b));
+    p->prof_ms[e.kind] += ms;
+    p->prof_n[e.kind] += 1;
+    p->prof_free.push_back(e);
+  }
+  p->prof_events.clear();
+  return MKV_OK;
+}
+
+mkv::SchedPolicy policy_from_env() {
+  mkv::SchedPolicy pol;
+  if (const char* e = std::getenv("MKV_CHUNK_PAGES")) pol.chunk_pages = std::max(1, std::atoi(e));
+  if (const char* e = std::getenv("MKV_MIN_ITEMS")) pol.min_items = std::max(1, std::atoi(e));
+  return pol;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mkv_pool_bytes(const mkv_pool_desc* desc) {
+  if (!desc) return 0;
+  mkv::Geom g;
+  if (mkv::validate_desc(to_desc(*desc), &g, nullptr) != MKV_S_OK) return 0;
+  return make_layout(to_desc(*desc), g).total;
+}
+
+size_t mkv_record_bytes(const mkv_pool_desc* desc, int32_t fmt) {
+  if (!desc) return 0;
+  mkv::Geom g;
+  if (mkv::validate_desc(to_desc(*desc), &g, nullptr) != MKV_S_OK) return 0;
+  if (fmt == MKV_FMT_FP8) return size_t(g.fp8_rec);
+  if (fmt == MKV_FMT_TQ3) return size_t(g.tq3_rec);
+  return 0;
+}
+
+mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t bytes,
+                           mkv_pool** out) {
+  if (!desc || !out) return set_err(MKV_EINVAL, "null argument");
+  *out = nullptr;
+  mkv_pool* p = new (std::nothrow) mkv_pool();
+  if (!p) return set_err(MKV_ENOMEM, "host allocation failed");
+  std::string err;
+  int st = p->meta.init(to_desc(*desc), &err);
+  if (st != MKV_S_OK) {
+    delete p;
+    return set_err(mkv_status(st), err);
+  }
+  p->desc = *desc;
+  p->lay = make_layout(to_desc(*desc), p->meta.geom());
+  auto cleanup = [&](mkv_status s, const std::string& msg) {
+    if (p->staging) (void)hipHostFree(p->staging);
+    if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
+    if (p->owns_mem && p->mem) (void)hipFree(p->mem);
+    delete p;
+    return set_err(s, msg);
+  };
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
+  if (device_mem) {
+    if (bytes < p->lay.total) return cleanup(MKV_ERANGE, "device buffer smaller than mkv_pool_bytes");
+    if (reinterpret_cast<uintptr_t>(device_mem) % 256)
+      return cleanup(MKV_EINVAL, "device buffer must be 256-byte aligned");
+    p->mem = static_cast<uint8_t*>(device_mem);
+  } else {
+    void* m = nullptr;
+    e = hipMalloc(&m, p->lay.total);
+    if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("hipMalloc: ") + hipGetErrorString(e));
+    p->mem = static_cast<uint8_t*>(m);
+    p->owns_mem = true;
+  }
+  p->staging_bytes = std::max(p->lay.sched_bytes, p->lay.plan_bytes +
+                                                      size_t(desc->max_pages_per_seq) * 4);
+  void* h = nullptr;
+  e = hipHostMalloc(&h, p->staging_bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  p->staging = static_cast<uint8_t*>(h);
+  e = hipEventCreateWithFlags(&p->staging_ev, hipEventDisableTiming);
+  if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
+  *out = p;
+  return MKV_OK;
+}
+
+mkv_status mkv_pool_destroy(mkv_pool* p) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  DeviceGuard guard(p->device);
+  hipError_t e = hipDeviceSynchronize();
+  for (ProfEvent& ev : p->prof_events) {
+    (void)hipEventDestroy(ev.a);
+    (void)hipEventDestroy(ev.b);
+  }
+  for (ProfEvent& ev : p->prof_free) {
+    (void)hipEventDestroy(ev.a);
+    (void)hipEventDestroy(ev.b);
+  }
+  if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
+  if (p->staging) (void)hipHostFree(p->staging);
+  if (p->owns_mem && p->mem) (void)hipFree(p->mem);
+  delete p;
+  if (e != hipSuccess) return set_err(MKV_EHIP, hipGetErrorString(e));
+  return MKV_OK;
+}
+
+mkv_status mkv_seq_reset(mkv_pool* p, int32_t seq, hipStream_t) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  std::string err;
+  int st = p->meta.reset(seq, &err);
+  if (st) return set_err(mkv_status(st), err);
+  return MKV_OK;
+}
+
+mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const float* v,
+                      hipStream_t s) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  if (n > 0 && (!k || !v)) return set_err(MKV_EINVAL, "null K or V");
+  DeviceGuard guard(p->device);
+  std::vector<mkv::AppendPage> plan;
+  std::string err;
+  int st = p->meta.append(seq, n, &plan, &err);
+  if (st) return set_err(mkv_status(st), err);
+  if (plan.empty()) return MKV_OK;
+  mkv_status r = upload_pt_row_and_plan(p, seq, plan.data(), plan.size() * sizeof(plan[0]), s);
+  if (r) return r;
+  MKV_HIP(mkv::launch_append(p->view(),
+                             reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan),
+                             int32_t(plan.size()), k, v, s));
+  return MKV_OK;
+}
+
+mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, hipStream_t s) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  DeviceGuard guard(p->device);
+  std::vector<mkv::DemotePage> plan;
+  std::string err;
+  int st = p->meta.demote(seq, lps, n, &plan, &err);
+  if (st) return set_err(mkv_status(st), err);
+  if (plan.empty()) return MKV_OK;
+  mkv_status r = upload_pt_row_and_plan(p, seq, plan.data(), plan.size() * sizeof(plan[0]), s);
+  if (r) return r;
+  MKV_HIP(mkv::launch_demote(p->view(),
+                             reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan),
+                             int32_t(plan.size()), s));
+  return MKV_OK;
+}
+
+mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void* q, int32_t Hq,
+                      float softmax_scale, float* out, float* lse, hipStream_t s) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  if (!q || !out || !lse || !seq_ids) return set_err(MKV_EINVAL, "null argument");
+  DeviceGuard guard(p->device);
+  const bool same = p->sched_valid && p->sched_version == p->meta.version() && p->sched_Hq == Hq &&
+                    int32_t(p->sched_ids.size()) == B &&
+                    std::memcmp(p->sched_ids.data(), seq_ids, size_t(B) * 4) == 0;
+  if (!same) {
+    std::string err;
+    mkv::Schedule sc;
+    int st = p->meta.build_schedule(seq_ids, B, Hq, policy_from_env(), &sc, &err);
+    if (st) return set_err(mkv_status(st), err);
+    mkv_status r = p->wait_staging();
+    if (r) return r;
+    const size_t n8 = sc.items[0].size(), n3 = sc.items[1].size();
+    uint8_t* st8 = p->staging;
+    std::memcpy(st8, sc.items[0].data(), n8 * 32);
+    std::memcpy(st8 + n8 * 32, sc.items[1].data(), n3 * 32);
+    const size_t items_bytes = (n8 + n3) * 32;
+    std::memcpy(st8 + items_bytes, sc.pages.data(), sc.pages.size() * 4);
+    std::memcpy(st8 + items_bytes + sc.pages.size() * 4, sc.chunk_base.data(),
+                sc.chunk_base.size() * 4);
+    std::vector<Upload> ups{{p->lay.sched, items_bytes},
+                            {p->lay.sched + p->lay.pages_off, sc.pages.size() * 4},
+                            {p->lay.sched + p->lay.base_off, sc.chunk_base.size() * 4}};
+    p->sched_valid = false;
+    r = flush_uploads(p, ups, s);
+    if (r) return r;
+    p->sched = std::move(sc);
+    p->sched_ids.assign(seq_ids, seq_ids + B);
+    p->sched_Hq = Hq;
+    p->sched_version = p->meta.version();
+    p->sched_valid = true;
+  }
+  const mkv::Schedule& sc = p->sched;
+  const mkv::WorkItem* items = reinterpret_cast<const mkv::WorkItem*>(p->mem + p->lay.sched);
+  mkv::DecodeArgs a{};
+  a.pv = p->view();
+  a.pages = reinterpret_cast<const int32_t*>(p->mem + p->lay.sched + p->lay.pages_off);
+  a.chunk_base = reinterpret_cast<const int32_t*>(p->mem + p->lay.sched + p->lay.base_off);
+  a.q = static_cast<const uint16_t*>(q);
+  a.B = B;
+  a.Hq = Hq;
+  a.scale = softmax_scale;
+  a.pm = reinterpret_cast<float*>(p->mem + p->lay.pm);
+  a.pl = reinterpret_cast<float*>(p->mem + p->lay.pl);
+  a.pacc = reinterpret_cast<float*>(p->mem + p->lay.pacc);
+  a.out = out;
+  a.lse = lse;
+  if (!sc.items[0].empty()) {
+    a.items = items;
+    a.n_items = int32_t(sc.items[0].size());
+    ProfEvent* e = prof_begin(p, 0, s);
+    MKV_HIP(mkv::launch_partial_fp8(a, s));
+    prof_end(p, e, s);
+  }
+  if (!sc.items[1].empty()) {
+    a.items = items + sc.items[0].size();
+    a.n_items = int32_t(sc.items[1].size());
+    ProfEvent* e = prof_begin(p, 1, s);
+    MKV_HIP(mkv::launch_partial_tq3(a, s));
+    prof_end(p, e, s);
+  }
+  ProfEvent* e = prof_begin(p, 2, s);
+  MKV_HIP(mkv::launch_merge(a, s));
+  prof_end(p, e, s);
+  return MKV_OK;
+}
+
+mkv_status mkv_seq_info(mkv_pool* p, int32_t seq, int32_t* len, int32_t* n_pages) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  if (seq < 0 || seq >= p->desc.max_seqs) return set_err(MKV_EINVAL, "sequence id out of range");
+  const mkv::Seq& q = p->meta.seq(seq);
+  if (len) *len = q.len;
+  if (n_pages) *n_pages = int32_t(q.pt.size());
+  return MKV_OK;
+}
+
+mkv_status mkv_page_table(mkv_pool* p, int32_t seq, int32_t* entries, int32_t cap) {
+  if (!p || !entries) return set_err(MKV_EINVAL, "null argument");
+  if (seq < 0 || seq >= p->desc.max_seqs) return set_err(MKV_EINVAL, "sequence id out of range");
+  const mkv::Seq& q = p->meta.seq(seq);
+  if (cap < int32_t(q.pt.size())) return set_err(MKV_ERANGE, "entries buffer too small");
+  std::memcpy(entries, q.pt.data(), q.pt.size() * 4);
+  return MKV_OK;
+}
+
+mkv_status mkv_pool_stats(mkv_pool* p, mkv_stats* o) {
+  if (!p || !o) return set_err(MKV_EINVAL, "null argument");
+  const mkv::Geom& g = p->meta.geom();
+  std::memset(o, 0, sizeof(*o));
+  o->live_tokens = p->meta.live_tokens();
+  o->fp8_pages_live = p->meta.live_pages(0);
+  o->tq3_pages_live = p->meta.live_pages(1);
+  o->fp8_pages_free = p->meta.fp8_free();
+  o->tq3_pages_free = p->meta.tq3_free();
+  int64_t kvb = 0;
+  for (int32_t sq = 0; sq < p->desc.max_seqs; ++sq) kvb += p->meta.seq_kv_bytes(sq);
+  o->kv_bytes = kvb;
+  if (o->live_tokens > 0) {
+    o->bytes_per_token = double(kvb) / double(o->live_tokens);
+    o->ratio_vs_bf16 = double(4ll * g.Hkv * g.d) / o->bytes_per_token;
+    o->ratio_vs_fp8 = double(2ll * g.Hkv * g.d) / o->bytes_per_token;
+  }
+  o->dense_shadow_bytes = 0;
+  o->dense_fallbacks = 0;
+  return MKV_OK;
+}
+
+mkv_status mkv_debug_gather(mkv_pool* p, int32_t seq, int32_t first, int32_t n, void* dst,
+                            hipStream_t s) {
+  if (!p || !dst) return set_err(MKV_EINVAL, "null argument");
+  if (seq < 0 || seq >= p->desc.max_seqs) return set_err(MKV_EINVAL, "sequence id out of range");
+  const mkv::Seq& q = p->meta.seq(seq);
+  if (first < 0 || n < 0 || int64_t(first) + n > int64_t(q.pt.size()))
+    return set_err(MKV_EINVAL, "page range outside the sequence");
+  DeviceGuard guard(p->device);
+  const mkv::Geom& g = p->meta.geom();
+  const int64_t slot = std::max(g.fp8_rec, g.tq3_rec);
+  MKV_HIP(mkv::launch_gather(p->view(), seq, first, n, static_cast<uint8_t*>(dst), slot, s));
+  return MKV_OK;
+}
+
+mkv_status mkv_profile_enable(mkv_pool* p, int32_t on) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  p->prof = on != 0;
+  return MKV_OK;
+}
+
+mkv_status mkv_profile_read(mkv_pool* p, mkv_profile* o) {
+  if (!p || !o) return set_err(MKV_EINVAL, "null argument");
+  DeviceGuard guard(p->device);
+  mkv_status r = prof_collect(p);
+  if (r) return r;
+  o->ms_partial_fp8 = p->prof_ms[0];
+  o->ms_partial_tq3 = p->prof_ms[1];
+  o->ms_merge = p->prof_ms[2];
+  o->n_partial_fp8 = p->prof_n[0];
+  o->n_partial_tq3 = p->prof_n[1];
+  o->n_merge = p->prof_n[2];
+  for (int i = 0; i < 3; ++i) {
+    p->prof_ms[i] = 0;
+    p->prof_n[i] = 0;
+  }
+  return MKV_OK;
+}
+
+const char* mkv_status_string(mkv_status s) {
+  switch (s) {
+    case MKV_OK: return "ok";
+    case MKV_EINVAL: return "invalid argument";
+    case MKV_ENOMEM: return "slab has too few free pages";
+    case MKV_ESTATE: return "operation not allowed in the sequence's state";
+    case MKV_ERANGE: return "capacity exceeded";
+    case MKV_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mkv_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mkv_meta.hpp"
+
+namespace mkv {
+
+// Device view of a pool: slab bases, page table and geometry.
+struct PoolView {
+  uint8_t* fp8;        // FP8 slab
+  uint8_t* tq3;        // TQ3 slab
+  const int32_t* pt;   // page table [max_seqs][pt_stride]
+  int64_t fp8_stride;  // bytes between FP8 records
+  int64_t tq3_stride;  // bytes between TQ3 records
+  int32_t Hkv, d, P, pt_stride;
+};
+
+struct DecodeArgs {
+  PoolView pv;
+  const WorkItem* items;    // work items of one format
+  int32_t n_items;
+  const int32_t* pages;     // logical page lists
+  const int32_t* chunk_base;// [B + 1]
+  const uint16_t* q;        // bf16 [B][Hq][d]
+  int32_t B, Hq;
+  float scale;              // softmax scale on <q, k>
+  float* pm;                // partial max      [chunks][Hq]
+  float* pl;                // partial denom    [chunks][Hq]
+  float* pacc;              // partial acc      [chunks][Hq][d]
+  float* out;               // [B][Hq][d]
+  float* lse;               // [B][Hq]
+};
+
+hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
+                         const float* k, const float* v, hipStream_t s);
+hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_pages,
+                         hipStream_t s);
+hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
+                         uint8_t* dst, int64_t slot_bytes, hipStream_t s);
+hipError_t launch_partial_fp8(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_partial_tq3(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace mkv

@@ -1,0 +1,255 @@
+// Host metadata of the mixed-format page pool (see mkv_meta.hpp).
+#include "mkv_meta.hpp"
+
+#include <algorithm>
+
+namespace mkv {
+
+namespace {
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// splitmix64: a small, well-mixed 64-bit generator for the placement shuffle.
+struct SplitMix64 {
+  uint64_t s;
+  uint64_t next() {
+    uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+};
+
+int fail(std::string* err, int code, const char* msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+}  // namespace
+
+int validate_desc(const Desc& d, Geom* g, std::string* err) {
+  if (d.Hkv < 1 || d.Hkv > 64) return fail(err, MKV_S_EINVAL, "num_kv_heads must be in 1..64");
+  if (d.d != 32 && d.d != 64 && d.d != 128 && d.d != 256)
+    return fail(err, MKV_S_EINVAL, "head_dim must be 32, 64, 128 or 256");
+  if (d.P < 16 || d.P > 256 || d.P % 16)
+    return fail(err, MKV_S_EINVAL, "page_size must be a multiple of 16 in 16..256");
+  if (d.max_seqs < 1 || d.max_pages_per_seq < 1 || d.max_batch < 1)
+    return fail(err, MKV_S_EINVAL, "max_seqs, max_pages_per_seq and max_batch must be >= 1");
+  if (int64_t(d.max_pages_per_seq) * d.P > int64_t(INT32_MAX))
+    return fail(err, MKV_S_EINVAL, "max_pages_per_seq * page_size overflows int32");
+  if (d.max_q_heads < d.Hkv || d.max_q_heads > 16 * d.Hkv)
+    return fail(err, MKV_S_EINVAL, "max_q_heads must be in Hkv..16*Hkv");
+  if (d.fp8_pages < 1 || d.fp8_pages > int64_t(kPtIndexMask) || d.tq3_pages < 0 ||
+      d.tq3_pages > int64_t(kPtIndexMask))
+    return fail(err, MKV_S_EINVAL, "slab page counts must be in 1..2^31-1 (FP8) and 0..2^31-1 (TQ3)");
+  if (d.max_chunks < 0) return fail(err, MKV_S_EINVAL, "max_chunks must be >= 0");
+  Geom r;
+  r.Hkv = d.Hkv;
+  r.d = d.d;
+  r.P = d.P;
+  r.fp8_rec = 2ll * d.Hkv * d.P * d.d + 16ll * d.Hkv;
+  r.tq3_rec = int64_t(d.Hkv) * d.P * d.d * 7 / 8;
+  r.fp8_stride = round_up(r.fp8_rec, kSlabAlign);
+  r.tq3_stride = round_up(r.tq3_rec, kSlabAlign);
+  r.max_chunks = d.max_chunks ? d.max_chunks : 4096 + 2 * d.max_batch;
+  if (r.max_chunks < 2 * d.max_batch)
+    return fail(err, MKV_S_EINVAL, "max_chunks must be at least 2 * max_batch");
+  if (g) *g = r;
+  return MKV_S_OK;
+}
+
+void FreeList::init(int64_t n, uint64_t seed) {
+  stack_.resize(size_t(n));
+  for (int64_t i = 0; i < n; ++i) stack_[size_t(i)] = int32_t(n - 1 - i);  // pop() yields 0, 1, ...
+  if (seed && n > 1) {
+    SplitMix64 rng{seed};
+    for (int64_t i = n - 1; i > 0; --i) {
+      int64_t j = int64_t(rng.next() % uint64_t(i + 1));
+      std::swap(stack_[size_t(i)], stack_[size_t(j)]);
+    }
+  }
+}
+
+int Meta::init(const Desc& d, std::string* err) {
+  int st = validate_desc(d, &g_, err);
+  if (st != MKV_S_OK) return st;
+  d_ = d;
+  free_[0].init(d.fp8_pages, d.placement_seed);
+  // A different stream of the same seed for the TQ3 slab.
+  free_[1].init(d.tq3_pages, d.placement_seed ? d.placement_seed ^ 0xA5A5A5A5DEADBEEFull : 0);
+  seqs_.assign(size_t(d.max_seqs), Seq{});
+  version_ = 1;
+  return MKV_S_OK;
+}
+
+int Meta::check_seq(int32_t s, std::string* err) const {
+  if (s < 0 || s >= d_.max_seqs) return fail(err, MKV_S_EINVAL, "sequence id out of range");
+  return MKV_S_OK;
+}
+
+int Meta::append(int32_t s, int32_t n, std::vector<AppendPage>* plan, std::string* err) {
+  plan->clear();
+  int st = check_seq(s, err);
+  if (st) return st;
+  if (n < 0) return fail(err, MKV_S_EINVAL, "token count must be >= 0");
+  if (n == 0) return MKV_S_OK;
+  Seq& q = seqs_[size_t(s)];
+  const int32_t P = g_.P;
+  if (q.len % P != 0 && pt_is_tq3(q.pt.back()))
+    return fail(err, MKV_S_ESTATE, "last page is TQ3 and partially filled; the sequence is frozen");
+  int64_t new_len = int64_t(q.len) + n;
+  int64_t need = (new_len + P - 1) / P;
+  if (need > d_.max_pages_per_seq)
+    return fail(err, MKV_S_ERANGE, "sequence would exceed max_pages_per_seq");
+  int64_t fresh = need - int64_t(q.pt.size());
+  if (fresh > free_[0].size()) return fail(err, MKV_S_ENOMEM, "FP8 slab has too few free pages");
+  // Commit.
+  for (int64_t i = 0; i < fresh; ++i) q.pt.push_back(pt_make(0, free_[0].pop()));
+  int32_t pos = q.len;
+  int32_t src = 0;
+  while (src < n) {
+    int32_t lp = pos / P;
+    int32_t row0 = pos % P;
+    int32_t take = std::min(P - row0, n - src);
+    plan->push_back(AppendPage{lp, pt_index(q.pt[size_t(lp)]), row0, take, src, 0, 0, 0});
+    pos += take;
+    src += take;
+  }
+  q.len = int32_t(new_len);
+  ++version_;
+  return MKV_S_OK;
+}
+
+int Meta::demote(int32_t s, const int32_t* lps, int32_t n, std::vector<DemotePage>* plan,
+                 std::string* err) {
+  plan->clear();
+  int st = check_seq(s, err);
+  if (st) return st;
+  if (n < 0 || (n > 0 && !lps)) return fail(err, MKV_S_EINVAL, "bad page list");
+  Seq& q = seqs_[size_t(s)];
+  std::vector<char> seen(q.pt.size(), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t lp = lps[i];
+    if (lp < 0 || size_t(lp) >= q.pt.size())
+      return fail(err, MKV_S_EINVAL, "logical page out of range");
+    if (seen[size_t(lp)]) return fail(err, MKV_S_EINVAL, "logical page listed twice");
+    seen[size_t(lp)] = 1;
+    if (pt_is_tq3(q.pt[size_t(lp)])) return fail(err, MKV_S_ESTATE, "page is already TQ3");
+  }
+  if (n > free_[1].size()) return fail(err, MKV_S_ENOMEM, "TQ3 slab has too few free pages");
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t lp = lps[i];
+    int32_t src = pt_index(q.pt[size_t(lp)]);
+    int32_t dst = free_[1].pop();
+    q.pt[size_t(lp)] = pt_make(1, dst);
+    free_[0].push(src);
+    plan->push_back(DemotePage{lp, src, dst, page_tokens(q.len, g_.P, lp), 0, 0, 0, 0});
+  }
+  if (n) ++version_;
+  return MKV_S_OK;
+}
+
+int Meta::reset(int32_t s, std::string* err) {
+  int st = check_seq(s, err);
+  if (st) return st;
+  Seq& q = seqs_[size_t(s)];
+  for (int32_t e : q.pt) free_[pt_is_tq3(e) ? 1 : 0].push(pt_index(e));
+  q.pt.clear();
+  q.len = 0;
+  ++version_;
+  return MKV_S_OK;
+}
+
+int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedPolicy& pol,
+                         Schedule* out, std::string* err) const {
+  if (B < 1 || !ids) return fail(err, MKV_S_EINVAL, "batch must hold at least one sequence");
+  if (B > d_.max_batch) return fail(err, MKV_S_ERANGE, "batch exceeds max_batch");
+  if (Hq < 1 || Hq % g_.Hkv) return fail(err, MKV_S_EINVAL, "Hq must be a positive multiple of Hkv");
+  if (Hq > d_.max_q_heads) return fail(err, MKV_S_ERANGE, "Hq exceeds max_q_heads");
+  if (Hq / g_.Hkv > 16) return fail(err, MKV_S_EINVAL, "Hq / Hkv must be at most 16");
+  for (int32_t b = 0; b < B; ++b) {
+    if (check_seq(ids[b], err)) return MKV_S_EINVAL;
+    if (seqs_[size_t(ids[b])].len == 0) return fail(err, MKV_S_EINVAL, "empty sequence in batch");
+  }
+  // Per-format counts of each sequence.
+  std::vector<int32_t> n8(size_t(B), 0), n3(size_t(B), 0);
+  int64_t total_pages = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t e : seqs_[size_t(ids[b])].pt) (pt_is_tq3(e) ? n3 : n8)[size_t(b)]++;
+    total_pages += int64_t(seqs_[size_t(ids[b])].pt.size());
+  }
+  auto count = [&](int64_t c) {
+    int64_t t = 0;
+    for (int32_t b = 0; b < B; ++b) t += (n8[size_t(b)] + c - 1) / c + (n3[size_t(b)] + c - 1) / c;
+    return t;
+  };
+  int64_t chunk = std::max(1, pol.chunk_pages);
+  while (chunk > pol.min_chunk_pages && count(chunk) * g_.Hkv < pol.min_items)
+    chunk = std::max<int64_t>(pol.min_chunk_pages, chunk / 2);
+  while (count(chunk) > g_.max_chunks) chunk *= 2;
+  out->items[0].clear();
+  out->items[1].clear();
+  out->pages.clear();
+  out->pages.reserve(size_t(total_pages));
+  out->chunk_base.assign(size_t(B) + 1, 0);
+  int32_t nc = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    out->chunk_base[size_t(b)] = nc;
+    const Seq& q = seqs_[size_t(ids[b])];
+    for (int fmt = 0; fmt < 2; ++fmt) {
+      int32_t in_chunk = 0;
+      bool open = false;
+      std::vector<WorkItem>& items = out->items[fmt];
+      for (int32_t lp = 0; lp < int32_t(q.pt.size()); ++lp) {
+        if (int(pt_is_tq3(q.pt[size_t(lp)])) != fmt) continue;
+        if (!open || in_chunk == chunk) {
+          items.push_back(WorkItem{b, ids[b], int32_t(out->pages.size()), 0, 0, nc++, fmt, 0});
+          open = true;
+          in_chunk = 0;
+        }
+        out->pages.push_back(lp);
+        items.back().npages++;
+        items.back().last_ntok = page_tokens(q.len, g_.P, lp);
+        ++in_chunk;
+      }
+    }
+  }
+  out->chunk_base[size_t(B)] = nc;
+  out->n_chunks = nc;
+  out->chunk_pages = int32_t(chunk);
+  return MKV_S_OK;
+}
+
+int64_t Meta::seq_kv_bytes(int32_t s) const {
+  const Seq& q = seqs_[size_t(s)];
+  int64_t t = 0;
+  for (int32_t lp = 0; lp < int32_t(q.pt.size()); ++lp) {
+    int64_t n = page_tokens(q.len, g_.P, lp);
+    if (pt_is_tq3(q.pt[size_t(lp)]))
+      t += n * g_.Hkv * g_.d * 7 / 8;
+    else
+      t += n * 2 * g_.Hkv * g_.d + 8ll * g_.Hkv;
+  }
+  return t;
+}
+
+int64_t Meta::kv_bytes(const int32_t* ids, int32_t B) const {
+  int64_t t = 0;
+  for (int32_t b = 0; b < B; ++b) t += seq_kv_bytes(ids[b]);
+  return t;
+}
+
+int64_t Meta::live_tokens() const {
+  int64_t t = 0;
+  for (const Seq& q : seqs_) t += q.len;
+  return t;
+}
+
+int64_t Meta::live_pages(int fmt) const {
+  int64_t t = 0;
+  for (const Seq& q : seqs_)
+    for (int32_t e : q.pt) t += (int(pt_is_tq3(e)) == fmt);
+  return t;
+}
+
+}  // namespace mkv

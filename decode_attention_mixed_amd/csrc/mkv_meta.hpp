@@ -1,0 +1,136 @@
+// Host-side metadata of a mixed-format page pool: geometry, slab free lists,
+// page tables, sequence lengths and the split-K decode schedule.
+//
+// Pure C++17 with no HIP dependency, so it is unit-tested on the CPU.  The
+// device mirrors (page table, schedule) are uploaded by the ABI layer.
+//
+// Page-table entries: bit 31 = format (0 FP8, 1 TQ3), bits 0..30 = physical
+// page index in that format's slab.  Every live page of a sequence keeps an
+// entry for as long as the sequence holds it (Minima-KV summary, brainszone.ai,
+// section "Ancoras em FP8, arquivo em TQ3": pages stay addressable; conversion
+// re-encodes a page, it never drops one).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "mkv_status.h"
+
+namespace mkv {
+
+constexpr int32_t kPtTq3Bit = int32_t(0x80000000u);
+constexpr int32_t kPtIndexMask = 0x7FFFFFFF;
+constexpr int kSlabAlign = 256;
+
+inline bool pt_is_tq3(int32_t e) { return e < 0; }
+inline int32_t pt_index(int32_t e) { return e & kPtIndexMask; }
+inline int32_t pt_make(int fmt, int32_t idx) { return fmt ? (idx | kPtTq3Bit) : idx; }
+
+struct Desc {  // mirror of mkv_pool_desc (kept free of the C header's HIP include)
+  int32_t Hkv, d, P, max_seqs, max_pages_per_seq, max_batch, max_q_heads, max_chunks;
+  int64_t fp8_pages, tq3_pages;
+  uint64_t placement_seed;
+};
+
+struct Geom {
+  int32_t Hkv = 0, d = 0, P = 0;
+  int64_t fp8_rec = 0, tq3_rec = 0;       // record bytes
+  int64_t fp8_stride = 0, tq3_stride = 0; // slab strides (records rounded up to 256 B)
+  int32_t max_chunks = 0;                 // resolved partial-state capacity
+};
+
+// Validates a descriptor and derives the geometry.  Returns MKV_OK or MKV_EINVAL.
+int validate_desc(const Desc& d, Geom* g, std::string* err);
+
+// Free list of physical page indices.  With seed 0 pages are handed out in
+// index order; otherwise the order is a seeded Fisher-Yates shuffle.
+class FreeList {
+ public:
+  void init(int64_t n, uint64_t seed);
+  int64_t size() const { return int64_t(stack_.size()); }
+  int32_t pop() { int32_t v = stack_.back(); stack_.pop_back(); return v; }
+  void push(int32_t v) { stack_.push_back(v); }
+ private:
+  std::vector<int32_t> stack_;
+};
+
+struct Seq {
+  int32_t len = 0;
+  std::vector<int32_t> pt;  // one entry per logical page
+};
+
+// One page an append touches: rows row0 .. row0+nrows-1 of page `phys`
+// receive source rows src_row .. src_row+nrows-1.
+struct AppendPage {
+  int32_t lp, phys, row0, nrows, src_row, pad0, pad1, pad2;
+};
+// One page a demote converts.
+struct DemotePage {
+  int32_t lp, src_phys, dst_phys, ntok, pad0, pad1, pad2, pad3;
+};
+
+// One unit of split-K work: `npages` logical pages of one format of one
+// sequence, listed at pages[list_off ..]; the last listed page holds
+// last_ntok valid tokens.  `chunk` is the partial-state slot.
+struct WorkItem {
+  int32_t b, seq, list_off, npages, last_ntok, chunk, fmt, pad;
+};
+
+struct SchedPolicy {
+  int32_t chunk_pages = 32;      // preferred pages per chunk
+  int32_t min_chunk_pages = 4;   // smallest chunk when shrinking for parallelism
+  int32_t min_items = 1024;      // shrink chunks until items * kv-heads reach this
+};
+
+struct Schedule {
+  std::vector<WorkItem> items[2];   // per format (FP8, TQ3)
+  std::vector<int32_t> pages;       // logical page ids referenced by the items
+  std::vector<int32_t> chunk_base;  // [B + 1] prefix sums of chunks per batch entry
+  int32_t n_chunks = 0;
+  int32_t chunk_pages = 0;
+};
+
+class Meta {
+ public:
+  int init(const Desc& d, std::string* err);
+
+  const Geom& geom() const { return g_; }
+  const Desc& desc() const { return d_; }
+  uint64_t version() const { return version_; }
+  const Seq& seq(int32_t s) const { return seqs_[size_t(s)]; }
+  int64_t fp8_free() const { return free_[0].size(); }
+  int64_t tq3_free() const { return free_[1].size(); }
+
+  // Each call validates everything first; on failure nothing changes.
+  int append(int32_t seq, int32_t n, std::vector<AppendPage>* plan, std::string* err);
+  int demote(int32_t seq, const int32_t* lps, int32_t n, std::vector<DemotePage>* plan,
+             std::string* err);
+  int reset(int32_t seq, std::string* err);
+
+  int build_schedule(const int32_t* seq_ids, int32_t B, int32_t Hq, const SchedPolicy& pol,
+                     Schedule* out, std::string* err) const;
+
+  // Algorithmic bytes a decode of the given sequences reads (codes, TQ3 group
+  // scales, FP8 page-head scales).
+  int64_t kv_bytes(const int32_t* seq_ids, int32_t B) const;
+  int64_t seq_kv_bytes(int32_t s) const;
+  int64_t live_tokens() const;
+  int64_t live_pages(int fmt) const;
+
+ private:
+  int check_seq(int32_t s, std::string* err) const;
+  Desc d_{};
+  Geom g_{};
+  FreeList free_[2];
+  std::vector<Seq> seqs_;
+  uint64_t version_ = 1;
+};
+
+// Number of tokens held by logical page lp of a sequence of length len.
+inline int32_t page_tokens(int32_t len, int32_t P, int32_t lp) {
+  int32_t rest = len - lp * P;
+  return rest < P ? rest : P;
+}
+
+}  // namespace mkv

@@ -1,0 +1,189 @@
+/*
+ * mkv.h — C-ABI of libmkv: decode attention run directly over a paged KV cache
+ * whose pages are held in mixed numeric formats (FP8 anchors, packed TQ3
+ * archive), for AMD Instinct MI355X (gfx950).
+ *
+ * What the library implements (Minima-KV summaries, brainszone.ai, pt and fr):
+ *  - "O que os autores propoem": the KV cache is a hierarchy of pages and each
+ *    page is stored in its own numeric format.
+ *  - "Ancoras em FP8, arquivo em TQ3": recent and anchor pages stay FP8, older
+ *    non-anchor pages are converted to packed TQ3, and every page of a live
+ *    request stays directly addressable.
+ *  - "Como os resultados parciais sao combinados": per-format kernels produce
+ *    partial attention states that a globally normalised online-softmax merge
+ *    combines, so decode runs on the heterogeneous cache with no dense
+ *    single-format copy.
+ *
+ * Formats (the pages name them but fix no layout; this library fixes):
+ *  - FP8 = OCP E4M3 with one fp32 scale per (page, kv-head, K or V):
+ *    sigma = amax / 448 (1.0 when amax == 0), codes rounded to nearest-even,
+ *    saturating at +-448.
+ *  - TQ3 = per 32-element group of head_dim an fp16 scale s = absmax / 3.5 and
+ *    32 three-bit codes c decoding to (c - 3.5) * s, packed as a little-endian
+ *    bit stream of 12 bytes (code j of a token row at stream bit 3j).
+ *  - Page records, with Hkv kv-heads, head dim d and P tokens per page:
+ *      FP8: codes [Hkv][2 (K,V)][P][d] u8 | scale [Hkv][2] f32 | amax [Hkv][2] f32
+ *      TQ3: per kv-head h a block of P*d*7/8 bytes:
+ *           K codes [P][3d/8] | V codes [P][3d/8] | K scale [P][d/32] f16 | V scale [P][d/32] f16
+ *  - Page-table entry: int32, bit 31 = format (0 FP8, 1 TQ3), bits 0..30 =
+ *    physical page index in that format's slab.
+ *
+ * Conventions shared by every call:
+ *  - All functions are extern "C"; no C++ exception crosses the boundary.
+ *  - Device pointers are plain HIP device addresses (e.g. from a torch tensor).
+ *    Host pointers are marked "host".
+ *  - Every device effect is enqueued on the caller's stream and the call
+ *    returns without waiting, except mkv_pool_create, mkv_pool_destroy and the
+ *    calls documented as synchronous.  All calls on one pool must be issued
+ *    from one host thread, on one stream (or the caller orders the streams).
+ *  - A call validates all of its arguments and capacity before it enqueues any
+ *    work or changes any metadata: a non-OK status leaves the pool unchanged.
+ *  - Errors: MKV_EINVAL bad argument, MKV_ENOMEM a slab has too few free
+ *    pages, MKV_ESTATE an operation the sequence's state forbids, MKV_ERANGE a
+ *    capacity of the pool descriptor is exceeded, MKV_EHIP a HIP runtime
+ *    error (text in mkv_last_error()).
+ */
+#ifndef MKV_H
+#define MKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MKV_OK = 0,
+  MKV_EINVAL = -1,
+  MKV_ENOMEM = -2,
+  MKV_ESTATE = -3,
+  MKV_ERANGE = -4,
+  MKV_EHIP = -5
+} mkv_status;
+
+enum { MKV_FMT_FP8 = 0, MKV_FMT_TQ3 = 1 };
+
+typedef struct mkv_pool mkv_pool; /* opaque; owned by the library */
+
+/* Pool geometry and capacities.  Limits: 1 <= num_kv_heads <= 64;
+ * head_dim in {32, 64, 128, 256}; page_size a multiple of 16, at most 256. */
+typedef struct {
+  int32_t num_kv_heads;      /* Hkv */
+  int32_t head_dim;          /* d */
+  int32_t page_size;         /* P tokens per page */
+  int32_t max_seqs;          /* sequence ids are 0 .. max_seqs-1 */
+  int32_t max_pages_per_seq; /* page-table row length */
+  int32_t max_batch;         /* largest B accepted by mkv_decode */
+  int32_t max_q_heads;       /* largest Hq accepted by mkv_decode */
+  int32_t max_chunks;        /* partial-state slots per decode; 0 = library default */
+  int64_t fp8_pages;         /* FP8 slab capacity in pages */
+  int64_t tq3_pages;         /* TQ3 slab capacity in pages */
+  uint64_t placement_seed;   /* 0: pages handed out in index order; else a seeded shuffle */
+} mkv_pool_desc;
+
+typedef struct {
+  int64_t live_tokens;
+  int64_t fp8_pages_live, tq3_pages_live;
+  int64_t fp8_pages_free, tq3_pages_free;
+  int64_t kv_bytes;            /* algorithmic bytes one decode of all live tokens reads:
+                                  codes + TQ3 group scales + FP8 page-head scales */
+  double bytes_per_token;      /* kv_bytes / live_tokens (one layer) */
+  double ratio_vs_bf16;        /* (2 * Hkv * d * 2 bytes) / bytes_per_token */
+  double ratio_vs_fp8;         /* (2 * Hkv * d * 1 byte) / bytes_per_token */
+  int64_t dense_shadow_bytes;  /* always 0: no dense single-format copy exists */
+  int64_t dense_fallbacks;     /* always 0: decode never leaves the mixed path */
+} mkv_stats;
+
+/* Per-kernel device time accumulated while profiling is on (milliseconds). */
+typedef struct {
+  double ms_partial_fp8, ms_partial_tq3, ms_merge;
+  int64_t n_partial_fp8, n_partial_tq3, n_merge;
+} mkv_profile;
+
+/* Device bytes a pool with this descriptor needs (slabs, page tables,
+ * schedule and partial-state workspace).  Returns 0 for an invalid descriptor. */
+size_t mkv_pool_bytes(const mkv_pool_desc* desc);
+
+/* Bytes of one page record of the given format (layout above); 0 if invalid. */
+size_t mkv_record_bytes(const mkv_pool_desc* desc, int32_t fmt);
+
+/* Create a pool on the current HIP device.  device_mem: NULL to let the
+ * library hipMalloc mkv_pool_bytes(desc) bytes (freed by mkv_pool_destroy), or
+ * a caller-owned device buffer of at least that many bytes that must outlive
+ * the pool.  Synchronous.  *out receives the pool on MKV_OK. */
+mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t bytes,
+                           mkv_pool** out);
+
+/* Destroy a pool: waits for the device, frees library-owned memory. */
+mkv_status mkv_pool_destroy(mkv_pool* pool);
+
+/* Free every page of sequence `seq` and set its length to 0 (host metadata
+ * immediately; freed pages are reused in stream order). */
+mkv_status mkv_seq_reset(mkv_pool* pool, int32_t seq, hipStream_t stream);
+
+/* Append n tokens to sequence `seq` as FP8 ("Ancoras em FP8": new pages start
+ * FP8).  k, v: device fp32 [n][Hkv][d], row-major, finite values.  New pages
+ * come from the FP8 free list.  The FP8 scale of a page-head is recomputed when
+ * new rows raise its running amax and the page's earlier rows are re-encoded
+ * against it, so a page filled by one call equals one-shot quantisation.
+ * MKV_ESTATE if the sequence's last page is TQ3 and partially filled;
+ * MKV_ENOMEM if the FP8 slab lacks pages; MKV_ERANGE past max_pages_per_seq. */
+mkv_status mkv_append(mkv_pool* pool, int32_t seq, int32_t n, const float* k, const float* v,
+                      hipStream_t stream);
+
+/* Convert the listed logical pages of `seq` from FP8 to packed TQ3
+ * ("Ancoras em FP8, arquivo em TQ3": older non-anchor pages are converted).
+ * logical_pages: host int32 [n], distinct, each an FP8 page of the sequence.
+ * Each page gets a TQ3 page, its page-table entry is rewritten and the FP8
+ * page returns to the free list.  Codes: x = fp32(e4m3(c) * sigma) per element,
+ * then per 32-group s = fp16(fp32(absmax / 3.5)) (clamped to 65504) and
+ * c = #{b in -3..3 : x >= b*s} (c = 4 when s == 0).  Demoting a partially
+ * filled last page is allowed; the sequence then accepts no more appends. */
+mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages, int32_t n,
+                      hipStream_t stream);
+
+/* Decode attention for one query token per sequence ("Como os resultados
+ * parciais sao combinados").  seq_ids: host int32 [B] of non-empty sequences.
+ * q: device bf16 [B][Hq][d]; query head h reads kv-head h / (Hq / Hkv).
+ * softmax_scale: fp32 factor on <q, k>.  out: device fp32 [B][Hq][d];
+ * lse: device fp32 [B][Hq], natural-log log-sum-exp of the scaled scores.
+ * Per-format partial kernels run over split-K page chunks of each sequence
+ * and a merge kernel combines their (max, denominator, unnormalised
+ * accumulator) states.  The split-K schedule is rebuilt only when page
+ * metadata, the batch or Hq changed since the previous decode.
+ * MKV_EINVAL for an empty sequence, Hq not a multiple of Hkv, or Hq / Hkv > 16;
+ * MKV_ERANGE for B > max_batch or Hq > max_q_heads. */
+mkv_status mkv_decode(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const void* q,
+                      int32_t Hq, float softmax_scale, float* out, float* lse,
+                      hipStream_t stream);
+
+/* Introspection (host metadata; no device work). */
+mkv_status mkv_seq_info(mkv_pool* pool, int32_t seq, int32_t* len, int32_t* n_pages);
+/* entries: host int32 [cap] receives the sequence's page-table entries. */
+mkv_status mkv_page_table(mkv_pool* pool, int32_t seq, int32_t* entries, int32_t cap);
+mkv_status mkv_pool_stats(mkv_pool* pool, mkv_stats* out);
+
+/* Copy the records of logical pages first .. first+n-1 of `seq`, read through
+ * the device page table with the same address function the partial kernels
+ * use, into dst (device), one slot of max(record bytes) per page in logical
+ * order.  For checking placement and packing. */
+mkv_status mkv_debug_gather(mkv_pool* pool, int32_t seq, int32_t first, int32_t n, void* dst,
+                            hipStream_t stream);
+
+/* Profiling: when enabled, decode brackets each kernel with HIP events;
+ * mkv_profile_read waits for the device and returns the accumulated times
+ * (then clears them). */
+mkv_status mkv_profile_enable(mkv_pool* pool, int32_t on);
+mkv_status mkv_profile_read(mkv_pool* pool, mkv_profile* out);
+
+const char* mkv_status_string(mkv_status s);
+const char* mkv_last_error(void); /* thread-local detail of the last error */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MKV_H */

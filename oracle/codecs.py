@@ -73,24 +73,23 @@ def e4m3_decode(codes) -> np.ndarray:
 def e4m3_encode(x) -> np.ndarray:
     """Round fp32 values to E4M3 codes: nearest, ties to even code, saturating.
 
-    Written as a search over the 127 non-negative finite values of the format,
-    so it does not depend on any bit trick.  Inputs must be finite.
+    Standard rounding to a binary format with 4 significant bits: with
+    mag = min(|x|, 448) and e' = max(floor(log2 mag), -6) (the subnormal
+    exponent floor), the representable neighbours of mag are spaced by the
+    quantum 2^(e'-3), so the rounded magnitude is rint(mag / quantum) * quantum
+    (rint = round half to even; an even multiple is an even mantissa, i.e. an
+    even code).  Writing r = rint(mag * 2^(3-e')), the code is 8*(e'+6) + r:
+    r in 8..15 gives exponent field e'+7 and mantissa r-8, r = 16 carries into
+    the next exponent, and for e' = -6 the same formula gives the subnormal
+    codes r = 0..8.  All steps are exact in fp64.  Inputs must be finite.
     """
     x = np.asarray(x, dtype=np.float32)
-    mag = np.abs(x.astype(np.float64))
-    neg = np.signbit(x)
-    mag_c = np.minimum(mag, E4M3_MAX)
-    hi = np.searchsorted(_E4M3_POS, mag_c, side="left")     # first value >= mag
-    hi = np.clip(hi, 0, 0x7E)
-    lo = np.clip(hi - 1, 0, 0x7E)
-    v_hi = _E4M3_POS[hi]
-    v_lo = _E4M3_POS[lo]
-    d_hi = v_hi - mag_c
-    d_lo = mag_c - v_lo
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    pick_hi |= (hi == lo)
-    code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    return np.where(neg, code | 0x80, code).astype(np.uint8)
+    mag = np.minimum(np.abs(x).astype(np.float64), E4M3_MAX)
+    _, E = np.frexp(mag)                       # mag = f * 2^E, f in [0.5, 1)
+    e = np.where(mag > 0, np.maximum(E - 1, -6), -6)
+    r = np.rint(np.ldexp(mag, 3 - e))           # exact scaling, round half to even
+    code = (8 * (e + 6) + r).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------

@@ -86,21 +86,35 @@ class SeqModel:
             raise ValueError("tail page is TQ3 and partially filled")
         kv = np.stack([k, v])                    # [2][n][Hkv][d]
         pos = 0
-        while pos < n:
-            slot = self.length % self.P
-            if slot == 0:
-                self.pages.append(Page(
-                    FP8, 0,
-                    codes=np.zeros((2, self.Hkv, self.P, self.d), np.uint8),
-                    scale=np.ones((2, self.Hkv), np.float32),
-                    amax=np.zeros((2, self.Hkv), np.float32)))
+        slot = self.length % self.P
+        if slot:                                 # grow the partially filled tail page
             page = self.pages[-1]
-            take = min(self.P - slot, n - pos)
-            rows = kv[:, pos:pos + take]          # [2][take][Hkv][d]
-            self._fill(page, slot, rows)
+            take = min(self.P - slot, n)
+            self._fill(page, slot, kv[:, :take])
             page.ntok = slot + take
             self.length += take
-            pos += take
+            pos = take
+        if pos < n:                              # fresh pages: one-shot quantisation each
+            self._fill_fresh(kv[:, pos:])
+            self.length += n - pos
+
+    def _fill_fresh(self, rows) -> None:
+        """Quantise rows [2][m][Hkv][d] into new pages, page by page (vectorised)."""
+        P, Hkv, d = self.P, self.Hkv, self.d
+        m = rows.shape[1]
+        npg = -(-m // P)
+        pad = np.zeros((2, npg * P, Hkv, d), np.float32)
+        pad[:, :m] = rows
+        x = pad.reshape(2, npg, P, Hkv, d).transpose(1, 0, 3, 2, 4)   # [npg][2][Hkv][P][d]
+        valid = (np.arange(npg * P) < m).reshape(npg, 1, 1, P, 1)
+        amax = np.max(np.abs(x), axis=(3, 4)).astype(np.float32)     # padding rows are 0
+        sigma = np.where(amax == 0, np.float32(1.0), amax / np.float32(448.0)).astype(np.float32)
+        codes = C.e4m3_encode((x / sigma[..., None, None]).astype(np.float32))
+        codes = np.where(valid, codes, np.uint8(0)).astype(np.uint8)
+        for i in range(npg):
+            ntok = min(P, m - i * P)
+            self.pages.append(Page(FP8, ntok, codes=codes[i], scale=sigma[i].copy(),
+                                   amax=amax[i].copy()))
 
     def _fill(self, page: Page, slot: int, rows) -> None:
         new_amax = np.max(np.abs(rows), axis=(1, 3)).astype(np.float32)  # [2][Hkv]

@@ -1,0 +1,29 @@
+"""Oracle-side helpers for the parity tests: the CPU model of a workload's cache
+built from the same seeded inputs (same append splits, same demote list)."""
+import numpy as np
+
+from oracle import attention as A
+from oracle import pool_model as PM
+
+
+def seq_model(wl, b, splits=None, kv=None):
+    k, v = wl.kv(b) if kv is None else kv
+    seq = PM.SeqModel(wl.Hkv, wl.d, wl.P)
+    if splits is None:
+        seq.append(k, v)
+    else:
+        pos = 0
+        for n in splits:
+            seq.append(k[pos:pos + n], v[pos:pos + n])
+            pos += n
+    for lp in wl.demote_pages(b):
+        seq.demote(int(lp))
+    return seq
+
+
+def decode_all(wl, models):
+    O = np.zeros((wl.B, wl.Hq, wl.d))
+    lse = np.zeros((wl.B, wl.Hq))
+    for b in range(wl.B):
+        O[b], lse[b] = A.decode_seq(models[b], wl.q_bits[b], wl.tau)
+    return O, lse

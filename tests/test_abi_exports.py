@@ -1,0 +1,48 @@
+"""The C-ABI library loads on the CPU and exports every function include/mkv.h
+declares (no compute calls: there is no GPU here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_attention_mixed_amd as mkv
+
+
+def _declared(repo_root):
+    text = open(os.path.join(repo_root, "include", "mkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary(repo_root):
+    names = _declared(repo_root)
+    for core in ("mkv_pool_create", "mkv_append", "mkv_demote", "mkv_decode"):
+        assert core in names
+    assert names == sorted(mkv.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(repo_root):
+    if not os.path.exists(mkv.LIB_PATH):
+        pytest.fail("libmkv.so is not built; run python -m decode_attention_mixed_amd.build")
+    out = subprocess.run(["nm", "-D", "--defined-only", mkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(mkv_[a-z_0-9]+)$", out, flags=re.M))
+    missing = [n for n in _declared(repo_root) if n not in exported]
+    assert not missing, missing
+
+
+def test_library_loads_and_answers_host_only_queries():
+    lib = mkv._load()
+    assert isinstance(lib, ctypes.CDLL)
+    assert mkv.status_string(mkv.ESTATE).startswith("operation")
+    desc = mkv.make_desc(num_kv_heads=8, head_dim=128, page_size=16, max_seqs=1,
+                         max_pages_per_seq=8192, max_batch=1, max_q_heads=48,
+                         fp8_pages=8192, tq3_pages=8192)
+    assert mkv.record_bytes(desc, mkv.FMT_FP8) == 2 * 8 * 16 * 128 + 16 * 8
+    assert mkv.record_bytes(desc, mkv.FMT_TQ3) == 8 * 16 * 128 * 7 // 8
+    assert mkv.pool_bytes(desc) > 8192 * (32896 + 14336)
+    bad = mkv.make_desc(num_kv_heads=8, head_dim=100, page_size=16, max_seqs=1,
+                        max_pages_per_seq=8, max_batch=1, max_q_heads=8, fp8_pages=8, tq3_pages=8)
+    assert mkv.pool_bytes(bad) == 0

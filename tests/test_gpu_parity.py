@@ -1,0 +1,238 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C-ABI.
+
+* page records (placement through the page table, FP8 append, TQ3 demote) are
+  compared bit for bit with the oracle's records, on every valid byte;
+* decode outputs are compared element by element: max |dO| <= 1e-3 and
+  max |dLSE| <= 1e-4 (the acceptance bounds of this library).
+Pool memory is poisoned with 0x7F before use, so unwritten slots hold NaN
+patterns and any unmasked read shows up in the outputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_mixed_amd as mkv
+from decode_attention_mixed_amd import harness as H
+from decode_attention_mixed_amd import workloads as W
+from oracle import attention as A
+from tests import oracle_side as OS
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 1e-3
+LSE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _run_decode(pool, wl, seq_ids=None):
+    seq_ids = list(range(wl.B)) if seq_ids is None else seq_ids
+    q = H.q_tensor(wl)
+    out = torch.full((wl.B, wl.Hq, wl.d), float("nan"), device="cuda")
+    lse = torch.full((wl.B, wl.Hq), float("nan"), device="cuda")
+    mkv.decode(pool.handle, seq_ids, q, float(wl.tau), out, lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(out, lse, O, L, what):
+    assert np.isfinite(out).all() and np.isfinite(lse).all(), what
+    do = np.max(np.abs(out - O))
+    dl = np.max(np.abs(lse - L))
+    print(f"[{what}] max|dO|={do:.3e} max|dLSE|={dl:.3e}", flush=True)
+    assert do <= O_TOL, (what, do)
+    assert dl <= LSE_TOL, (what, dl)
+
+
+def _check_records(pool, wl, models, seq_ids=None):
+    seq_ids = list(range(wl.B)) if seq_ids is None else seq_ids
+    for b, sid in enumerate(seq_ids):
+        m = models[b]
+        n = len(m.pages)
+        recs = H.gather_records(pool, sid, n)
+        pt = mkv.page_table(pool.handle, sid)
+        anchors = set(int(x) for x in wl.anchors[b])
+        for lp in range(n):
+            want_tq3 = lp not in anchors
+            assert (pt[lp] < 0) == want_tq3, (b, lp)
+            ref = m.record(lp)
+            mask = m.valid_mask(lp)
+            got = recs[lp, :ref.size]
+            bad = np.nonzero((got != ref) & mask)[0]
+            assert bad.size == 0, f"seq {b} page {lp}: {bad.size} bytes differ, first at {bad[:8]}"
+
+
+SMALL_CASES = {
+    # name: kwargs of workloads.small
+    "d128_p16_g4": dict(seed=11, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(200, 37, 513)),
+    "d64_p32_g6": dict(seed=12, B=2, Hq=12, Hkv=2, d=64, P=32, lengths=(1, 650)),
+    "d32_p16_g1": dict(seed=13, B=2, Hq=4, Hkv=4, d=32, P=16, lengths=(97, 16)),
+    "d256_p64_g4": dict(seed=14, B=3, Hq=16, Hkv=4, d=256, P=64, lengths=(300, 64, 129),
+                        outliers={"k": (6, 20.0)}),
+    "d128_p16_g16": dict(seed=15, B=2, Hq=32, Hkv=2, d=128, P=16, lengths=(333, 48)),
+    "d128_all_fp8": dict(seed=16, B=2, Hq=8, Hkv=2, d=128, P=16, lengths=(300, 17), anchor_frac=1.0),
+    "d128_p48_outl": dict(seed=17, B=2, Hq=12, Hkv=2, d=128, P=48, lengths=(500, 95),
+                          outliers={"k": (3, 8.0), "v": (3, 8.0)}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_small_records_and_decode(name):
+    wl = W.small(**SMALL_CASES[name])
+    print(f"case {name}: lengths={list(wl.lengths)}", flush=True)
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    _check_records(pool, wl, models)
+    out, lse = _run_decode(pool, wl)
+    O, L = OS.decode_all(wl, models)
+    _check(out, lse, O, L, name)
+    st = mkv.pool_stats(pool.handle)
+    from oracle import pool_model as PM
+    assert st["kv_bytes"] == sum(PM.kv_bytes(m) for m in models)
+    assert st["dense_shadow_bytes"] == 0 and st["dense_fallbacks"] == 0
+    assert st["ratio_vs_bf16"] == pytest.approx(2 * st["ratio_vs_fp8"])
+    pool.close()
+
+
+def test_all_tq3_with_partial_tail_and_single_token():
+    wl = W.small(seed=21, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(77, 1, 16), anchor_frac=0.0)
+    wl.anchors = [np.zeros(0, np.int64) for _ in range(wl.B)]       # every page TQ3
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    _check_records(pool, wl, models)
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, *OS.decode_all(wl, models), "all_tq3")
+    with pytest.raises(mkv.MkvError) as e:                           # frozen partial TQ3 tail
+        mkv.append(pool.handle, 0, torch.zeros(1, 2, 128, device="cuda"),
+                   torch.zeros(1, 2, 128, device="cuda"))
+    assert e.value.status == mkv.ESTATE
+    pool.close()
+
+
+def test_append_in_pieces_rescales_bit_exactly():
+    wl = W.small(seed=31, B=2, Hq=8, Hkv=2, d=128, P=16, lengths=(150, 70))
+    splits = [[1, 5, 10, 3, 40, 1, 90], [16, 16, 7, 31]]
+    # make later rows raise the running amax so earlier rows get re-encoded
+    kvs = []
+    for b in range(wl.B):
+        k, v = wl.kv(b)
+        k[3::7] *= 3.0
+        v[5::11] *= 5.0
+        kvs.append((k, v))
+    pool = H.DevicePool(H.pool_desc(wl))
+    for b in range(wl.B):
+        H.load_sequence(pool, wl, b, splits=splits[b], kv=kvs[b])
+    models = [OS.seq_model(wl, b, splits=splits[b], kv=kvs[b]) for b in range(wl.B)]
+    _check_records(pool, wl, models)
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, *OS.decode_all(wl, models), "append_pieces")
+    pool.close()
+
+
+def test_schedule_is_rebuilt_after_metadata_changes():
+    wl = W.small(seed=41, B=2, Hq=8, Hkv=2, d=128, P=16, lengths=(64, 40))
+    pool = H.DevicePool(H.pool_desc(wl, max_seqs=3, fp8_pages=64, tq3_pages=64,
+                                    max_pages_per_seq=16))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, *OS.decode_all(wl, models), "before")
+    # grow sequence 1 and decode again: the cached schedule must be replaced
+    extra = np.random.default_rng(5).standard_normal((30, 2, 128)).astype(np.float32)
+    mkv.append(pool.handle, 1, torch.from_numpy(extra).cuda(), torch.from_numpy(extra).cuda())
+    models[1].append(extra, extra)
+    out, lse = _run_decode(pool, wl)
+    O = np.zeros((2, 8, 128))
+    L = np.zeros((2, 8))
+    for b in range(2):
+        O[b], L[b] = A.decode_seq(models[b], wl.q_bits[b], wl.tau)
+    _check(out, lse, O, L, "after_append")
+    # reordered batch and a repeated sequence
+    q = H.q_tensor(wl)
+    out2 = torch.zeros(2, 8, 128, device="cuda")
+    lse2 = torch.zeros(2, 8, device="cuda")
+    mkv.decode(pool.handle, [1, 1], q, float(wl.tau), out2, lse2)
+    torch.cuda.synchronize()
+    for b in range(2):
+        Ob, Lb = A.decode_seq(models[1], wl.q_bits[b], wl.tau)
+        assert np.max(np.abs(out2[b].cpu().numpy() - Ob)) <= O_TOL
+        assert np.max(np.abs(lse2[b].cpu().numpy() - Lb)) <= LSE_TOL
+    pool.close()
+
+
+def test_error_paths_through_the_abi():
+    wl = W.small(seed=51, B=1, Hq=8, Hkv=2, d=128, P=16, lengths=(40,))
+    pool = H.DevicePool(H.pool_desc(wl, max_seqs=2, fp8_pages=3, tq3_pages=2))
+    H.load_cache(pool, wl)
+    q = H.q_tensor(wl)
+    out = torch.zeros(1, 8, 128, device="cuda")
+    lse = torch.zeros(1, 8, device="cuda")
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.decode(pool.handle, [1], q, 0.1, out, lse)              # empty sequence
+    assert e.value.status == mkv.EINVAL
+    big = torch.zeros(100, 2, 128, device="cuda")
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.append(pool.handle, 1, big, big)                         # needs 7 pages, 1 free...
+    assert e.value.status in (mkv.ENOMEM, mkv.ERANGE)
+    assert mkv.seq_info(pool.handle, 1) == (0, 0)                    # no partial effect
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.demote(pool.handle, 0, [0])                              # page 0 is already TQ3
+    assert e.value.status == mkv.ESTATE
+    pool.close()
+
+
+NAMED = ["tiny", "ragged", "sweep0", "sweep10", "sweep50", "sweep100"]
+
+
+def _named(name):
+    if name.startswith("sweep"):
+        return W.sweep(int(name[5:]) / 100.0)
+    return getattr(W, name)()
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_named_workloads_full_parity(name):
+    wl = _named(name)
+    print(f"workload {name}: B={wl.B} lengths={list(wl.lengths)}", flush=True)
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    _check_records(pool, wl, models)
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, *OS.decode_all(wl, models), name)
+    pool.close()
+
+
+@pytest.fixture(scope="module")
+def long_case():
+    wl = W.long()
+    model = OS.seq_model(wl, 0)
+    O, L = A.decode_seq(model, wl.q_bits[0], wl.tau)
+    return wl, model, O, L
+
+
+def test_long_context_full_parity(long_case):
+    """131072-token, Hq=48/Hkv=8 cache, decoded in the launch configuration the
+    benchmark times (one sequence per call, default split-K schedule)."""
+    wl, model, O, L = long_case
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    recs = H.gather_records(pool, 0, len(model.pages))
+    for lp in (0, 1, 4000, 7935, 7936, 8191):       # TQ3 and FP8 pages, both ends
+        ref = model.record(lp)
+        assert np.array_equal(recs[lp, :ref.size][model.valid_mask(lp)], ref[model.valid_mask(lp)])
+    out, lse = _run_decode(pool, wl)
+    _check(out[0], lse[0], O, L, "long")
+    # repeated calls reuse the cached schedule and give identical results
+    out2, lse2 = _run_decode(pool, wl)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    pool.close()

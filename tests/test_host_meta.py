@@ -1,0 +1,279 @@
+"""CPU tests of the host metadata layer (pool geometry, free lists, page tables,
+split-K scheduler, error handling), through the CPU-only test library that is
+built from the same C++ source as libmkv.so."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from decode_attention_mixed_amd import PoolDesc, make_desc
+from decode_attention_mixed_amd import build as B
+
+OK, EINVAL, ENOMEM, ESTATE, ERANGE = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = B.build_host_test()
+    L = ctypes.CDLL(path)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.mkvh_create.argtypes = [ctypes.POINTER(PoolDesc), ctypes.POINTER(P)]
+    L.mkvh_destroy.argtypes = [P]
+    L.mkvh_append.argtypes = [P, I32, I32, P, I32, ctypes.POINTER(I32)]
+    L.mkvh_demote.argtypes = [P, I32, P, I32, P, I32, ctypes.POINTER(I32)]
+    L.mkvh_reset.argtypes = [P, I32]
+    L.mkvh_seq_len.argtypes = [P, I32]
+    L.mkvh_page_table.argtypes = [P, I32, P, I32]
+    L.mkvh_free.argtypes = [P, I32]
+    L.mkvh_free.restype = I64
+    L.mkvh_kv_bytes.argtypes = [P, P, I32]
+    L.mkvh_kv_bytes.restype = I64
+    L.mkvh_version.argtypes = [P]
+    L.mkvh_version.restype = ctypes.c_uint64
+    L.mkvh_schedule.argtypes = [P, P, I32, I32, I32, I32, P, I32, P, I32, P, P]
+    L.mkvh_last_error.restype = ctypes.c_char_p
+    return L
+
+
+class Host:
+    def __init__(self, lib, **kw):
+        self.L = lib
+        self.h = ctypes.c_void_p()
+        self.desc = make_desc(**kw)
+        st = lib.mkvh_create(ctypes.byref(self.desc), ctypes.byref(self.h))
+        if st:
+            raise ValueError(st)
+
+    def close(self):
+        self.L.mkvh_destroy(self.h)
+
+    def append(self, seq, n):
+        buf = np.zeros((4096, 8), np.int32)
+        cnt = ctypes.c_int32()
+        st = self.L.mkvh_append(self.h, seq, n, buf.ctypes.data, 4096, ctypes.byref(cnt))
+        return st, buf[:cnt.value]
+
+    def demote(self, seq, lps):
+        arr = np.asarray(lps, np.int32)
+        buf = np.zeros((4096, 8), np.int32)
+        cnt = ctypes.c_int32()
+        st = self.L.mkvh_demote(self.h, seq, arr.ctypes.data, arr.size, buf.ctypes.data, 4096,
+                                ctypes.byref(cnt))
+        return st, buf[:cnt.value]
+
+    def pt(self, seq):
+        buf = np.zeros(1 << 16, np.int32)
+        n = self.L.mkvh_page_table(self.h, seq, buf.ctypes.data, buf.size)
+        return buf[:n].copy()
+
+    def free(self, fmt):
+        return self.L.mkvh_free(self.h, fmt)
+
+    def schedule(self, ids, Hq, chunk_pages=0, min_items=0):
+        ids = np.asarray(ids, np.int32)
+        items = np.zeros((1 << 16, 8), np.int32)
+        pages = np.zeros(1 << 20, np.int32)
+        base = np.zeros(ids.size + 1, np.int32)
+        counts = np.zeros(5, np.int32)
+        st = self.L.mkvh_schedule(self.h, ids.ctypes.data, ids.size, Hq, chunk_pages, min_items,
+                                  items.ctypes.data, items.shape[0], pages.ctypes.data,
+                                  pages.size, base.ctypes.data, counts.ctypes.data)
+        if st:
+            return st, None
+        n8, n3, npg, nch, cp = counts
+        return st, dict(items=items[:n8 + n3].copy(), n8=int(n8), n3=int(n3),
+                        pages=pages[:npg].copy(), base=base.copy(), n_chunks=int(nch),
+                        chunk_pages=int(cp))
+
+
+def _host(lib, **over):
+    kw = dict(num_kv_heads=2, head_dim=128, page_size=16, max_seqs=4, max_pages_per_seq=64,
+              max_batch=4, max_q_heads=8, fp8_pages=32, tq3_pages=32, placement_seed=0)
+    kw.update(over)
+    return Host(lib, **kw)
+
+
+TQ3_BIT = -2**31
+
+
+def is_tq3(e):
+    return e < 0
+
+
+def test_descriptor_validation(lib):
+    for bad in (dict(head_dim=96), dict(page_size=8), dict(page_size=24), dict(num_kv_heads=0),
+                dict(max_q_heads=1, num_kv_heads=2), dict(max_q_heads=64, num_kv_heads=2),
+                dict(fp8_pages=0), dict(max_batch=0)):
+        with pytest.raises(ValueError):
+            _host(lib, **bad)
+
+
+def test_append_allocates_pages_in_order_without_seed(lib):
+    h = _host(lib)
+    st, plan = h.append(0, 40)
+    assert st == OK
+    # pages 0,1,2 touched: rows 0-15, 0-15, 0-7 from source rows 0, 16, 32
+    assert plan[:, :5].tolist() == [[0, 0, 0, 16, 0], [1, 1, 0, 16, 16], [2, 2, 0, 8, 32]]
+    st, plan = h.append(0, 10)
+    assert plan[:, :5].tolist() == [[2, 2, 8, 8, 0], [3, 3, 0, 2, 8]]
+    assert h.L.mkvh_seq_len(h.h, 0) == 50
+    assert h.pt(0).tolist() == [0, 1, 2, 3]
+    h.close()
+
+
+def test_placement_is_seeded_and_deterministic(lib):
+    a, b, c = (_host(lib, placement_seed=s, fp8_pages=64) for s in (7, 7, 8))
+    for x in (a, b, c):
+        x.append(0, 64 * 16)
+    assert a.pt(0).tolist() == b.pt(0).tolist()
+    assert a.pt(0).tolist() != c.pt(0).tolist()
+    assert sorted(a.pt(0).tolist()) == list(range(64))
+    assert a.pt(0).tolist() != list(range(64))
+    for x in (a, b, c):
+        x.close()
+
+
+def test_enomem_has_no_partial_effect(lib):
+    h = _host(lib, fp8_pages=4, tq3_pages=1)
+    assert h.append(0, 48)[0] == OK
+    v = h.L.mkvh_version(h.h)
+    st, _ = h.append(1, 33)             # needs 3 pages, 1 free
+    assert st == ENOMEM
+    assert h.free(0) == 1 and h.L.mkvh_seq_len(h.h, 1) == 0 and h.L.mkvh_version(h.h) == v
+    st, _ = h.demote(0, [0, 1])         # needs 2 TQ3 pages, 1 free
+    assert st == ENOMEM
+    assert (h.pt(0) >= 0).all() and h.free(1) == 1
+    h.close()
+
+
+def test_invalid_arguments_and_states(lib):
+    h = _host(lib)
+    assert h.append(5, 1)[0] == EINVAL
+    assert h.append(-1, 1)[0] == EINVAL
+    assert h.append(0, -3)[0] == EINVAL
+    assert h.append(0, 64 * 16 + 1)[0] == ERANGE
+    assert h.append(0, 20)[0] == OK
+    assert h.demote(0, [2])[0] == EINVAL      # out of range
+    assert h.demote(0, [0, 0])[0] == EINVAL   # duplicate
+    assert h.demote(0, [0])[0] == OK
+    assert h.demote(0, [0])[0] == ESTATE      # already TQ3
+    assert h.demote(0, [1])[0] == OK          # partial tail page: allowed
+    assert h.append(0, 1)[0] == ESTATE        # ... and then the sequence is frozen
+    assert h.schedule([1], 8)[0] == EINVAL    # empty sequence
+    assert h.schedule([0], 5)[0] == EINVAL    # Hq not a multiple of Hkv
+    assert h.schedule([0], 10)[0] == ERANGE   # Hq > max_q_heads
+    assert h.schedule([0, 0, 0, 0, 0], 8)[0] == ERANGE  # B > max_batch
+    h.close()
+
+
+def test_full_tq3_tail_accepts_appends(lib):
+    h = _host(lib)
+    assert h.append(0, 32)[0] == OK
+    assert h.demote(0, [1])[0] == OK
+    st, plan = h.append(0, 3)
+    assert st == OK and plan[:, :4].tolist() == [[2, plan[0, 1], 0, 3]]
+    h.close()
+
+
+def test_demote_rewrites_entries_and_recycles_fp8_pages(lib):
+    h = _host(lib, fp8_pages=8, tq3_pages=8, placement_seed=3)
+    h.append(0, 100)
+    before = h.pt(0)
+    st, plan = h.demote(0, [1, 6])
+    assert st == OK
+    after = h.pt(0)
+    assert is_tq3(after[1]) and is_tq3(after[6])
+    assert (after[1] & 0x7FFFFFFF) == plan[0, 2] and plan[0, 1] == before[1]
+    assert plan[0, 3] == 16 and plan[1, 3] == 100 - 6 * 16   # ntok of the partial last page
+    assert h.free(0) == 8 - 7 + 2 and h.free(1) == 6
+    h.L.mkvh_reset(h.h, 0)
+    assert h.free(0) == 8 and h.free(1) == 8 and h.pt(0).size == 0
+    h.close()
+
+
+def _check_coverage(h, ids, sched, P):
+    items = sched["items"]
+    seen = {}
+    chunks = set()
+    for it in items:
+        b, seq, off, npg, last, chunk, fmt, _ = it.tolist()
+        assert ids[b] == seq and npg >= 1
+        assert chunk not in chunks
+        chunks.add(chunk)
+        assert sched["base"][b] <= chunk < sched["base"][b + 1]
+        pt = h.pt(seq)
+        length = h.L.mkvh_seq_len(h.h, seq)
+        lps = sched["pages"][off:off + npg]
+        assert all(np.diff(lps) > 0)
+        for lp in lps:
+            assert int(is_tq3(pt[lp])) == fmt
+            key = (b, int(lp))
+            assert key not in seen
+            seen[key] = True
+        assert last == min(P, length - int(lps[-1]) * P)
+    for b, seq in enumerate(ids):
+        n_pages = h.pt(seq).size
+        assert all((b, lp) in seen for lp in range(n_pages))
+    assert chunks == set(range(sched["n_chunks"]))
+
+
+def test_schedule_covers_every_page_once_ragged_and_scattered(lib):
+    rng = np.random.default_rng(0)
+    h = _host(lib, num_kv_heads=8, max_seqs=8, max_pages_per_seq=600, max_batch=8,
+              max_q_heads=32, fp8_pages=4096, tq3_pages=4096, placement_seed=11)
+    ids = [0, 3, 5, 7]
+    for s in ids:
+        L = int(rng.integers(1, 9000))
+        assert h.append(s, L)[0] == OK
+        n = -(-L // 16)
+        dem = [p for p in range(n) if rng.random() < 0.8]
+        assert h.demote(s, dem)[0] == OK
+    for cp in (1, 3, 32, 1000):
+        st, sc = h.schedule(ids, 32, chunk_pages=cp, min_items=1)
+        assert st == OK
+        _check_coverage(h, ids, sc, 16)
+    h.close()
+
+
+def test_long_context_schedule_has_at_least_256_chunks(lib):
+    # 131072 tokens, last 4096 FP8: 8192 pages split into >= 256 chunks.
+    h = _host(lib, num_kv_heads=8, max_seqs=1, max_pages_per_seq=8192, max_batch=1,
+              max_q_heads=48, fp8_pages=8192, tq3_pages=8192, placement_seed=5)
+    assert h.append(0, 131072)[0] == OK
+    assert h.demote(0, list(range(8192 - 256)))[0] == OK
+    st, sc = h.schedule([0], 48)
+    assert st == OK
+    assert sc["n_chunks"] >= 256 and sc["n8"] >= 1 and sc["n3"] >= 1
+    _check_coverage(h, [0], sc, 16)
+    # algorithmic bytes: 126976 TQ3 tokens * 896 B + 4096 FP8 tokens * 2048 B + 256 pages * 64 B
+    ids = np.array([0], np.int32)
+    assert h.L.mkvh_kv_bytes(h.h, ids.ctypes.data, 1) == 122175488
+    h.close()
+
+
+def test_schedule_respects_chunk_capacity(lib):
+    h = _host(lib, max_pages_per_seq=512, fp8_pages=2048, tq3_pages=2048, max_chunks=8)
+    for s in range(4):
+        h.append(s, 512 * 16)
+    st, sc = h.schedule([0, 1, 2, 3], 8, chunk_pages=1, min_items=1)
+    assert st == OK and sc["n_chunks"] <= 8
+    _check_coverage(h, [0, 1, 2, 3], sc, 16)
+    h.close()
+
+
+def test_host_metadata_under_asan_ubsan(tmp_path, repo_root):
+    """Randomised append/demote/reset/schedule sequence in a sanitizer build."""
+    import shutil
+    if not shutil.which("g++"):
+        pytest.skip("no host compiler")
+    csrc = os.path.join(repo_root, "decode_attention_mixed_amd", "csrc")
+    exe = str(tmp_path / "meta_fuzz")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I", csrc, os.path.join(csrc, "mkv_meta.cpp"),
+           os.path.join(repo_root, "tests", "meta_fuzz.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "ok" in r.stdout
