@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "mixed FP8/TQ3 paged decode: µs/step and achieved KV HBM GB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["kernels_partial_ref.hip", "kernels_merge.hip", "mkv_device.hpp",
+KERNEL_SOURCES = ["kernels_partial.hip", "kernels_merge.hip", "mkv_device.hpp",
                   "mkv_kernels.hpp"]
 
 

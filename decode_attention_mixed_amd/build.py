@@ -35,7 +35,7 @@ LIB_SOURCES = [
     ("mkv_meta.cpp", []),
     ("mkv_api.cpp", []),
     ("kernels_quant.hip", ["-ffp-contract=off"]),
-    ("kernels_partial_ref.hip", []),
+    ("kernels_partial.hip", []),
     ("kernels_merge.hip", []),
 ]
 

@@ -3,10 +3,13 @@
 // Minima-KV summary (brainszone.ai), "Como os resultados parciais sao
 // combinados": the per-format partial states are combined by a globally
 // normalised online-softmax merge.  For query head h of sequence b with
-// partial states (m_i, l_i, acc_i):
-//   M = max_i m_i,  L = sum_i l_i exp(m_i - M),
-//   O = sum_i acc_i exp(m_i - M) / L,  LSE = M + ln L.
+// partial states (m_i, l_i, acc_i) in the base-2 domain:
+//   M = max_i m_i,  L = sum_i l_i 2^(m_i - M),
+//   O = sum_i acc_i 2^(m_i - M) / L,  LSE = (M + log2 L) * ln 2.
 // A chunk with l == 0 holds no token and is skipped.
+//
+// One block per (b, h, 32-dim slice); its threads take one chunk each (looping
+// when there are more chunks than threads) and the block reduces.
 #include <hip/hip_runtime.h>
 
 #include "mkv_device.hpp"
@@ -15,50 +18,82 @@ namespace mkv {
 
 namespace {
 
-constexpr int kMergeThreads = 64;
+constexpr int kMergeThreads = 256;
+constexpr int kSlice = 32;
 
-// One wave per (b, h); lanes split head_dim.  Partial maxima are in the
-// base-2 domain (see the partial kernels): scores there are s * log2(e).
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
-  const int b = blockIdx.x / a.Hq;
-  const int h = blockIdx.x % a.Hq;
-  const int lane = threadIdx.x;
-  const int c0 = a.chunk_base[b], c1 = a.chunk_base[b + 1];
+  __shared__ float red[kMergeThreads / 64][kSlice + 1];
+  __shared__ float redm[kMergeThreads / 64];
   const int d = a.pv.d;
+  const int nslices = d / kSlice;
+  const int bh = blockIdx.x / nslices;
+  const int slice = blockIdx.x % nslices;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int c0 = a.chunk_base[b], c1 = a.chunk_base[b + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // global reference maximum over the live chunks
   float M = -INFINITY;
-  for (int c = c0; c < c1; ++c) {
+  for (int c = c0 + threadIdx.x; c < c1; c += kMergeThreads) {
     const int64_t i = int64_t(c) * a.Hq + h;
     if (a.pl[i] > 0.0f) M = fmaxf(M, a.pm[i]);
   }
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) redm[wave] = M;
+  __syncthreads();
+  M = redm[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, redm[w]);
+
   float L = 0.0f;
-  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c = c0; c < c1; ++c) {
+  float o[kSlice];
+#pragma unroll
+  for (int j = 0; j < kSlice; ++j) o[j] = 0.0f;
+  for (int c = c0 + threadIdx.x; c < c1; c += kMergeThreads) {
     const int64_t i = int64_t(c) * a.Hq + h;
     const float l = a.pl[i];
     if (!(l > 0.0f)) continue;
     const float w = exp2f(a.pm[i] - M);
     L += l * w;
-    const float* acc = a.pacc + i * d;
+    const float4* src = reinterpret_cast<const float4*>(a.pacc + i * d + slice * kSlice);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = lane + 64 * u;
-      if (j < d) o[u] += acc[j] * w;
+    for (int j = 0; j < kSlice / 4; ++j) {
+      const float4 v = src[j];
+      o[4 * j] += v.x * w;
+      o[4 * j + 1] += v.y * w;
+      o[4 * j + 2] += v.z * w;
+      o[4 * j + 3] += v.w * w;
     }
   }
-  const float inv = 1.0f / L;
-  float* out = a.out + (int64_t(b) * a.Hq + h) * d;
+  // reduce over the block: within each wave by shuffles, then across waves
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = lane + 64 * u;
-    if (j < d) out[j] = o[u] * inv;
+  for (int j = 0; j < kSlice; ++j)
+    for (int off = 32; off > 0; off >>= 1) o[j] += __shfl_xor(o[j], off, 64);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < kSlice; ++j) red[wave][j] = o[j];
+    red[wave][kSlice] = L;
   }
-  if (lane == 0) a.lse[int64_t(b) * a.Hq + h] = (M + log2f(L)) * 0.69314718055994531f;
+  __syncthreads();
+  if (threadIdx.x < kSlice + 1) {
+    float t = 0.0f;
+    for (int w = 0; w < kMergeThreads / 64; ++w) t += red[w][threadIdx.x];
+    red[0][threadIdx.x] = t;
+  }
+  __syncthreads();
+  const float Ltot = red[0][kSlice];
+  if (threadIdx.x < kSlice)
+    a.out[(int64_t(b) * a.Hq + h) * d + slice * kSlice + threadIdx.x] = red[0][threadIdx.x] / Ltot;
+  if (threadIdx.x == 0 && slice == 0)
+    a.lse[int64_t(b) * a.Hq + h] = (M + log2f(Ltot)) * 0.69314718055994531f;
 }
 
 }  // namespace
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(a.B * a.Hq)), dim3(kMergeThreads), 0, s, a);
+  const int nslices = a.pv.d / kSlice;
+  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(a.B * a.Hq * nslices)), dim3(kMergeThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 
