@@ -68,11 +68,9 @@ class Stats(ctypes.Structure):
 
 class Profile(ctypes.Structure):
     _fields_ = [
-        ("ms_partial_fp8", ctypes.c_double),
-        ("ms_partial_tq3", ctypes.c_double),
+        ("ms_partial", ctypes.c_double),
         ("ms_merge", ctypes.c_double),
-        ("n_partial_fp8", ctypes.c_int64),
-        ("n_partial_tq3", ctypes.c_int64),
+        ("n_partial", ctypes.c_int64),
         ("n_merge", ctypes.c_int64),
     ]
 

@@ -35,7 +35,7 @@ LIB_SOURCES = [
     ("mkv_meta.cpp", []),
     ("mkv_api.cpp", []),
     ("kernels_quant.hip", ["-ffp-contract=off"]),
-    ("kernels_partial.hip", []),
+    ("kernels_partial.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("kernels_merge.hip", []),
 ]
 

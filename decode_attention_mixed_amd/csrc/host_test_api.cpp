@@ -76,11 +76,11 @@ uint64_t mkvh_version(mkvh* h) { return h->meta.version(); }
 // items_out: 8 int32 per item (b, seq, list_off, npages, last_ntok, chunk, fmt, 0), FP8 items
 // first.  counts_out: n_fp8_items, n_tq3_items, n_pages, n_chunks, chunk_pages.
 int mkvh_schedule(mkvh* h, const int32_t* ids, int32_t B, int32_t Hq, int32_t chunk_pages,
-                  int32_t min_items, int32_t* items_out, int32_t items_cap, int32_t* pages_out,
+                  int32_t target_waves, int32_t* items_out, int32_t items_cap, int32_t* pages_out,
                   int32_t pages_cap, int32_t* base_out, int32_t* counts_out) {
   mkv::SchedPolicy pol;
-  if (chunk_pages > 0) pol.chunk_pages = chunk_pages;
-  if (min_items > 0) pol.min_items = min_items;
+  pol.fixed_chunk_pages = chunk_pages > 0 ? chunk_pages : 0;
+  if (target_waves > 0) pol.target_waves = target_waves;
   mkv::Schedule sc;
   int st = h->meta.build_schedule(ids, B, Hq, pol, &sc, &g_herr);
   if (st) return st;

@@ -9,20 +9,23 @@
 //   s2 = t2 * <q, k>,  m = reference maximum,  l = sum 2^(s2 - m),
 //   acc = sum 2^(s2 - m) * v.
 //
-// Work decomposition.  One workgroup (4 wave64) per (work item = chunk of
-// pages of one format of one sequence, kv-head).  A page is cut into 16-token
-// tiles; wave w takes tiles w, w+4, ... and keeps its own state; the four
-// states are merged through LDS and one partial state per query head of the
-// kv-head is written.
+// Work decomposition.  One launch covers both formats: one workgroup (4
+// wave64) per (work item = chunk of at most 256 pages of one format of one
+// sequence, block of 4 kv-heads).  The workgroup first copies the chunk's
+// page-table entries to LDS; then each wave owns one kv-head and walks every
+// 16-token tile of the chunk on its own, with the raw bytes of the next R
+// tiles in flight (a ring of register buffers), and writes one partial state
+// per query head of its kv-head.
 //
-// Tile computation (16 tokens x one kv-head x up to 16 query heads):
-//  * QK^T on MFMA 16x16x32 f16 with A = key tile (tokens x 32 dims), B = the
-//    query heads (32 dims x 16 head columns): D[t][h].  TQ3 multiplies each
-//    32-dim group's D by its per-token fp16 scale before summing groups; FP8
-//    applies its per-page scale once.
-//  * Softmax: a reference maximum m per head column, raised (with headroom)
-//    only when a tile exceeds it, so exp2 arguments stay <= 0 and rescaling
-//    the accumulator is rare.
+// Tile computation (16 tokens x up to 16 query-head columns; column c is
+// query head hk*G + c of kv-head hk, columns c >= G are zero):
+//  * QK^T on MFMA 16x16x32 f16: A = the key tile (tokens x 32 dims), B = the
+//    query columns, D[t][c].  TQ3 scales each 32-dim group
+//    by its per-token fp16 scale before summing the groups; FP8 applies its
+//    per-page scale once.
+//  * Softmax: a reference maximum per column, raised (with headroom) only when
+//    a tile exceeds it, so exp2 arguments stay <= 0 and rescaling the
+//    accumulator is rare.
 //  * PV on MFMA 16x16x32 f16.  P' (probabilities times the value scale) is
 //    split into an f16 high part and an f16 low part (about 22 significant
 //    bits together); A holds both parts of the lane's 4 tokens, exactly in
@@ -38,7 +41,7 @@
 //    subtracted (one packed add): the operand is c * 2^(k-10), finite for any
 //    bit pattern, including unwritten poisoned slots.  The offset 3.5 is
 //    restored exactly: for keys through the MFMA accumulator input
-//    (-3.5 * sum q per group), for values through Z = sum_t P'[h][t],
+//    (-3.5 * sum q per group), for values through Z = sum_t P'[c][t],
 //    accumulated by an MFMA against ones.
 //  * FP8 E4M3 codes are widened by the hardware conversion to fp32 and packed
 //    to f16 (every E4M3 value is an f16 normal number).  Value rows past the
@@ -49,6 +52,8 @@
 //    the score scale.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "mkv_device.hpp"
 
 namespace mkv {
@@ -56,18 +61,38 @@ namespace mkv {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kWavesPerWorkgroup;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kHeadroom = 2.0f;   // log2 units added when the reference max is raised
 constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- small ALU helpers -------------------------------------------------------
+// (x & m) | b in one instruction; m lives in an SGPR and b in a VGPR (a VOP3
+// encoding on this architecture takes neither literals nor two scalars).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(b));
+  return r;
+}
+
+// A VGPR holding the f16 pair (1.0, 1.0), opaque to constant folding.
+__device__ __forceinline__ uint32_t vgpr_one_pair() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(r));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t minus_one(uint32_t biased) {
+  const half2v h = __builtin_bit_cast(half2v, biased) - half2v{_Float16(1.0f), _Float16(1.0f)};
+  return __builtin_bit_cast(uint32_t, h);
+}
 
 // ---- TQ3 unit unpack -------------------------------------------------------
 // A unit is 8 consecutive codes (24 bits, code i at bit 3i; bits 24..31 are
@@ -77,41 +102,41 @@ constexpr float kLog2e = 1.4426950408889634f;
 //   bit pos k:   0   7   3   4   0   4   3   7     (kSlotShift)
 // built from the unit rotated right by 18 and by 12 (the rotations put two
 // codes of each dword inside the two 10-bit mantissa fields).
-__device__ constexpr int kSlotCode[8] = {6, 3, 7, 2, 4, 0, 5, 1};
-__device__ constexpr int kSlotShift[8] = {0, 7, 3, 4, 0, 4, 3, 7};
-
-__device__ __forceinline__ uint32_t one_minus(uint32_t biased) {
-  const half2v h = __builtin_bit_cast(half2v, biased) - half2v{_Float16(1.0f), _Float16(1.0f)};
-  return __builtin_bit_cast(uint32_t, h);
+constexpr int kSlotCode[8] = {6, 3, 7, 2, 4, 0, 5, 1};
+constexpr int kSlotShift[8] = {0, 7, 3, 4, 0, 4, 3, 7};
+// The same tables as nibbles (entry s at bits 4s..4s+3) for run-time lookups.
+constexpr uint32_t pack_nibbles(const int (&v)[8]) {
+  uint32_t r = 0;
+  for (int i = 0; i < 8; ++i) r |= uint32_t(v[i]) << (4 * i);
+  return r;
 }
+constexpr uint32_t kSlotCodePacked = pack_nibbles(kSlotCode);
+constexpr uint32_t kSlotShiftPacked = pack_nibbles(kSlotShift);
+static_assert(kSlotCodePacked == 0x15042736u && kSlotShiftPacked == 0x73404370u, "slot tables");
 
-__device__ __forceinline__ u32x4 tq3_unit_to_f16(uint32_t x) {
+__device__ __forceinline__ u32x4 tq3_unit_to_f16(uint32_t x, uint32_t one) {
   const uint32_t r18 = __builtin_amdgcn_alignbit(x, x, 18);
   const uint32_t r12 = __builtin_amdgcn_alignbit(x, x, 12);
   u32x4 o;
-  o[0] = one_minus((r18 & 0x03800007u) | 0x3C003C00u);   // c6 -> bits 0..2,   c3 -> bits 23..25
-  o[1] = one_minus((r18 & 0x00700038u) | 0x3C003C00u);   // c7 -> bits 3..5,   c2 -> bits 20..22
-  o[2] = one_minus((r12 & 0x00700007u) | 0x3C003C00u);   // c4 -> bits 0..2,   c0 -> bits 20..22
-  o[3] = one_minus((r12 & 0x03800038u) | 0x3C003C00u);   // c5 -> bits 3..5,   c1 -> bits 23..25
+  o[0] = minus_one(and_or(r18, 0x03800007u, one));   // c6 -> bits 0..2,   c3 -> bits 23..25
+  o[1] = minus_one(and_or(r18, 0x00700038u, one));   // c7 -> bits 3..5,   c2 -> bits 20..22
+  o[2] = minus_one(and_or(r12, 0x00700007u, one));   // c4 -> bits 0..2,   c0 -> bits 20..22
+  o[3] = minus_one(and_or(r12, 0x03800038u, one));   // c5 -> bits 3..5,   c1 -> bits 23..25
   return o;
 }
 
 // The four 24-bit units of a 12-byte group held as three little-endian dwords.
-__device__ __forceinline__ void tq3_split_units(uint32_t d0, uint32_t d1, uint32_t d2,
-                                                uint32_t u[4]) {
-  u[0] = d0;
-  u[1] = __builtin_amdgcn_alignbit(d1, d0, 24);
-  u[2] = __builtin_amdgcn_alignbit(d2, d1, 16);
-  u[3] = d2 >> 8;
+__device__ __forceinline__ void tq3_split_units(const uint32_t d[3], uint32_t u[4]) {
+  u[0] = d[0];
+  u[1] = __builtin_amdgcn_alignbit(d[1], d[0], 24);
+  u[2] = __builtin_amdgcn_alignbit(d[2], d[1], 16);
+  u[3] = d[2] >> 8;
 }
 
 // ---- FP8 -> f16 -------------------------------------------------------------
-// Two fp32 values -> an f16 pair, rounded toward zero.
 __device__ __forceinline__ uint32_t pkrtz(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
-__device__ __forceinline__ float f16lo(uint32_t u) { return float(__builtin_bit_cast(half2v, u)[0]); }
-__device__ __forceinline__ float f16hi(uint32_t u) { return float(__builtin_bit_cast(half2v, u)[1]); }
 
 // Four E4M3 bytes -> two dwords of f16 pairs (exact: the hardware widening to
 // fp32 is exact and every finite E4M3 value is an f16 normal number).
@@ -124,30 +149,58 @@ __device__ __forceinline__ u32x2 fp8x4_to_f16(uint32_t w) {
   return o;
 }
 
-// P' of the lane's 4 tokens -> MFMA 16x16x32 A operand: slots 0..3 hold the
-// f16 high parts (round toward zero), slots 4..7 the f16 low parts of the
-// exact fp32 remainders.
-__device__ __forceinline__ half8 split_hi_lo(const float w[4]) {
-  const uint32_t h01 = pkrtz(w[0], w[1]);
-  const uint32_t h23 = pkrtz(w[2], w[3]);
-  const uint32_t l01 = pkrtz(w[0] - f16lo(h01), w[1] - f16hi(h01));
-  const uint32_t l23 = pkrtz(w[2] - f16lo(h23), w[3] - f16hi(h23));
-  const u32x4 u = {h01, h23, l01, l23};
-  return __builtin_bit_cast(half8, u);
+// ---- P' hi/lo ----------------------------------------------------------------
+// Given the lane's 4 probabilities p and the 4 fp16 value scales s (raw bits),
+// build the MFMA 16x16x32 A operand: slots 0..3 hold hi = f16(p*s), slots
+// 4..7 lo = f16(p*s - hi).  Each is one fused multiply-add of mixed precision
+// rounded once to f16, so hi + lo carries p*s to about 22 bits.
+__device__ __forceinline__ half8 pprime_hi_lo(const float p[4], const uint16_t s[4]) {
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sv = float(__builtin_bit_cast(_Float16, s[i]));
+    const _Float16 hi = _Float16(__builtin_fmaf(p[i], sv, 0.0f));
+    r[i] = hi;
+    r[4 + i] = _Float16(__builtin_fmaf(p[i], sv, -float(hi)));
+  }
+  return r;
 }
 
-// B operand for the hi/lo PV MFMA: the 4 value entries twice.
-__device__ __forceinline__ half8 dup4(short4v v) {
-  const u32x2 u = __builtin_bit_cast(u32x2, v);
-  const u32x4 d = {u[0], u[1], u[0], u[1]};
-  return __builtin_bit_cast(half8, d);
+// Same with one scale for all four tokens (FP8 page-head scale).
+__device__ __forceinline__ half8 pprime_hi_lo_uniform(const float p[4], float sv) {
+  half8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 hi = _Float16(p[i] * sv);
+    r[i] = hi;
+    r[4 + i] = _Float16(__builtin_fmaf(p[i], sv, -float(hi)));
+  }
+  return r;
 }
 
 __device__ __forceinline__ short4v read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
 }
 
+// B operand for the hi/lo PV MFMA: the lane's 4 value entries twice (read
+// twice from LDS so the operand lands in place without register copies).
+__device__ __forceinline__ half8 value_operand(const uint8_t* p) {
+  const u32x2 a = __builtin_bit_cast(u32x2, read_tr(p));
+  const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p));
+  const u32x4 d = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(half8, d);
+}
+
 // ---- cross-lane helpers -----------------------------------------------------
+// Orders one wave's LDS writes before its later LDS reads of other lanes' data.
+// The lanes of a wave issue LDS operations in program order, so no hardware
+// wait is needed; the fence only stops the compiler from moving accesses
+// across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Reduce over the four lanes {c, c+16, c+32, c+48} (same column, four quads).
 __device__ __forceinline__ float quad_max(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -164,111 +217,238 @@ __device__ __forceinline__ float quad_sum(float x) {
 
 // Power-of-two exponent E with max|q| * 2^E in [64, 128) (0 for a zero row).
 __device__ __forceinline__ int q_shift(float amax) {
-  return amax > 0.0f ? 6 - __builtin_amdgcn_frexp_expf(amax) + 1 : 0;
+  return amax > 0.0f ? 7 - __builtin_amdgcn_frexp_expf(amax) : 0;
 }
 
-// Number of 16-token tiles in work item `it` and the page/tile of tile i.
-struct TileRef {
-  int page, sub, nvalid;
+// ---- tiles -------------------------------------------------------------------
+// A work item's tiles are visited in order: tile (page, sub) covers tokens
+// 16*sub .. 16*sub+15 of the item's page `page` (pages hold P = 16 * tpp
+// tokens).  Cursors are wave-uniform and advance without division.
+struct Cursor {
+  int page = 0, sub = 0;
 };
-__device__ __forceinline__ int n_tiles(const WorkItem& it, int tpp) {
-  return (it.npages - 1) * tpp + (it.last_ntok + 15) / 16;
+struct TileGeom {
+  int tpp;        // tiles per page
+  int last_page;  // npages - 1
+  int last_sub;   // index of the last (possibly partial) tile of the last page
+  int last_ntok;  // valid tokens of the last page
+  int ntiles;
+};
+__device__ __forceinline__ TileGeom tile_geom(const WorkItem& it, int tpp) {
+  TileGeom g;
+  g.tpp = tpp;
+  g.last_page = it.npages - 1;
+  g.last_sub = (it.last_ntok + 15) / 16 - 1;
+  g.last_ntok = it.last_ntok;
+  g.ntiles = g.last_page * tpp + g.last_sub + 1;
+  return g;
 }
-__device__ __forceinline__ TileRef tile_ref(const WorkItem& it, int tpp, int i) {
-  TileRef r;
-  r.page = i / tpp;
-  r.sub = i % tpp;
-  const int ntok = (r.page == it.npages - 1) ? it.last_ntok : tpp * 16;
-  r.nvalid = min(16, ntok - 16 * r.sub);
-  return r;
+__device__ __forceinline__ void advance(Cursor& c, const TileGeom& g) {
+  if (++c.sub == g.tpp) {
+    c.sub = 0;
+    ++c.page;
+  }
+}
+// Prefetch cursor: stops on the last tile, so loads issued past the end
+// re-read it (every wave issues the same number of loads per tile, which
+// keeps the compiler's memory-counter waits exact).
+__device__ __forceinline__ void advance_clamped(Cursor& c, const TileGeom& g) {
+  if (c.page != g.last_page || c.sub != g.last_sub) advance(c, g);
+}
+__device__ __forceinline__ int valid_in_tile(const Cursor& c, const TileGeom& g) {
+  return c.page == g.last_page ? min(16, g.last_ntok - 16 * c.sub) : 16;
 }
 
-// Per-wave softmax state of the 16 head columns (lane (col, quad) holds the
-// state of column col for its 4 tokens of each tile).
+// Page-table entries of a work item's pages, staged once per workgroup.
+__device__ __forceinline__ void stage_entries(int32_t* ent, const DecodeArgs& a, const WorkItem& it) {
+  const int32_t* pt_row = a.pv.pt + int64_t(it.seq) * a.pv.pt_stride;
+  for (int p = threadIdx.x; p < it.npages; p += kThreads) ent[p] = pt_row[a.pages[it.list_off + p]];
+  __syncthreads();
+}
+__device__ __forceinline__ const uint8_t* entry_page(const PoolView& pv, const int32_t* ent, int page) {
+  return page_address(pv, __builtin_amdgcn_readfirstlane(ent[page]));
+}
+
+// Runs the tile pipeline: R raw buffers in flight; process(raw, cursor,
+// prefetch) consumes one tile and, if prefetch, refills raw from the load
+// cursor.  The steady-state loop issues the same loads on every path.
+template <int R, typename Raw, typename Load, typename Process>
+__device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Process process) {
+  Raw ring[R];
+  Cursor lc;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    load(lc, ring[k]);
+    advance_clamped(lc, g);
+  }
+  Cursor pc;
+  int ti = 0;
+  for (; ti + R <= g.ntiles; ti += R) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      process(ring[k], pc, [&](Raw& r) {
+        load(lc, r);
+        advance_clamped(lc, g);
+      });
+      advance(pc, g);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < R - 1; ++k) {
+    if (ti + k < g.ntiles) {
+      process(ring[k], pc, [](Raw&) {});
+      advance(pc, g);
+    }
+  }
+}
+
+// Per-wave softmax state of column col (lane (col, quad) holds the state of
+// column col for its 4 tokens of each tile).
 struct SoftState {
   float m = -INFINITY;   // reference max of column col (same in the 4 quads)
   float l = 0.0f;        // this lane's share of the denominator
 };
 
-// LDS image used after the tile loop to merge the four waves' states of the
-// 16 head columns before one partial state per query head is written.
-template <int D>
-struct MergeLds {
-  float m[kWaves][16];
-  float l[kWaves][16];
-  float acc[kWaves][16][D + 1];
+// Softmax step of one tile for the lane's column: scores s (fp32, already
+// multiplied by the column's score factor and masked) -> probabilities p;
+// rescales the accumulators when the reference max must rise.
+template <int NACC, int NZ>
+__device__ __forceinline__ void softmax_step(SoftState& st, float s[4], float p[4],
+                                             f32x4 (&acc)[NACC], f32x4 (&zacc)[NZ], float* corr_lds,
+                                             int col, int quad) {
+  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  tmax = quad_max(tmax);
+  if (__any(tmax > st.m)) {
+    const float m_new = tmax > st.m ? tmax + kHeadroom : st.m;
+    const float corr = exp2f(st.m - m_new);   // 0 on the first tile
+    st.m = m_new;
+    st.l *= corr;
+    if (quad == 0) corr_lds[col] = corr;
+    wave_lds_sync();
+    // accumulator rows are columns 4quad..4quad+3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float c = corr_lds[4 * quad + i];
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) acc[j][i] *= c;
+#pragma unroll
+      for (int g = 0; g < NZ; ++g) zacc[g][i] *= c;
+    }
+    wave_lds_sync();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(s[i] - st.m);
+    st.l += p[i];
+  }
+}
+
+// Query row of column col -> MFMA B operands.  For MFMA g the lane's 8
+// k-slots hold head dims base_dim(g) + perm(s), s = 0..7 (8 consecutive dims,
+// read as one 16-byte load); shift(s) is the slot's extra power-of-two
+// exponent.  Columns past the kv-head's G query heads are zero.  Returns the
+// column's exponent E.
+template <int NG, typename BaseDim, typename SlotPerm, typename SlotShift>
+__device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, int col, int G,
+                                          half8 (&qop)[NG], BaseDim base_dim, SlotPerm perm,
+                                          SlotShift shift) {
+  constexpr int D = 32 * NG;
+  const bool live = col < G;
+  const uint16_t* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (live ? col : 0)) * D;
+  float qv[NG][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + base_dim(g));
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int e = perm(s);
+      const float x = bf16_to_f32(uint16_t(w[e >> 1] >> (16 * (e & 1))));
+      qv[g][s] = live ? x : 0.0f;
+      amax = fmaxf(amax, fabsf(qv[g][s]));
+    }
+  }
+  amax = quad_max(amax);
+  const int E = q_shift(amax);
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qop[g][s] = _Float16(__builtin_amdgcn_ldexpf(qv[g][s], E + shift(s)));
+  return E;
+}
+
+// LDS images of the two work-item kinds (one of them per workgroup).
+template <int NG>
+struct Tq3Lds {
+  static constexpr int D = 32 * NG;
+  static constexpr int VROW = 2 * D + 16;       // value-tile row stride (bytes)
+  static constexpr int KST = 4 * NG;            // dwords per token in the key staging
+  static constexpr int SD = 16 * NG;            // scale dwords of a tile (K then V)
+  struct Wave {
+    alignas(16) uint32_t kst[16 * KST];         // key units, [token][unit][group]
+    alignas(16) uint8_t vt[16 * VROW];          // value tile, [token][D] f16
+    alignas(16) uint32_t sc[SD];                // tile scales: K [16][NG] f16, then V
+    float corr[16];
+  };
+  int32_t ent[kMaxChunkPages];                  // page-table entries of the work item
+  Wave w[kWaves];
+};
+
+template <int NG>
+struct Fp8Lds {
+  static constexpr int D = 32 * NG;
+  static constexpr int VROW = 2 * D + 16;
+  struct Wave {
+    alignas(16) uint8_t vt[16 * VROW];
+    float corr[16];
+  };
+  int32_t ent[kMaxChunkPages];
+  Wave w[kWaves];
 };
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// TQ3 partial kernel
+// TQ3 work item: one wave per kv-head
 // ---------------------------------------------------------------------------
-template <int NG>
-__global__ void __launch_bounds__(kThreads) partial_tq3_mfma(DecodeArgs a) {
+template <int NG, int R>
+__device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it, Tq3Lds<NG>& lds) {
   constexpr int D = 32 * NG;
   constexpr int GPL = NG > 4 ? NG / 4 : 1;      // groups each lane loads
   constexpr int NT = D / 16;                    // PV N-tiles
-  constexpr int VROW = 2 * D + 16;              // LDS value-tile row stride (bytes)
-  constexpr int KST = 4 * NG;                   // dwords per token in the key staging
-  struct WaveLds {
-    uint32_t kst[16 * KST];                     // key units, [token][unit][group]
-    uint8_t vt[16 * VROW];                      // value tile, [token][D] f16
-    float corr[16];
-  };
-  union Lds {
-    WaveLds w[kWaves];
-    MergeLds<D> mg;
-  };
-  __shared__ Lds lds;
+  constexpr int VROW = Tq3Lds<NG>::VROW;
+  constexpr int KST = Tq3Lds<NG>::KST;
+  constexpr int ROWB = 3 * D / 8;               // code bytes per token row
+  constexpr int SD = Tq3Lds<NG>::SD;
+  constexpr int SPL = (SD + 63) / 64;           // scale dwords each lane loads
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;                    // token (loads) / head column (outputs)
   const int quad = lane >> 4;
-  const WorkItem it = a.items[blockIdx.x];
-  const int hk = blockIdx.y;
   const PoolView& pv = a.pv;
+  stage_entries(lds.ent, a, it);
+  const int hk = blockIdx.y * kWaves + wave;
+  if (hk >= pv.Hkv) return;
   const int G = a.Hq / pv.Hkv;
-  const int tpp = pv.P / 16;
-  WaveLds& W = lds.w[wave];
+  const int hq0 = hk * G;
+  auto& W = lds.w[wave];
+  const uint32_t one = vgpr_one_pair();
 
-  // ---- query operand: column col = query head hk*G + col (zero if col >= G)
+  // ---- query operands and the key-offset bias
   half8 qop[NG];
-  float F;                                      // score multiplier of this column
-  {
-    const bool live = col < G;
-    const uint16_t* qrow = a.q + (int64_t(it.b) * a.Hq + int64_t(hk) * G + col) * D;
-    float qv[NG][8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (live) raw = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w = raw[i >> 1];
-        qv[g][i] = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
-        amax = fmaxf(amax, fabsf(qv[g][i]));
-      }
-    }
-    amax = quad_max(amax);
-    const int E = q_shift(amax);
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qop[g][s] = _Float16(__builtin_amdgcn_ldexpf(qv[g][kSlotCode[s]], E + 7 - kSlotShift[s]));
-    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
-  }
-  // bias_g = -3.5 * 2^(E-3) * sum_{j in g} q_j, from an MFMA against all-ones codes
   f32x4 bias[NG];
+  float F;
   {
-    const half8 ones = __builtin_bit_cast(half8, tq3_unit_to_f16(0x00249249u));
+    const int E = load_query<NG>(
+        a, it.b, hq0, col, G, qop, [&](int g) { return 32 * g + 8 * quad; },
+        [](int s) { return kSlotCode[s]; }, [](int s) { return 7 - kSlotShift[s]; });
+    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
+    const half8 ones = __builtin_bit_cast(half8, tq3_unit_to_f16(0x00249249u, one));
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, qop[g], z, 0, 0, 0);
+      const f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, qop[g], z, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) bias[g][i] = -3.5f * s[i];
     }
@@ -284,378 +464,343 @@ __global__ void __launch_bounds__(kThreads) partial_tq3_mfma(DecodeArgs a) {
   const half8 ones8 = {_Float16(1.0f), _Float16(1.0f), _Float16(1.0f), _Float16(1.0f),
                        _Float16(1.0f), _Float16(1.0f), _Float16(1.0f), _Float16(1.0f)};
 
-  const int ntiles = n_tiles(it, tpp);
-  const int32_t* pt_row = pv.pt + int64_t(it.seq) * pv.pt_stride;
-  const int64_t kc_off = tq3_codes_off(pv, hk, 0), vc_off = tq3_codes_off(pv, hk, 1);
-  const int64_t ks_off = tq3_scale_off(pv, hk, 0), vs_off = tq3_scale_off(pv, hk, 1);
-  constexpr int ROWB = 3 * D / 8;
+  // Per-lane byte offsets inside a record (the tile's first token is added per
+  // tile).  Lane (token col, quad) loads group quad (+4i) of that token; with
+  // fewer than 4 groups the spare quads repeat a real group's load, and spare
+  // lanes of the scale load repeat a real scale dword (results unused).
+  int32_t code_off[GPL], sc_off[SPL];
+  {
+    const int32_t cb = int32_t(tq3_codes_off(pv, hk, 0));
+    const int32_t kb = int32_t(tq3_scale_off(pv, hk, 0));
+    const int32_t vb = int32_t(tq3_scale_off(pv, hk, 1));
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) code_off[i] = cb + col * ROWB + 12 * ((quad + 4 * i) % NG);
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int e = (lane + 64 * i) & (SD - 1);
+      sc_off[i] = e < 8 * NG ? kb + 4 * e : vb + 4 * (e - 8 * NG);
+    }
+  }
+  const int32_t vcode_delta = pv.P * ROWB;      // V codes follow the K codes
 
-  for (int ti = wave; ti < ntiles; ti += kWaves) {
-    const TileRef tr = tile_ref(it, tpp, ti);
-    const uint8_t* page = page_address(pv, pt_row[a.pages[it.list_off + tr.page]]);
-    const int t0 = 16 * tr.sub;
-    // ---- loads: codes of group(s) quad(+4i) of token col; scales of tokens 4quad..+3
-    uint32_t kc[GPL][3], vc[GPL][3];
+  struct Raw {
+    uint32_t kc[GPL][3];                        // K codes: one 12-byte group of token col
+    uint32_t vc[GPL][3];                        // V codes, same group and token
+    uint32_t sc[SPL];                           // the lane's share of the tile's scales
+  };
+  auto load = [&](const Cursor& c, Raw& r) {
+    const uint8_t* page = entry_page(pv, lds.ent, c.page);
+    const int t0 = 16 * c.sub;
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
-      const int g = quad + 4 * i;
-      if (g < NG) {
-        const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + kc_off + (t0 + col) * ROWB + 12 * g);
-        const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + vc_off + (t0 + col) * ROWB + 12 * g);
-        kc[i][0] = kp[0]; kc[i][1] = kp[1]; kc[i][2] = kp[2];
-        vc[i][0] = vp[0]; vc[i][1] = vp[1]; vc[i][2] = vp[2];
-      }
-    }
-    // scales of tokens 4quad..4quad+3, all groups: 8*NG contiguous bytes
-    uint32_t skw[2 * NG], svw[2 * NG];
-    {
-      const uint32_t* ksp = reinterpret_cast<const uint32_t*>(page + ks_off + 2 * (t0 + 4 * quad) * NG);
-      const uint32_t* vsp = reinterpret_cast<const uint32_t*>(page + vs_off + 2 * (t0 + 4 * quad) * NG);
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off[i] + t0 * ROWB);
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + code_off[i] + t0 * ROWB + vcode_delta);
 #pragma unroll
-      for (int i = 0; i < 2 * NG; ++i) {
-        skw[i] = ksp[i];
-        svw[i] = vsp[i];
+      for (int x = 0; x < 3; ++x) {
+        r.kc[i][x] = kp[x];
+        r.vc[i][x] = vp[x];
       }
     }
-    auto scale_of = [](const uint32_t* w, int i, int g) {
-      const int e = i * NG + g;
-      return f16_bits_to_f32(uint16_t(w[e >> 1] >> (16 * (e & 1))));
-    };
-    // ---- keys: stage units as [token][unit][group], read back [token][quad][*]
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      r.sc[i] = *reinterpret_cast<const uint32_t*>(page + sc_off[i] + 2 * t0 * NG);
+  };
+  auto scale_of = [](const uint32_t* w, int i, int g) {
+    const int e = i * NG + g;
+    return float(__builtin_bit_cast(_Float16, uint16_t(w[e >> 1] >> (16 * (e & 1)))));
+  };
+  const TileGeom tg = tile_geom(it, pv.P / 16);
+
+  // Tile body: the raw buffer is consumed into LDS, refilled with a later
+  // tile, and the tile is computed from LDS.
+  auto process = [&](Raw& raw, const Cursor& c, auto refill) {
+    const int nvalid = valid_in_tile(c, tg);
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      if (lane + 64 * i < SD) W.sc[lane + 64 * i] = raw.sc[i];
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
       const int g = quad + 4 * i;
       if (g < NG) {
         uint32_t u[4];
-        tq3_split_units(kc[i][0], kc[i][1], kc[i][2], u);
+        tq3_split_units(raw.kc[i], u);
 #pragma unroll
         for (int un = 0; un < 4; ++un) W.kst[col * KST + un * NG + g] = u[un];
-      }
-    }
-    // ---- values: unpack to f16 rows of the LDS tile
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int g = quad + 4 * i;
-      if (g < NG) {
-        uint32_t u[4];
-        tq3_split_units(vc[i][0], vc[i][1], vc[i][2], u);
+        tq3_split_units(raw.vc[i], u);
 #pragma unroll
         for (int un = 0; un < 4; ++un)
-          *reinterpret_cast<u32x4*>(W.vt + col * VROW + 2 * (32 * g + 8 * un)) = tq3_unit_to_f16(u[un]);
+          *reinterpret_cast<u32x4*>(W.vt + col * VROW + 2 * (32 * g + 8 * un)) = tq3_unit_to_f16(u[un], one);
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    refill(raw);
+    wave_lds_sync();
+
+    // ---- scales of the lane's 4 tokens
+    uint32_t skw[2 * NG], svw[2 * NG];
+#pragma unroll
+    for (int x = 0; x < 2 * NG; ++x) {
+      skw[x] = W.sc[2 * quad * NG + x];
+      svw[x] = W.sc[8 * NG + 2 * quad * NG + x];
+    }
     // ---- QK^T per group, scaled by the per-token group scale
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const uint32_t unit = W.kst[col * KST + quad * NG + g];
-      const half8 kop = __builtin_bit_cast(half8, tq3_unit_to_f16(unit));
+      const half8 kop = __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[col * KST + quad * NG + g], one));
       const f32x4 dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[g], bias[g], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] += dg[i] * scale_of(skw, i, g);
+      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dg[i], scale_of(skw, i, g), s[i]);
     }
-    // ---- softmax bookkeeping (column col, tokens 4quad..4quad+3)
-    float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = (4 * quad + i < tr.nvalid) ? s[i] * F : -INFINITY;
-      tmax = fmaxf(tmax, s[i]);
-    }
-    tmax = quad_max(tmax);
-    if (__any(tmax > st.m)) {
-      const float m_new = tmax > st.m ? tmax + kHeadroom : st.m;
-      const float corr = exp2f(st.m - m_new);          // 0 on the first tile
-      st.m = m_new;
-      st.l *= corr;
-      if (quad == 0) W.corr[col] = corr;
-      __builtin_amdgcn_wave_barrier();
-      // accumulator rows are heads 4quad..4quad+3
+    for (int i = 0; i < 4; ++i) s[i] *= F;
+    if (nvalid < 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float c = W.corr[4 * quad + i];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j][i] *= c;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) zacc[g][i] *= c;
-      }
-      __builtin_amdgcn_wave_barrier();
+      for (int i = 0; i < 4; ++i)
+        if (4 * quad + i >= nvalid) s[i] = -INFINITY;
     }
     float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = exp2f(s[i] - st.m);
-      st.l += p[i];
-    }
+    softmax_step(st, s, p, acc, zacc, W.corr, col, quad);
+
     // ---- P' = p * value scale (hi/lo f16), Z += P' * 1, acc += P' * V
     half8 pp[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      float w[4];
+      uint16_t sv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = (4 * quad + i < tr.nvalid) ? p[i] * scale_of(svw, i, g) : 0.0f;
-      pp[g] = split_hi_lo(w);
+      for (int i = 0; i < 4; ++i) {
+        const int e = i * NG + g;
+        sv[i] = uint16_t(svw[e >> 1] >> (16 * (e & 1)));
+      }
+      if (nvalid < 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * quad + i >= nvalid) sv[i] = 0;   // masked token (its scale may be NaN)
+      }
+      pp[g] = pprime_hi_lo(p, sv);
       zacc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[g], ones8, zacc[g], 0, 0, 0);
     }
+    const int row = 4 * quad + (col >> 2);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int row = 4 * quad + (col >> 2);
-      const int colb = 2 * (16 * j + 4 * (col & 3));
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[j >> 1], dup4(read_tr(W.vt + row * VROW + colb)),
-                                                       acc[j], 0, 0, 0);
+    for (int jt = 0; jt < NT; ++jt) {
+      const half8 bv = value_operand(W.vt + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[jt >> 1], bv, acc[jt], 0, 0, 0);
     }
-    __builtin_amdgcn_wave_barrier();
-  }
+    wave_lds_sync();
+  };
+  run_tiles<R, Raw>(tg, load, process);
 
-  // ---- per-wave finalisation: l per column, acc in true units
+  // ---- write this wave's partial state: l per column, acc in true units
   const float lcol = quad_sum(st.l);
-  __syncthreads();                               // tile buffers are reused below
-  MergeLds<D>& M = lds.mg;
-  if (quad == 0) {
-    M.m[wave][col] = st.m;
-    M.l[wave][col] = lcol;
+  const int64_t base_h = int64_t(it.chunk) * a.Hq + hq0;
+  if (quad == 0 && col < G) {
+    a.pm[base_h + col] = st.m;
+    a.pl[base_h + col] = lcol;
   }
-  // acc[j][i] holds head 4quad+i, value-tile column p = 16j+col
+  // accumulator column col of N-tile jt is dim 16*jt + col in slot order;
+  // slot s of a unit holds code kSlotCode[s] scaled by 2^(kSlotShift[s]-10)
+  const int slot = col & 7;
+  const int dim_in_unit = int(kSlotCodePacked >> (4 * slot)) & 15;
+  const float up = __builtin_amdgcn_ldexpf(1.0f, 10 - (int(kSlotShiftPacked >> (4 * slot)) & 15));
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int p = 16 * j + col;
-    const int slot = p & 7;
-    const int dim = (p & ~7) + kSlotCode[slot];
-    const float up = __builtin_amdgcn_ldexpf(1.0f, 10 - kSlotShift[slot]);
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * quad + i;
+    if (c >= G) continue;
+    float* dst = a.pacc + (base_h + c) * D + (col & 8) + dim_in_unit;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) M.acc[wave][4 * quad + i][dim] = acc[j][i] * up - 3.5f * zacc[j >> 1][i];
-  }
-  __syncthreads();
-  // ---- merge the four waves and write the partial state
-  const int64_t base = int64_t(it.chunk) * a.Hq + int64_t(hk) * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, dim = idx % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (M.l[w][h] > 0.0f) mx = fmaxf(mx, M.m[w][h]);
-    float lsum = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (!(M.l[w][h] > 0.0f)) continue;
-      const float f = exp2f(M.m[w][h] - mx);
-      lsum += M.l[w][h] * f;
-      o += M.acc[w][h][dim] * f;
-    }
-    a.pacc[(base + h) * D + dim] = o;
-    if (dim == 0) {
-      a.pm[base + h] = mx;
-      a.pl[base + h] = lsum;
-    }
+    for (int jt = 0; jt < NT; ++jt) dst[16 * jt] = acc[jt][i] * up - 3.5f * zacc[jt >> 1][i];
   }
 }
 
 // ---------------------------------------------------------------------------
-// FP8 partial kernel
+// FP8 work item: one wave per kv-head
 // ---------------------------------------------------------------------------
-template <int NG>
-__global__ void __launch_bounds__(kThreads) partial_fp8_mfma(DecodeArgs a) {
+template <int NG, int R>
+__device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it, Fp8Lds<NG>& lds) {
   constexpr int D = 32 * NG;
   constexpr int NT = D / 16;
-  constexpr int VROW = 2 * D + 16;
+  constexpr int VROW = Fp8Lds<NG>::VROW;
   constexpr int LB = D / 4;                     // bytes of a row each lane loads
-  struct WaveLds {
-    uint8_t vt[16 * VROW];
-    float corr[16];
-  };
-  union Lds {
-    WaveLds w[kWaves];
-    MergeLds<D> mg;
-  };
-  __shared__ Lds lds;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
   const int quad = lane >> 4;
-  const WorkItem it = a.items[blockIdx.x];
-  const int hk = blockIdx.y;
   const PoolView& pv = a.pv;
+  stage_entries(lds.ent, a, it);
+  const int hk = blockIdx.y * kWaves + wave;
+  if (hk >= pv.Hkv) return;
   const int G = a.Hq / pv.Hkv;
-  const int tpp = pv.P / 16;
-  WaveLds& W = lds.w[wave];
+  const int hq0 = hk * G;
+  auto& W = lds.w[wave];
 
   // ---- query operand: MFMA r, lane (col, quad), slot s <-> dim quad*LB + 8r + s
   half8 qop[NG];
   float F;
   {
-    const bool live = col < G;
-    const uint16_t* qrow = a.q + (int64_t(it.b) * a.Hq + int64_t(hk) * G + col) * D;
-    float qv[NG][8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int r = 0; r < NG; ++r) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (live) raw = *reinterpret_cast<const u32x4*>(qrow + quad * LB + 8 * r);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w = raw[i >> 1];
-        qv[r][i] = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
-        amax = fmaxf(amax, fabsf(qv[r][i]));
-      }
-    }
-    amax = quad_max(amax);
-    const int E = q_shift(amax);
-#pragma unroll
-    for (int r = 0; r < NG; ++r)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qop[r][s] = _Float16(__builtin_amdgcn_ldexpf(qv[r][s], E));
+    const int E = load_query<NG>(
+        a, it.b, hq0, col, G, qop, [&](int r) { return quad * LB + 8 * r; }, [](int s) { return s; },
+        [](int) { return 0; });
     F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
   }
 
   f32x4 acc[NT];
+  f32x4 zacc[1];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  zacc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
 
-  const int ntiles = n_tiles(it, tpp);
-  const int32_t* pt_row = pv.pt + int64_t(it.seq) * pv.pt_stride;
-  const int64_t kc_off = fp8_codes_off(pv, hk, 0), vc_off = fp8_codes_off(pv, hk, 1);
-  const int64_t ks_off = fp8_scale_off(pv, hk, 0), vs_off = fp8_scale_off(pv, hk, 1);
-
-  for (int ti = wave; ti < ntiles; ti += kWaves) {
-    const TileRef tr = tile_ref(it, tpp, ti);
-    const uint8_t* page = page_address(pv, pt_row[a.pages[it.list_off + tr.page]]);
-    const int t0 = 16 * tr.sub;
-    const float sigk = *reinterpret_cast<const float*>(page + ks_off);
-    const float sigv = *reinterpret_cast<const float*>(page + vs_off);
-    uint32_t kw[LB / 4], vw[LB / 4];
-    {
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + kc_off + (t0 + col) * D + quad * LB);
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + vc_off + (t0 + col) * D + quad * LB);
+  const int32_t code_off = int32_t(fp8_codes_off(pv, hk, 0)) + col * D + quad * LB;
+  const int32_t ks_off = int32_t(fp8_scale_off(pv, hk, 0));
+  const int32_t vs_off = int32_t(fp8_scale_off(pv, hk, 1));
+  const int32_t vcode_delta = pv.P * D;
+  struct Raw {
+    uint32_t kw[LB / 4];
+    uint32_t vw[LB / 4];
+    float sigk, sigv;
+  };
+  auto load = [&](const Cursor& c, Raw& r) {
+    const uint8_t* page = entry_page(pv, lds.ent, c.page);
+    const int t0 = 16 * c.sub;
+    const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off + t0 * D);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + code_off + t0 * D + vcode_delta);
 #pragma unroll
-      for (int i = 0; i < LB / 4; ++i) {
-        kw[i] = kp[i];
-        vw[i] = vp[i];
-      }
+    for (int x = 0; x < LB / 4; ++x) {
+      r.kw[x] = kp[x];
+      r.vw[x] = vp[x];
     }
+    r.sigk = *reinterpret_cast<const float*>(page + ks_off);
+    r.sigv = *reinterpret_cast<const float*>(page + vs_off);
+  };
+  const TileGeom tg = tile_geom(it, pv.P / 16);
+
+  auto process = [&](Raw& raw, const Cursor& c, auto refill) {
+    const int nvalid = valid_in_tile(c, tg);
     // ---- values: f16 rows of the LDS tile (rows past the valid tokens zeroed)
-    const bool vrow_ok = col < tr.nvalid;
+    const bool vrow_ok = col < nvalid;
 #pragma unroll
     for (int i = 0; i < LB / 4; i += 2) {
-      const u32x2 a0 = fp8x4_to_f16(vw[i]);
-      const u32x2 a1 = fp8x4_to_f16(vw[i + 1]);
+      const u32x2 a0 = fp8x4_to_f16(raw.vw[i]);
+      const u32x2 a1 = fp8x4_to_f16(raw.vw[i + 1]);
       u32x4 o = {a0[0], a0[1], a1[0], a1[1]};
       if (!vrow_ok) o = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(W.vt + col * VROW + 2 * (quad * LB + 4 * i)) = o;
     }
-    __builtin_amdgcn_wave_barrier();
-    // ---- QK^T over all dims
-    f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ---- keys to f16 MFMA operands
+    half8 kop[NG];
 #pragma unroll
     for (int r = 0; r < NG; ++r) {
-      const u32x2 k0 = fp8x4_to_f16(kw[2 * r]);
-      const u32x2 k1 = fp8x4_to_f16(kw[2 * r + 1]);
+      const u32x2 k0 = fp8x4_to_f16(raw.kw[2 * r]);
+      const u32x2 k1 = fp8x4_to_f16(raw.kw[2 * r + 1]);
       const u32x4 ku = {k0[0], k0[1], k1[0], k1[1]};
-      dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ku), qop[r], dsum, 0, 0, 0);
+      kop[r] = __builtin_bit_cast(half8, ku);
     }
+    const float sigk = raw.sigk, sigv = raw.sigv;
+    refill(raw);
+    wave_lds_sync();
+
+    // ---- QK^T over all dims (page-head scale applied once)
+    f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < NG; ++r) dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[r], qop[r], dsum, 0, 0, 0);
     const float fk = F * sigk;
     float s[4];
-    float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = (4 * quad + i < tr.nvalid) ? dsum[i] * fk : -INFINITY;
-      tmax = fmaxf(tmax, s[i]);
+    for (int i = 0; i < 4; ++i) s[i] = dsum[i] * fk;
+    if (nvalid < 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * quad + i >= nvalid) s[i] = -INFINITY;
     }
-    tmax = quad_max(tmax);
-    if (__any(tmax > st.m)) {
-      const float m_new = tmax > st.m ? tmax + kHeadroom : st.m;
-      const float corr = exp2f(st.m - m_new);
-      st.m = m_new;
-      st.l *= corr;
-      if (quad == 0) W.corr[col] = corr;
-      __builtin_amdgcn_wave_barrier();
+    float p[4];
+    softmax_step(st, s, p, acc, zacc, W.corr, col, quad);
+
+    const half8 pp = pprime_hi_lo_uniform(p, sigv);
+    const int row = 4 * quad + (col >> 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float c = W.corr[4 * quad + i];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j][i] *= c;
-      }
-      __builtin_amdgcn_wave_barrier();
+    for (int jt = 0; jt < NT; ++jt) {
+      const half8 bv = value_operand(W.vt + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp, bv, acc[jt], 0, 0, 0);
     }
-    float w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(s[i] - st.m);
-      st.l += p;
-      w[i] = (4 * quad + i < tr.nvalid) ? p * sigv : 0.0f;
-    }
-    const half8 pp = split_hi_lo(w);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int row = 4 * quad + (col >> 2);
-      const int colb = 2 * (16 * j + 4 * (col & 3));
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp, dup4(read_tr(W.vt + row * VROW + colb)),
-                                                       acc[j], 0, 0, 0);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+    wave_lds_sync();
+  };
+  run_tiles<R, Raw>(tg, load, process);
 
   const float lcol = quad_sum(st.l);
-  __syncthreads();
-  MergeLds<D>& M = lds.mg;
-  if (quad == 0) {
-    M.m[wave][col] = st.m;
-    M.l[wave][col] = lcol;
+  const int64_t base_h = int64_t(it.chunk) * a.Hq + hq0;
+  if (quad == 0 && col < G) {
+    a.pm[base_h + col] = st.m;
+    a.pl[base_h + col] = lcol;
   }
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * quad + i;
+    if (c >= G) continue;
+    float* dst = a.pacc + (base_h + c) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) M.acc[wave][4 * quad + i][16 * j + col] = acc[j][i];
-  __syncthreads();
-  const int64_t base = int64_t(it.chunk) * a.Hq + int64_t(hk) * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, dim = idx % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2)
-      if (M.l[w2][h] > 0.0f) mx = fmaxf(mx, M.m[w2][h]);
-    float lsum = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      if (!(M.l[w2][h] > 0.0f)) continue;
-      const float f = exp2f(M.m[w2][h] - mx);
-      lsum += M.l[w2][h] * f;
-      o += M.acc[w2][h][dim] * f;
-    }
-    a.pacc[(base + h) * D + dim] = o;
-    if (dim == 0) {
-      a.pm[base + h] = mx;
-      a.pl[base + h] = lsum;
-    }
+    for (int jt = 0; jt < NT; ++jt) dst[16 * jt + col] = acc[jt][i];
   }
 }
 
-hipError_t launch_partial_tq3(const DecodeArgs& a, hipStream_t s) {
-  if (a.n_items <= 0) return hipSuccess;
-  const dim3 grid(unsigned(a.n_items), unsigned(a.pv.Hkv));
-  switch (a.pv.d) {
-    case 32: hipLaunchKernelGGL(partial_tq3_mfma<1>, grid, dim3(kThreads), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(partial_tq3_mfma<2>, grid, dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(partial_tq3_mfma<4>, grid, dim3(kThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(partial_tq3_mfma<8>, grid, dim3(kThreads), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+// ---------------------------------------------------------------------------
+// One launch for both formats: workgroup x takes work item x (FP8 or TQ3).
+// ---------------------------------------------------------------------------
+constexpr int kRingTq3 = 4;   // TQ3 tiles in flight per wave
+constexpr int kRingFp8 = 2;   // FP8 tiles in flight per wave
+
+template <int NG>
+constexpr size_t smem_bytes() {
+  return sizeof(Tq3Lds<NG>) > sizeof(Fp8Lds<NG>) ? sizeof(Tq3Lds<NG>) : sizeof(Fp8Lds<NG>);
 }
 
-hipError_t launch_partial_fp8(const DecodeArgs& a, hipStream_t s) {
-  if (a.n_items <= 0) return hipSuccess;
-  const dim3 grid(unsigned(a.n_items), unsigned(a.pv.Hkv));
-  switch (a.pv.d) {
-    case 32: hipLaunchKernelGGL(partial_fp8_mfma<1>, grid, dim3(kThreads), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(partial_fp8_mfma<2>, grid, dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(partial_fp8_mfma<4>, grid, dim3(kThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(partial_fp8_mfma<8>, grid, dim3(kThreads), 0, s, a); break;
+template <int NG>
+__global__ void __launch_bounds__(kThreads) partial_mixed(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<NG>()];
+  const WorkItem it = a.items[blockIdx.x];
+  if (it.fmt == 0)
+    fp8_item<NG, kRingFp8>(a, it, *reinterpret_cast<Fp8Lds<NG>*>(smem));
+  else
+    tq3_item<NG, kRingTq3>(a, it, *reinterpret_cast<Tq3Lds<NG>*>(smem));
+}
+
+namespace {
+
+template <typename F>
+hipError_t with_kernel(int d, F f) {
+  switch (d) {
+    case 32: return f(partial_mixed<1>);
+    case 64: return f(partial_mixed<2>);
+    case 128: return f(partial_mixed<4>);
+    case 256: return f(partial_mixed<8>);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+}  // namespace
+
+// Grid: one workgroup per (work item, block of kWaves kv-heads); each wave
+// owns one kv-head of the item.
+hipError_t launch_partial(const DecodeArgs& a, hipStream_t s) {
+  if (a.n_items <= 0) return hipSuccess;
+  const dim3 grid(unsigned(a.n_items), unsigned((a.pv.Hkv + kWaves - 1) / kWaves));
+  return with_kernel(a.pv.d, [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t partial_resident_waves(int d, int* waves) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  return with_kernel(d, [&](auto kernel) {
+    int blocks = 0;
+    const hipError_t r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kThreads, 0);
+    if (r == hipSuccess) *waves = cus * blocks * kWaves;
+    return r;
+  });
 }
 
 }  // namespace mkv

@@ -119,12 +119,13 @@ struct mkv_pool {
   int32_t sched_Hq = 0;
   std::vector<int32_t> sched_ids;
   mkv::Schedule sched;
+  int32_t target_waves = 2048;   // resident partial-kernel waves on this device
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
   std::vector<ProfEvent> prof_free;
-  double prof_ms[3] = {0, 0, 0};
-  int64_t prof_n[3] = {0, 0, 0};
+  double prof_ms[2] = {0, 0};    // partial, merge
+  int64_t prof_n[2] = {0, 0};
 
   mkv::PoolView view() const {
     const mkv::Geom& g = meta.geom();
@@ -209,10 +210,15 @@ mkv_status prof_collect(mkv_pool* p) {
   return MKV_OK;
 }
 
-mkv::SchedPolicy policy_from_env() {
+// Split-K policy of a pool: balanced chunks for the device's resident
+// partial-kernel waves.  Environment overrides (for tuning): MKV_CHUNK_PAGES
+// (fixed chunk length), MKV_TARGET_WAVES, MKV_FP8_PAGE_COST.
+mkv::SchedPolicy pool_policy(const mkv_pool* p) {
   mkv::SchedPolicy pol;
-  if (const char* e = std::getenv("MKV_CHUNK_PAGES")) pol.chunk_pages = std::max(1, std::atoi(e));
-  if (const char* e = std::getenv("MKV_MIN_ITEMS")) pol.min_items = std::max(1, std::atoi(e));
+  pol.target_waves = p->target_waves;
+  if (const char* e = std::getenv("MKV_CHUNK_PAGES")) pol.fixed_chunk_pages = std::max(0, std::atoi(e));
+  if (const char* e = std::getenv("MKV_TARGET_WAVES")) pol.target_waves = std::max(1, std::atoi(e));
+  if (const char* e = std::getenv("MKV_FP8_PAGE_COST")) pol.fp8_page_cost = float(std::atof(e));
   return pol;
 }
 
@@ -259,6 +265,10 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
   };
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
+  int waves = 0;
+  e = mkv::partial_resident_waves(desc->head_dim, &waves);
+  if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
+  if (waves > 0) p->target_waves = waves;
   if (device_mem) {
     if (bytes < p->lay.total) return cleanup(MKV_ERANGE, "device buffer smaller than mkv_pool_bytes");
     if (reinterpret_cast<uintptr_t>(device_mem) % 256)
@@ -349,6 +359,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
                       float softmax_scale, float* out, float* lse, hipStream_t s) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
   if (!q || !out || !lse || !seq_ids) return set_err(MKV_EINVAL, "null argument");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return set_err(MKV_EINVAL, "q must be 16-byte aligned");
   DeviceGuard guard(p->device);
   const bool same = p->sched_valid && p->sched_version == p->meta.version() && p->sched_Hq == Hq &&
                     int32_t(p->sched_ids.size()) == B &&
@@ -356,7 +367,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   if (!same) {
     std::string err;
     mkv::Schedule sc;
-    int st = p->meta.build_schedule(seq_ids, B, Hq, policy_from_env(), &sc, &err);
+    int st = p->meta.build_schedule(seq_ids, B, Hq, pool_policy(p), &sc, &err);
     if (st) return set_err(mkv_status(st), err);
     mkv_status r = p->wait_staging();
     if (r) return r;
@@ -395,21 +406,14 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   a.pacc = reinterpret_cast<float*>(p->mem + p->lay.pacc);
   a.out = out;
   a.lse = lse;
-  if (!sc.items[0].empty()) {
-    a.items = items;
-    a.n_items = int32_t(sc.items[0].size());
+  a.items = items;
+  a.n_items = int32_t(sc.items[0].size() + sc.items[1].size());
+  {
     ProfEvent* e = prof_begin(p, 0, s);
-    MKV_HIP(mkv::launch_partial_fp8(a, s));
+    MKV_HIP(mkv::launch_partial(a, s));
     prof_end(p, e, s);
   }
-  if (!sc.items[1].empty()) {
-    a.items = items + sc.items[0].size();
-    a.n_items = int32_t(sc.items[1].size());
-    ProfEvent* e = prof_begin(p, 1, s);
-    MKV_HIP(mkv::launch_partial_tq3(a, s));
-    prof_end(p, e, s);
-  }
-  ProfEvent* e = prof_begin(p, 2, s);
+  ProfEvent* e = prof_begin(p, 1, s);
   MKV_HIP(mkv::launch_merge(a, s));
   prof_end(p, e, s);
   return MKV_OK;
@@ -480,13 +484,11 @@ mkv_status mkv_profile_read(mkv_pool* p, mkv_profile* o) {
   DeviceGuard guard(p->device);
   mkv_status r = prof_collect(p);
   if (r) return r;
-  o->ms_partial_fp8 = p->prof_ms[0];
-  o->ms_partial_tq3 = p->prof_ms[1];
-  o->ms_merge = p->prof_ms[2];
-  o->n_partial_fp8 = p->prof_n[0];
-  o->n_partial_tq3 = p->prof_n[1];
-  o->n_merge = p->prof_n[2];
-  for (int i = 0; i < 3; ++i) {
+  o->ms_partial = p->prof_ms[0];
+  o->ms_merge = p->prof_ms[1];
+  o->n_partial = p->prof_n[0];
+  o->n_merge = p->prof_n[1];
+  for (int i = 0; i < 2; ++i) {
     p->prof_ms[i] = 0;
     p->prof_n[i] = 0;
   }

@@ -21,7 +21,7 @@ struct PoolView {
 
 struct DecodeArgs {
   PoolView pv;
-  const WorkItem* items;    // work items of one format
+  const WorkItem* items;    // work items (each of one format)
   int32_t n_items;
   const int32_t* pages;     // logical page lists
   const int32_t* chunk_base;// [B + 1]
@@ -41,8 +41,9 @@ hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_p
                          hipStream_t s);
 hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
                          uint8_t* dst, int64_t slot_bytes, hipStream_t s);
-hipError_t launch_partial_fp8(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_partial_tq3(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_partial(const DecodeArgs& a, hipStream_t s);
+// Waves of the partial kernel (head dim d) resident on the current device at once.
+hipError_t partial_resident_waves(int d, int* waves);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace mkv

@@ -51,9 +51,15 @@ int validate_desc(const Desc& d, Geom* g, std::string* err) {
   r.tq3_rec = int64_t(d.Hkv) * d.P * d.d * 7 / 8;
   r.fp8_stride = round_up(r.fp8_rec, kSlabAlign);
   r.tq3_stride = round_up(r.tq3_rec, kSlabAlign);
-  r.max_chunks = d.max_chunks ? d.max_chunks : 4096 + 2 * d.max_batch;
-  if (r.max_chunks < 2 * d.max_batch)
-    return fail(err, MKV_S_EINVAL, "max_chunks must be at least 2 * max_batch");
+  // A batch entry needs at most ceil(n8 / C) + ceil(n3 / C) chunks at the
+  // largest chunk C = kMaxChunkPages, which is below 2 + ceil(pages / C).
+  const int64_t need =
+      int64_t(d.max_batch) * (2 + (int64_t(d.max_pages_per_seq) + kMaxChunkPages - 1) / kMaxChunkPages);
+  const int64_t mc = d.max_chunks ? int64_t(d.max_chunks) : std::max<int64_t>(4096 + 2 * int64_t(d.max_batch), need);
+  if (mc < need || mc > (int64_t(1) << 30))
+    return fail(err, MKV_S_EINVAL,
+                "max_chunks must be at least max_batch * (2 + ceil(max_pages_per_seq / 256))");
+  r.max_chunks = int32_t(mc);
   if (g) *g = r;
   return MKV_S_OK;
 }
@@ -171,52 +177,89 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     if (check_seq(ids[b], err)) return MKV_S_EINVAL;
     if (seqs_[size_t(ids[b])].len == 0) return fail(err, MKV_S_EINVAL, "empty sequence in batch");
   }
-  // Per-format counts of each sequence.
+  // Per-format page counts of each batch entry.
   std::vector<int32_t> n8(size_t(B), 0), n3(size_t(B), 0);
   int64_t total_pages = 0;
+  double total_cost = 0.0;
+  const double c8 = pol.fp8_page_cost > 0.0f ? double(pol.fp8_page_cost) : 1.0;
   for (int32_t b = 0; b < B; ++b) {
     for (int32_t e : seqs_[size_t(ids[b])].pt) (pt_is_tq3(e) ? n3 : n8)[size_t(b)]++;
     total_pages += int64_t(seqs_[size_t(ids[b])].pt.size());
+    total_cost += c8 * n8[size_t(b)] + n3[size_t(b)];
   }
-  auto count = [&](int64_t c) {
-    int64_t t = 0;
-    for (int32_t b = 0; b < B; ++b) t += (n8[size_t(b)] + c - 1) / c + (n3[size_t(b)] + c - 1) / c;
-    return t;
+  // Chunk count of each (entry, format) list: chunks of `fixed` pages, or
+  // near-equal chunks of about `budget` cost.
+  int64_t fixed = pol.fixed_chunk_pages;
+  auto chunks_of = [&](int32_t n, double page_cost, double budget) -> int64_t {
+    if (n == 0) return 0;
+    int64_t per;
+    if (fixed > 0) {
+      per = fixed;
+    } else {
+      const int64_t k = std::max<int64_t>(1, int64_t(n * page_cost / budget));
+      per = std::max<int64_t>((n + k - 1) / k, std::min<int32_t>(n, std::max(1, pol.min_chunk_pages)));
+    }
+    per = std::min<int64_t>(per, kMaxChunkPages);
+    return (n + per - 1) / per;
   };
-  int64_t chunk = std::max(1, pol.chunk_pages);
-  while (chunk > pol.min_chunk_pages && count(chunk) * g_.Hkv < pol.min_items)
-    chunk = std::max<int64_t>(pol.min_chunk_pages, chunk / 2);
-  while (count(chunk) > g_.max_chunks) chunk *= 2;
+  const int64_t waves_per_item =
+      int64_t(kWavesPerWorkgroup) * ((g_.Hkv + kWavesPerWorkgroup - 1) / kWavesPerWorkgroup);
+  const int64_t target_items = std::max<int64_t>(1, pol.target_waves / waves_per_item);
+  double budget = std::max(1.0, total_cost / double(target_items));
+  std::vector<int64_t> k8(static_cast<size_t>(B)), k3(static_cast<size_t>(B));
+  int64_t count = 0;
+  for (int attempt = 0;; ++attempt) {
+    count = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      k8[size_t(b)] = chunks_of(n8[size_t(b)], c8, budget);
+      k3[size_t(b)] = chunks_of(n3[size_t(b)], 1.0, budget);
+      count += k8[size_t(b)] + k3[size_t(b)];
+    }
+    if (count <= g_.max_chunks) break;
+    // Too many chunks: coarser chunks (fixed chunks double, balanced budgets grow).
+    bool at_cap = true;
+    for (int32_t b = 0; b < B; ++b)
+      at_cap = at_cap && k8[size_t(b)] == (n8[size_t(b)] + kMaxChunkPages - 1) / kMaxChunkPages &&
+               k3[size_t(b)] == (n3[size_t(b)] + kMaxChunkPages - 1) / kMaxChunkPages;
+    if (at_cap || attempt > 64) return fail(err, MKV_S_ERANGE, "batch needs more than max_chunks chunks");
+    budget *= 1.5;
+    fixed *= 2;
+  }
   out->items[0].clear();
   out->items[1].clear();
   out->pages.clear();
   out->pages.reserve(size_t(total_pages));
   out->chunk_base.assign(size_t(B) + 1, 0);
-  int32_t nc = 0;
+  int32_t nc = 0, largest = 0;
   for (int32_t b = 0; b < B; ++b) {
     out->chunk_base[size_t(b)] = nc;
     const Seq& q = seqs_[size_t(ids[b])];
     for (int fmt = 0; fmt < 2; ++fmt) {
-      int32_t in_chunk = 0;
-      bool open = false;
+      const int32_t n = fmt ? n3[size_t(b)] : n8[size_t(b)];
+      const int64_t k = fmt ? k3[size_t(b)] : k8[size_t(b)];
+      if (n == 0) continue;
+      // chunk i holds n / k pages, the first n % k chunks one more
+      const int32_t small = int32_t(n / k), extra = int32_t(n % k);
       std::vector<WorkItem>& items = out->items[fmt];
+      int32_t chunk_idx = -1, left = 0;
       for (int32_t lp = 0; lp < int32_t(q.pt.size()); ++lp) {
         if (int(pt_is_tq3(q.pt[size_t(lp)])) != fmt) continue;
-        if (!open || in_chunk == chunk) {
+        if (left == 0) {
+          ++chunk_idx;
+          left = small + (chunk_idx < extra ? 1 : 0);
           items.push_back(WorkItem{b, ids[b], int32_t(out->pages.size()), 0, 0, nc++, fmt, 0});
-          open = true;
-          in_chunk = 0;
         }
         out->pages.push_back(lp);
         items.back().npages++;
         items.back().last_ntok = page_tokens(q.len, g_.P, lp);
-        ++in_chunk;
+        largest = std::max(largest, items.back().npages);
+        --left;
       }
     }
   }
   out->chunk_base[size_t(B)] = nc;
   out->n_chunks = nc;
-  out->chunk_pages = int32_t(chunk);
+  out->chunk_pages = largest;
   return MKV_S_OK;
 }
 

@@ -77,10 +77,26 @@ struct WorkItem {
   int32_t b, seq, list_off, npages, last_ntok, chunk, fmt, pad;
 };
 
+// Upper bound on WorkItem::npages: the partial kernel stages a work item's
+// page-table entries in a fixed LDS array of this length.
+constexpr int32_t kMaxChunkPages = 256;
+// Waves per partial-kernel workgroup; a workgroup takes one work item and
+// this many kv-heads of it (one per wave).
+constexpr int32_t kWavesPerWorkgroup = 4;
+
+// Split-K policy.  By default the page list of each (sequence, format) is cut
+// into near-equal chunks so that all items of a batch cost about the same and
+// together they fill the partial kernel's resident waves once (an item takes
+// ceil(Hkv / kWavesPerWorkgroup) workgroups); an FP8 page counts
+// fp8_page_cost TQ3 pages.  A
+// nonzero fixed_chunk_pages cuts every list into chunks of exactly that many
+// pages instead (the last one shorter).  Chunks grow when a batch would need
+// more than max_chunks of them; no chunk exceeds kMaxChunkPages.
 struct SchedPolicy {
-  int32_t chunk_pages = 32;      // preferred pages per chunk
-  int32_t min_chunk_pages = 4;   // smallest chunk when shrinking for parallelism
-  int32_t min_items = 1024;      // shrink chunks until items * kv-heads reach this
+  int32_t target_waves = 2048;   // resident partial-kernel waves on the device
+  int32_t min_chunk_pages = 4;   // smallest balanced chunk (shorter lists stay whole)
+  int32_t fixed_chunk_pages = 0; // 0: balanced chunks
+  float fp8_page_cost = 1.5f;    // cost of an FP8 page relative to a TQ3 page
 };
 
 struct Schedule {
@@ -88,7 +104,7 @@ struct Schedule {
   std::vector<int32_t> pages;       // logical page ids referenced by the items
   std::vector<int32_t> chunk_base;  // [B + 1] prefix sums of chunks per batch entry
   int32_t n_chunks = 0;
-  int32_t chunk_pages = 0;
+  int32_t chunk_pages = 0;          // largest chunk of the schedule
 };
 
 class Meta {

@@ -78,7 +78,10 @@ typedef struct {
   int32_t max_pages_per_seq; /* page-table row length */
   int32_t max_batch;         /* largest B accepted by mkv_decode */
   int32_t max_q_heads;       /* largest Hq accepted by mkv_decode */
-  int32_t max_chunks;        /* partial-state slots per decode; 0 = library default */
+  int32_t max_chunks;        /* partial-state slots per decode; 0 = library default,
+                                max(4096 + 2 * max_batch, floor below); a nonzero value
+                                must be >= max_batch * (2 + ceil(max_pages_per_seq / 256)),
+                                since a split-K chunk spans at most 256 pages */
   int64_t fp8_pages;         /* FP8 slab capacity in pages */
   int64_t tq3_pages;         /* TQ3 slab capacity in pages */
   uint64_t placement_seed;   /* 0: pages handed out in index order; else a seeded shuffle */
@@ -97,10 +100,11 @@ typedef struct {
   int64_t dense_fallbacks;     /* always 0: decode never leaves the mixed path */
 } mkv_stats;
 
-/* Per-kernel device time accumulated while profiling is on (milliseconds). */
+/* Per-kernel device time accumulated while profiling is on (milliseconds):
+ * the partial kernel (both formats, one launch per decode) and the merge. */
 typedef struct {
-  double ms_partial_fp8, ms_partial_tq3, ms_merge;
-  int64_t n_partial_fp8, n_partial_tq3, n_merge;
+  double ms_partial, ms_merge;
+  int64_t n_partial, n_merge;
 } mkv_profile;
 
 /* Device bytes a pool with this descriptor needs (slabs, page tables,
@@ -147,14 +151,16 @@ mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages,
 
 /* Decode attention for one query token per sequence ("Como os resultados
  * parciais sao combinados").  seq_ids: host int32 [B] of non-empty sequences.
- * q: device bf16 [B][Hq][d]; query head h reads kv-head h / (Hq / Hkv).
+ * q: device bf16 [B][Hq][d], 16-byte aligned; query head h reads kv-head
+ * h / (Hq / Hkv).
  * softmax_scale: fp32 factor on <q, k>.  out: device fp32 [B][Hq][d];
  * lse: device fp32 [B][Hq], natural-log log-sum-exp of the scaled scores.
- * Per-format partial kernels run over split-K page chunks of each sequence
- * and a merge kernel combines their (max, denominator, unnormalised
- * accumulator) states.  The split-K schedule is rebuilt only when page
+ * One partial-kernel launch reduces split-K page chunks of each sequence,
+ * each chunk in its own format (FP8 and TQ3 code paths), and a merge kernel
+ * combines their (max, denominator, unnormalised accumulator) states.  The split-K schedule is rebuilt only when page
  * metadata, the batch or Hq changed since the previous decode.
- * MKV_EINVAL for an empty sequence, Hq not a multiple of Hkv, or Hq / Hkv > 16;
+ * MKV_EINVAL for an empty sequence, Hq not a multiple of Hkv, Hq / Hkv > 16,
+ * or a misaligned q;
  * MKV_ERANGE for B > max_batch or Hq > max_q_heads. */
 mkv_status mkv_decode(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const void* q,
                       int32_t Hq, float softmax_scale, float* out, float* lse,

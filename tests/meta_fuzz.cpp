@@ -45,8 +45,9 @@ int main() {
       for (int i = 0; i < 1 + int(rng() % 6); ++i) ids.push_back(int32_t(rng() % 6));
       Schedule sc;
       SchedPolicy pol;
-      pol.chunk_pages = 1 + int(rng() % 9);
-      pol.min_items = 1 + int(rng() % 100);
+      pol.fixed_chunk_pages = int(rng() % 9);          // 0: balanced chunks
+      pol.target_waves = 1 + int(rng() % 4096);
+      pol.fp8_page_cost = 0.25f + float(rng() % 8);
       if (m.build_schedule(ids.data(), int32_t(ids.size()), 16, pol, &sc, &err) == 0) {
         size_t total = 0;
         for (int32_t id : ids) total += m.seq(id).pt.size();

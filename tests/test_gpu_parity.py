@@ -187,6 +187,12 @@ def test_error_paths_through_the_abi():
     with pytest.raises(mkv.MkvError) as e:
         mkv.demote(pool.handle, 0, [0])                              # page 0 is already TQ3
     assert e.value.status == mkv.ESTATE
+    buf = torch.zeros(q.numel() + 8, dtype=q.dtype, device="cuda")
+    q_odd = buf[1:1 + q.numel()].view(q.shape)                       # 2-byte offset
+    q_odd.copy_(q)
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.decode(pool.handle, [0], q_odd, 0.1, out, lse)
+    assert e.value.status == mkv.EINVAL
     pool.close()
 
 

@@ -71,13 +71,13 @@ class Host:
     def free(self, fmt):
         return self.L.mkvh_free(self.h, fmt)
 
-    def schedule(self, ids, Hq, chunk_pages=0, min_items=0):
+    def schedule(self, ids, Hq, chunk_pages=0, target_waves=0):
         ids = np.asarray(ids, np.int32)
         items = np.zeros((1 << 16, 8), np.int32)
         pages = np.zeros(1 << 20, np.int32)
         base = np.zeros(ids.size + 1, np.int32)
         counts = np.zeros(5, np.int32)
-        st = self.L.mkvh_schedule(self.h, ids.ctypes.data, ids.size, Hq, chunk_pages, min_items,
+        st = self.L.mkvh_schedule(self.h, ids.ctypes.data, ids.size, Hq, chunk_pages, target_waves,
                                   items.ctypes.data, items.shape[0], pages.ctypes.data,
                                   pages.size, base.ctypes.data, counts.ctypes.data)
         if st:
@@ -231,22 +231,32 @@ def test_schedule_covers_every_page_once_ragged_and_scattered(lib):
         dem = [p for p in range(n) if rng.random() < 0.8]
         assert h.demote(s, dem)[0] == OK
     for cp in (1, 3, 32, 1000):
-        st, sc = h.schedule(ids, 32, chunk_pages=cp, min_items=1)
+        st, sc = h.schedule(ids, 32, chunk_pages=cp)
+        assert st == OK
+        _check_coverage(h, ids, sc, 16)
+        assert sc["chunk_pages"] <= min(cp, 256)
+    for waves in (1, 64, 2048, 100000):
+        st, sc = h.schedule(ids, 32, target_waves=waves)
         assert st == OK
         _check_coverage(h, ids, sc, 16)
     h.close()
 
 
-def test_long_context_schedule_has_at_least_256_chunks(lib):
-    # 131072 tokens, last 4096 FP8: 8192 pages split into >= 256 chunks.
+def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
+    # 131072 tokens, last 4096 FP8; 2048 resident waves / 8 kv-heads = 256
+    # items at most, of near-equal cost (an FP8 page costs 1.5 TQ3 pages).
     h = _host(lib, num_kv_heads=8, max_seqs=1, max_pages_per_seq=8192, max_batch=1,
               max_q_heads=48, fp8_pages=8192, tq3_pages=8192, placement_seed=5)
     assert h.append(0, 131072)[0] == OK
     assert h.demote(0, list(range(8192 - 256)))[0] == OK
-    st, sc = h.schedule([0], 48)
+    st, sc = h.schedule([0], 48, target_waves=2048)
     assert st == OK
-    assert sc["n_chunks"] >= 256 and sc["n8"] >= 1 and sc["n3"] >= 1
+    assert 240 <= sc["n_chunks"] <= 256 and sc["n8"] >= 1 and sc["n3"] >= 1
     _check_coverage(h, [0], sc, 16)
+    cost = np.array([it[3] * (1.5 if it[6] == 0 else 1.0) for it in sc["items"]])
+    assert cost.max() <= 1.15 * (7936 + 1.5 * 256) / 256
+    sizes3 = sc["items"][sc["n8"]:, 3]
+    assert sizes3.max() - sizes3.min() <= 1
     # algorithmic bytes: 126976 TQ3 tokens * 896 B + 4096 FP8 tokens * 2048 B + 256 pages * 64 B
     ids = np.array([0], np.int32)
     assert h.L.mkvh_kv_bytes(h.h, ids.ctypes.data, 1) == 122175488
@@ -254,12 +264,27 @@ def test_long_context_schedule_has_at_least_256_chunks(lib):
 
 
 def test_schedule_respects_chunk_capacity(lib):
-    h = _host(lib, max_pages_per_seq=512, fp8_pages=2048, tq3_pages=2048, max_chunks=8)
+    # 4 * (2 + ceil(512 / 256)) = 16 is the smallest max_chunks this descriptor accepts
+    with pytest.raises(ValueError):
+        _host(lib, max_pages_per_seq=512, fp8_pages=2048, max_chunks=15)
+    h = _host(lib, max_pages_per_seq=512, fp8_pages=2048, tq3_pages=2048, max_chunks=16)
     for s in range(4):
         h.append(s, 512 * 16)
-    st, sc = h.schedule([0, 1, 2, 3], 8, chunk_pages=1, min_items=1)
-    assert st == OK and sc["n_chunks"] <= 8
+    st, sc = h.schedule([0, 1, 2, 3], 8, chunk_pages=1)
+    assert st == OK and sc["n_chunks"] <= 16
     _check_coverage(h, [0, 1, 2, 3], sc, 16)
+    h.close()
+
+
+def test_chunks_never_exceed_256_pages(lib):
+    h = _host(lib, max_pages_per_seq=1024, fp8_pages=1024, tq3_pages=1024, max_seqs=2)
+    h.append(0, 1000 * 16 + 3)
+    assert h.demote(0, list(range(0, 900)))[0] == OK
+    st, sc = h.schedule([0], 8, chunk_pages=4096)
+    assert st == OK and sc["chunk_pages"] <= 256
+    assert sc["n3"] == 4 and sc["n8"] == 1          # ceil(900 / 256), ceil(101 / 256)
+    assert sc["items"][:, 3].max() <= 256
+    _check_coverage(h, [0], sc, 16)
     h.close()
 
 
