@@ -15,7 +15,8 @@ Prints one JSON line:
   roofline     the dominant kernel (the partial kernel, which reads every KV
                byte of the step in one launch): its algorithmic bytes per
                launch / its mean launch time from HIP events recorded on the
-               decode stream during the timed region, against 8 TB/s
+               decode stream during a second timed region of the same steps
+               (the first, without library events, gives value), against 8 TB/s
   cpu_baseline the CPU oracle on the same workload (bounded repetitions)
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
@@ -227,24 +228,35 @@ def main():
     for i in range(max(args.warmup, R)):
         mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
     torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+
+    def timed_steps():
+        torch.cuda.synchronize()
+        ev0.record()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
+        host_s = time.perf_counter() - t0
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps, host_s / args.steps
+
+    # Timed region 1: the step as a caller sees it (no library events).
+    ms, host_s = timed_steps()
+    # Timed region 2: the same steps with the library's per-kernel HIP events
+    # recorded on the decode stream (kernel durations for the roofline).
     for p in pools:
         mkv.profile_enable(p.handle, True)
         mkv.profile_read(p.handle)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for i in range(args.steps):
-        mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms_ev, _ = timed_steps()
     prof = {}
     for p in pools:
         for k2, v2 in mkv.profile_read(p.handle).items():
             prof[k2] = prof.get(k2, 0) + v2
         mkv.profile_enable(p.handle, False)
-    log(f"step {ms * 1e3:.2f} us; kernel profile {prof}")
+    log(f"step {ms * 1e3:.2f} us (host {host_s * 1e6:.1f} us per call; {ms_ev * 1e3:.2f} us with "
+        f"kernel events); kernel profile {prof}")
 
     kernel_ms = {"partial": prof["ms_partial"] / max(1, prof["n_partial"]),
                  "merge": prof["ms_merge"] / max(1, prof["n_merge"])}
@@ -276,6 +288,8 @@ def main():
             "kv_bytes_tq3": tq3_b,
             "replicas_rotated": R,
             "kernel_us": {k: round(v * 1e3, 3) for k, v in kernel_ms.items()},
+            "host_us_per_call": round(host_s * 1e6, 2),
+            "us_per_step_with_kernel_events": round(ms_ev * 1e3, 3),
         },
         "roofline": {
             "kernel": dom,

@@ -8,8 +8,13 @@
 //   O = sum_i acc_i 2^(m_i - M) / L,  LSE = (M + log2 L) * ln 2.
 // A chunk with l == 0 holds no token and is skipped.
 //
-// One block per (b, h, 32-dim slice); its threads take one chunk each (looping
-// when there are more chunks than threads) and the block reduces.
+// One workgroup per (b, h, 16-dim slice).  Thread (j, k) owns dims 4j..4j+3
+// of the slice for chunks k, k+64, ...; it loads a batch of up to kUnroll of
+// them (max, denominator and a float4 of the accumulator) at once, so a
+// batch of 64 * kUnroll chunks costs one memory round trip.  The batch
+// maximum is reduced over the workgroup, the thread accumulates its chunks
+// with weights 2^(m_i - M) (rescaling earlier batches if M rose), and the 64
+// chunk lanes are summed through shuffles and LDS at the end.
 #include <hip/hip_runtime.h>
 
 #include "mkv_device.hpp"
@@ -19,73 +24,96 @@ namespace mkv {
 namespace {
 
 constexpr int kMergeThreads = 256;
-constexpr int kSlice = 32;
+constexpr int kSlice = 16;                         // dims per workgroup
+constexpr int kVecLanes = kSlice / 4;              // threads per chunk (float4 each)
+constexpr int kChunkLanes = kMergeThreads / kVecLanes;
+constexpr int kUnroll = 8;
+constexpr int kMergeWaves = kMergeThreads / 64;
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
 
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
-  __shared__ float red[kMergeThreads / 64][kSlice + 1];
-  __shared__ float redm[kMergeThreads / 64];
+  __shared__ float red_m[kMergeWaves];
+  __shared__ float red_acc[kMergeWaves][kVecLanes][5];
   const int d = a.pv.d;
   const int nslices = d / kSlice;
   const int bh = blockIdx.x / nslices;
   const int slice = blockIdx.x % nslices;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int c0 = a.chunk_base[b], c1 = a.chunk_base[b + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  const int j = t % kVecLanes, k = t / kVecLanes;
+  const int lane = t & 63, wave = t >> 6;
 
-  // global reference maximum over the live chunks
-  float M = -INFINITY;
-  for (int c = c0 + threadIdx.x; c < c1; c += kMergeThreads) {
-    const int64_t i = int64_t(c) * a.Hq + h;
-    if (a.pl[i] > 0.0f) M = fmaxf(M, a.pm[i]);
-  }
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  if (lane == 0) redm[wave] = M;
-  __syncthreads();
-  M = redm[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, redm[w]);
-
-  float L = 0.0f;
-  float o[kSlice];
+  float M = -INFINITY;                 // running maximum over live chunks
+  float L = 0.0f;                      // this thread's share of the denominator
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int cb = c0; cb < c1; cb += kChunkLanes * kUnroll) {
+    float m[kUnroll], l[kUnroll];
+    float4 v[kUnroll];
 #pragma unroll
-  for (int j = 0; j < kSlice; ++j) o[j] = 0.0f;
-  for (int c = c0 + threadIdx.x; c < c1; c += kMergeThreads) {
-    const int64_t i = int64_t(c) * a.Hq + h;
-    const float l = a.pl[i];
-    if (!(l > 0.0f)) continue;
-    const float w = exp2f(a.pm[i] - M);
-    L += l * w;
-    const float4* src = reinterpret_cast<const float4*>(a.pacc + i * d + slice * kSlice);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = cb + k + kChunkLanes * u;
+      const bool ok = c < c1;
+      const int64_t i = int64_t(ok ? c : c0) * a.Hq + h;
+      m[u] = a.pm[i];
+      l[u] = ok ? a.pl[i] : 0.0f;
+      v[u] = *reinterpret_cast<const float4*>(a.pacc + i * d + slice * kSlice + 4 * j);
+    }
+    float bm = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kSlice / 4; ++j) {
-      const float4 v = src[j];
-      o[4 * j] += v.x * w;
-      o[4 * j + 1] += v.y * w;
-      o[4 * j + 2] += v.z * w;
-      o[4 * j + 3] += v.w * w;
+    for (int u = 0; u < kUnroll; ++u)
+      if (l[u] > 0.0f) bm = fmaxf(bm, m[u]);
+    bm = wave_max(bm);
+    if (lane == 0) red_m[wave] = bm;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) bm = fmaxf(bm, red_m[w]);
+    __syncthreads();
+    if (bm > M) {                      // rescale what earlier batches accumulated
+      const float r = exp2f(M - bm);   // 0 on the first live batch
+      L *= r;
+      acc.x *= r;
+      acc.y *= r;
+      acc.z *= r;
+      acc.w *= r;
+      M = bm;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (!(l[u] > 0.0f)) continue;
+      const float w = exp2f(m[u] - M);
+      L += l[u] * w;
+      acc.x += v[u].x * w;
+      acc.y += v[u].y * w;
+      acc.z += v[u].z * w;
+      acc.w += v[u].w * w;
     }
   }
-  // reduce over the block: within each wave by shuffles, then across waves
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off, 64);
+  // sum over the chunk lanes: within a wave (lanes j + 8k'), then across waves
+  float r5[5] = {acc.x, acc.y, acc.z, acc.w, L};
 #pragma unroll
-  for (int j = 0; j < kSlice; ++j)
-    for (int off = 32; off > 0; off >>= 1) o[j] += __shfl_xor(o[j], off, 64);
-  if (lane == 0) {
+  for (int e = 0; e < 5; ++e)
+    for (int off = kVecLanes; off < 64; off <<= 1) r5[e] += __shfl_xor(r5[e], off, 64);
+  if (lane < kVecLanes) {
 #pragma unroll
-    for (int j = 0; j < kSlice; ++j) red[wave][j] = o[j];
-    red[wave][kSlice] = L;
+    for (int e = 0; e < 5; ++e) red_acc[wave][lane][e] = r5[e];
   }
   __syncthreads();
-  if (threadIdx.x < kSlice + 1) {
-    float t = 0.0f;
-    for (int w = 0; w < kMergeThreads / 64; ++w) t += red[w][threadIdx.x];
-    red[0][threadIdx.x] = t;
+  if (t < kVecLanes) {
+    float s5[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w)
+#pragma unroll
+      for (int e = 0; e < 5; ++e) s5[e] += red_acc[w][t][e];
+    const float inv = 1.0f / s5[4];
+    *reinterpret_cast<float4*>(a.out + (int64_t(b) * a.Hq + h) * d + slice * kSlice + 4 * t) =
+        make_float4(s5[0] * inv, s5[1] * inv, s5[2] * inv, s5[3] * inv);
+    if (t == 0 && slice == 0) a.lse[int64_t(b) * a.Hq + h] = (M + log2f(s5[4])) * 0.69314718055994531f;
   }
-  __syncthreads();
-  const float Ltot = red[0][kSlice];
-  if (threadIdx.x < kSlice)
-    a.out[(int64_t(b) * a.Hq + h) * d + slice * kSlice + threadIdx.x] = red[0][threadIdx.x] / Ltot;
-  if (threadIdx.x == 0 && slice == 0)
-    a.lse[int64_t(b) * a.Hq + h] = (M + log2f(Ltot)) * 0.69314718055994531f;
 }
 
 }  // namespace

@@ -36,13 +36,11 @@
 //
 // Operand encodings (all exact, all in the f16 normal range: MFMA products
 // with subnormal f16 operands are not accumulated to full fp32 precision):
-//  * TQ3: a 3-bit code c is masked into mantissa bits k..k+2 of an f16 whose
-//    exponent encodes 1.0 (one AND-OR per two elements), then 1.0 is
-//    subtracted (one packed add): the operand is c * 2^(k-10), finite for any
-//    bit pattern, including unwritten poisoned slots.  The offset 3.5 is
-//    restored exactly: for keys through the MFMA accumulator input
-//    (-3.5 * sum q per group), for values through Z = sum_t P'[c][t],
-//    accumulated by an MFMA against ones.
+//  * TQ3: a 3-bit code c is masked into mantissa bits k..k+2 (1 <= k <= 7)
+//    of an f16 whose exponent encodes 1.0 (one AND-OR per two elements), then
+//    1 + 3.5 * 2^(k-10) is subtracted (one packed add): the operand is the
+//    centred code (c - 3.5) * 2^(k-10), exact and finite for any bit pattern,
+//    including unwritten poisoned slots.
 //  * FP8 E4M3 codes are widened by the hardware conversion to fp32 and packed
 //    to f16 (every E4M3 value is an f16 normal number).  Value rows past the
 //    valid tokens are zeroed because a poisoned byte may decode to NaN.
@@ -89,21 +87,26 @@ __device__ __forceinline__ uint32_t vgpr_one_pair() {
   return r;
 }
 
-__device__ __forceinline__ uint32_t minus_one(uint32_t biased) {
-  const half2v h = __builtin_bit_cast(half2v, biased) - half2v{_Float16(1.0f), _Float16(1.0f)};
+// f16 pair subtraction (x - c) with c given as the bits of two f16 values.
+__device__ __forceinline__ uint32_t sub_f16x2(uint32_t x, uint32_t c) {
+  const half2v h = __builtin_bit_cast(half2v, x) - __builtin_bit_cast(half2v, c);
   return __builtin_bit_cast(uint32_t, h);
 }
 
 // ---- TQ3 unit unpack -------------------------------------------------------
 // A unit is 8 consecutive codes (24 bits, code i at bit 3i; bits 24..31 are
-// ignored).  It becomes four dwords of f16 pairs holding c * 2^(k-10):
+// ignored).  It becomes four dwords of f16 pairs holding (c - 3.5) * 2^(k-10):
 //   slot:        0   1   2   3   4   5   6   7
-//   code index:  6   3   7   2   4   0   5   1     (kSlotCode)
-//   bit pos k:   0   7   3   4   0   4   3   7     (kSlotShift)
-// built from the unit rotated right by 18 and by 12 (the rotations put two
-// codes of each dword inside the two 10-bit mantissa fields).
-constexpr int kSlotCode[8] = {6, 3, 7, 2, 4, 0, 5, 1};
-constexpr int kSlotShift[8] = {0, 7, 3, 4, 0, 4, 3, 7};
+//   code index:  2   6   3   7   4   0   5   1     (kSlotCode)
+//   bit pos k:   6   2   7   3   3   7   3   7     (kSlotShift)
+// Dword j takes the unit rotated right by 0, 2, 9 or 12 bits, which puts two
+// codes inside the two 10-bit mantissa fields at positions k >= 1; the codes
+// are AND-ed into the mantissas of (1.0, 1.0) and (1 + 3.5 * 2^(k-10)) is
+// subtracted.  Both operands of the subtraction lie in [1, 2) and the
+// constant has at most 10 fraction bits because k >= 1, so the result is
+// exact and, as |c - 3.5| >= 1/2, an f16 normal number.
+constexpr int kSlotCode[8] = {2, 6, 3, 7, 4, 0, 5, 1};
+constexpr int kSlotShift[8] = {6, 2, 7, 3, 3, 7, 3, 7};
 // The same tables as nibbles (entry s at bits 4s..4s+3) for run-time lookups.
 constexpr uint32_t pack_nibbles(const int (&v)[8]) {
   uint32_t r = 0;
@@ -112,16 +115,24 @@ constexpr uint32_t pack_nibbles(const int (&v)[8]) {
 }
 constexpr uint32_t kSlotCodePacked = pack_nibbles(kSlotCode);
 constexpr uint32_t kSlotShiftPacked = pack_nibbles(kSlotShift);
-static_assert(kSlotCodePacked == 0x15042736u && kSlotShiftPacked == 0x73404370u, "slot tables");
+// f16 bits of 1 + 3.5 * 2^(k-10) = 1 + 7 * 2^(k-11)
+constexpr uint32_t center_bits(int k) { return 0x3C00u + (7u << (k - 1)); }
+constexpr uint32_t center_pair(int slot) {
+  return center_bits(kSlotShift[slot]) | (center_bits(kSlotShift[slot + 1]) << 16);
+}
+static_assert(center_pair(0) == 0x3C0E3CE0u && center_pair(2) == 0x3C1C3DC0u &&
+                  center_pair(4) == 0x3DC03C1Cu && center_pair(6) == 0x3DC03C1Cu,
+              "centering constants");
 
 __device__ __forceinline__ u32x4 tq3_unit_to_f16(uint32_t x, uint32_t one) {
-  const uint32_t r18 = __builtin_amdgcn_alignbit(x, x, 18);
+  const uint32_t r2 = __builtin_amdgcn_alignbit(x, x, 2);
+  const uint32_t r9 = __builtin_amdgcn_alignbit(x, x, 9);
   const uint32_t r12 = __builtin_amdgcn_alignbit(x, x, 12);
   u32x4 o;
-  o[0] = minus_one(and_or(r18, 0x03800007u, one));   // c6 -> bits 0..2,   c3 -> bits 23..25
-  o[1] = minus_one(and_or(r18, 0x00700038u, one));   // c7 -> bits 3..5,   c2 -> bits 20..22
-  o[2] = minus_one(and_or(r12, 0x00700007u, one));   // c4 -> bits 0..2,   c0 -> bits 20..22
-  o[3] = minus_one(and_or(r12, 0x03800038u, one));   // c5 -> bits 3..5,   c1 -> bits 23..25
+  o[0] = sub_f16x2(and_or(x, 0x001C01C0u, one), center_pair(0));     // c2 -> bits 6..8, c6 -> 18..20
+  o[1] = sub_f16x2(and_or(r2, 0x00380380u, one), center_pair(2));    // c3 -> bits 7..9, c7 -> 19..21
+  o[2] = sub_f16x2(and_or(r9, 0x03800038u, one), center_pair(4));    // c4 -> bits 3..5, c0 -> 23..25
+  o[3] = sub_f16x2(and_or(r12, 0x03800038u, one), center_pair(6));   // c5 -> bits 3..5, c1 -> 23..25
   return o;
 }
 
@@ -183,15 +194,25 @@ __device__ __forceinline__ short4v read_tr(const uint8_t* p) {
 }
 
 // B operand for the hi/lo PV MFMA: the lane's 4 value entries twice (read
-// twice from LDS so the operand lands in place without register copies).
+// twice from LDS so the operand lands in place without register copies; the
+// fence keeps the compiler from merging the two reads).
 __device__ __forceinline__ half8 value_operand(const uint8_t* p) {
   const u32x2 a = __builtin_bit_cast(u32x2, read_tr(p));
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p));
   const u32x4 d = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(half8, d);
 }
 
 // ---- cross-lane helpers -----------------------------------------------------
+// max without the NaN-quieting canonicalisation fmaxf adds (operands here are
+// never signalling NaNs).
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Orders one wave's LDS writes before its later LDS reads of other lanes' data.
 // The lanes of a wave issue LDS operations in program order, so no hardware
 // wait is needed; the fence only stops the compiler from moving accesses
@@ -204,9 +225,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Reduce over the four lanes {c, c+16, c+32, c+48} (same column, four quads).
 __device__ __forceinline__ float quad_max(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float quad_sum(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -312,11 +333,10 @@ struct SoftState {
 // Softmax step of one tile for the lane's column: scores s (fp32, already
 // multiplied by the column's score factor and masked) -> probabilities p;
 // rescales the accumulators when the reference max must rise.
-template <int NACC, int NZ>
+template <int NACC>
 __device__ __forceinline__ void softmax_step(SoftState& st, float s[4], float p[4],
-                                             f32x4 (&acc)[NACC], f32x4 (&zacc)[NZ], float* corr_lds,
-                                             int col, int quad) {
-  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                                             f32x4 (&acc)[NACC], float* corr_lds, int col, int quad) {
+  float tmax = vmax(vmax(s[0], s[1]), vmax(s[2], s[3]));
   tmax = quad_max(tmax);
   if (__any(tmax > st.m)) {
     const float m_new = tmax > st.m ? tmax + kHeadroom : st.m;
@@ -331,8 +351,6 @@ __device__ __forceinline__ void softmax_step(SoftState& st, float s[4], float p[
       const float c = corr_lds[4 * quad + i];
 #pragma unroll
       for (int j = 0; j < NACC; ++j) acc[j][i] *= c;
-#pragma unroll
-      for (int g = 0; g < NZ; ++g) zacc[g][i] *= c;
     }
     wave_lds_sync();
   }
@@ -343,17 +361,19 @@ __device__ __forceinline__ void softmax_step(SoftState& st, float s[4], float p[
   }
 }
 
-// Query row of column col -> MFMA B operands.  For MFMA g the lane's 8
+// Query rows -> MFMA B operands, NH kv-heads per wave.  Column col is query
+// head hq0 + col (live if col < NH * G) and belongs to kv-head jcol = col / G
+// of the wave; qop[j] holds the column only for j == jcol (zero otherwise), so
+// the MFMAs of the NH kv-heads accumulate into one D.  For MFMA g the lane's 8
 // k-slots hold head dims base_dim(g) + perm(s), s = 0..7 (8 consecutive dims,
 // read as one 16-byte load); shift(s) is the slot's extra power-of-two
-// exponent.  Columns past the kv-head's G query heads are zero.  Returns the
-// column's exponent E.
-template <int NG, typename BaseDim, typename SlotPerm, typename SlotShift>
-__device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, int col, int G,
-                                          half8 (&qop)[NG], BaseDim base_dim, SlotPerm perm,
-                                          SlotShift shift) {
+// exponent.  Returns the column's exponent E.
+template <int NG, int NH, typename BaseDim, typename SlotPerm, typename SlotShift>
+__device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, int col, int ncol,
+                                          int jcol, half8 (&qop)[NH][NG], BaseDim base_dim,
+                                          SlotPerm perm, SlotShift shift) {
   constexpr int D = 32 * NG;
-  const bool live = col < G;
+  const bool live = col < ncol;
   const uint16_t* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (live ? col : 0)) * D;
   float qv[NG][8];
   float amax = 0.0f;
@@ -371,56 +391,69 @@ __device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, i
   amax = quad_max(amax);
   const int E = q_shift(amax);
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
+  for (int j = 0; j < NH; ++j)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qop[g][s] = _Float16(__builtin_amdgcn_ldexpf(qv[g][s], E + shift(s)));
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qop[j][g][s] = jcol == j ? _Float16(__builtin_amdgcn_ldexpf(qv[g][s], E + shift(s))) : _Float16(0.0f);
   return E;
 }
 
 // LDS images of the two work-item kinds (one of them per workgroup).
-template <int NG>
+template <int NG, int NH>
 struct Tq3Lds {
   static constexpr int D = 32 * NG;
-  static constexpr int VROW = 2 * D + 16;       // value-tile row stride (bytes)
-  static constexpr int KST = 4 * NG;            // dwords per token in the key staging
+  static constexpr int VROW = 2 * D + 32;       // value-tile row stride (bytes, padded)
+  static constexpr int KST = 4 * NG + 4;        // dwords per token in the key staging (padded)
   static constexpr int SD = 16 * NG;            // scale dwords of a tile (K then V)
   struct Wave {
-    alignas(16) uint32_t kst[16 * KST];         // key units, [token][unit][group]
-    alignas(16) uint8_t vt[16 * VROW];          // value tile, [token][D] f16
-    alignas(16) uint32_t sc[SD];                // tile scales: K [16][NG] f16, then V
+    alignas(16) uint32_t kst[NH][16 * KST];     // key units, [token][unit][group]
+    alignas(16) uint8_t vt[NH][16 * VROW];      // value tiles, [token][D] f16
+    alignas(16) uint32_t sc[NH][SD];            // tile scales: K [16][NG] f16, then V
     float corr[16];
   };
   int32_t ent[kMaxChunkPages];                  // page-table entries of the work item
   Wave w[kWaves];
 };
 
-template <int NG>
+template <int NG, int NH>
 struct Fp8Lds {
   static constexpr int D = 32 * NG;
-  static constexpr int VROW = 2 * D + 16;
+  static constexpr int VROW = 2 * D + 32;
   struct Wave {
-    alignas(16) uint8_t vt[16 * VROW];
+    alignas(16) uint8_t vt[NH][16 * VROW];
     float corr[16];
   };
   int32_t ent[kMaxChunkPages];
   Wave w[kWaves];
 };
 
+// Accumulator of head j for output row i: acc[j * NT + jt][i]; rows of the
+// other heads of the wave hold unused sums.
+template <int NH, int NT>
+__device__ __forceinline__ float pick_head(const f32x4 (&acc)[NH * NT], int jc, int jt, int i) {
+  float v = acc[jt][i];
+#pragma unroll
+  for (int j = 1; j < NH; ++j) v = jc == j ? acc[j * NT + jt][i] : v;
+  return v;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// TQ3 work item: one wave per kv-head
+// TQ3 work item: each wave owns NH kv-heads
 // ---------------------------------------------------------------------------
-template <int NG, int R>
-__device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it, Tq3Lds<NG>& lds) {
+template <int NG, int NH, int R>
+__device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it, Tq3Lds<NG, NH>& lds) {
   constexpr int D = 32 * NG;
-  constexpr int GPL = NG > 4 ? NG / 4 : 1;      // groups each lane loads
-  constexpr int NT = D / 16;                    // PV N-tiles
-  constexpr int VROW = Tq3Lds<NG>::VROW;
-  constexpr int KST = Tq3Lds<NG>::KST;
+  constexpr int GPL = NG > 4 ? NG / 4 : 1;      // groups each lane loads per head
+  constexpr int NT = D / 16;                    // PV N-tiles per head
+  constexpr int VROW = Tq3Lds<NG, NH>::VROW;
+  constexpr int KST = Tq3Lds<NG, NH>::KST;
   constexpr int ROWB = 3 * D / 8;               // code bytes per token row
-  constexpr int SD = Tq3Lds<NG>::SD;
-  constexpr int SPL = (SD + 63) / 64;           // scale dwords each lane loads
+  constexpr int SD = Tq3Lds<NG, NH>::SD;
+  constexpr int SPL = (SD + 63) / 64;           // scale dwords each lane loads per head
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -428,82 +461,73 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   const int quad = lane >> 4;
   const PoolView& pv = a.pv;
   stage_entries(lds.ent, a, it);
-  const int hk = blockIdx.y * kWaves + wave;
-  if (hk >= pv.Hkv) return;
+  const int hk0 = (blockIdx.y * kWaves + wave) * NH;
+  if (hk0 >= pv.Hkv) return;
   const int G = a.Hq / pv.Hkv;
-  const int hq0 = hk * G;
+  const int ncol = NH * G;
+  const int hq0 = hk0 * G;
+  const int jcol = col < ncol ? col / G : 0;    // kv-head (within the wave) of column col
   auto& W = lds.w[wave];
   const uint32_t one = vgpr_one_pair();
 
-  // ---- query operands and the key-offset bias
-  half8 qop[NG];
-  f32x4 bias[NG];
-  float F;
-  {
-    const int E = load_query<NG>(
-        a, it.b, hq0, col, G, qop, [&](int g) { return 32 * g + 8 * quad; },
-        [](int s) { return kSlotCode[s]; }, [](int s) { return 7 - kSlotShift[s]; });
-    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
-    const half8 ones = __builtin_bit_cast(half8, tq3_unit_to_f16(0x00249249u, one));
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, qop[g], z, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bias[g][i] = -3.5f * s[i];
-    }
-  }
+  // ---- query operands: slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s],
+  // scaled by 2^(E + 7 - kSlotShift[s]) against the key slot's 2^(k-10)
+  half8 qop[NH][NG];
+  const int E = load_query<NG, NH>(
+      a, it.b, hq0, col, ncol, jcol, qop, [&](int g) { return 32 * g + 8 * quad; },
+      [](int s) { return kSlotCode[s]; }, [](int s) { return 7 - kSlotShift[s]; });
+  const float F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
 
-  f32x4 acc[NT];
-  f32x4 zacc[NG];
+  f32x4 acc[NH * NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int g = 0; g < NG; ++g) zacc[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NH * NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
-  const half8 ones8 = {_Float16(1.0f), _Float16(1.0f), _Float16(1.0f), _Float16(1.0f),
-                       _Float16(1.0f), _Float16(1.0f), _Float16(1.0f), _Float16(1.0f)};
 
   // Per-lane byte offsets inside a record (the tile's first token is added per
   // tile).  Lane (token col, quad) loads group quad (+4i) of that token; with
   // fewer than 4 groups the spare quads repeat a real group's load, and spare
   // lanes of the scale load repeat a real scale dword (results unused).
-  int32_t code_off[GPL], sc_off[SPL];
-  {
-    const int32_t cb = int32_t(tq3_codes_off(pv, hk, 0));
-    const int32_t kb = int32_t(tq3_scale_off(pv, hk, 0));
-    const int32_t vb = int32_t(tq3_scale_off(pv, hk, 1));
+  int32_t code_off[NH][GPL], sc_off[NH][SPL];
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) code_off[i] = cb + col * ROWB + 12 * ((quad + 4 * i) % NG);
+  for (int j = 0; j < NH; ++j) {
+    const int32_t cb = int32_t(tq3_codes_off(pv, hk0 + j, 0));
+    const int32_t kb = int32_t(tq3_scale_off(pv, hk0 + j, 0));
+    const int32_t vb = int32_t(tq3_scale_off(pv, hk0 + j, 1));
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) code_off[j][i] = cb + col * ROWB + 12 * ((quad + 4 * i) % NG);
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       const int e = (lane + 64 * i) & (SD - 1);
-      sc_off[i] = e < 8 * NG ? kb + 4 * e : vb + 4 * (e - 8 * NG);
+      sc_off[j][i] = e < 8 * NG ? kb + 4 * e : vb + 4 * (e - 8 * NG);
     }
   }
   const int32_t vcode_delta = pv.P * ROWB;      // V codes follow the K codes
 
   struct Raw {
-    uint32_t kc[GPL][3];                        // K codes: one 12-byte group of token col
-    uint32_t vc[GPL][3];                        // V codes, same group and token
-    uint32_t sc[SPL];                           // the lane's share of the tile's scales
+    uint32_t kc[NH][GPL][3];                    // K codes: one 12-byte group of token col
+    uint32_t vc[NH][GPL][3];                    // V codes, same group and token
+    uint32_t sc[NH][SPL];                       // the lane's share of the tile's scales
   };
   auto load = [&](const Cursor& c, Raw& r) {
     const uint8_t* page = entry_page(pv, lds.ent, c.page);
     const int t0 = 16 * c.sub;
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off[i] + t0 * ROWB);
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + code_off[i] + t0 * ROWB + vcode_delta);
+    for (int j = 0; j < NH; ++j) {
 #pragma unroll
-      for (int x = 0; x < 3; ++x) {
-        r.kc[i][x] = kp[x];
-        r.vc[i][x] = vp[x];
+      for (int i = 0; i < GPL; ++i) {
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off[j][i] + t0 * ROWB);
+        const uint32_t* vp =
+            reinterpret_cast<const uint32_t*>(page + code_off[j][i] + t0 * ROWB + vcode_delta);
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+          r.kc[j][i][x] = kp[x];
+          r.vc[j][i][x] = vp[x];
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < SPL; ++i)
-      r.sc[i] = *reinterpret_cast<const uint32_t*>(page + sc_off[i] + 2 * t0 * NG);
+      for (int i = 0; i < SPL; ++i)
+        r.sc[j][i] = *reinterpret_cast<const uint32_t*>(page + sc_off[j][i] + 2 * t0 * NG);
+    }
   };
   auto scale_of = [](const uint32_t* w, int i, int g) {
     const int e = i * NG + g;
@@ -516,38 +540,47 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   auto process = [&](Raw& raw, const Cursor& c, auto refill) {
     const int nvalid = valid_in_tile(c, tg);
 #pragma unroll
-    for (int i = 0; i < SPL; ++i)
-      if (lane + 64 * i < SD) W.sc[lane + 64 * i] = raw.sc[i];
+    for (int j = 0; j < NH; ++j) {
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int g = quad + 4 * i;
-      if (g < NG) {
-        uint32_t u[4];
-        tq3_split_units(raw.kc[i], u);
+      for (int i = 0; i < SPL; ++i)
+        if (lane + 64 * i < SD) W.sc[j][lane + 64 * i] = raw.sc[j][i];
 #pragma unroll
-        for (int un = 0; un < 4; ++un) W.kst[col * KST + un * NG + g] = u[un];
-        tq3_split_units(raw.vc[i], u);
+      for (int i = 0; i < GPL; ++i) {
+        const int g = quad + 4 * i;
+        if (g < NG) {
+          uint32_t u[4];
+          tq3_split_units(raw.kc[j][i], u);
 #pragma unroll
-        for (int un = 0; un < 4; ++un)
-          *reinterpret_cast<u32x4*>(W.vt + col * VROW + 2 * (32 * g + 8 * un)) = tq3_unit_to_f16(u[un], one);
+          for (int un = 0; un < 4; ++un) W.kst[j][col * KST + un * NG + g] = u[un];
+          tq3_split_units(raw.vc[j][i], u);
+#pragma unroll
+          for (int un = 0; un < 4; ++un)
+            *reinterpret_cast<u32x4*>(W.vt[j] + col * VROW + 2 * (32 * g + 8 * un)) =
+                tq3_unit_to_f16(u[un], one);
+        }
       }
     }
     refill(raw);
     wave_lds_sync();
 
-    // ---- scales of the lane's 4 tokens
+    // ---- scales of the lane's 4 tokens for its column's kv-head
     uint32_t skw[2 * NG], svw[2 * NG];
 #pragma unroll
     for (int x = 0; x < 2 * NG; ++x) {
-      skw[x] = W.sc[2 * quad * NG + x];
-      svw[x] = W.sc[8 * NG + 2 * quad * NG + x];
+      skw[x] = W.sc[jcol][2 * quad * NG + x];
+      svw[x] = W.sc[jcol][8 * NG + 2 * quad * NG + x];
     }
-    // ---- QK^T per group, scaled by the per-token group scale
+    // ---- QK^T per group (the NH kv-heads into one D), scaled per token and group
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const half8 kop = __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[col * KST + quad * NG + g], one));
-      const f32x4 dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[g], bias[g], 0, 0, 0);
+      f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const half8 kop =
+            __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[j][col * KST + quad * NG + g], one));
+        dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[j][g], dg, 0, 0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dg[i], scale_of(skw, i, g), s[i]);
     }
@@ -559,9 +592,9 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
         if (4 * quad + i >= nvalid) s[i] = -INFINITY;
     }
     float p[4];
-    softmax_step(st, s, p, acc, zacc, W.corr, col, quad);
+    softmax_step(st, s, p, acc, W.corr, col, quad);
 
-    // ---- P' = p * value scale (hi/lo f16), Z += P' * 1, acc += P' * V
+    // ---- P' = p * value scale (hi/lo f16), acc_j += P' * V_j
     half8 pp[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -577,14 +610,15 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
           if (4 * quad + i >= nvalid) sv[i] = 0;   // masked token (its scale may be NaN)
       }
       pp[g] = pprime_hi_lo(p, sv);
-      zacc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[g], ones8, zacc[g], 0, 0, 0);
     }
     const int row = 4 * quad + (col >> 2);
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) {
-      const half8 bv = value_operand(W.vt + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[jt >> 1], bv, acc[jt], 0, 0, 0);
-    }
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+        acc[j * NT + jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[jt >> 1], bv, acc[j * NT + jt], 0, 0, 0);
+      }
     wave_lds_sync();
   };
   run_tiles<R, Raw>(tg, load, process);
@@ -592,33 +626,34 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   // ---- write this wave's partial state: l per column, acc in true units
   const float lcol = quad_sum(st.l);
   const int64_t base_h = int64_t(it.chunk) * a.Hq + hq0;
-  if (quad == 0 && col < G) {
+  if (quad == 0 && col < ncol) {
     a.pm[base_h + col] = st.m;
     a.pl[base_h + col] = lcol;
   }
   // accumulator column col of N-tile jt is dim 16*jt + col in slot order;
-  // slot s of a unit holds code kSlotCode[s] scaled by 2^(kSlotShift[s]-10)
+  // slot s of a unit holds dim kSlotCode[s] scaled by 2^(kSlotShift[s]-10)
   const int slot = col & 7;
   const int dim_in_unit = int(kSlotCodePacked >> (4 * slot)) & 15;
   const float up = __builtin_amdgcn_ldexpf(1.0f, 10 - (int(kSlotShiftPacked >> (4 * slot)) & 15));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
-    if (c >= G) continue;
+    if (c >= ncol) continue;
+    const int jc = c / G;
     float* dst = a.pacc + (base_h + c) * D + (col & 8) + dim_in_unit;
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) dst[16 * jt] = acc[jt][i] * up - 3.5f * zacc[jt >> 1][i];
+    for (int jt = 0; jt < NT; ++jt) dst[16 * jt] = pick_head<NH, NT>(acc, jc, jt, i) * up;
   }
 }
 
 // ---------------------------------------------------------------------------
-// FP8 work item: one wave per kv-head
+// FP8 work item: each wave owns NH kv-heads
 // ---------------------------------------------------------------------------
-template <int NG, int R>
-__device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it, Fp8Lds<NG>& lds) {
+template <int NG, int NH, int R>
+__device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it, Fp8Lds<NG, NH>& lds) {
   constexpr int D = 32 * NG;
   constexpr int NT = D / 16;
-  constexpr int VROW = Fp8Lds<NG>::VROW;
+  constexpr int VROW = Fp8Lds<NG, NH>::VROW;
   constexpr int LB = D / 4;                     // bytes of a row each lane loads
 
   const int lane = threadIdx.x & 63;
@@ -627,175 +662,209 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   const int quad = lane >> 4;
   const PoolView& pv = a.pv;
   stage_entries(lds.ent, a, it);
-  const int hk = blockIdx.y * kWaves + wave;
-  if (hk >= pv.Hkv) return;
+  const int hk0 = (blockIdx.y * kWaves + wave) * NH;
+  if (hk0 >= pv.Hkv) return;
   const int G = a.Hq / pv.Hkv;
-  const int hq0 = hk * G;
+  const int ncol = NH * G;
+  const int hq0 = hk0 * G;
+  const int jcol = col < ncol ? col / G : 0;
   auto& W = lds.w[wave];
 
   // ---- query operand: MFMA r, lane (col, quad), slot s <-> dim quad*LB + 8r + s
-  half8 qop[NG];
-  float F;
-  {
-    const int E = load_query<NG>(
-        a, it.b, hq0, col, G, qop, [&](int r) { return quad * LB + 8 * r; }, [](int s) { return s; },
-        [](int) { return 0; });
-    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
-  }
+  half8 qop[NH][NG];
+  const int E = load_query<NG, NH>(
+      a, it.b, hq0, col, ncol, jcol, qop, [&](int r) { return quad * LB + 8 * r; },
+      [](int s) { return s; }, [](int) { return 0; });
+  const float F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
 
-  f32x4 acc[NT];
-  f32x4 zacc[1];
+  f32x4 acc[NH * NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  zacc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NH * NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
 
-  const int32_t code_off = int32_t(fp8_codes_off(pv, hk, 0)) + col * D + quad * LB;
-  const int32_t ks_off = int32_t(fp8_scale_off(pv, hk, 0));
-  const int32_t vs_off = int32_t(fp8_scale_off(pv, hk, 1));
+  int32_t code_off[NH], ks_off[NH], vs_off[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    code_off[j] = int32_t(fp8_codes_off(pv, hk0 + j, 0)) + col * D + quad * LB;
+    ks_off[j] = int32_t(fp8_scale_off(pv, hk0 + j, 0));
+    vs_off[j] = int32_t(fp8_scale_off(pv, hk0 + j, 1));
+  }
   const int32_t vcode_delta = pv.P * D;
   struct Raw {
-    uint32_t kw[LB / 4];
-    uint32_t vw[LB / 4];
-    float sigk, sigv;
+    uint32_t kw[NH][LB / 4];
+    uint32_t vw[NH][LB / 4];
+    float sigk[NH], sigv[NH];
   };
   auto load = [&](const Cursor& c, Raw& r) {
     const uint8_t* page = entry_page(pv, lds.ent, c.page);
     const int t0 = 16 * c.sub;
-    const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off + t0 * D);
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + code_off + t0 * D + vcode_delta);
 #pragma unroll
-    for (int x = 0; x < LB / 4; ++x) {
-      r.kw[x] = kp[x];
-      r.vw[x] = vp[x];
+    for (int j = 0; j < NH; ++j) {
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off[j] + t0 * D);
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + code_off[j] + t0 * D + vcode_delta);
+#pragma unroll
+      for (int x = 0; x < LB / 4; ++x) {
+        r.kw[j][x] = kp[x];
+        r.vw[j][x] = vp[x];
+      }
+      r.sigk[j] = *reinterpret_cast<const float*>(page + ks_off[j]);
+      r.sigv[j] = *reinterpret_cast<const float*>(page + vs_off[j]);
     }
-    r.sigk = *reinterpret_cast<const float*>(page + ks_off);
-    r.sigv = *reinterpret_cast<const float*>(page + vs_off);
   };
   const TileGeom tg = tile_geom(it, pv.P / 16);
 
   auto process = [&](Raw& raw, const Cursor& c, auto refill) {
     const int nvalid = valid_in_tile(c, tg);
-    // ---- values: f16 rows of the LDS tile (rows past the valid tokens zeroed)
+    // ---- values: f16 rows of the LDS tiles (rows past the valid tokens zeroed)
     const bool vrow_ok = col < nvalid;
 #pragma unroll
-    for (int i = 0; i < LB / 4; i += 2) {
-      const u32x2 a0 = fp8x4_to_f16(raw.vw[i]);
-      const u32x2 a1 = fp8x4_to_f16(raw.vw[i + 1]);
-      u32x4 o = {a0[0], a0[1], a1[0], a1[1]};
-      if (!vrow_ok) o = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(W.vt + col * VROW + 2 * (quad * LB + 4 * i)) = o;
-    }
-    // ---- keys to f16 MFMA operands
-    half8 kop[NG];
+    for (int j = 0; j < NH; ++j)
 #pragma unroll
-    for (int r = 0; r < NG; ++r) {
-      const u32x2 k0 = fp8x4_to_f16(raw.kw[2 * r]);
-      const u32x2 k1 = fp8x4_to_f16(raw.kw[2 * r + 1]);
-      const u32x4 ku = {k0[0], k0[1], k1[0], k1[1]};
-      kop[r] = __builtin_bit_cast(half8, ku);
+      for (int i = 0; i < LB / 4; i += 2) {
+        const u32x2 a0 = fp8x4_to_f16(raw.vw[j][i]);
+        const u32x2 a1 = fp8x4_to_f16(raw.vw[j][i + 1]);
+        u32x4 o = {a0[0], a0[1], a1[0], a1[1]};
+        if (!vrow_ok) o = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(W.vt[j] + col * VROW + 2 * (quad * LB + 4 * i)) = o;
+      }
+    // ---- keys to f16 MFMA operands
+    half8 kop[NH][NG];
+    float sigk[NH], sigv[NH];
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+#pragma unroll
+      for (int r = 0; r < NG; ++r) {
+        const u32x2 k0 = fp8x4_to_f16(raw.kw[j][2 * r]);
+        const u32x2 k1 = fp8x4_to_f16(raw.kw[j][2 * r + 1]);
+        const u32x4 ku = {k0[0], k0[1], k1[0], k1[1]};
+        kop[j][r] = __builtin_bit_cast(half8, ku);
+      }
+      sigk[j] = raw.sigk[j];
+      sigv[j] = raw.sigv[j];
     }
-    const float sigk = raw.sigk, sigv = raw.sigv;
     refill(raw);
     wave_lds_sync();
 
-    // ---- QK^T over all dims (page-head scale applied once)
-    f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ---- QK^T over all dims, per kv-head (page-head scale applied per column)
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < NG; ++r) dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[r], qop[r], dsum, 0, 0, 0);
-    const float fk = F * sigk;
-    float s[4];
+    for (int j = 0; j < NH; ++j) {
+      f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = dsum[i] * fk;
+      for (int r = 0; r < NG; ++r)
+        dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[j][r], qop[j][r], dsum, 0, 0, 0);
+      const float fk = jcol == j ? F * sigk[j] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dsum[i], fk, s[i]);
+    }
     if (nvalid < 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (4 * quad + i >= nvalid) s[i] = -INFINITY;
     }
     float p[4];
-    softmax_step(st, s, p, acc, zacc, W.corr, col, quad);
+    softmax_step(st, s, p, acc, W.corr, col, quad);
 
-    const half8 pp = pprime_hi_lo_uniform(p, sigv);
+    float sv = sigv[0];
+#pragma unroll
+    for (int j = 1; j < NH; ++j) sv = jcol == j ? sigv[j] : sv;
+    const half8 pp = pprime_hi_lo_uniform(p, sv);
     const int row = 4 * quad + (col >> 2);
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) {
-      const half8 bv = value_operand(W.vt + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp, bv, acc[jt], 0, 0, 0);
-    }
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+        acc[j * NT + jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp, bv, acc[j * NT + jt], 0, 0, 0);
+      }
     wave_lds_sync();
   };
   run_tiles<R, Raw>(tg, load, process);
 
   const float lcol = quad_sum(st.l);
   const int64_t base_h = int64_t(it.chunk) * a.Hq + hq0;
-  if (quad == 0 && col < G) {
+  if (quad == 0 && col < ncol) {
     a.pm[base_h + col] = st.m;
     a.pl[base_h + col] = lcol;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
-    if (c >= G) continue;
+    if (c >= ncol) continue;
+    const int jc = c / G;
     float* dst = a.pacc + (base_h + c) * D;
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) dst[16 * jt + col] = acc[jt][i];
+    for (int jt = 0; jt < NT; ++jt) dst[16 * jt + col] = pick_head<NH, NT>(acc, jc, jt, i);
   }
 }
 
 // ---------------------------------------------------------------------------
 // One launch for both formats: workgroup x takes work item x (FP8 or TQ3).
 // ---------------------------------------------------------------------------
-constexpr int kRingTq3 = 4;   // TQ3 tiles in flight per wave
-constexpr int kRingFp8 = 2;   // FP8 tiles in flight per wave
+template <int NG, int NH>
+struct PartialCfg {
+  static constexpr int kRingTq3 = NH == 1 && NG <= 4 ? 4 : 2;   // TQ3 tiles in flight per wave
+  static constexpr int kRingFp8 = NH == 1 ? 2 : 1;   // FP8 tiles in flight per wave
+  static constexpr size_t kSmem =
+      sizeof(Tq3Lds<NG, NH>) > sizeof(Fp8Lds<NG, NH>) ? sizeof(Tq3Lds<NG, NH>) : sizeof(Fp8Lds<NG, NH>);
+};
 
-template <int NG>
-constexpr size_t smem_bytes() {
-  return sizeof(Tq3Lds<NG>) > sizeof(Fp8Lds<NG>) ? sizeof(Tq3Lds<NG>) : sizeof(Fp8Lds<NG>);
-}
-
-template <int NG>
-__global__ void __launch_bounds__(kThreads) partial_mixed(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<NG>()];
+// At least two waves per SIMD (256 VGPRs) except for head dim 256, which
+// keeps its registers unspilled at one wave per SIMD.
+template <int NG, int NH>
+__global__ void __launch_bounds__(kThreads, NG == 8 ? 1 : 2) partial_mixed(DecodeArgs a) {
+  using Cfg = PartialCfg<NG, NH>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
   const WorkItem it = a.items[blockIdx.x];
   if (it.fmt == 0)
-    fp8_item<NG, kRingFp8>(a, it, *reinterpret_cast<Fp8Lds<NG>*>(smem));
+    fp8_item<NG, NH, Cfg::kRingFp8>(a, it, *reinterpret_cast<Fp8Lds<NG, NH>*>(smem));
   else
-    tq3_item<NG, kRingTq3>(a, it, *reinterpret_cast<Tq3Lds<NG>*>(smem));
+    tq3_item<NG, NH, Cfg::kRingTq3>(a, it, *reinterpret_cast<Tq3Lds<NG, NH>*>(smem));
 }
 
 namespace {
 
 template <typename F>
-hipError_t with_kernel(int d, F f) {
+hipError_t with_kernel(int d, int nh, F f) {
+  if (nh == 2) {
+    switch (d) {
+      case 32: return f(partial_mixed<1, 2>);
+      case 64: return f(partial_mixed<2, 2>);
+      case 128: return f(partial_mixed<4, 2>);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (d) {
-    case 32: return f(partial_mixed<1>);
-    case 64: return f(partial_mixed<2>);
-    case 128: return f(partial_mixed<4>);
-    case 256: return f(partial_mixed<8>);
+    case 32: return f(partial_mixed<1, 1>);
+    case 64: return f(partial_mixed<2, 1>);
+    case 128: return f(partial_mixed<4, 1>);
+    case 256: return f(partial_mixed<8, 1>);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-// Grid: one workgroup per (work item, block of kWaves kv-heads); each wave
-// owns one kv-head of the item.
+// Grid: one workgroup per (work item, block of kWaves * NH kv-heads); each
+// wave owns NH kv-heads of the item (NH from heads_per_wave).
 hipError_t launch_partial(const DecodeArgs& a, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
-  const dim3 grid(unsigned(a.n_items), unsigned((a.pv.Hkv + kWaves - 1) / kWaves));
-  return with_kernel(a.pv.d, [&](auto kernel) {
+  const int nh = heads_per_wave(a.pv.d, a.pv.Hkv, a.Hq / a.pv.Hkv);
+  const int per_block = kWaves * nh;
+  const dim3 grid(unsigned(a.n_items), unsigned((a.pv.Hkv + per_block - 1) / per_block));
+  return with_kernel(a.pv.d, nh, [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
   });
 }
 
-hipError_t partial_resident_waves(int d, int* waves) {
+hipError_t partial_resident_waves(int d, int nh, int* waves) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  return with_kernel(d, [&](auto kernel) {
+  return with_kernel(d, nh, [&](auto kernel) {
     int blocks = 0;
     const hipError_t r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kThreads, 0);
     if (r == hipSuccess) *waves = cus * blocks * kWaves;

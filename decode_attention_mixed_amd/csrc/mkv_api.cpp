@@ -119,7 +119,7 @@ struct mkv_pool {
   int32_t sched_Hq = 0;
   std::vector<int32_t> sched_ids;
   mkv::Schedule sched;
-  int32_t target_waves = 2048;   // resident partial-kernel waves on this device
+  int32_t target_waves[2] = {2048, 1024};   // resident partial-kernel waves, 1 or 2 heads per wave
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
@@ -213,9 +213,10 @@ mkv_status prof_collect(mkv_pool* p) {
 // Split-K policy of a pool: balanced chunks for the device's resident
 // partial-kernel waves.  Environment overrides (for tuning): MKV_CHUNK_PAGES
 // (fixed chunk length), MKV_TARGET_WAVES, MKV_FP8_PAGE_COST.
-mkv::SchedPolicy pool_policy(const mkv_pool* p) {
+mkv::SchedPolicy pool_policy(const mkv_pool* p, int32_t Hq) {
   mkv::SchedPolicy pol;
-  pol.target_waves = p->target_waves;
+  const mkv::Geom& g = p->meta.geom();
+  pol.target_waves = p->target_waves[mkv::heads_per_wave(g.d, g.Hkv, Hq / g.Hkv) - 1];
   if (const char* e = std::getenv("MKV_CHUNK_PAGES")) pol.fixed_chunk_pages = std::max(0, std::atoi(e));
   if (const char* e = std::getenv("MKV_TARGET_WAVES")) pol.target_waves = std::max(1, std::atoi(e));
   if (const char* e = std::getenv("MKV_FP8_PAGE_COST")) pol.fp8_page_cost = float(std::atof(e));
@@ -265,10 +266,13 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
   };
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
-  int waves = 0;
-  e = mkv::partial_resident_waves(desc->head_dim, &waves);
-  if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
-  if (waves > 0) p->target_waves = waves;
+  for (int nh = 1; nh <= 2; ++nh) {
+    if (nh == 2 && desc->head_dim > 128) break;
+    int waves = 0;
+    e = mkv::partial_resident_waves(desc->head_dim, nh, &waves);
+    if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
+    if (waves > 0) p->target_waves[nh - 1] = waves;
+  }
   if (device_mem) {
     if (bytes < p->lay.total) return cleanup(MKV_ERANGE, "device buffer smaller than mkv_pool_bytes");
     if (reinterpret_cast<uintptr_t>(device_mem) % 256)
@@ -367,7 +371,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   if (!same) {
     std::string err;
     mkv::Schedule sc;
-    int st = p->meta.build_schedule(seq_ids, B, Hq, pool_policy(p), &sc, &err);
+    int st = p->meta.build_schedule(seq_ids, B, Hq, pool_policy(p, Hq), &sc, &err);
     if (st) return set_err(mkv_status(st), err);
     mkv_status r = p->wait_staging();
     if (r) return r;

@@ -42,8 +42,9 @@ hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_p
 hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
                          uint8_t* dst, int64_t slot_bytes, hipStream_t s);
 hipError_t launch_partial(const DecodeArgs& a, hipStream_t s);
-// Waves of the partial kernel (head dim d) resident on the current device at once.
-hipError_t partial_resident_waves(int d, int* waves);
+// Waves of the partial kernel (head dim d, nh kv-heads per wave) resident on
+// the current device at once.
+hipError_t partial_resident_waves(int d, int nh, int* waves);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace mkv

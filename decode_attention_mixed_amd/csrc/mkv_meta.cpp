@@ -202,8 +202,9 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     per = std::min<int64_t>(per, kMaxChunkPages);
     return (n + per - 1) / per;
   };
+  const int32_t heads_per_block = kWavesPerWorkgroup * heads_per_wave(g_.d, g_.Hkv, Hq / g_.Hkv);
   const int64_t waves_per_item =
-      int64_t(kWavesPerWorkgroup) * ((g_.Hkv + kWavesPerWorkgroup - 1) / kWavesPerWorkgroup);
+      int64_t(kWavesPerWorkgroup) * ((g_.Hkv + heads_per_block - 1) / heads_per_block);
   const int64_t target_items = std::max<int64_t>(1, pol.target_waves / waves_per_item);
   double budget = std::max(1.0, total_cost / double(target_items));
   std::vector<int64_t> k8(static_cast<size_t>(B)), k3(static_cast<size_t>(B));

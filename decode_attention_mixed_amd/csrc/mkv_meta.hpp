@@ -81,8 +81,16 @@ struct WorkItem {
 // page-table entries in a fixed LDS array of this length.
 constexpr int32_t kMaxChunkPages = 256;
 // Waves per partial-kernel workgroup; a workgroup takes one work item and
-// this many kv-heads of it (one per wave).
+// kWavesPerWorkgroup * heads_per_wave kv-heads of it.
 constexpr int32_t kWavesPerWorkgroup = 4;
+
+// kv-heads per partial-kernel wave: two when the query columns of two
+// kv-heads fit the 16 MFMA columns (G <= 8), the kv-head count is even and
+// d <= 128 (register budget); else one.  The work that does not depend on the
+// kv-head (softmax, probability scaling) is then shared by two heads.
+inline int32_t heads_per_wave(int32_t d, int32_t Hkv, int32_t G) {
+  return (d <= 128 && 2 * G <= 16 && Hkv % 2 == 0) ? 2 : 1;
+}
 
 // Split-K policy.  By default the page list of each (sequence, format) is cut
 // into near-equal chunks so that all items of a batch cost about the same and
