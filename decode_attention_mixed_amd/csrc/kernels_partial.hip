@@ -11,11 +11,11 @@
 //
 // Work decomposition.  One launch covers both formats: one workgroup (4
 // wave64) per (work item = chunk of at most 256 pages of one format of one
-// sequence, block of 4 kv-heads).  The workgroup first copies the chunk's
-// page-table entries to LDS; then each wave owns one kv-head and walks every
-// 16-token tile of the chunk on its own, with the raw bytes of the next R
-// tiles in flight (a ring of register buffers), and writes one partial state
-// per query head of its kv-head.
+// sequence, block of NH kv-heads).  The workgroup first copies the chunk's
+// page-table entries to LDS; each wave then walks its quarter of the chunk's
+// 16-token tiles for the NH kv-heads, with the raw bytes of the next R tiles
+// in flight (a ring of register buffers).  The four waves' softmax states are
+// combined through LDS and one partial state per query head is written.
 //
 // Tile computation (16 tokens x up to 16 query-head columns; column c is
 // query head hk*G + c of kv-head hk, columns c >= G are zero):
@@ -26,13 +26,13 @@
 //  * Softmax: a reference maximum per column, raised (with headroom) only when
 //    a tile exceeds it, so exp2 arguments stay <= 0 and rescaling the
 //    accumulator is rare.
-//  * PV on MFMA 16x16x32 f16.  P' (probabilities times the value scale) is
+//  * PV on MFMA 16x16x16 f16.  P' (probabilities times the value scale) is
 //    split into an f16 high part and an f16 low part (about 22 significant
-//    bits together); A holds both parts of the lane's 4 tokens, exactly in
-//    the lane layout QK^T produced, and B holds the value tile (read from LDS
-//    with ds_read_b64_tr_b16) twice, so one MFMA adds hi*V + lo*V.  A single
-//    f16 rounding of P' costs up to 2^-12 * |v| per weight, too much for
-//    values with outlier channels.
+//    bits together), each already in the lane layout QK^T produced (4
+//    tokens per lane); two MFMAs add hi*V and lo*V against the same value
+//    operand, read from the LDS tile with ds_read_b64_tr_b16.  A single f16
+//    rounding of P' costs up to 2^-12 * |v| per weight, too much for values
+//    with outlier channels.
 //
 // Operand encodings (all exact, all in the f16 normal range: MFMA products
 // with subnormal f16 operands are not accumulated to full fp32 precision):
@@ -59,6 +59,7 @@ namespace mkv {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -85,6 +86,11 @@ __device__ __forceinline__ uint32_t vgpr_one_pair() {
   uint32_t r;
   asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(r));
   return r;
+}
+
+// Half h (0 low, 1 high) of an f16 pair as fp32.
+__device__ __forceinline__ float f16_half(uint32_t w, int h) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(w >> (16 * h))));
 }
 
 // f16 pair subtraction (x - c) with c given as the bits of two f16 values.
@@ -161,57 +167,56 @@ __device__ __forceinline__ u32x2 fp8x4_to_f16(uint32_t w) {
 }
 
 // ---- P' hi/lo ----------------------------------------------------------------
-// Given the lane's 4 probabilities p and the 4 fp16 value scales s (raw bits),
-// build the MFMA 16x16x32 A operand: slots 0..3 hold hi = f16(p*s), slots
-// 4..7 lo = f16(p*s - hi).  Each is one fused multiply-add of mixed precision
-// rounded once to f16, so hi + lo carries p*s to about 22 bits.
-__device__ __forceinline__ half8 pprime_hi_lo(const float p[4], const uint16_t s[4]) {
-  half8 r;
+// P' of the lane's 4 tokens as two MFMA 16x16x16 A operands (tokens in
+// k-slots 0..3): hi = f16(p*s) and lo = f16(p*s - hi), each one fused
+// multiply-add of fp32 p and the scale rounded to f16 (the compiler emits
+// v_fma_mix{lo,hi}_f16), so hi + lo carries p*s to about 22 bits.
+struct PPrime {
+  half4 hi, lo;
+};
+
+__device__ __forceinline__ PPrime pprime(const float p[4], const float sv[4]) {
+  PPrime r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float sv = float(__builtin_bit_cast(_Float16, s[i]));
-    const _Float16 hi = _Float16(__builtin_fmaf(p[i], sv, 0.0f));
-    r[i] = hi;
-    r[4 + i] = _Float16(__builtin_fmaf(p[i], sv, -float(hi)));
+    const _Float16 h = _Float16(__builtin_fmaf(p[i], sv[i], 0.0f));
+    r.hi[i] = h;
+    r.lo[i] = _Float16(__builtin_fmaf(p[i], sv[i], -float(h)));
   }
   return r;
 }
 
-// Same with one scale for all four tokens (FP8 page-head scale).
-__device__ __forceinline__ half8 pprime_hi_lo_uniform(const float p[4], float sv) {
-  half8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const _Float16 hi = _Float16(p[i] * sv);
-    r[i] = hi;
-    r[4 + i] = _Float16(__builtin_fmaf(p[i], sv, -float(hi)));
-  }
-  return r;
+// TQ3: the value scales of the lane's 4 tokens for one group, as f16 pairs
+// (tokens 0, 1 in w0 and 2, 3 in w1).
+__device__ __forceinline__ PPrime pprime_group(const float p[4], uint32_t w0, uint32_t w1) {
+  const float sv[4] = {f16_half(w0, 0), f16_half(w0, 1), f16_half(w1, 0), f16_half(w1, 1)};
+  return pprime(p, sv);
+}
+
+// FP8: one scale for all four tokens (page-head scale).
+__device__ __forceinline__ PPrime pprime_uniform(const float p[4], float s) {
+  const float sv[4] = {s, s, s, s};
+  return pprime(p, sv);
+}
+
+// acc += P' * V for one 16-dim N-tile: the hi and lo parts against the same
+// value operand (MFMA 16x16x16, products exact in fp32).
+__device__ __forceinline__ f32x4 pv_mfma(const PPrime& pp, half4 v, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pp.hi, v, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(pp.lo, v, acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ short4v read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
 }
 
-// B operand for the hi/lo PV MFMA: the lane's 4 value entries twice (read
-// twice from LDS so the operand lands in place without register copies; the
-// fence keeps the compiler from merging the two reads).
-__device__ __forceinline__ half8 value_operand(const uint8_t* p) {
-  const u32x2 a = __builtin_bit_cast(u32x2, read_tr(p));
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p));
-  const u32x4 d = {a[0], a[1], b[0], b[1]};
-  return __builtin_bit_cast(half8, d);
+// B operand of the PV MFMA 16x16x16: the value entries V[4quad + j][n] of
+// the lane's column n, transposed out of the row-major LDS tile.
+__device__ __forceinline__ half4 value_operand(const uint8_t* p) {
+  return __builtin_bit_cast(half4, read_tr(p));
 }
 
 // ---- cross-lane helpers -----------------------------------------------------
-// max without the NaN-quieting canonicalisation fmaxf adds (operands here are
-// never signalling NaNs).
-__device__ __forceinline__ float vmax(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
 
 // Orders one wave's LDS writes before its later LDS reads of other lanes' data.
 // The lanes of a wave issue LDS operations in program order, so no hardware
@@ -225,9 +230,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Reduce over the four lanes {c, c+16, c+32, c+48} (same column, four quads).
 __device__ __forceinline__ float quad_max(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float quad_sum(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -242,26 +247,35 @@ __device__ __forceinline__ int q_shift(float amax) {
 }
 
 // ---- tiles -------------------------------------------------------------------
-// A work item's tiles are visited in order: tile (page, sub) covers tokens
-// 16*sub .. 16*sub+15 of the item's page `page` (pages hold P = 16 * tpp
-// tokens).  Cursors are wave-uniform and advance without division.
+// A work item's tiles: tile (page, sub) covers tokens 16*sub .. 16*sub+15 of
+// the item's page `page` (pages hold P = 16 * tpp tokens); tiles are numbered
+// page * tpp + sub.  The four waves of a workgroup take consecutive quarters
+// of the item's tiles.  Cursors are wave-uniform and advance without division.
 struct Cursor {
   int page = 0, sub = 0;
 };
 struct TileGeom {
-  int tpp;        // tiles per page
-  int last_page;  // npages - 1
-  int last_sub;   // index of the last (possibly partial) tile of the last page
-  int last_ntok;  // valid tokens of the last page
-  int ntiles;
+  int tpp;          // tiles per page
+  int item_last;    // the item's last page (npages - 1)
+  int last_ntok;    // valid tokens of that page
+  int stop_page;    // last tile of this wave's range
+  int stop_sub;
+  int ntiles;       // tiles in this wave's range (may be 0)
+  Cursor first;     // first tile of the range
 };
-__device__ __forceinline__ TileGeom tile_geom(const WorkItem& it, int tpp) {
+__device__ __forceinline__ TileGeom wave_tiles(const WorkItem& it, int tpp, int wave) {
   TileGeom g;
   g.tpp = tpp;
-  g.last_page = it.npages - 1;
-  g.last_sub = (it.last_ntok + 15) / 16 - 1;
+  g.item_last = it.npages - 1;
   g.last_ntok = it.last_ntok;
-  g.ntiles = g.last_page * tpp + g.last_sub + 1;
+  const int total = g.item_last * tpp + (it.last_ntok + 15) / 16;
+  const int t0 = (total * wave) / kWaves, t1 = (total * (wave + 1)) / kWaves;
+  g.ntiles = t1 - t0;
+  g.first.page = t0 / tpp;
+  g.first.sub = t0 - g.first.page * tpp;
+  const int tl = max(t1 - 1, t0);
+  g.stop_page = tl / tpp;
+  g.stop_sub = tl - g.stop_page * tpp;
   return g;
 }
 __device__ __forceinline__ void advance(Cursor& c, const TileGeom& g) {
@@ -270,14 +284,14 @@ __device__ __forceinline__ void advance(Cursor& c, const TileGeom& g) {
     ++c.page;
   }
 }
-// Prefetch cursor: stops on the last tile, so loads issued past the end
-// re-read it (every wave issues the same number of loads per tile, which
+// Prefetch cursor: stops on the range's last tile, so loads issued past the
+// end re-read it (every wave issues the same number of loads per tile, which
 // keeps the compiler's memory-counter waits exact).
 __device__ __forceinline__ void advance_clamped(Cursor& c, const TileGeom& g) {
-  if (c.page != g.last_page || c.sub != g.last_sub) advance(c, g);
+  if (c.page != g.stop_page || c.sub != g.stop_sub) advance(c, g);
 }
 __device__ __forceinline__ int valid_in_tile(const Cursor& c, const TileGeom& g) {
-  return c.page == g.last_page ? min(16, g.last_ntok - 16 * c.sub) : 16;
+  return c.page == g.item_last ? min(16, g.last_ntok - 16 * c.sub) : 16;
 }
 
 // Page-table entries of a work item's pages, staged once per workgroup.
@@ -290,19 +304,21 @@ __device__ __forceinline__ const uint8_t* entry_page(const PoolView& pv, const i
   return page_address(pv, __builtin_amdgcn_readfirstlane(ent[page]));
 }
 
-// Runs the tile pipeline: R raw buffers in flight; process(raw, cursor,
-// prefetch) consumes one tile and, if prefetch, refills raw from the load
-// cursor.  The steady-state loop issues the same loads on every path.
+// Runs the tile pipeline over the wave's range: R raw buffers in flight;
+// process(raw, cursor, refill) consumes one tile and calls refill(raw) to
+// load a later one.  The steady-state loop issues the same loads on every
+// path.
 template <int R, typename Raw, typename Load, typename Process>
 __device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Process process) {
+  if (g.ntiles == 0) return;
   Raw ring[R];
-  Cursor lc;
+  Cursor lc = g.first;
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     load(lc, ring[k]);
     advance_clamped(lc, g);
   }
-  Cursor pc;
+  Cursor pc = g.first;
   int ti = 0;
   for (; ti + R <= g.ntiles; ti += R) {
 #pragma unroll
@@ -330,13 +346,63 @@ struct SoftState {
   float l = 0.0f;        // this lane's share of the denominator
 };
 
+// LDS image for combining the four waves' states of one work item: per wave
+// the reference max and denominator of the 16 columns and the accumulator
+// rows of the live columns in true units (row stride padded); then per wave
+// and column the weight 2^(m_w - M) of that wave's state.
+template <int D>
+struct MergeLds {
+  static constexpr int ROW = D + 4;
+  float m[kWaves][16];
+  float l[kWaves][16];
+  float f[kWaves][16];
+  float acc[kWaves][16 * ROW];
+};
+
+// Combine the waves' states in M and write the item's partial state of the
+// ncol query heads starting at hq0 (all threads of the workgroup call this,
+// with M.m, M.l and M.acc written and visible).
+template <int D>
+__device__ __forceinline__ void merge_waves_and_store(MergeLds<D>& M, const DecodeArgs& a, int chunk,
+                                                      int hq0, int ncol) {
+  const int64_t base = int64_t(chunk) * a.Hq + hq0;
+  if (threadIdx.x < 16) {
+    // per column: the common reference max and the waves' weights
+    const int c = threadIdx.x;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (M.l[w][c] > 0.0f) mx = fmaxf(mx, M.m[w][c]);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = M.l[w][c] > 0.0f ? exp2f(M.m[w][c] - mx) : 0.0f;
+      M.f[w][c] = f;
+      lsum += M.l[w][c] * f;
+    }
+    if (c < ncol) {
+      a.pm[base + c] = mx;
+      a.pl[base + c] = lsum;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads) {
+    const int c = idx / D, dim = idx - (idx / D) * D;
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (M.f[w][c] > 0.0f) o += M.acc[w][c * MergeLds<D>::ROW + dim] * M.f[w][c];
+    a.pacc[(base + c) * D + dim] = o;
+  }
+}
+
 // Softmax step of one tile for the lane's column: scores s (fp32, already
 // multiplied by the column's score factor and masked) -> probabilities p;
 // rescales the accumulators when the reference max must rise.
 template <int NACC>
 __device__ __forceinline__ void softmax_step(SoftState& st, float s[4], float p[4],
                                              f32x4 (&acc)[NACC], float* corr_lds, int col, int quad) {
-  float tmax = vmax(vmax(s[0], s[1]), vmax(s[2], s[3]));
+  float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   tmax = quad_max(tmax);
   if (__any(tmax > st.m)) {
     const float m_new = tmax > st.m ? tmax + kHeadroom : st.m;
@@ -400,17 +466,25 @@ __device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, i
   return E;
 }
 
+// Row stride (bytes) of an f16 value tile in LDS: the stride in dwords is
+// 12 mod 64, so the 16 rows of a 16-byte row write and the 4 x 4 lanes of a
+// transposing 8-byte read each hit distinct banks.
+constexpr int value_row_bytes(int D) { return 2 * D + 4 * (((12 - D / 2) % 64 + 64) % 64); }
+static_assert(value_row_bytes(128) == 304 && value_row_bytes(64) % 16 == 0 &&
+                  (value_row_bytes(32) / 4) % 64 == 12 && (value_row_bytes(256) / 4) % 64 == 12,
+              "value row stride");
+
 // LDS images of the two work-item kinds (one of them per workgroup).
 template <int NG, int NH>
 struct Tq3Lds {
   static constexpr int D = 32 * NG;
-  static constexpr int VROW = 2 * D + 32;       // value-tile row stride (bytes, padded)
+  static constexpr int VROW = value_row_bytes(D);
   static constexpr int KST = 4 * NG + 4;        // dwords per token in the key staging (padded)
   static constexpr int SD = 16 * NG;            // scale dwords of a tile (K then V)
   struct Wave {
     alignas(16) uint32_t kst[NH][16 * KST];     // key units, [token][unit][group]
     alignas(16) uint8_t vt[NH][16 * VROW];      // value tiles, [token][D] f16
-    alignas(16) uint32_t sc[NH][SD];            // tile scales: K [16][NG] f16, then V
+    alignas(16) uint32_t sc[NH][SD + 4];        // tile scales as f16 [K, V][group][token] (padded)
     float corr[16];
   };
   int32_t ent[kMaxChunkPages];                  // page-table entries of the work item
@@ -420,7 +494,7 @@ struct Tq3Lds {
 template <int NG, int NH>
 struct Fp8Lds {
   static constexpr int D = 32 * NG;
-  static constexpr int VROW = 2 * D + 32;
+  static constexpr int VROW = value_row_bytes(D);
   struct Wave {
     alignas(16) uint8_t vt[NH][16 * VROW];
     float corr[16];
@@ -442,10 +516,11 @@ __device__ __forceinline__ float pick_head(const f32x4 (&acc)[NH * NT], int jc, 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// TQ3 work item: each wave owns NH kv-heads
+// TQ3 work item: the workgroup owns NH kv-heads; each wave a quarter of the tiles
 // ---------------------------------------------------------------------------
 template <int NG, int NH, int R>
-__device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it, Tq3Lds<NG, NH>& lds) {
+__device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it, uint8_t* smem) {
+  auto& lds = *reinterpret_cast<Tq3Lds<NG, NH>*>(smem);
   constexpr int D = 32 * NG;
   constexpr int GPL = NG > 4 ? NG / 4 : 1;      // groups each lane loads per head
   constexpr int NT = D / 16;                    // PV N-tiles per head
@@ -461,7 +536,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   const int quad = lane >> 4;
   const PoolView& pv = a.pv;
   stage_entries(lds.ent, a, it);
-  const int hk0 = (blockIdx.y * kWaves + wave) * NH;
+  const int hk0 = blockIdx.y * NH;               // the workgroup's kv-heads
   if (hk0 >= pv.Hkv) return;
   const int G = a.Hq / pv.Hkv;
   const int ncol = NH * G;
@@ -529,11 +604,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
         r.sc[j][i] = *reinterpret_cast<const uint32_t*>(page + sc_off[j][i] + 2 * t0 * NG);
     }
   };
-  auto scale_of = [](const uint32_t* w, int i, int g) {
-    const int e = i * NG + g;
-    return float(__builtin_bit_cast(_Float16, uint16_t(w[e >> 1] >> (16 * (e & 1)))));
-  };
-  const TileGeom tg = tile_geom(it, pv.P / 16);
+  const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
 
   // Tile body: the raw buffer is consumed into LDS, refilled with a later
   // tile, and the tile is computed from LDS.
@@ -541,9 +612,28 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     const int nvalid = valid_in_tile(c, tg);
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
+      // scales: the lane's dword holds f16 k0 = 2e' and k0 + 1 of the tile's
+      // K (e < 8NG) or V block, f16 k being (token k / NG, group k % NG);
+      // they are stored transposed, [group][token], so a lane later reads
+      // its 4 tokens of a group as one 8-byte word.  Value scales of masked
+      // tokens become 0 (an unwritten slot may hold NaN, and p = 0 times NaN
+      // is NaN).
+      uint16_t* sc16 = reinterpret_cast<uint16_t*>(W.sc[j]);
 #pragma unroll
-      for (int i = 0; i < SPL; ++i)
-        if (lane + 64 * i < SD) W.sc[j][lane + 64 * i] = raw.sc[j][i];
+      for (int i = 0; i < SPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < SD) {
+          const bool is_v = e >= 8 * NG;
+          const int k0 = 2 * (is_v ? e - 8 * NG : e);
+          const int base = is_v ? 16 * NG : 0;
+          const int t0 = k0 / NG, g0 = k0 % NG, t1 = (k0 + 1) / NG, g1 = (k0 + 1) % NG;
+          uint16_t lo = uint16_t(raw.sc[j][i]), hi = uint16_t(raw.sc[j][i] >> 16);
+          if (is_v && t0 >= nvalid) lo = 0;
+          if (is_v && t1 >= nvalid) hi = 0;
+          sc16[base + 16 * g0 + t0] = lo;
+          sc16[base + 16 * g1 + t1] = hi;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < GPL; ++i) {
         const int g = quad + 4 * i;
@@ -563,14 +653,9 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     refill(raw);
     wave_lds_sync();
 
-    // ---- scales of the lane's 4 tokens for its column's kv-head
-    uint32_t skw[2 * NG], svw[2 * NG];
-#pragma unroll
-    for (int x = 0; x < 2 * NG; ++x) {
-      skw[x] = W.sc[jcol][2 * quad * NG + x];
-      svw[x] = W.sc[jcol][8 * NG + 2 * quad * NG + x];
-    }
-    // ---- QK^T per group (the NH kv-heads into one D), scaled per token and group
+    // ---- QK^T per group (the NH kv-heads into one D), scaled per token by
+    // the group's key scale of the lane's column's kv-head
+    const uint32_t* scl = W.sc[jcol] + 2 * quad;   // + 8g: K scales, + 8NG + 8g: V scales
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -581,8 +666,9 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
             __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[j][col * KST + quad * NG + g], one));
         dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[j][g], dg, 0, 0, 0);
       }
+      const u32x2 ks = *reinterpret_cast<const u32x2*>(scl + 8 * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dg[i], scale_of(skw, i, g), s[i]);
+      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dg[i], f16_half(ks[i >> 1], i & 1), s[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] *= F;
@@ -594,41 +680,32 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     float p[4];
     softmax_step(st, s, p, acc, W.corr, col, quad);
 
-    // ---- P' = p * value scale (hi/lo f16), acc_j += P' * V_j
-    half8 pp[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      uint16_t sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = i * NG + g;
-        sv[i] = uint16_t(svw[e >> 1] >> (16 * (e & 1)));
-      }
-      if (nvalid < 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * quad + i >= nvalid) sv[i] = 0;   // masked token (its scale may be NaN)
-      }
-      pp[g] = pprime_hi_lo(p, sv);
-    }
+    // ---- per group: P' = p * value scale (hi/lo f16), acc_j += P' * V_j
     const int row = 4 * quad + (col >> 2);
 #pragma unroll
-    for (int j = 0; j < NH; ++j)
+    for (int g = 0; g < NG; ++g) {
+      const u32x2 vs = *reinterpret_cast<const u32x2*>(scl + 8 * NG + 8 * g);
+      const PPrime pp = pprime_group(p, vs[0], vs[1]);
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt) {
-        const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
-        acc[j * NT + jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp[jt >> 1], bv, acc[j * NT + jt], 0, 0, 0);
-      }
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int jt = 2 * g; jt < 2 * g + 2; ++jt) {
+          const half4 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+          acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
+        }
+    }
     wave_lds_sync();
   };
   run_tiles<R, Raw>(tg, load, process);
 
-  // ---- write this wave's partial state: l per column, acc in true units
+  // ---- combine the four waves' states through LDS (the tile staging is
+  // reused once every wave is past its last tile) and write the item's state
   const float lcol = quad_sum(st.l);
-  const int64_t base_h = int64_t(it.chunk) * a.Hq + hq0;
-  if (quad == 0 && col < ncol) {
-    a.pm[base_h + col] = st.m;
-    a.pl[base_h + col] = lcol;
+  __syncthreads();
+  auto& M = *reinterpret_cast<MergeLds<D>*>(smem);
+  if (quad == 0) {
+    M.m[wave][col] = st.m;
+    M.l[wave][col] = lcol;
   }
   // accumulator column col of N-tile jt is dim 16*jt + col in slot order;
   // slot s of a unit holds dim kSlotCode[s] scaled by 2^(kSlotShift[s]-10)
@@ -640,17 +717,20 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     const int c = 4 * quad + i;
     if (c >= ncol) continue;
     const int jc = c / G;
-    float* dst = a.pacc + (base_h + c) * D + (col & 8) + dim_in_unit;
+    float* dst = M.acc[wave] + c * MergeLds<D>::ROW + (col & 8) + dim_in_unit;
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) dst[16 * jt] = pick_head<NH, NT>(acc, jc, jt, i) * up;
   }
+  __syncthreads();
+  merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
 }
 
 // ---------------------------------------------------------------------------
-// FP8 work item: each wave owns NH kv-heads
+// FP8 work item: the workgroup owns NH kv-heads; each wave a quarter of the tiles
 // ---------------------------------------------------------------------------
 template <int NG, int NH, int R>
-__device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it, Fp8Lds<NG, NH>& lds) {
+__device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it, uint8_t* smem) {
+  auto& lds = *reinterpret_cast<Fp8Lds<NG, NH>*>(smem);
   constexpr int D = 32 * NG;
   constexpr int NT = D / 16;
   constexpr int VROW = Fp8Lds<NG, NH>::VROW;
@@ -662,7 +742,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   const int quad = lane >> 4;
   const PoolView& pv = a.pv;
   stage_entries(lds.ent, a, it);
-  const int hk0 = (blockIdx.y * kWaves + wave) * NH;
+  const int hk0 = blockIdx.y * NH;               // the workgroup's kv-heads
   if (hk0 >= pv.Hkv) return;
   const int G = a.Hq / pv.Hkv;
   const int ncol = NH * G;
@@ -711,7 +791,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
       r.sigv[j] = *reinterpret_cast<const float*>(page + vs_off[j]);
     }
   };
-  const TileGeom tg = tile_geom(it, pv.P / 16);
+  const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
 
   auto process = [&](Raw& raw, const Cursor& c, auto refill) {
     const int nvalid = valid_in_tile(c, tg);
@@ -727,36 +807,27 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
         if (!vrow_ok) o = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(W.vt[j] + col * VROW + 2 * (quad * LB + 4 * i)) = o;
       }
-    // ---- keys to f16 MFMA operands
-    half8 kop[NH][NG];
-    float sigk[NH], sigv[NH];
+    // ---- QK^T over all dims, per kv-head, keys widened to f16 operands from
+    // the raw words (page-head scale applied per column)
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float sv = raw.sigv[0];
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
+      f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < NG; ++r) {
         const u32x2 k0 = fp8x4_to_f16(raw.kw[j][2 * r]);
         const u32x2 k1 = fp8x4_to_f16(raw.kw[j][2 * r + 1]);
         const u32x4 ku = {k0[0], k0[1], k1[0], k1[1]};
-        kop[j][r] = __builtin_bit_cast(half8, ku);
+        dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ku), qop[j][r], dsum, 0, 0, 0);
       }
-      sigk[j] = raw.sigk[j];
-      sigv[j] = raw.sigv[j];
+      const float fk = jcol == j ? F * raw.sigk[j] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dsum[i], fk, s[i]);
+      if (j > 0) sv = jcol == j ? raw.sigv[j] : sv;
     }
     refill(raw);
     wave_lds_sync();
-
-    // ---- QK^T over all dims, per kv-head (page-head scale applied per column)
-    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int r = 0; r < NG; ++r)
-        dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[j][r], qop[j][r], dsum, 0, 0, 0);
-      const float fk = jcol == j ? F * sigk[j] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dsum[i], fk, s[i]);
-    }
     if (nvalid < 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -765,37 +836,37 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
     float p[4];
     softmax_step(st, s, p, acc, W.corr, col, quad);
 
-    float sv = sigv[0];
-#pragma unroll
-    for (int j = 1; j < NH; ++j) sv = jcol == j ? sigv[j] : sv;
-    const half8 pp = pprime_hi_lo_uniform(p, sv);
+    const PPrime pp = pprime_uniform(p, sv);
     const int row = 4 * quad + (col >> 2);
 #pragma unroll
     for (int j = 0; j < NH; ++j)
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
-        acc[j * NT + jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp, bv, acc[j * NT + jt], 0, 0, 0);
+        const half4 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+        acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
       }
     wave_lds_sync();
   };
   run_tiles<R, Raw>(tg, load, process);
 
   const float lcol = quad_sum(st.l);
-  const int64_t base_h = int64_t(it.chunk) * a.Hq + hq0;
-  if (quad == 0 && col < ncol) {
-    a.pm[base_h + col] = st.m;
-    a.pl[base_h + col] = lcol;
+  __syncthreads();
+  auto& M = *reinterpret_cast<MergeLds<D>*>(smem);
+  if (quad == 0) {
+    M.m[wave][col] = st.m;
+    M.l[wave][col] = lcol;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
     if (c >= ncol) continue;
     const int jc = c / G;
-    float* dst = a.pacc + (base_h + c) * D;
+    float* dst = M.acc[wave] + c * MergeLds<D>::ROW;
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) dst[16 * jt + col] = pick_head<NH, NT>(acc, jc, jt, i);
   }
+  __syncthreads();
+  merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
 }
 
 // ---------------------------------------------------------------------------
@@ -803,23 +874,24 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
 // ---------------------------------------------------------------------------
 template <int NG, int NH>
 struct PartialCfg {
-  static constexpr int kRingTq3 = NH == 1 && NG <= 4 ? 4 : 2;   // TQ3 tiles in flight per wave
+  static constexpr int kRingTq3 = 2;                 // TQ3 tiles in flight per wave
   static constexpr int kRingFp8 = NH == 1 ? 2 : 1;   // FP8 tiles in flight per wave
+  static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
   static constexpr size_t kSmem =
-      sizeof(Tq3Lds<NG, NH>) > sizeof(Fp8Lds<NG, NH>) ? sizeof(Tq3Lds<NG, NH>) : sizeof(Fp8Lds<NG, NH>);
+      cmax(cmax(sizeof(Tq3Lds<NG, NH>), sizeof(Fp8Lds<NG, NH>)), sizeof(MergeLds<32 * NG>));
 };
 
 // At least two waves per SIMD (256 VGPRs) except for head dim 256, which
 // keeps its registers unspilled at one wave per SIMD.
 template <int NG, int NH>
-__global__ void __launch_bounds__(kThreads, NG == 8 ? 1 : 2) partial_mixed(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, NG == 8 ? 1 : (NH == 1 ? 3 : 2)) partial_mixed(DecodeArgs a) {
   using Cfg = PartialCfg<NG, NH>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
   const WorkItem it = a.items[blockIdx.x];
   if (it.fmt == 0)
-    fp8_item<NG, NH, Cfg::kRingFp8>(a, it, *reinterpret_cast<Fp8Lds<NG, NH>*>(smem));
+    fp8_item<NG, NH, Cfg::kRingFp8>(a, it, smem);
   else
-    tq3_item<NG, NH, Cfg::kRingTq3>(a, it, *reinterpret_cast<Tq3Lds<NG, NH>*>(smem));
+    tq3_item<NG, NH, Cfg::kRingTq3>(a, it, smem);
 }
 
 namespace {
@@ -845,13 +917,12 @@ hipError_t with_kernel(int d, int nh, F f) {
 
 }  // namespace
 
-// Grid: one workgroup per (work item, block of kWaves * NH kv-heads); each
-// wave owns NH kv-heads of the item (NH from heads_per_wave).
+// Grid: one workgroup per (work item, block of NH kv-heads); the workgroup's
+// waves split the item's tiles (NH chosen by the schedule).
 hipError_t launch_partial(const DecodeArgs& a, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
-  const int nh = heads_per_wave(a.pv.d, a.pv.Hkv, a.Hq / a.pv.Hkv);
-  const int per_block = kWaves * nh;
-  const dim3 grid(unsigned(a.n_items), unsigned((a.pv.Hkv + per_block - 1) / per_block));
+  const int nh = a.nh;
+  const dim3 grid(unsigned(a.n_items), unsigned((a.pv.Hkv + nh - 1) / nh));
   return with_kernel(a.pv.d, nh, [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();

@@ -216,7 +216,12 @@ mkv_status prof_collect(mkv_pool* p) {
 mkv::SchedPolicy pool_policy(const mkv_pool* p, int32_t Hq) {
   mkv::SchedPolicy pol;
   const mkv::Geom& g = p->meta.geom();
-  pol.target_waves = p->target_waves[mkv::heads_per_wave(g.d, g.Hkv, Hq / g.Hkv) - 1];
+  pol.heads_per_wave = mkv::heads_per_wave(g.d, g.Hkv, Hq / g.Hkv);
+  if (const char* e = std::getenv("MKV_HEADS_PER_WAVE")) {
+    const int nh = std::atoi(e);
+    if (nh == 1 || (nh == 2 && g.d <= 128 && g.Hkv % 2 == 0 && 2 * (Hq / g.Hkv) <= 16)) pol.heads_per_wave = nh;
+  }
+  pol.target_waves = p->target_waves[pol.heads_per_wave - 1];
   if (const char* e = std::getenv("MKV_CHUNK_PAGES")) pol.fixed_chunk_pages = std::max(0, std::atoi(e));
   if (const char* e = std::getenv("MKV_TARGET_WAVES")) pol.target_waves = std::max(1, std::atoi(e));
   if (const char* e = std::getenv("MKV_FP8_PAGE_COST")) pol.fp8_page_cost = float(std::atof(e));
@@ -410,6 +415,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   a.pacc = reinterpret_cast<float*>(p->mem + p->lay.pacc);
   a.out = out;
   a.lse = lse;
+  a.nh = sc.heads_per_wave;
   a.items = items;
   a.n_items = int32_t(sc.items[0].size() + sc.items[1].size());
   {

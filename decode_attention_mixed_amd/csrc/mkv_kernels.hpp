@@ -33,6 +33,7 @@ struct DecodeArgs {
   float* pacc;              // partial acc      [chunks][Hq][d]
   float* out;               // [B][Hq][d]
   float* lse;               // [B][Hq]
+  int32_t nh;               // kv-heads per partial-kernel workgroup (1 or 2)
 };
 
 hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_pages,

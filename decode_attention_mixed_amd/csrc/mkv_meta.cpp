@@ -202,7 +202,10 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     per = std::min<int64_t>(per, kMaxChunkPages);
     return (n + per - 1) / per;
   };
-  const int32_t heads_per_block = kWavesPerWorkgroup * heads_per_wave(g_.d, g_.Hkv, Hq / g_.Hkv);
+  const int32_t heads_per_block =
+      pol.heads_per_wave > 0 ? pol.heads_per_wave : heads_per_wave(g_.d, g_.Hkv, Hq / g_.Hkv);
+  if (heads_per_block != 1 && (heads_per_block != 2 || g_.Hkv % 2 || 2 * (Hq / g_.Hkv) > 16 || g_.d > 128))
+    return fail(err, MKV_S_EINVAL, "unsupported kv-heads per wave");
   const int64_t waves_per_item =
       int64_t(kWavesPerWorkgroup) * ((g_.Hkv + heads_per_block - 1) / heads_per_block);
   const int64_t target_items = std::max<int64_t>(1, pol.target_waves / waves_per_item);
@@ -215,6 +218,30 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
       k8[size_t(b)] = chunks_of(n8[size_t(b)], c8, budget);
       k3[size_t(b)] = chunks_of(n3[size_t(b)], 1.0, budget);
       count += k8[size_t(b)] + k3[size_t(b)];
+    }
+    // Balanced chunks are counted down (floor); hand the spare slots up to the
+    // target, one at a time, to the lists whose chunks cost the most.
+    if (fixed == 0 && attempt == 0) {
+      const int64_t cap = std::min<int64_t>(target_items, g_.max_chunks);
+      while (count < cap) {
+        double worst = 0.0;
+        int32_t wb = -1, wf = 0;
+        for (int32_t b = 0; b < B; ++b)
+          for (int f = 0; f < 2; ++f) {
+            const int32_t n = f ? n3[size_t(b)] : n8[size_t(b)];
+            const int64_t k = f ? k3[size_t(b)] : k8[size_t(b)];
+            if (n == 0 || k >= n || (n + k) / (k + 1) < pol.min_chunk_pages) continue;
+            const double per = double(n) * (f ? 1.0 : c8) / double(k);
+            if (per > worst) {
+              worst = per;
+              wb = b;
+              wf = f;
+            }
+          }
+        if (wb < 0) break;
+        ++(wf ? k3 : k8)[size_t(wb)];
+        ++count;
+      }
     }
     if (count <= g_.max_chunks) break;
     // Too many chunks: coarser chunks (fixed chunks double, balanced budgets grow).
@@ -261,6 +288,7 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
   out->chunk_base[size_t(B)] = nc;
   out->n_chunks = nc;
   out->chunk_pages = largest;
+  out->heads_per_wave = heads_per_block;
   return MKV_S_OK;
 }
 

@@ -81,13 +81,14 @@ struct WorkItem {
 // page-table entries in a fixed LDS array of this length.
 constexpr int32_t kMaxChunkPages = 256;
 // Waves per partial-kernel workgroup; a workgroup takes one work item and
-// kWavesPerWorkgroup * heads_per_wave kv-heads of it.
+// heads_per_wave kv-heads of it, its waves splitting the item's tiles.
 constexpr int32_t kWavesPerWorkgroup = 4;
 
-// kv-heads per partial-kernel wave: two when the query columns of two
-// kv-heads fit the 16 MFMA columns (G <= 8), the kv-head count is even and
-// d <= 128 (register budget); else one.  The work that does not depend on the
-// kv-head (softmax, probability scaling) is then shared by two heads.
+// kv-heads per partial-kernel wave (and workgroup): two when the query
+// columns of two kv-heads fit the 16 MFMA columns (G <= 8), the kv-head count
+// is even and d <= 128 (register budget); else one.  The work that does not
+// depend on the kv-head (softmax, probability scaling) is then shared by two
+// heads.
 inline int32_t heads_per_wave(int32_t d, int32_t Hkv, int32_t G) {
   return (d <= 128 && 2 * G <= 16 && Hkv % 2 == 0) ? 2 : 1;
 }
@@ -104,6 +105,7 @@ struct SchedPolicy {
   int32_t target_waves = 2048;   // resident partial-kernel waves on the device
   int32_t min_chunk_pages = 4;   // smallest balanced chunk (shorter lists stay whole)
   int32_t fixed_chunk_pages = 0; // 0: balanced chunks
+  int32_t heads_per_wave = 0;    // kv-heads per partial-kernel workgroup; 0: heads_per_wave()
   float fp8_page_cost = 1.5f;    // cost of an FP8 page relative to a TQ3 page
 };
 
@@ -111,6 +113,7 @@ struct Schedule {
   std::vector<WorkItem> items[2];   // per format (FP8, TQ3)
   std::vector<int32_t> pages;       // logical page ids referenced by the items
   std::vector<int32_t> chunk_base;  // [B + 1] prefix sums of chunks per batch entry
+  int32_t heads_per_wave = 1;       // kv-heads per partial-kernel workgroup
   int32_t n_chunks = 0;
   int32_t chunk_pages = 0;          // largest chunk of the schedule
 };
