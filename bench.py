@@ -132,6 +132,8 @@ def cpu_baseline(wl, per_step_bytes, budget_s=20.0):
 
 
 def load_traffic(kernel: str, wl_name: str):
+    """HBM bytes per launch measured by rocprofv3 counters (see write_traffic),
+    if taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{wl_name}.json")
     if not os.path.exists(path):
         return None
@@ -140,6 +142,42 @@ def load_traffic(kernel: str, wl_name: str):
     if t.get("kernel_src_sha") != kernel_src_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def _pmc_means(csv_path: str, name_part: str, counter: str):
+    """Per-dispatch mean of a rocprofv3 counter over the kernels whose name
+    contains name_part (counter_collection.csv of one --pmc pass)."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"{csv_path}: no {counter} samples for kernels matching {name_part!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, wl_name):
+    """HBM bytes per launch of the partial kernel from two rocprofv3 --pmc
+    passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what
+    the same counter reads for a plain copy of copy_bytes (read and written
+    once).  Writes profiles/traffic_partial_<workload>.json."""
+    fetch, nf = _pmc_means(fetch_csv, "partial_mixed", "FETCH_SIZE")
+    write, nw = _pmc_means(write_csv, "partial_mixed", "WRITE_SIZE")
+    cfetch, _ = _pmc_means(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
+    cwrite, _ = _pmc_means(copy_write_csv, "copyBuffer", "WRITE_SIZE")
+    kib = copy_bytes / 1024.0
+    ffac, wfac = kib / cfetch, kib / cwrite
+    total = (fetch * ffac + write * wfac) * 1024.0
+    out = {
+        "kernel": "partial", "workload": wl_name, "kernel_src_sha": kernel_src_hash(),
+        "bytes_per_launch": round(total), "fetch_kib_per_dispatch": round(fetch, 1),
+        "write_kib_per_dispatch": round(write, 1), "dispatches": [nf, nw],
+        "copy_bytes": copy_bytes, "copy_fetch_kib": round(cfetch, 1), "copy_write_kib": round(cwrite, 1),
+        "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_partial_{wl_name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -174,6 +212,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps "
                          "times (reference for the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                          "COPY_WRITE_CSV", "COPY_BYTES"),
+                    help="only turn rocprofv3 --pmc counter files into the partial kernel's "
+                         "HBM traffic record under profiles/ (no GPU needed)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this library "
@@ -181,6 +223,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration, args.steps)
+        return
+    if args.write_traffic:
+        f1, f2, f3, f4, nb = args.write_traffic
+        write_traffic(f1, f2, f3, f4, int(nb), args.workload)
         return
 
     import numpy as np
