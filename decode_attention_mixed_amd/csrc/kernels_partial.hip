@@ -26,13 +26,13 @@
 //  * Softmax: a reference maximum per column, raised (with headroom) only when
 //    a tile exceeds it, so exp2 arguments stay <= 0 and rescaling the
 //    accumulator is rare.
-//  * PV on MFMA 16x16x16 f16.  P' (probabilities times the value scale) is
+//  * PV on MFMA 16x16x32 f16.  P' (probabilities times the value scale) is
 //    split into an f16 high part and an f16 low part (about 22 significant
-//    bits together), each already in the lane layout QK^T produced (4
-//    tokens per lane); two MFMAs add hi*V and lo*V against the same value
-//    operand, read from the LDS tile with ds_read_b64_tr_b16.  A single f16
-//    rounding of P' costs up to 2^-12 * |v| per weight, too much for values
-//    with outlier channels.
+//    bits together); A holds both parts of the lane's 4 tokens, exactly in
+//    the lane layout QK^T produced, and B holds the value tile (read from LDS
+//    with ds_read_b64_tr_b16) twice, so one MFMA adds hi*V + lo*V.  A single
+//    f16 rounding of P' costs up to 2^-12 * |v| per weight, too much for
+//    values with outlier channels.
 //
 // Operand encodings (all exact, all in the f16 normal range: MFMA products
 // with subnormal f16 operands are not accumulated to full fp32 precision):
@@ -167,53 +167,55 @@ __device__ __forceinline__ u32x2 fp8x4_to_f16(uint32_t w) {
 }
 
 // ---- P' hi/lo ----------------------------------------------------------------
-// P' of the lane's 4 tokens as two MFMA 16x16x16 A operands (tokens in
-// k-slots 0..3): hi = f16(p*s) and lo = f16(p*s - hi), each one fused
-// multiply-add of fp32 p and the scale rounded to f16 (the compiler emits
-// v_fma_mix{lo,hi}_f16), so hi + lo carries p*s to about 22 bits.
-struct PPrime {
-  half4 hi, lo;
-};
-
-__device__ __forceinline__ PPrime pprime(const float p[4], const float sv[4]) {
-  PPrime r;
+// The PV MFMA 16x16x32 A operand of the lane's 4 tokens: k-slots 0..3 hold
+// hi = f16(p*s), k-slots 4..7 lo = f16(p*s - hi), each one fused multiply-
+// add of fp32 p and the scale rounded to f16 (the compiler emits
+// v_fma_mix{lo,hi}_f16), so hi + lo carries p*s to about 22 bits.  The B
+// operand holds the lane's 4 value entries in both halves, so one MFMA adds
+// hi*V + lo*V (products exact in fp32).
+__device__ __forceinline__ half8 pprime(const float p[4], const float sv[4]) {
+  half8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const _Float16 h = _Float16(__builtin_fmaf(p[i], sv[i], 0.0f));
-    r.hi[i] = h;
-    r.lo[i] = _Float16(__builtin_fmaf(p[i], sv[i], -float(h)));
+    r[i] = h;
+    r[4 + i] = _Float16(__builtin_fmaf(p[i], sv[i], -float(h)));
   }
   return r;
 }
 
 // TQ3: the value scales of the lane's 4 tokens for one group, as f16 pairs
 // (tokens 0, 1 in w0 and 2, 3 in w1).
-__device__ __forceinline__ PPrime pprime_group(const float p[4], uint32_t w0, uint32_t w1) {
+__device__ __forceinline__ half8 pprime_group(const float p[4], uint32_t w0, uint32_t w1) {
   const float sv[4] = {f16_half(w0, 0), f16_half(w0, 1), f16_half(w1, 0), f16_half(w1, 1)};
   return pprime(p, sv);
 }
 
 // FP8: one scale for all four tokens (page-head scale).
-__device__ __forceinline__ PPrime pprime_uniform(const float p[4], float s) {
+__device__ __forceinline__ half8 pprime_uniform(const float p[4], float s) {
   const float sv[4] = {s, s, s, s};
   return pprime(p, sv);
 }
 
-// acc += P' * V for one 16-dim N-tile: the hi and lo parts against the same
-// value operand (MFMA 16x16x16, products exact in fp32).
-__device__ __forceinline__ f32x4 pv_mfma(const PPrime& pp, half4 v, f32x4 acc) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x16f16(pp.hi, v, acc, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(pp.lo, v, acc, 0, 0, 0);
+// acc += P' * V for one 16-dim N-tile.
+__device__ __forceinline__ f32x4 pv_mfma(half8 pp, half8 v, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(pp, v, acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ short4v read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
 }
 
-// B operand of the PV MFMA 16x16x16: the value entries V[4quad + j][n] of
-// the lane's column n, transposed out of the row-major LDS tile.
-__device__ __forceinline__ half4 value_operand(const uint8_t* p) {
-  return __builtin_bit_cast(half4, read_tr(p));
+// B operand of the PV MFMA: the value entries V[4quad + j][n] of the lane's
+// column n, transposed out of the row-major LDS tile, in both halves (read
+// twice, so the operand lands in place without register copies; the fence
+// keeps the compiler from merging the two reads).
+__device__ __forceinline__ half8 value_operand(const uint8_t* p) {
+  const u32x2 a = __builtin_bit_cast(u32x2, read_tr(p));
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p));
+  const u32x4 d = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(half8, d);
 }
 
 // ---- cross-lane helpers -----------------------------------------------------
@@ -562,12 +564,14 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   // tile).  Lane (token col, quad) loads group quad (+4i) of that token; with
   // fewer than 4 groups the spare quads repeat a real group's load, and spare
   // lanes of the scale load repeat a real scale dword (results unused).
-  int32_t code_off[NH][GPL], sc_off[NH][SPL];
+  // (unsigned 32-bit lane offsets added to a wave-uniform base address map
+  // to loads with a scalar base and a vector offset)
+  uint32_t code_off[NH][GPL], sc_off[NH][SPL];
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
-    const int32_t cb = int32_t(tq3_codes_off(pv, hk0 + j, 0));
-    const int32_t kb = int32_t(tq3_scale_off(pv, hk0 + j, 0));
-    const int32_t vb = int32_t(tq3_scale_off(pv, hk0 + j, 1));
+    const uint32_t cb = uint32_t(tq3_codes_off(pv, hk0 + j, 0));
+    const uint32_t kb = uint32_t(tq3_scale_off(pv, hk0 + j, 0));
+    const uint32_t vb = uint32_t(tq3_scale_off(pv, hk0 + j, 1));
 #pragma unroll
     for (int i = 0; i < GPL; ++i) code_off[j][i] = cb + col * ROWB + 12 * ((quad + 4 * i) % NG);
 #pragma unroll
@@ -576,7 +580,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       sc_off[j][i] = e < 8 * NG ? kb + 4 * e : vb + 4 * (e - 8 * NG);
     }
   }
-  const int32_t vcode_delta = pv.P * ROWB;      // V codes follow the K codes
+  const uint32_t vcode_delta = uint32_t(pv.P * ROWB);   // V codes follow the K codes
 
   struct Raw {
     uint32_t kc[NH][GPL][3];                    // K codes: one 12-byte group of token col
@@ -585,14 +589,14 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   };
   auto load = [&](const Cursor& c, Raw& r) {
     const uint8_t* page = entry_page(pv, lds.ent, c.page);
-    const int t0 = 16 * c.sub;
+    const uint8_t* codes = page + 16 * c.sub * ROWB;     // the tile's first row
+    const uint8_t* scales = page + 32 * c.sub * NG;
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
 #pragma unroll
       for (int i = 0; i < GPL; ++i) {
-        const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off[j][i] + t0 * ROWB);
-        const uint32_t* vp =
-            reinterpret_cast<const uint32_t*>(page + code_off[j][i] + t0 * ROWB + vcode_delta);
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(codes + code_off[j][i]);
+        const uint32_t* vp = reinterpret_cast<const uint32_t*>(codes + (code_off[j][i] + vcode_delta));
 #pragma unroll
         for (int x = 0; x < 3; ++x) {
           r.kc[j][i][x] = kp[x];
@@ -600,8 +604,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
         }
       }
 #pragma unroll
-      for (int i = 0; i < SPL; ++i)
-        r.sc[j][i] = *reinterpret_cast<const uint32_t*>(page + sc_off[j][i] + 2 * t0 * NG);
+      for (int i = 0; i < SPL; ++i) r.sc[j][i] = *reinterpret_cast<const uint32_t*>(scales + sc_off[j][i]);
     }
   };
   const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
@@ -685,12 +688,12 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const u32x2 vs = *reinterpret_cast<const u32x2*>(scl + 8 * NG + 8 * g);
-      const PPrime pp = pprime_group(p, vs[0], vs[1]);
+      const half8 pp = pprime_group(p, vs[0], vs[1]);
 #pragma unroll
       for (int j = 0; j < NH; ++j)
 #pragma unroll
         for (int jt = 2 * g; jt < 2 * g + 2; ++jt) {
-          const half4 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+          const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
           acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
         }
     }
@@ -762,14 +765,14 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   for (int j = 0; j < NH * NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
 
-  int32_t code_off[NH], ks_off[NH], vs_off[NH];
+  uint32_t code_off[NH], ks_off[NH], vs_off[NH];
 #pragma unroll
   for (int j = 0; j < NH; ++j) {
-    code_off[j] = int32_t(fp8_codes_off(pv, hk0 + j, 0)) + col * D + quad * LB;
-    ks_off[j] = int32_t(fp8_scale_off(pv, hk0 + j, 0));
-    vs_off[j] = int32_t(fp8_scale_off(pv, hk0 + j, 1));
+    code_off[j] = uint32_t(fp8_codes_off(pv, hk0 + j, 0)) + col * D + quad * LB;
+    ks_off[j] = uint32_t(fp8_scale_off(pv, hk0 + j, 0));
+    vs_off[j] = uint32_t(fp8_scale_off(pv, hk0 + j, 1));
   }
-  const int32_t vcode_delta = pv.P * D;
+  const uint32_t vcode_delta = uint32_t(pv.P * D);
   struct Raw {
     uint32_t kw[NH][LB / 4];
     uint32_t vw[NH][LB / 4];
@@ -777,11 +780,11 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   };
   auto load = [&](const Cursor& c, Raw& r) {
     const uint8_t* page = entry_page(pv, lds.ent, c.page);
-    const int t0 = 16 * c.sub;
+    const uint8_t* codes = page + 16 * c.sub * D;        // the tile's first row
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(page + code_off[j] + t0 * D);
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(page + code_off[j] + t0 * D + vcode_delta);
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(codes + code_off[j]);
+      const uint32_t* vp = reinterpret_cast<const uint32_t*>(codes + (code_off[j] + vcode_delta));
 #pragma unroll
       for (int x = 0; x < LB / 4; ++x) {
         r.kw[j][x] = kp[x];
@@ -836,13 +839,13 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
     float p[4];
     softmax_step(st, s, p, acc, W.corr, col, quad);
 
-    const PPrime pp = pprime_uniform(p, sv);
+    const half8 pp = pprime_uniform(p, sv);
     const int row = 4 * quad + (col >> 2);
 #pragma unroll
     for (int j = 0; j < NH; ++j)
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        const half4 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+        const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
         acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
       }
     wave_lds_sync();
