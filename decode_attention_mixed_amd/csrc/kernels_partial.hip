@@ -66,6 +66,7 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int kWaves = kWavesPerWorkgroup;
 constexpr int kThreads = 64 * kWaves;
@@ -294,6 +295,29 @@ __device__ __forceinline__ void advance_clamped(Cursor& c, const TileGeom& g) {
 }
 __device__ __forceinline__ int valid_in_tile(const Cursor& c, const TileGeom& g) {
   return c.page == g.item_last ? min(16, g.last_ntok - 16 * c.sub) : 16;
+}
+
+// ---- record loads -------------------------------------------------------------
+// A page record is read through a buffer resource: the record base sits in
+// scalar registers, each lane adds a fixed 32-bit offset and the tile's
+// position is a wave-uniform scalar offset, so a tile's loads need no per-lane
+// address arithmetic.  Dword 3 selects 32-bit untyped data; the record size
+// bounds the lane offsets (anything past it would read as zero).
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const uint8_t* rec, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec), 0, int(bytes), kRawBufferWord3);
+}
+__device__ __forceinline__ uint32_t rec_load1(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int tile_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, tile_off, 0);
+}
+__device__ __forceinline__ u32x2 rec_load2(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int tile_off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, lane_off, tile_off, 0);
+}
+__device__ __forceinline__ u32x3 rec_load3(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int tile_off) {
+  return __builtin_amdgcn_raw_buffer_load_b96(r, lane_off, tile_off, 0);
+}
+__device__ __forceinline__ u32x4 rec_load4(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, int tile_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, tile_off, 0);
 }
 
 // Page-table entries of a work item's pages, staged once per workgroup.
@@ -580,7 +604,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       sc_off[j][i] = e < 8 * NG ? kb + 4 * e : vb + 4 * (e - 8 * NG);
     }
   }
-  const uint32_t vcode_delta = uint32_t(pv.P * ROWB);   // V codes follow the K codes
+  const int vcode_delta = pv.P * ROWB;                  // V codes follow the K codes
 
   struct Raw {
     uint32_t kc[NH][GPL][3];                    // K codes: one 12-byte group of token col
@@ -588,23 +612,24 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     uint32_t sc[NH][SPL];                       // the lane's share of the tile's scales
   };
   auto load = [&](const Cursor& c, Raw& r) {
-    const uint8_t* page = entry_page(pv, lds.ent, c.page);
-    const uint8_t* codes = page + 16 * c.sub * ROWB;     // the tile's first row
-    const uint8_t* scales = page + 32 * c.sub * NG;
+    const auto rec = record_rsrc(entry_page(pv, lds.ent, c.page), pv.tq3_stride);
+    const int kso = 16 * c.sub * ROWB;                   // the tile's first K row
+    const int vso = kso + vcode_delta;                   // and its first V row
+    const int sso = 32 * c.sub * NG;                     // and its scales
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
 #pragma unroll
       for (int i = 0; i < GPL; ++i) {
-        const uint32_t* kp = reinterpret_cast<const uint32_t*>(codes + code_off[j][i]);
-        const uint32_t* vp = reinterpret_cast<const uint32_t*>(codes + (code_off[j][i] + vcode_delta));
+        const u32x3 kw = rec_load3(rec, code_off[j][i], kso);
+        const u32x3 vw = rec_load3(rec, code_off[j][i], vso);
 #pragma unroll
         for (int x = 0; x < 3; ++x) {
-          r.kc[j][i][x] = kp[x];
-          r.vc[j][i][x] = vp[x];
+          r.kc[j][i][x] = kw[x];
+          r.vc[j][i][x] = vw[x];
         }
       }
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) r.sc[j][i] = *reinterpret_cast<const uint32_t*>(scales + sc_off[j][i]);
+      for (int i = 0; i < SPL; ++i) r.sc[j][i] = rec_load1(rec, sc_off[j][i], sso);
     }
   };
   const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
@@ -772,26 +797,40 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
     ks_off[j] = uint32_t(fp8_scale_off(pv, hk0 + j, 0));
     vs_off[j] = uint32_t(fp8_scale_off(pv, hk0 + j, 1));
   }
-  const uint32_t vcode_delta = uint32_t(pv.P * D);
+  const int vcode_delta = pv.P * D;
   struct Raw {
     uint32_t kw[NH][LB / 4];
     uint32_t vw[NH][LB / 4];
     float sigk[NH], sigv[NH];
   };
   auto load = [&](const Cursor& c, Raw& r) {
-    const uint8_t* page = entry_page(pv, lds.ent, c.page);
-    const uint8_t* codes = page + 16 * c.sub * D;        // the tile's first row
+    const auto rec = record_rsrc(entry_page(pv, lds.ent, c.page), pv.fp8_stride);
+    const int kso = 16 * c.sub * D;                      // the tile's first K row
+    const int vso = kso + vcode_delta;                   // and its first V row
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(codes + code_off[j]);
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(codes + (code_off[j] + vcode_delta));
+      if constexpr (LB % 16 == 0) {
 #pragma unroll
-      for (int x = 0; x < LB / 4; ++x) {
-        r.kw[j][x] = kp[x];
-        r.vw[j][x] = vp[x];
+        for (int x = 0; x < LB / 16; ++x) {
+          const u32x4 kw = rec_load4(rec, code_off[j] + 16 * x, kso);
+          const u32x4 vw = rec_load4(rec, code_off[j] + 16 * x, vso);
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            r.kw[j][4 * x + y] = kw[y];
+            r.vw[j][4 * x + y] = vw[y];
+          }
+        }
+      } else {
+        static_assert(LB == 8, "an FP8 lane row share is 8 or a multiple of 16 bytes");
+        const u32x2 kw = rec_load2(rec, code_off[j], kso);
+        const u32x2 vw = rec_load2(rec, code_off[j], vso);
+        r.kw[j][0] = kw[0];
+        r.kw[j][1] = kw[1];
+        r.vw[j][0] = vw[0];
+        r.vw[j][1] = vw[1];
       }
-      r.sigk[j] = *reinterpret_cast<const float*>(page + ks_off[j]);
-      r.sigv[j] = *reinterpret_cast<const float*>(page + vs_off[j]);
+      r.sigk[j] = __builtin_bit_cast(float, rec_load1(rec, 0, ks_off[j]));
+      r.sigv[j] = __builtin_bit_cast(float, rec_load1(rec, 0, vs_off[j]));
     }
   };
   const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
