@@ -100,7 +100,10 @@ __device__ __forceinline__ uint32_t sub_f16x2(uint32_t x, uint32_t c) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// ---- TQ3 unit unpack -------------------------------------------------------
+// f16 bits of 1 + 3.5 * 2^(k-10) = 1 + 7 * 2^(k-11)
+constexpr uint32_t center_bits(int k) { return 0x3C00u + (7u << (k - 1)); }
+
+// ---- TQ3 key unit unpack ---------------------------------------------------
 // A unit is 8 consecutive codes (24 bits, code i at bit 3i; bits 24..31 are
 // ignored).  It becomes four dwords of f16 pairs holding (c - 3.5) * 2^(k-10):
 //   slot:        0   1   2   3   4   5   6   7
@@ -114,16 +117,6 @@ __device__ __forceinline__ uint32_t sub_f16x2(uint32_t x, uint32_t c) {
 // exact and, as |c - 3.5| >= 1/2, an f16 normal number.
 constexpr int kSlotCode[8] = {2, 6, 3, 7, 4, 0, 5, 1};
 constexpr int kSlotShift[8] = {6, 2, 7, 3, 3, 7, 3, 7};
-// The same tables as nibbles (entry s at bits 4s..4s+3) for run-time lookups.
-constexpr uint32_t pack_nibbles(const int (&v)[8]) {
-  uint32_t r = 0;
-  for (int i = 0; i < 8; ++i) r |= uint32_t(v[i]) << (4 * i);
-  return r;
-}
-constexpr uint32_t kSlotCodePacked = pack_nibbles(kSlotCode);
-constexpr uint32_t kSlotShiftPacked = pack_nibbles(kSlotShift);
-// f16 bits of 1 + 3.5 * 2^(k-10) = 1 + 7 * 2^(k-11)
-constexpr uint32_t center_bits(int k) { return 0x3C00u + (7u << (k - 1)); }
 constexpr uint32_t center_pair(int slot) {
   return center_bits(kSlotShift[slot]) | (center_bits(kSlotShift[slot + 1]) << 16);
 }
@@ -149,6 +142,78 @@ __device__ __forceinline__ void tq3_split_units(const uint32_t d[3], uint32_t u[
   u[1] = __builtin_amdgcn_alignbit(d[1], d[0], 24);
   u[2] = __builtin_amdgcn_alignbit(d[2], d[1], 16);
   u[3] = d[2] >> 8;
+}
+
+// ---- TQ3 value group unpack ------------------------------------------------
+// A group is 32 codes held as three little-endian dwords, code i at bits
+// 3i .. 3i+2.  Read as a ring of 96 bits, any 32-bit window starting at bit b
+// is one funnel shift of two of the dwords (no shift for b = 0, 32, 64).  One
+// AND-OR of a window keeps two codes, code lo at bits k_lo .. k_lo+2 of the
+// low half and code hi at bits 16+k_hi .. 18+k_hi (1 <= k <= 7, inside the
+// f16 mantissa field), on top of the exponent of 1.0; subtracting
+// 1 + 3.5 * 2^(k-10) leaves (c - 3.5) * 2^(k-10).  Both operands lie in
+// [1, 2) and the constant has at most 10 fraction bits because k >= 1, so the
+// difference is exact and, as |c - 3.5| >= 1/2, an f16 normal number.  The
+// sixteen pairs below, (window start, lo, hi), cover the group with six
+// shifted windows; the bit offsets follow from them.  (Value tiles are
+// unpacked once per tile by the lane that loads the group, so the whole group
+// is at hand; key operands are unpacked per MFMA chunk from units instead.)
+struct Tq3Pair {
+  int win, lo, hi;
+};
+constexpr Tq3Pair kValuePairs[16] = {
+    {0, 2, 7},    {6, 3, 8},    {6, 4, 9},    {13, 5, 10},  {13, 6, 12},  {32, 11, 17},
+    {32, 13, 18}, {40, 14, 19}, {41, 15, 20}, {41, 16, 21}, {64, 22, 28}, {64, 23, 29},
+    {70, 24, 30}, {70, 25, 31}, {77, 26, 0},  {77, 27, 1}};
+constexpr int kappa_lo(const Tq3Pair& p) { return (3 * p.lo - p.win + 96) % 96; }
+constexpr int kappa_hi(const Tq3Pair& p) { return (3 * p.hi - p.win + 96) % 96 - 16; }
+constexpr uint32_t pair_mask(const Tq3Pair& p) {
+  return (7u << kappa_lo(p)) | (7u << (16 + kappa_hi(p)));
+}
+constexpr bool is_cover(const Tq3Pair (&t)[16], int kmin) {
+  uint32_t seen = 0;
+  for (const Tq3Pair& p : t) {
+    const int a = kappa_lo(p), b = kappa_hi(p);
+    if (a < kmin || a > 7 || b < kmin || b > 7 || p.win < 0 || p.win >= 96) return false;
+    const uint32_t bits = (1u << p.lo) | (1u << p.hi);
+    if ((seen & bits) != 0 || p.lo == p.hi) return false;
+    seen |= bits;
+  }
+  return seen == 0xFFFFFFFFu;
+}
+static_assert(is_cover(kValuePairs, 1), "TQ3 value pair cover");
+constexpr uint32_t value_center(const Tq3Pair& p) {
+  return center_bits(kappa_lo(p)) | (center_bits(kappa_hi(p)) << 16);
+}
+
+// Value position 2p + h (half h of pair p) as a byte (dim-in-group | k << 5),
+// 8 per 64-bit word, for run-time lookups.
+constexpr uint64_t value_pos_word(int w) {
+  uint64_t r = 0;
+  for (int i = 0; i < 8; ++i) {
+    const int pos = 8 * w + i;
+    const Tq3Pair& p = kValuePairs[pos / 2];
+    const int e = (pos & 1) ? (p.hi | (kappa_hi(p) << 5)) : (p.lo | (kappa_lo(p) << 5));
+    r |= uint64_t(e) << (8 * i);
+  }
+  return r;
+}
+constexpr uint64_t kValuePos[4] = {value_pos_word(0), value_pos_word(1), value_pos_word(2),
+                                   value_pos_word(3)};
+
+// 32-bit window of a group starting at ring bit b (a constant after unrolling).
+__device__ __forceinline__ uint32_t group_window(const uint32_t (&w)[3], int b) {
+  const uint32_t lo = w[b >> 5], hi = w[((b >> 5) + 1) % 3];
+  return (b & 31) == 0 ? lo : __builtin_amdgcn_alignbit(hi, lo, b & 31);
+}
+
+// Value group -> 16 dwords of centred f16 pairs, pair p in dword p.
+__device__ __forceinline__ void tq3_value_group(const uint32_t (&w)[3], uint32_t one,
+                                                uint32_t (&o)[16]) {
+#pragma unroll
+  for (int p = 0; p < 16; ++p)
+    o[p] = sub_f16x2(and_or(group_window(w, kValuePairs[p].win), pair_mask(kValuePairs[p]), one),
+                     value_center(kValuePairs[p]));
 }
 
 // ---- FP8 -> f16 -------------------------------------------------------------
@@ -331,11 +396,13 @@ __device__ __forceinline__ const uint8_t* entry_page(const PoolView& pv, const i
 }
 
 // Runs the tile pipeline over the wave's range: R raw buffers in flight;
-// process(raw, cursor, refill) consumes one tile and calls refill(raw) to
+// prepare() runs once the first loads are issued; process(raw, cursor,
+// refill) consumes one tile and calls refill(raw) to
 // load a later one.  The steady-state loop issues the same loads on every
 // path.
-template <int R, typename Raw, typename Load, typename Process>
-__device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Process process) {
+template <int R, typename Raw, typename Load, typename Prepare, typename Process>
+__device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Prepare prepare,
+                                          Process process) {
   if (g.ntiles == 0) return;
   Raw ring[R];
   Cursor lc = g.first;
@@ -344,6 +411,7 @@ __device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Process 
     load(lc, ring[k]);
     advance_clamped(lc, g);
   }
+  prepare();
   Cursor pc = g.first;
   int ti = 0;
   for (; ti + R <= g.ntiles; ti += R) {
@@ -457,13 +525,14 @@ __device__ __forceinline__ void softmax_step(SoftState& st, float s[4], float p[
 // head hq0 + col (live if col < NH * G) and belongs to kv-head jcol = col / G
 // of the wave; qop[j] holds the column only for j == jcol (zero otherwise), so
 // the MFMAs of the NH kv-heads accumulate into one D.  For MFMA g the lane's 8
-// k-slots hold head dims base_dim(g) + perm(s), s = 0..7 (8 consecutive dims,
-// read as one 16-byte load); shift(s) is the slot's extra power-of-two
-// exponent.  Returns the column's exponent E.
-template <int NG, int NH, typename BaseDim, typename SlotPerm, typename SlotShift>
+// k-slots hold the head dims fetch(qrow, g, v) reads into v[0..7]; conv(x, E,
+// s) turns value x of slot s into the operand, given the column's exponent E
+// (max|q| * 2^E in [64, 128)).  qh[g] is the column's operand before the
+// kv-head selection.  Returns E.
+template <int NG, int NH, typename Fetch, typename Conv>
 __device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, int col, int ncol,
-                                          int jcol, half8 (&qop)[NH][NG], BaseDim base_dim,
-                                          SlotPerm perm, SlotShift shift) {
+                                          int jcol, half8 (&qop)[NH][NG], half8 (&qh)[NG],
+                                          Fetch fetch, Conv conv) {
   constexpr int D = 32 * NG;
   const bool live = col < ncol;
   const uint16_t* qrow = a.q + (int64_t(b) * a.Hq + hq0 + (live ? col : 0)) * D;
@@ -471,24 +540,28 @@ __device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, i
   float amax = 0.0f;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + base_dim(g));
+    fetch(qrow, g, qv[g]);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int e = perm(s);
-      const float x = bf16_to_f32(uint16_t(w[e >> 1] >> (16 * (e & 1))));
-      qv[g][s] = live ? x : 0.0f;
+      qv[g][s] = live ? qv[g][s] : 0.0f;
       amax = fmaxf(amax, fabsf(qv[g][s]));
     }
   }
   amax = quad_max(amax);
   const int E = q_shift(amax);
 #pragma unroll
-  for (int j = 0; j < NH; ++j)
+  for (int g = 0; g < NG; ++g) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int s = 0; s < 8; ++s) qh[g][s] = conv(qv[g][s], E, s);
+    const u32x4 w = __builtin_bit_cast(u32x4, qh[g]);
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qop[j][g][s] = jcol == j ? _Float16(__builtin_amdgcn_ldexpf(qv[g][s], E + shift(s))) : _Float16(0.0f);
+    for (int j = 0; j < NH; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) o[x] = jcol == j ? w[x] : 0u;
+      qop[j][g] = __builtin_bit_cast(half8, o);
+    }
+  }
   return E;
 }
 
@@ -573,11 +646,24 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 
   // ---- query operands: slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s],
   // scaled by 2^(E + 7 - kSlotShift[s]) against the key slot's 2^(k-10)
+  // (prepared once the first tiles' loads are in flight)
   half8 qop[NH][NG];
-  const int E = load_query<NG, NH>(
-      a, it.b, hq0, col, ncol, jcol, qop, [&](int g) { return 32 * g + 8 * quad; },
-      [](int s) { return kSlotCode[s]; }, [](int s) { return 7 - kSlotShift[s]; });
-  const float F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
+  float F;
+  auto prepare = [&]() {
+    half8 qh[NG];
+    const int E = load_query<NG, NH>(
+        a, it.b, hq0, col, ncol, jcol, qop, qh,
+        [&](const uint16_t* qrow, int g, float (&v)[8]) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const int e = kSlotCode[s];
+            v[s] = bf16_to_f32(uint16_t(w[e >> 1] >> (16 * (e & 1))));
+          }
+        },
+        [](float x, int E, int s) { return _Float16(__builtin_amdgcn_ldexpf(x, E + 7 - kSlotShift[s])); });
+    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
+  };
 
   f32x4 acc[NH * NT];
 #pragma unroll
@@ -670,11 +756,12 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
           tq3_split_units(raw.kc[j][i], u);
 #pragma unroll
           for (int un = 0; un < 4; ++un) W.kst[j][col * KST + un * NG + g] = u[un];
-          tq3_split_units(raw.vc[j][i], u);
+          uint32_t o[16];
+          tq3_value_group(raw.vc[j][i], one, o);
+          uint8_t* vd = W.vt[j] + col * VROW + 64 * g;
 #pragma unroll
-          for (int un = 0; un < 4; ++un)
-            *reinterpret_cast<u32x4*>(W.vt[j] + col * VROW + 2 * (32 * g + 8 * un)) =
-                tq3_unit_to_f16(u[un], one);
+          for (int c4 = 0; c4 < 4; ++c4)
+            *reinterpret_cast<u32x4*>(vd + 16 * c4) = u32x4{o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]};
         }
       }
     }
@@ -724,7 +811,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     }
     wave_lds_sync();
   };
-  run_tiles<R, Raw>(tg, load, process);
+  run_tiles<R, Raw>(tg, load, prepare, process);
 
   // ---- combine the four waves' states through LDS (the tile staging is
   // reused once every wave is past its last tile) and write the item's state
@@ -735,19 +822,23 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     M.m[wave][col] = st.m;
     M.l[wave][col] = lcol;
   }
-  // accumulator column col of N-tile jt is dim 16*jt + col in slot order;
-  // slot s of a unit holds dim kSlotCode[s] scaled by 2^(kSlotShift[s]-10)
-  const int slot = col & 7;
-  const int dim_in_unit = int(kSlotCodePacked >> (4 * slot)) & 15;
-  const float up = __builtin_amdgcn_ldexpf(1.0f, 10 - (int(kSlotShiftPacked >> (4 * slot)) & 15));
+  // accumulator column col of N-tile jt holds value position 16 (jt & 1) + col
+  // of group jt / 2 (half pos & 1 of value pair pos / 2), scaled by 2^(k-10)
+  const uint64_t we = (col & 8) ? kValuePos[1] : kValuePos[0];
+  const uint64_t wo = (col & 8) ? kValuePos[3] : kValuePos[2];
+  const int ee = int(we >> (8 * (col & 7))) & 255, eo = int(wo >> (8 * (col & 7))) & 255;
+  const float up_e = __builtin_amdgcn_ldexpf(1.0f, 10 - (ee >> 5));
+  const float up_o = __builtin_amdgcn_ldexpf(1.0f, 10 - (eo >> 5));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
     if (c >= ncol) continue;
     const int jc = c / G;
-    float* dst = M.acc[wave] + c * MergeLds<D>::ROW + (col & 8) + dim_in_unit;
+    float* dst = M.acc[wave] + c * MergeLds<D>::ROW;
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) dst[16 * jt] = pick_head<NH, NT>(acc, jc, jt, i) * up;
+    for (int jt = 0; jt < NT; ++jt)
+      dst[32 * (jt >> 1) + ((jt & 1) ? (eo & 31) : (ee & 31))] =
+          pick_head<NH, NT>(acc, jc, jt, i) * ((jt & 1) ? up_o : up_e);
   }
   __syncthreads();
   merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
@@ -779,11 +870,21 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   auto& W = lds.w[wave];
 
   // ---- query operand: MFMA r, lane (col, quad), slot s <-> dim quad*LB + 8r + s
+  // (prepared once the first tiles' loads are in flight)
   half8 qop[NH][NG];
-  const int E = load_query<NG, NH>(
-      a, it.b, hq0, col, ncol, jcol, qop, [&](int r) { return quad * LB + 8 * r; },
-      [](int s) { return s; }, [](int) { return 0; });
-  const float F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
+  float F;
+  auto prepare = [&]() {
+    half8 qh[NG];
+    const int E = load_query<NG, NH>(
+        a, it.b, hq0, col, ncol, jcol, qop, qh,
+        [&](const uint16_t* qrow, int r, float (&v)[8]) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + quad * LB + 8 * r);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) v[s] = bf16_to_f32(uint16_t(w[s >> 1] >> (16 * (s & 1))));
+        },
+        [](float x, int E, int) { return _Float16(__builtin_amdgcn_ldexpf(x, E)); });
+    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
+  };
 
   f32x4 acc[NH * NT];
 #pragma unroll
@@ -889,7 +990,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
       }
     wave_lds_sync();
   };
-  run_tiles<R, Raw>(tg, load, process);
+  run_tiles<R, Raw>(tg, load, prepare, process);
 
   const float lcol = quad_sum(st.l);
   __syncthreads();
