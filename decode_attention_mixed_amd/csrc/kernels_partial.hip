@@ -274,11 +274,12 @@ __device__ __forceinline__ short4v read_tr(const uint8_t* p) {
 
 // B operand of the PV MFMA: the value entries V[4quad + j][n] of the lane's
 // column n, transposed out of the row-major LDS tile, in both halves (read
-// twice, so the operand lands in place without register copies; the fence
-// keeps the compiler from merging the two reads).
+// twice, so the operand lands in place without register copies; the empty
+// asm with a memory clobber keeps the compiler from merging the two reads
+// without making the hardware wait between them).
 __device__ __forceinline__ half8 value_operand(const uint8_t* p) {
   const u32x2 a = __builtin_bit_cast(u32x2, read_tr(p));
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  asm volatile("" ::: "memory");
   const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p));
   const u32x4 d = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(half8, d);
@@ -286,12 +287,13 @@ __device__ __forceinline__ half8 value_operand(const uint8_t* p) {
 
 // ---- cross-lane helpers -----------------------------------------------------
 
-// Orders one wave's LDS writes before its later LDS reads of other lanes' data.
-// The lanes of a wave issue LDS operations in program order, so no hardware
-// wait is needed; the fence only stops the compiler from moving accesses
-// across this point.
+// Orders one wave's LDS accesses around this point (writes before later reads
+// of other lanes' data, reads before later overwrites).  The LDS executes one
+// wave's operations in program order, so no hardware wait is needed: this is
+// a compiler barrier only (a memory fence here would wait for every
+// outstanding LDS operation).
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_wave_barrier();
 }
 

@@ -246,7 +246,7 @@ def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
     # 131072 tokens, last 4096 FP8.  G = 6 puts two kv-heads on a workgroup,
     # so an item takes four 4-wave workgroups for its 8 kv-heads: 2048
     # resident waves give 128 items at most, of near-equal cost (an FP8 page
-    # costs 1.5 TQ3 pages).
+    # costs as much as a TQ3 page by default).
     h = _host(lib, num_kv_heads=8, max_seqs=1, max_pages_per_seq=8192, max_batch=1,
               max_q_heads=48, fp8_pages=8192, tq3_pages=8192, placement_seed=5)
     assert h.append(0, 131072)[0] == OK
@@ -255,8 +255,8 @@ def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
     assert st == OK
     assert 120 <= sc["n_chunks"] <= 128 and sc["n8"] >= 1 and sc["n3"] >= 1
     _check_coverage(h, [0], sc, 16)
-    cost = np.array([it[3] * (1.5 if it[6] == 0 else 1.0) for it in sc["items"]])
-    assert cost.max() <= 1.15 * (7936 + 1.5 * 256) / 128
+    cost = np.array([float(it[3]) for it in sc["items"]])
+    assert cost.max() <= 1.15 * (7936 + 256) / 128
     sizes3 = sc["items"][sc["n8"]:, 3]
     assert sizes3.max() - sizes3.min() <= 1
     # algorithmic bytes: 126976 TQ3 tokens * 896 B + 4096 FP8 tokens * 2048 B + 256 pages * 64 B
