@@ -8,13 +8,17 @@
 //   O = sum_i acc_i 2^(m_i - M) / L,  LSE = (M + log2 L) * ln 2.
 // A chunk with l == 0 holds no token and is skipped.
 //
-// One workgroup per (b, h, 16-dim slice).  Thread (j, k) owns dims 4j..4j+3
-// of the slice for chunks k, k+64, ...; it loads a batch of up to kUnroll of
-// them (max, denominator and a float4 of the accumulator) at once, so a
-// batch of 64 * kUnroll chunks costs one memory round trip.  The batch
-// maximum is reduced over the workgroup, the thread accumulates its chunks
-// with weights 2^(m_i - M) (rescaling earlier batches if M rose), and the 64
-// chunk lanes are summed through shuffles and LDS at the end.
+// Two variants.  Wide (many chunks per sequence): one workgroup per (b, h,
+// 16-dim slice).  Thread (j, k) owns dims 4j..4j+3 of the slice for chunks k,
+// k+64, ...; it loads a batch of up to kUnroll of them (max, denominator and
+// a float4 of the accumulator) at once, so a batch of 64 * kUnroll chunks
+// costs one memory round trip.  The batch maximum is reduced over the
+// workgroup, the thread accumulates its chunks with weights 2^(m_i - M)
+// (rescaling earlier batches if M rose), and the 64 chunk lanes are summed
+// through shuffles and LDS at the end.  Narrow (few chunks per sequence, as
+// in large batches): one wave per 256/d query heads, d/4 lanes per head; a
+// lane owns dims 4j..4j+3 of its head and walks all of the head's chunks
+// itself in batches of kUnroll, so it needs no cross-lane reduction.
 #include <hip/hip_runtime.h>
 
 #include "mkv_device.hpp"
@@ -116,9 +120,70 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(64) merge_narrow_kernel(DecodeArgs a) {
+  const int d = a.pv.d;
+  const int lanes_per_head = d / 4;                // 8 .. 64
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x * (64 / lanes_per_head) + lane / lanes_per_head;   // b * Hq + h
+  const int j = lane % lanes_per_head;
+  if (row >= a.B * a.Hq) return;
+  const int b = row / a.Hq, h = row % a.Hq;
+  const int c0 = a.chunk_base[b], c1 = a.chunk_base[b + 1];
+  float M = -INFINITY;
+  float L = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int cb = c0; cb < c1; cb += kUnroll) {
+    float m[kUnroll], l[kUnroll];
+    float4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = cb + u;
+      const bool ok = c < c1;
+      const int64_t i = int64_t(ok ? c : c0) * a.Hq + h;
+      m[u] = a.pm[i];
+      l[u] = ok ? a.pl[i] : 0.0f;
+      v[u] = *reinterpret_cast<const float4*>(a.pacc + i * d + 4 * j);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (l[u] > 0.0f) bm = fmaxf(bm, m[u]);
+    if (bm > M) {
+      const float r = exp2f(M - bm);
+      L *= r;
+      acc.x *= r;
+      acc.y *= r;
+      acc.z *= r;
+      acc.w *= r;
+      M = bm;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (!(l[u] > 0.0f)) continue;
+      const float w = exp2f(m[u] - M);
+      L += l[u] * w;
+      acc.x += v[u].x * w;
+      acc.y += v[u].y * w;
+      acc.z += v[u].z * w;
+      acc.w += v[u].w * w;
+    }
+  }
+  const float inv = 1.0f / L;
+  *reinterpret_cast<float4*>(a.out + int64_t(row) * d + 4 * j) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (j == 0) a.lse[row] = (M + log2f(L)) * 0.69314718055994531f;
+}
+
 }  // namespace
 
-hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_merge(const DecodeArgs& a, int narrow_max, hipStream_t s) {
+  if (a.max_seq_chunks <= narrow_max) {
+    const int heads_per_wave = 256 / a.pv.d;
+    const int rows = a.B * a.Hq;
+    hipLaunchKernelGGL(merge_narrow_kernel, dim3(unsigned((rows + heads_per_wave - 1) / heads_per_wave)),
+                       dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   const int nslices = a.pv.d / kSlice;
   hipLaunchKernelGGL(merge_kernel, dim3(unsigned(a.B * a.Hq * nslices)), dim3(kMergeThreads), 0,
                      s, a);

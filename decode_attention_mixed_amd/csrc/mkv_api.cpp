@@ -120,6 +120,7 @@ struct mkv_pool {
   std::vector<int32_t> sched_ids;
   mkv::Schedule sched;
   int32_t target_waves[2] = {2048, 1024};   // resident partial-kernel waves, 1 or 2 heads per wave
+  int32_t merge_narrow_max = 16;            // per-lane merge up to this many chunks per entry
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
@@ -212,7 +213,9 @@ mkv_status prof_collect(mkv_pool* p) {
 
 // Split-K policy of a pool: balanced chunks for the device's resident
 // partial-kernel waves.  Environment overrides (for tuning): MKV_CHUNK_PAGES
-// (fixed chunk length), MKV_TARGET_WAVES, MKV_FP8_PAGE_COST.
+// (fixed chunk length), MKV_TARGET_WAVES, MKV_FP8_PAGE_COST,
+// MKV_HEADS_PER_WAVE; MKV_MERGE_NARROW_MAX (read at pool creation) sets the
+// largest per-entry chunk count merged by the per-lane merge kernel.
 mkv::SchedPolicy pool_policy(const mkv_pool* p, int32_t Hq) {
   mkv::SchedPolicy pol;
   const mkv::Geom& g = p->meta.geom();
@@ -278,6 +281,7 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
     if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
     if (waves > 0) p->target_waves[nh - 1] = waves;
   }
+  if (const char* ev = std::getenv("MKV_MERGE_NARROW_MAX")) p->merge_narrow_max = std::max(0, std::atoi(ev));
   if (device_mem) {
     if (bytes < p->lay.total) return cleanup(MKV_ERANGE, "device buffer smaller than mkv_pool_bytes");
     if (reinterpret_cast<uintptr_t>(device_mem) % 256)
@@ -416,6 +420,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   a.out = out;
   a.lse = lse;
   a.nh = sc.heads_per_wave;
+  a.max_seq_chunks = sc.max_seq_chunks;
   a.items = items;
   a.n_items = int32_t(sc.items[0].size() + sc.items[1].size());
   {
@@ -424,7 +429,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     prof_end(p, e, s);
   }
   ProfEvent* e = prof_begin(p, 1, s);
-  MKV_HIP(mkv::launch_merge(a, s));
+  MKV_HIP(mkv::launch_merge(a, p->merge_narrow_max, s));
   prof_end(p, e, s);
   return MKV_OK;
 }

@@ -34,6 +34,7 @@ struct DecodeArgs {
   float* out;               // [B][Hq][d]
   float* lse;               // [B][Hq]
   int32_t nh;               // kv-heads per partial-kernel workgroup (1 or 2)
+  int32_t max_seq_chunks;   // most partial states of one batch entry
 };
 
 hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
@@ -46,6 +47,8 @@ hipError_t launch_partial(const DecodeArgs& a, hipStream_t s);
 // Waves of the partial kernel (head dim d, nh kv-heads per wave) resident on
 // the current device at once.
 hipError_t partial_resident_waves(int d, int nh, int* waves);
-hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
+// Merge of the partial states; batches with at most narrow_max chunks per
+// entry use the per-lane variant (no cross-lane reduction).
+hipError_t launch_merge(const DecodeArgs& a, int narrow_max, hipStream_t s);
 
 }  // namespace mkv

@@ -287,6 +287,10 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
   }
   out->chunk_base[size_t(B)] = nc;
   out->n_chunks = nc;
+  out->max_seq_chunks = 0;
+  for (int32_t b = 0; b < B; ++b)
+    out->max_seq_chunks =
+        std::max(out->max_seq_chunks, out->chunk_base[size_t(b) + 1] - out->chunk_base[size_t(b)]);
   out->chunk_pages = largest;
   out->heads_per_wave = heads_per_block;
   return MKV_S_OK;

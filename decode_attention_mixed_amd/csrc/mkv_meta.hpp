@@ -116,6 +116,7 @@ struct Schedule {
   int32_t heads_per_wave = 1;       // kv-heads per partial-kernel workgroup
   int32_t n_chunks = 0;
   int32_t chunk_pages = 0;          // largest chunk of the schedule
+  int32_t max_seq_chunks = 0;       // most chunks of one batch entry
 };
 
 class Meta {

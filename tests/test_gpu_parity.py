@@ -196,6 +196,22 @@ def test_error_paths_through_the_abi():
     pool.close()
 
 
+@pytest.mark.parametrize("narrow_max", ["0", "1000"])
+def test_both_merge_kernels(monkeypatch, narrow_max):
+    """The per-lane merge (few chunks per entry) and the workgroup-reduced merge
+    (many), each forced through MKV_MERGE_NARROW_MAX on a schedule of one page
+    per chunk (up to 38 chunks per sequence, 1 for the 33-token one)."""
+    monkeypatch.setenv("MKV_MERGE_NARROW_MAX", narrow_max)
+    monkeypatch.setenv("MKV_CHUNK_PAGES", "1")
+    wl = W.small(seed=61, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(600, 33, 257))
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, *OS.decode_all(wl, models), f"merge_narrow_max={narrow_max}")
+    pool.close()
+
+
 NAMED = ["tiny", "ragged", "sweep0", "sweep10", "sweep50", "sweep100"]
 
 
@@ -242,3 +258,29 @@ def test_long_context_full_parity(long_case):
     out2, lse2 = _run_decode(pool, wl)
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
     pool.close()
+
+
+def test_throughput_batch_sampled_parity():
+    """The B=64 throughput batch at full size: 16K-32K-token sequences whose
+    pages scatter over slabs holding 60% of HBM, decoded in one call over the
+    whole batch as the benchmark times it.  Every output is finite; a seeded
+    sample of sequences (the shortest, the longest and two others) is checked
+    element by element against the oracle."""
+    wl = W.throughput()
+    print(f"throughput: B={wl.B} tokens={int(np.sum(wl.lengths))} "
+          f"slabs fp8={wl.fp8_pages} tq3={wl.tq3_pages} pages", flush=True)
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    print("throughput: cache built", flush=True)
+    out, lse = _run_decode(pool, wl)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    lengths = np.asarray(wl.lengths)
+    picks = {int(lengths.argmin()), int(lengths.argmax())}
+    picks |= set(int(x) for x in np.random.default_rng(7).choice(wl.B, 2, replace=False))
+    for b in sorted(picks):
+        model = OS.seq_model(wl, b)
+        Ob, Lb = A.decode_seq(model, wl.q_bits[b], wl.tau)
+        _check(out[b], lse[b], Ob, Lb, f"throughput[{b}] L={int(lengths[b])}")
+    pool.close()
+    del pool
+    torch.cuda.empty_cache()
