@@ -8,14 +8,14 @@
 //   O = sum_i acc_i 2^(m_i - M) / L,  LSE = (M + log2 L) * ln 2.
 // A chunk with l == 0 holds no token and is skipped.
 //
-// Two variants.  Wide (many chunks per sequence): one workgroup per (b, h,
-// 16-dim slice).  Thread (j, k) owns dims 4j..4j+3 of the slice for chunks k,
-// k+64, ...; it loads a batch of up to kUnroll of them (max, denominator and
-// a float4 of the accumulator) at once, so a batch of 64 * kUnroll chunks
-// costs one memory round trip.  The batch maximum is reduced over the
-// workgroup, the thread accumulates its chunks with weights 2^(m_i - M)
-// (rescaling earlier batches if M rose), and the 64 chunk lanes are summed
-// through shuffles and LDS at the end.  Narrow (few chunks per sequence, as
+// Two variants.  Wide (many chunks per sequence): one wave per (b, h, 16-dim
+// slice).  Lane (j, k) owns dims 4j..4j+3 of the slice for chunks k, k+16,
+// ...; it loads a batch of up to kUnroll of them (max, denominator and a
+// float4 of the accumulator) at once, so a batch of 16 * kUnroll chunks costs
+// one memory round trip.  The batch maximum is reduced over the wave, the lane
+// accumulates its chunks with weights 2^(m_i - M) (rescaling earlier batches
+// if M rose), and the 16 chunk lanes are summed with shuffles at the end (no
+// LDS, no workgroup barrier).  Narrow (few chunks per sequence, as
 // in large batches): one wave per 256/d query heads, d/4 lanes per head; a
 // lane owns dims 4j..4j+3 of its head and walks all of the head's chunks
 // itself in batches of kUnroll, so it needs no cross-lane reduction.
@@ -27,12 +27,11 @@ namespace mkv {
 
 namespace {
 
-constexpr int kMergeThreads = 256;
-constexpr int kSlice = 16;                         // dims per workgroup
-constexpr int kVecLanes = kSlice / 4;              // threads per chunk (float4 each)
+constexpr int kMergeThreads = 64;
+constexpr int kSlice = 16;                         // dims per wave
+constexpr int kVecLanes = kSlice / 4;              // lanes per chunk (float4 each)
 constexpr int kChunkLanes = kMergeThreads / kVecLanes;
 constexpr int kUnroll = 8;
-constexpr int kMergeWaves = kMergeThreads / 64;
 
 __device__ __forceinline__ float wave_max(float x) {
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
@@ -40,8 +39,6 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
-  __shared__ float red_m[kMergeWaves];
-  __shared__ float red_acc[kMergeWaves][kVecLanes][5];
   const int d = a.pv.d;
   const int nslices = d / kSlice;
   const int bh = blockIdx.x / nslices;
@@ -50,7 +47,6 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   const int c0 = a.chunk_base[b], c1 = a.chunk_base[b + 1];
   const int t = threadIdx.x;
   const int j = t % kVecLanes, k = t / kVecLanes;
-  const int lane = t & 63, wave = t >> 6;
 
   float M = -INFINITY;                 // running maximum over live chunks
   float L = 0.0f;                      // this thread's share of the denominator
@@ -72,11 +68,6 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
     for (int u = 0; u < kUnroll; ++u)
       if (l[u] > 0.0f) bm = fmaxf(bm, m[u]);
     bm = wave_max(bm);
-    if (lane == 0) red_m[wave] = bm;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) bm = fmaxf(bm, red_m[w]);
-    __syncthreads();
     if (bm > M) {                      // rescale what earlier batches accumulated
       const float r = exp2f(M - bm);   // 0 on the first live batch
       L *= r;
@@ -97,26 +88,16 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
       acc.w += v[u].w * w;
     }
   }
-  // sum over the chunk lanes: within a wave (lanes j + 8k'), then across waves
+  // sum over the chunk lanes (lanes j + 4k')
   float r5[5] = {acc.x, acc.y, acc.z, acc.w, L};
 #pragma unroll
   for (int e = 0; e < 5; ++e)
     for (int off = kVecLanes; off < 64; off <<= 1) r5[e] += __shfl_xor(r5[e], off, 64);
-  if (lane < kVecLanes) {
-#pragma unroll
-    for (int e = 0; e < 5; ++e) red_acc[wave][lane][e] = r5[e];
-  }
-  __syncthreads();
   if (t < kVecLanes) {
-    float s5[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w)
-#pragma unroll
-      for (int e = 0; e < 5; ++e) s5[e] += red_acc[w][t][e];
-    const float inv = 1.0f / s5[4];
+    const float inv = 1.0f / r5[4];
     *reinterpret_cast<float4*>(a.out + (int64_t(b) * a.Hq + h) * d + slice * kSlice + 4 * t) =
-        make_float4(s5[0] * inv, s5[1] * inv, s5[2] * inv, s5[3] * inv);
-    if (t == 0 && slice == 0) a.lse[int64_t(b) * a.Hq + h] = (M + log2f(s5[4])) * 0.69314718055994531f;
+        make_float4(r5[0] * inv, r5[1] * inv, r5[2] * inv, r5[3] * inv);
+    if (t == 0 && slice == 0) a.lse[int64_t(b) * a.Hq + h] = (M + log2f(r5[4])) * 0.69314718055994531f;
   }
 }
 
