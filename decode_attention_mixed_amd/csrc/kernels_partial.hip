@@ -250,13 +250,6 @@ __device__ __forceinline__ half8 pprime(const float p[4], const float sv[4]) {
   return r;
 }
 
-// TQ3: the value scales of the lane's 4 tokens for one group, as f16 pairs
-// (tokens 0, 1 in w0 and 2, 3 in w1).
-__device__ __forceinline__ half8 pprime_group(const float p[4], uint32_t w0, uint32_t w1) {
-  const float sv[4] = {f16_half(w0, 0), f16_half(w0, 1), f16_half(w1, 0), f16_half(w1, 1)};
-  return pprime(p, sv);
-}
-
 // FP8: one scale for all four tokens (page-head scale).
 __device__ __forceinline__ half8 pprime_uniform(const float p[4], float s) {
   const float sv[4] = {s, s, s, s};
@@ -575,6 +568,24 @@ static_assert(value_row_bytes(128) == 304 && value_row_bytes(64) % 16 == 0 &&
                   (value_row_bytes(32) / 4) % 64 == 12 && (value_row_bytes(256) / 4) % 64 == 12,
               "value row stride");
 
+// The 2NG scale dwords of a lane's four tokens (16-byte reads; 8 bytes when
+// NG = 1).
+template <int NG>
+__device__ __forceinline__ void load_scale_dwords(const uint32_t* p, uint32_t (&o)[2 * NG]) {
+  if constexpr (NG == 1) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    o[0] = w[0];
+    o[1] = w[1];
+  } else {
+#pragma unroll
+    for (int x = 0; x < NG / 2; ++x) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p + 4 * x);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) o[4 * x + y] = w[y];
+    }
+  }
+}
+
 // LDS images of the two work-item kinds (one of them per workgroup).
 template <int NG, int NH>
 struct Tq3Lds {
@@ -585,7 +596,7 @@ struct Tq3Lds {
   struct Wave {
     alignas(16) uint32_t kst[NH][16 * KST];     // key units, [token][unit][group]
     alignas(16) uint8_t vt[NH][16 * VROW];      // value tiles, [token][D] f16
-    alignas(16) uint32_t sc[NH][SD + 4];        // tile scales as f16 [K, V][group][token] (padded)
+    alignas(16) uint32_t sc[NH][SD + 4];        // tile scales as f16 [K, V][token][group] (padded)
     float corr[16];
   };
   int32_t ent[kMaxChunkPages];                  // page-table entries of the work item
@@ -729,25 +740,21 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
       // scales: the lane's dword holds f16 k0 = 2e' and k0 + 1 of the tile's
-      // K (e < 8NG) or V block, f16 k being (token k / NG, group k % NG);
-      // they are stored transposed, [group][token], so a lane later reads
-      // its 4 tokens of a group as one 8-byte word.  Value scales of masked
+      // K (e < 8NG) or V block, f16 k being (token k / NG, group k % NG), and
+      // is stored in place ([K, V][token][group]).  Value scales of masked
       // tokens become 0 (an unwritten slot may hold NaN, and p = 0 times NaN
       // is NaN).
-      uint16_t* sc16 = reinterpret_cast<uint16_t*>(W.sc[j]);
 #pragma unroll
       for (int i = 0; i < SPL; ++i) {
         const int e = lane + 64 * i;
         if (e < SD) {
           const bool is_v = e >= 8 * NG;
           const int k0 = 2 * (is_v ? e - 8 * NG : e);
-          const int base = is_v ? 16 * NG : 0;
-          const int t0 = k0 / NG, g0 = k0 % NG, t1 = (k0 + 1) / NG, g1 = (k0 + 1) % NG;
-          uint16_t lo = uint16_t(raw.sc[j][i]), hi = uint16_t(raw.sc[j][i] >> 16);
-          if (is_v && t0 >= nvalid) lo = 0;
-          if (is_v && t1 >= nvalid) hi = 0;
-          sc16[base + 16 * g0 + t0] = lo;
-          sc16[base + 16 * g1 + t1] = hi;
+          const int t0 = k0 / NG, t1 = (k0 + 1) / NG;
+          uint32_t w = raw.sc[j][i];
+          if (is_v && t0 >= nvalid) w &= 0xFFFF0000u;
+          if (is_v && t1 >= nvalid) w &= 0x0000FFFFu;
+          W.sc[j][e] = w;
         }
       }
 #pragma unroll
@@ -772,7 +779,12 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 
     // ---- QK^T per group (the NH kv-heads into one D), scaled per token by
     // the group's key scale of the lane's column's kv-head
-    const uint32_t* scl = W.sc[jcol] + 2 * quad;   // + 8g: K scales, + 8NG + 8g: V scales
+    // the lane's tokens 4quad .. 4quad+3 hold 2NG consecutive scale dwords of
+    // each block: token 4quad+i, group g is half (i NG + g) & 1 of dword
+    // (i NG + g) >> 1
+    const uint32_t* scl = W.sc[jcol] + 2 * NG * quad;   // + 8NG: V scales
+    uint32_t ksd[2 * NG];
+    load_scale_dwords<NG>(scl, ksd);
     float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -783,9 +795,9 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
             __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[j][col * KST + quad * NG + g], one));
         dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[j][g], dg, 0, 0, 0);
       }
-      const u32x2 ks = *reinterpret_cast<const u32x2*>(scl + 8 * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dg[i], f16_half(ks[i >> 1], i & 1), s[i]);
+      for (int i = 0; i < 4; ++i)
+        s[i] = __builtin_fmaf(dg[i], f16_half(ksd[(i * NG + g) >> 1], (i * NG + g) & 1), s[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] *= F;
@@ -799,10 +811,14 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 
     // ---- per group: P' = p * value scale (hi/lo f16), acc_j += P' * V_j
     const int row = 4 * quad + (col >> 2);
+    uint32_t vsd[2 * NG];
+    load_scale_dwords<NG>(scl + 8 * NG, vsd);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const u32x2 vs = *reinterpret_cast<const u32x2*>(scl + 8 * NG + 8 * g);
-      const half8 pp = pprime_group(p, vs[0], vs[1]);
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = f16_half(vsd[(i * NG + g) >> 1], (i * NG + g) & 1);
+      const half8 pp = pprime(p, sv);
 #pragma unroll
       for (int j = 0; j < NH; ++j)
 #pragma unroll
