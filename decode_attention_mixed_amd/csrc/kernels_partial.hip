@@ -380,10 +380,11 @@ __device__ __forceinline__ u32x4 rec_load4(__amdgpu_buffer_rsrc_t r, uint32_t la
   return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, tile_off, 0);
 }
 
-// Page-table entries of a work item's pages, staged once per workgroup.
+// Page-table entries of a work item's pages (resolved by the host when it
+// builds the schedule, which any page-table change invalidates), staged once
+// per workgroup.
 __device__ __forceinline__ void stage_entries(int32_t* ent, const DecodeArgs& a, const WorkItem& it) {
-  const int32_t* pt_row = a.pv.pt + int64_t(it.seq) * a.pv.pt_stride;
-  for (int p = threadIdx.x; p < it.npages; p += kThreads) ent[p] = pt_row[a.pages[it.list_off + p]];
+  for (int p = threadIdx.x; p < it.npages; p += kThreads) ent[p] = a.entries[it.list_off + p];
   __syncthreads();
 }
 __device__ __forceinline__ const uint8_t* entry_page(const PoolView& pv, const int32_t* ent, int page) {

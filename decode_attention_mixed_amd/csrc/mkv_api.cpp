@@ -389,11 +389,11 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     std::memcpy(st8, sc.items[0].data(), n8 * 32);
     std::memcpy(st8 + n8 * 32, sc.items[1].data(), n3 * 32);
     const size_t items_bytes = (n8 + n3) * 32;
-    std::memcpy(st8 + items_bytes, sc.pages.data(), sc.pages.size() * 4);
-    std::memcpy(st8 + items_bytes + sc.pages.size() * 4, sc.chunk_base.data(),
+    std::memcpy(st8 + items_bytes, sc.entries.data(), sc.entries.size() * 4);
+    std::memcpy(st8 + items_bytes + sc.entries.size() * 4, sc.chunk_base.data(),
                 sc.chunk_base.size() * 4);
     std::vector<Upload> ups{{p->lay.sched, items_bytes},
-                            {p->lay.sched + p->lay.pages_off, sc.pages.size() * 4},
+                            {p->lay.sched + p->lay.pages_off, sc.entries.size() * 4},
                             {p->lay.sched + p->lay.base_off, sc.chunk_base.size() * 4}};
     p->sched_valid = false;
     r = flush_uploads(p, ups, s);
@@ -408,7 +408,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   const mkv::WorkItem* items = reinterpret_cast<const mkv::WorkItem*>(p->mem + p->lay.sched);
   mkv::DecodeArgs a{};
   a.pv = p->view();
-  a.pages = reinterpret_cast<const int32_t*>(p->mem + p->lay.sched + p->lay.pages_off);
+  a.entries = reinterpret_cast<const int32_t*>(p->mem + p->lay.sched + p->lay.pages_off);
   a.chunk_base = reinterpret_cast<const int32_t*>(p->mem + p->lay.sched + p->lay.base_off);
   a.q = static_cast<const uint16_t*>(q);
   a.B = B;

@@ -23,7 +23,7 @@ struct DecodeArgs {
   PoolView pv;
   const WorkItem* items;    // work items (each of one format)
   int32_t n_items;
-  const int32_t* pages;     // logical page lists
+  const int32_t* entries;   // page-table entries of the items' pages (schedule order)
   const int32_t* chunk_base;// [B + 1]
   const uint16_t* q;        // bf16 [B][Hq][d]
   int32_t B, Hq;

@@ -257,6 +257,8 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
   out->items[1].clear();
   out->pages.clear();
   out->pages.reserve(size_t(total_pages));
+  out->entries.clear();
+  out->entries.reserve(size_t(total_pages));
   out->chunk_base.assign(size_t(B) + 1, 0);
   int32_t nc = 0, largest = 0;
   for (int32_t b = 0; b < B; ++b) {
@@ -278,6 +280,7 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
           items.push_back(WorkItem{b, ids[b], int32_t(out->pages.size()), 0, 0, nc++, fmt, 0});
         }
         out->pages.push_back(lp);
+        out->entries.push_back(q.pt[size_t(lp)]);
         items.back().npages++;
         items.back().last_ntok = page_tokens(q.len, g_.P, lp);
         largest = std::max(largest, items.back().npages);

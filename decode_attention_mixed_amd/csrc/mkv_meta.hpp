@@ -112,6 +112,7 @@ struct SchedPolicy {
 struct Schedule {
   std::vector<WorkItem> items[2];   // per format (FP8, TQ3)
   std::vector<int32_t> pages;       // logical page ids referenced by the items
+  std::vector<int32_t> entries;     // their page-table entries (what the device reads)
   std::vector<int32_t> chunk_base;  // [B + 1] prefix sums of chunks per batch entry
   int32_t heads_per_wave = 1;       // kv-heads per partial-kernel workgroup
   int32_t n_chunks = 0;
