@@ -82,6 +82,13 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
   return r;
 }
 
+// A VGPR holding zero, opaque to the compiler.
+__device__ __forceinline__ uint32_t vgpr_opaque_zero() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(r));
+  return r;
+}
+
 // A VGPR holding the f16 pair (1.0, 1.0), opaque to constant folding.
 __device__ __forceinline__ uint32_t vgpr_one_pair() {
   uint32_t r;
@@ -267,13 +274,12 @@ __device__ __forceinline__ short4v read_tr(const uint8_t* p) {
 
 // B operand of the PV MFMA: the value entries V[4quad + j][n] of the lane's
 // column n, transposed out of the row-major LDS tile, in both halves (read
-// twice, so the operand lands in place without register copies; the empty
-// asm with a memory clobber keeps the compiler from merging the two reads
-// without making the hardware wait between them).
-__device__ __forceinline__ half8 value_operand(const uint8_t* p) {
+// twice, so the operand lands in place without register copies).  p2 is p
+// plus a zero the compiler cannot see through, so the two reads are not
+// merged and remain free to be scheduled early.
+__device__ __forceinline__ half8 value_operand(const uint8_t* p, const uint8_t* p2) {
   const u32x2 a = __builtin_bit_cast(u32x2, read_tr(p));
-  asm volatile("" ::: "memory");
-  const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p));
+  const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p2));
   const u32x4 d = {a[0], a[1], b[0], b[1]};
   return __builtin_bit_cast(half8, d);
 }
@@ -657,6 +663,10 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   const int jcol = col < ncol ? col / G : 0;    // kv-head (within the wave) of column col
   auto& W = lds.w[wave];
   const uint32_t one = vgpr_one_pair();
+  // the lane's value-tile reads (head 0, N-tile 0): row 4quad + col/4, dims
+  // 4(col & 3) .. +3; a second base for the duplicate read
+  const uint8_t* vbase = W.vt[0] + (4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
+  const uint8_t* vbase2 = vbase + vgpr_opaque_zero();
 
   // ---- query operands: slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s],
   // scaled by 2^(E + 7 - kSlotShift[s]) against the key slot's 2^(k-10)
@@ -811,7 +821,6 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     softmax_step(st, s, p, acc, W.corr, col, quad);
 
     // ---- per group: P' = p * value scale (hi/lo f16), acc_j += P' * V_j
-    const int row = 4 * quad + (col >> 2);
     uint32_t vsd[2 * NG];
     load_scale_dwords<NG>(scl + 8 * NG, vsd);
 #pragma unroll
@@ -824,7 +833,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       for (int j = 0; j < NH; ++j)
 #pragma unroll
         for (int jt = 2 * g; jt < 2 * g + 2; ++jt) {
-          const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+          const half8 bv = value_operand(vbase + j * (16 * VROW) + 32 * jt, vbase2 + j * (16 * VROW) + 32 * jt);
           acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
         }
     }
@@ -887,6 +896,8 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   const int hq0 = hk0 * G;
   const int jcol = col < ncol ? col / G : 0;
   auto& W = lds.w[wave];
+  const uint8_t* vbase = W.vt[0] + (4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
+  const uint8_t* vbase2 = vbase + vgpr_opaque_zero();
 
   // ---- query operand: MFMA r, lane (col, quad), slot s <-> dim quad*LB + 8r + s
   // (prepared once the first tiles' loads are in flight)
@@ -999,12 +1010,11 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
     softmax_step(st, s, p, acc, W.corr, col, quad);
 
     const half8 pp = pprime_uniform(p, sv);
-    const int row = 4 * quad + (col >> 2);
 #pragma unroll
     for (int j = 0; j < NH; ++j)
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        const half8 bv = value_operand(W.vt[j] + row * VROW + 2 * (16 * jt + 4 * (col & 3)));
+        const half8 bv = value_operand(vbase + j * (16 * VROW) + 32 * jt, vbase2 + j * (16 * VROW) + 32 * jt);
         acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
       }
     wave_lds_sync();
