@@ -462,33 +462,41 @@ template <int D>
 __device__ __forceinline__ void merge_waves_and_store(MergeLds<D>& M, const DecodeArgs& a, int chunk,
                                                       int hq0, int ncol) {
   const int64_t base = int64_t(chunk) * a.Hq + hq0;
+  float mx = -INFINITY, lsum = 0.0f;
   if (threadIdx.x < 16) {
     // per column: the common reference max and the waves' weights
     const int c = threadIdx.x;
-    float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
       if (M.l[w][c] > 0.0f) mx = fmaxf(mx, M.m[w][c]);
-    float lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float f = M.l[w][c] > 0.0f ? exp2f(M.m[w][c] - mx) : 0.0f;
       M.f[w][c] = f;
       lsum += M.l[w][c] * f;
     }
-    if (c < ncol) {
-      a.pm[base + c] = mx;
-      a.pl[base + c] = lsum;
-    }
   }
+  // (the global stores come after the barrier: a barrier's release fence
+  // would otherwise wait for them to reach memory)
   __syncthreads();
-  for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads) {
-    const int c = idx / D, dim = idx - (idx / D) * D;
-    float o = 0.0f;
+  if (threadIdx.x < ncol) {
+    a.pm[base + threadIdx.x] = mx;
+    a.pl[base + threadIdx.x] = lsum;
+  }
+  // (a wave without tiles has weight 0 and a zero accumulator, so every wave
+  // enters the sum; the loop has its maximum trip count so that all LDS
+  // reads can be issued together)
+  constexpr int kIter = (16 * D + kThreads - 1) / kThreads;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (M.f[w][c] > 0.0f) o += M.acc[w][c * MergeLds<D>::ROW + dim] * M.f[w][c];
-    a.pacc[(base + c) * D + dim] = o;
+  for (int k = 0; k < kIter; ++k) {
+    const int idx = threadIdx.x + kThreads * k;
+    const int c = idx / D, dim = idx % D;
+    if (c < ncol) {
+      float o = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) o = __builtin_fmaf(M.acc[w][c * MergeLds<D>::ROW + dim], M.f[w][c], o);
+      a.pacc[(base + c) * D + dim] = o;
+    }
   }
 }
 
