@@ -1055,16 +1055,18 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
 template <int NG, int NH>
 struct PartialCfg {
   static constexpr int kRingTq3 = 2;                 // TQ3 tiles in flight per wave
-  static constexpr int kRingFp8 = NH == 1 ? 2 : 1;   // FP8 tiles in flight per wave
+  // FP8 rows are 4x the TQ3 bytes: one tile in flight with two kv-heads or
+  // head dim 256, so the kernel keeps two waves per SIMD
+  static constexpr int kRingFp8 = NH == 1 && NG < 8 ? 2 : 1;
   static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
   static constexpr size_t kSmem =
       cmax(cmax(sizeof(Tq3Lds<NG, NH>), sizeof(Fp8Lds<NG, NH>)), sizeof(MergeLds<32 * NG>));
 };
 
-// At least two waves per SIMD (256 VGPRs) except for head dim 256, which
-// keeps its registers unspilled at one wave per SIMD.
+// Two waves per SIMD (256 VGPRs); three for one kv-head per wave at head
+// dim <= 128.
 template <int NG, int NH>
-__global__ void __launch_bounds__(kThreads, NG == 8 ? 1 : (NH == 1 ? 3 : 2)) partial_mixed(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, NH == 1 && NG < 8 ? 3 : 2) partial_mixed(DecodeArgs a) {
   using Cfg = PartialCfg<NG, NH>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
   const WorkItem it = a.items[blockIdx.x];
