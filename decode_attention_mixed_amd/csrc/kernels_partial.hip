@@ -576,9 +576,14 @@ __device__ __forceinline__ int load_query(const DecodeArgs& a, int b, int hq0, i
 }
 
 // Row stride (bytes) of an f16 value tile in LDS: the stride in dwords is
-// 12 mod 64, so the 16 rows of a 16-byte row write and the 4 x 4 lanes of a
-// transposing 8-byte read each hit distinct banks.
+// 12 mod 64, so row r starts at bank 12r mod 64 and the 16 rows of a 16-byte
+// row write hit distinct banks.
 constexpr int value_row_bytes(int D) { return 2 * D + 4 * (((12 - D / 2) % 64 + 64) % 64); }
+// LDS row of token t in a value tile: tokens 0..7 take the even rows and
+// 8..15 the odd ones.  A transposing 8-byte read serves 32 lanes at a time,
+// 8 rows (tokens 0..7 or 8..15) of 8 banks each; the even (odd) rows start
+// 24 banks apart mod 64 and so cover all 64 banks once.
+__device__ __forceinline__ int value_row(int t) { return t < 8 ? 2 * t : 2 * t - 15; }
 static_assert(value_row_bytes(128) == 304 && value_row_bytes(64) % 16 == 0 &&
                   (value_row_bytes(32) / 4) % 64 == 12 && (value_row_bytes(256) / 4) % 64 == 12,
               "value row stride");
@@ -606,10 +611,12 @@ template <int NG, int NH>
 struct Tq3Lds {
   static constexpr int D = 32 * NG;
   static constexpr int VROW = value_row_bytes(D);
-  static constexpr int KST = 4 * NG + 4;        // dwords per token in the key staging (padded)
+  // key units as [group][token][unit]: a lane stores its group's four units
+  // with one 16-byte write, and the 64 lanes reading one unit each for a
+  // group hit the 64 banks once
   static constexpr int SD = 16 * NG;            // scale dwords of a tile (K then V)
   struct Wave {
-    alignas(16) uint32_t kst[NH][16 * KST];     // key units, [token][unit][group]
+    alignas(16) uint32_t kst[NH][64 * NG];      // key units, [group][token][unit]
     alignas(16) uint8_t vt[NH][16 * VROW];      // value tiles, [token][D] f16
     alignas(16) uint32_t sc[NH][SD + 4];        // tile scales as f16 [K, V][token][group] (padded)
     float corr[16];
@@ -652,7 +659,6 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   constexpr int GPL = NG > 4 ? NG / 4 : 1;      // groups each lane loads per head
   constexpr int NT = D / 16;                    // PV N-tiles per head
   constexpr int VROW = Tq3Lds<NG, NH>::VROW;
-  constexpr int KST = Tq3Lds<NG, NH>::KST;
   constexpr int ROWB = 3 * D / 8;               // code bytes per token row
   constexpr int SD = Tq3Lds<NG, NH>::SD;
   constexpr int SPL = (SD + 63) / 64;           // scale dwords each lane loads per head
@@ -673,7 +679,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   const uint32_t one = vgpr_one_pair();
   // the lane's value-tile reads (head 0, N-tile 0): row 4quad + col/4, dims
   // 4(col & 3) .. +3; a second base for the duplicate read
-  const uint8_t* vbase = W.vt[0] + (4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
+  const uint8_t* vbase = W.vt[0] + value_row(4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
   const uint8_t* vbase2 = vbase + vgpr_opaque_zero();
 
   // ---- query operands: slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s],
@@ -782,11 +788,10 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
         if (g < NG) {
           uint32_t u[4];
           tq3_split_units(raw.kc[j][i], u);
-#pragma unroll
-          for (int un = 0; un < 4; ++un) W.kst[j][col * KST + un * NG + g] = u[un];
+          *reinterpret_cast<u32x4*>(&W.kst[j][64 * g + 4 * col]) = u32x4{u[0], u[1], u[2], u[3]};
           uint32_t o[16];
           tq3_value_group(raw.vc[j][i], one, o);
-          uint8_t* vd = W.vt[j] + col * VROW + 64 * g;
+          uint8_t* vd = W.vt[j] + value_row(col) * VROW + 64 * g;
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4)
             *reinterpret_cast<u32x4*>(vd + 16 * c4) = u32x4{o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]};
@@ -811,7 +816,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
         const half8 kop =
-            __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[j][col * KST + quad * NG + g], one));
+            __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[j][64 * g + 4 * col + quad], one));
         dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[j][g], dg, 0, 0, 0);
       }
 #pragma unroll
@@ -904,7 +909,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   const int hq0 = hk0 * G;
   const int jcol = col < ncol ? col / G : 0;
   auto& W = lds.w[wave];
-  const uint8_t* vbase = W.vt[0] + (4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
+  const uint8_t* vbase = W.vt[0] + value_row(4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
   const uint8_t* vbase2 = vbase + vgpr_opaque_zero();
 
   // ---- query operand: MFMA r, lane (col, quad), slot s <-> dim quad*LB + 8r + s
@@ -986,7 +991,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
         const u32x2 a1 = fp8x4_to_f16(raw.vw[j][i + 1]);
         u32x4 o = {a0[0], a0[1], a1[0], a1[1]};
         if (!vrow_ok) o = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(W.vt[j] + col * VROW + 2 * (quad * LB + 4 * i)) = o;
+        *reinterpret_cast<u32x4*>(W.vt[j] + value_row(col) * VROW + 2 * (quad * LB + 4 * i)) = o;
       }
     // ---- QK^T over all dims, per kv-head, keys widened to f16 operands from
     // the raw words (page-head scale applied per column)
