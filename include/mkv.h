@@ -157,8 +157,11 @@ mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages,
  * lse: device fp32 [B][Hq], natural-log log-sum-exp of the scaled scores.
  * One partial-kernel launch reduces split-K page chunks of each sequence,
  * each chunk in its own format (FP8 and TQ3 code paths), and a merge kernel
- * combines their (max, denominator, unnormalised accumulator) states.  The split-K schedule is rebuilt only when page
- * metadata, the batch or Hq changed since the previous decode.
+ * combines their (max, denominator, unnormalised accumulator) states (a
+ * per-lane merge when no sequence has more than 16 chunks, else a
+ * wave-reduced one).  The split-K schedule is rebuilt only when page
+ * metadata, the batch or Hq changed since the previous decode; the result of
+ * a given schedule is bit-reproducible.
  * MKV_EINVAL for an empty sequence, Hq not a multiple of Hkv, Hq / Hkv > 16,
  * or a misaligned q;
  * MKV_ERANGE for B > max_batch or Hq > max_q_heads. */
