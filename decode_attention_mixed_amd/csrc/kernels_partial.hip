@@ -397,13 +397,29 @@ __device__ __forceinline__ const uint8_t* entry_page(const PoolView& pv, const i
   return page_address(pv, __builtin_amdgcn_readfirstlane(ent[page]));
 }
 
+// Issue priority from the share of the wave's tiles already done: 3 in the
+// first quarter down to 0 in the last.  The two waves sharing a SIMD come from
+// different workgroups, and among ready waves the hardware issues the older
+// one first, so with equal priorities the workgroup dispatched first runs well
+// ahead and the other one ends its range alone on the SIMD.  With these levels
+// a wave that gets ahead yields to the one behind, and the pair ends closer
+// together.  Only used when every workgroup of the launch is resident from the
+// start (otherwise a newly started wave would hold back nearly finished ones).
+__device__ __forceinline__ void pace_priority(int done, int total) {
+  const int x = 4 * done;
+  if (x < total) __builtin_amdgcn_s_setprio(3);
+  else if (x < 2 * total) __builtin_amdgcn_s_setprio(2);
+  else if (x < 3 * total) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Runs the tile pipeline over the wave's range: R raw buffers in flight;
 // prepare() runs once the first loads are issued; process(raw, cursor,
 // refill) consumes one tile and calls refill(raw) to
 // load a later one.  The steady-state loop issues the same loads on every
-// path.
+// path.  pace: set the wave's issue priority from its progress.
 template <int R, typename Raw, typename Load, typename Prepare, typename Process>
-__device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Prepare prepare,
+__device__ __forceinline__ void run_tiles(const TileGeom& g, bool pace, Load load, Prepare prepare,
                                           Process process) {
   if (g.ntiles == 0) return;
   Raw ring[R];
@@ -417,6 +433,7 @@ __device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Prepare 
   Cursor pc = g.first;
   int ti = 0;
   for (; ti + R <= g.ntiles; ti += R) {
+    if (pace) pace_priority(ti, g.ntiles);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       process(ring[k], pc, [&](Raw& r) {
@@ -426,6 +443,7 @@ __device__ __forceinline__ void run_tiles(const TileGeom& g, Load load, Prepare 
       advance(pc, g);
     }
   }
+  if (pace) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int k = 0; k < R - 1; ++k) {
     if (ti + k < g.ntiles) {
@@ -852,7 +870,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     }
     wave_lds_sync();
   };
-  run_tiles<R, Raw>(tg, load, prepare, process);
+  run_tiles<R, Raw>(tg, a.pace != 0, load, prepare, process);
 
   // ---- combine the four waves' states through LDS (the tile staging is
   // reused once every wave is past its last tile) and write the item's state
@@ -1032,7 +1050,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
       }
     wave_lds_sync();
   };
-  run_tiles<R, Raw>(tg, load, prepare, process);
+  run_tiles<R, Raw>(tg, a.pace != 0, load, prepare, process);
 
   const float lcol = quad_sum(st.l);
   __syncthreads();

@@ -121,6 +121,7 @@ struct mkv_pool {
   mkv::Schedule sched;
   int32_t target_waves[2] = {2048, 1024};   // resident partial-kernel waves, 1 or 2 heads per wave
   int32_t merge_narrow_max = 16;            // per-lane merge up to this many chunks per entry
+  bool pace = true;                         // progress-paced wave priorities (one-round launches)
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
@@ -215,7 +216,9 @@ mkv_status prof_collect(mkv_pool* p) {
 // partial-kernel waves.  Environment overrides (for tuning): MKV_CHUNK_PAGES
 // (fixed chunk length), MKV_TARGET_WAVES, MKV_FP8_PAGE_COST,
 // MKV_HEADS_PER_WAVE; MKV_MERGE_NARROW_MAX (read at pool creation) sets the
-// largest per-entry chunk count merged by the per-lane merge kernel.
+// largest per-entry chunk count merged by the per-lane merge kernel, and
+// MKV_PACE=0 (read at pool creation) turns off the progress-paced wave
+// priorities of one-round partial launches.
 mkv::SchedPolicy pool_policy(const mkv_pool* p, int32_t Hq) {
   mkv::SchedPolicy pol;
   const mkv::Geom& g = p->meta.geom();
@@ -282,6 +285,7 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
     if (waves > 0) p->target_waves[nh - 1] = waves;
   }
   if (const char* ev = std::getenv("MKV_MERGE_NARROW_MAX")) p->merge_narrow_max = std::max(0, std::atoi(ev));
+  if (const char* ev = std::getenv("MKV_PACE")) p->pace = std::atoi(ev) != 0;
   if (device_mem) {
     if (bytes < p->lay.total) return cleanup(MKV_ERANGE, "device buffer smaller than mkv_pool_bytes");
     if (reinterpret_cast<uintptr_t>(device_mem) % 256)
@@ -423,6 +427,10 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   a.max_seq_chunks = sc.max_seq_chunks;
   a.items = items;
   a.n_items = int32_t(sc.items[0].size() + sc.items[1].size());
+  {
+    const int64_t waves = int64_t(a.n_items) * ((a.pv.Hkv + a.nh - 1) / a.nh) * mkv::kWavesPerWorkgroup;
+    a.pace = p->pace && waves <= p->target_waves[a.nh - 1] ? 1 : 0;
+  }
   {
     ProfEvent* e = prof_begin(p, 0, s);
     MKV_HIP(mkv::launch_partial(a, s));

@@ -35,6 +35,7 @@ struct DecodeArgs {
   float* lse;               // [B][Hq]
   int32_t nh;               // kv-heads per partial-kernel workgroup (1 or 2)
   int32_t max_seq_chunks;   // most partial states of one batch entry
+  int32_t pace;             // 1: all partial-kernel workgroups are resident at once
 };
 
 hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_pages,

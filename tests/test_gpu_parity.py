@@ -212,6 +212,24 @@ def test_both_merge_kernels(monkeypatch, narrow_max):
     pool.close()
 
 
+def test_paced_priorities_change_no_bits(monkeypatch):
+    """Progress-paced wave priorities (on for launches whose workgroups are all
+    resident at once, as here) only reorder instruction issue: the results are
+    bit-identical to those of unpaced launches, and within tolerance of the
+    oracle."""
+    wl = W.small(seed=67, B=3, Hq=16, Hkv=4, d=128, P=16, lengths=(2000, 700, 1333))
+    res = {}
+    for pace in ("0", "1"):
+        monkeypatch.setenv("MKV_PACE", pace)
+        pool = H.DevicePool(H.pool_desc(wl))
+        H.load_cache(pool, wl)
+        res[pace] = _run_decode(pool, wl)
+        pool.close()
+    assert np.array_equal(res["0"][0], res["1"][0]) and np.array_equal(res["0"][1], res["1"][1])
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    _check(*res["1"], *OS.decode_all(wl, models), "paced")
+
+
 NAMED = ["tiny", "ragged", "sweep0", "sweep10", "sweep50", "sweep100"]
 
 
