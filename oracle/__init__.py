@@ -13,7 +13,7 @@ shares no code with the HIP path.
 Modules:
   codecs      FP8 E4M3, fp16/bf16 and TQ3 codecs written from their definitions
   pool_model  CPU model of pages: append with rescale-on-grow, FP8->TQ3 demote,
-              page byte records
+              page byte records; the dense BF16 control cache
   attention   fp64 softmax attention on the dequantised cache, partial states
               and the merge
 

@@ -104,6 +104,21 @@ def bf16_bits_to_value(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def bf16_encode(x32) -> np.ndarray:
+    """fp32 -> bf16 bits, rounding to nearest with ties to the even bf16 value
+    (IEEE 754 roundTiesToEven).  bf16 is the upper half of an fp32 pattern, so
+    rounding keeps the upper 16 bits and adds one unit in their last place
+    when the dropped lower 16 bits exceed half of that unit, or equal half and
+    the kept part is odd.  A carry out of the significand moves into the
+    exponent, which is again the correctly rounded result (up to infinity past
+    the largest finite bf16).  Finite inputs only (the cache stores no NaN)."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    upper = u >> np.uint64(16)
+    lower = u & np.uint64(0xFFFF)
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & np.uint64(1)) == 1))
+    return (upper + up.astype(np.uint64)).astype(np.uint16)
+
+
 # --------------------------------------------------------------------------
 # TQ3
 # --------------------------------------------------------------------------

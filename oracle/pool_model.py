@@ -31,6 +31,10 @@ records in logical order).  With Hkv kv-heads, head dim d and P tokens per page:
   (token rows as 3-bit streams), V codes [P][3d/8], K scales [P][d/32] f16 and
   V scales [P][d/32] f16.
 Rows at or beyond the page's valid-token count are unspecified in both formats.
+
+The dense BF16 control cache (Bf16SeqModel) is the single-format baseline of the
+same summary, section "O que foi medido" (compression "em relacao ao BF16"):
+every row stored as bf16, record [Hkv][2 (K, V)][P][d] bf16.
 """
 from __future__ import annotations
 
@@ -232,6 +236,70 @@ class SeqModel:
                 r[:n] = True
                 parts.append(r.reshape(-1))
         return np.concatenate(parts)
+
+
+def bf16_record_bytes(Hkv: int, P: int, d: int) -> int:
+    return 4 * Hkv * P * d
+
+
+@dataclass
+class Bf16SeqModel:
+    """A sequence of the dense BF16 control cache: the single-format baseline the
+    summaries compare the mixed cache against ("3,50x de compressao em relacao
+    ao BF16", section "O que foi medido").  Every row is stored as bf16
+    (round to nearest even); pages are never converted.
+    Record of a page: [Hkv][2 (K, V)][P][d] bf16, little-endian."""
+    Hkv: int
+    d: int
+    P: int
+    bits: list = field(default_factory=list)     # per page: [2][Hkv][P][d] u16
+    ntok: list = field(default_factory=list)
+    length: int = 0
+
+    def append(self, k, v) -> None:
+        k = np.asarray(k, dtype=np.float32)
+        v = np.asarray(v, dtype=np.float32)
+        n = k.shape[0]
+        assert k.shape == (n, self.Hkv, self.d) and v.shape == k.shape
+        rows = np.stack([C.bf16_encode(k), C.bf16_encode(v)])   # [2][n][Hkv][d]
+        for t in range(n):
+            slot = self.length % self.P
+            if slot == 0:
+                self.bits.append(np.zeros((2, self.Hkv, self.P, self.d), np.uint16))
+                self.ntok.append(0)
+            self.bits[-1][:, :, slot, :] = rows[:, t]
+            self.ntok[-1] += 1
+            self.length += 1
+
+    def dense(self, heads=None):
+        """K, V fp64 [L][Hkv][d] (or the listed kv-heads)."""
+        ks, vs = [], []
+        for b, n in zip(self.bits, self.ntok):
+            val = C.bf16_bits_to_value(b[:, :, :n, :])           # [2][Hkv][n][d]
+            val = np.transpose(val, (0, 2, 1, 3))
+            if heads is not None:
+                val = val[:, :, heads]
+            ks.append(val[0])
+            vs.append(val[1])
+        return np.concatenate(ks), np.concatenate(vs)
+
+    def record(self, lp: int) -> np.ndarray:
+        """Byte record of page lp (rows past the valid count zero)."""
+        b = self.bits[lp].copy()
+        b[:, :, self.ntok[lp]:, :] = 0
+        out = np.ascontiguousarray(np.transpose(b, (1, 0, 2, 3))).astype('<u2').view(np.uint8).reshape(-1)
+        assert out.size == bf16_record_bytes(self.Hkv, self.P, self.d)
+        return out
+
+    def valid_mask(self, lp: int) -> np.ndarray:
+        m = np.zeros((self.Hkv, 2, self.P, self.d, 2), bool)
+        m[:, :, :self.ntok[lp]] = True
+        return m.reshape(-1)
+
+
+def bf16_kv_bytes(seq: Bf16SeqModel) -> int:
+    """Bytes a decode step reads for a control sequence: K and V bf16 rows."""
+    return seq.length * 4 * seq.Hkv * seq.d
 
 
 def kv_bytes(seq: SeqModel) -> int:

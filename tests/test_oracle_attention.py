@@ -323,3 +323,50 @@ def test_record_sizes_and_masks():
     # page 1 holds 5 valid rows: K codes of head 0 span 5 * 24 bytes
     m = seq.valid_mask(1)
     assert m[:5 * 24].all() and not m[5 * 24:16 * 24].any()
+
+
+# ------------------------------------------------------------ BF16 control cache
+def test_bf16_control_record_layout_hand_built():
+    """Record [Hkv][2][P][d] bf16 little-endian, rows past the valid count zero."""
+    Hkv, P, d = 2, 16, 32
+    n = 3
+    k = np.zeros((n, Hkv, d), np.float32)
+    v = np.zeros((n, Hkv, d), np.float32)
+    k[1, 1, 5] = 1.0          # bf16 0x3F80
+    v[2, 0, 31] = -2.0        # bf16 0xC000
+    seq = PM.Bf16SeqModel(Hkv, d, P)
+    seq.append(k, v)
+    rec = seq.record(0)
+    assert rec.size == PM.bf16_record_bytes(Hkv, P, d) == 4 * Hkv * P * d
+    off_k = ((1 * 2 + 0) * P + 1) * d * 2 + 5 * 2       # head 1, K, token 1, dim 5
+    off_v = ((0 * 2 + 1) * P + 2) * d * 2 + 31 * 2      # head 0, V, token 2, dim 31
+    assert rec[off_k] == 0x80 and rec[off_k + 1] == 0x3F
+    assert rec[off_v] == 0x00 and rec[off_v + 1] == 0xC0
+    nz = np.flatnonzero(rec)
+    assert set(nz.tolist()) == {off_k + 1, off_k, off_v + 1}
+    assert seq.valid_mask(0).sum() == Hkv * 2 * n * d * 2
+
+
+def test_bf16_control_dense_and_decode():
+    """Values are the bf16 roundings of the rows; with bf16-representable rows
+    the control decode equals plain attention on the fp32 rows."""
+    rng = np.random.default_rng(8)
+    Hkv, P, d, L, Hq = 2, 16, 64, 37, 6
+    k = (rng.integers(-64, 64, (L, Hkv, d)) / 16.0).astype(np.float32)   # exact in bf16
+    v = (rng.integers(-64, 64, (L, Hkv, d)) / 8.0).astype(np.float32)
+    seq = PM.Bf16SeqModel(Hkv, d, P)
+    seq.append(k[:20], v[:20])
+    seq.append(k[20:], v[20:])
+    K, V = seq.dense()
+    assert np.array_equal(K, k.astype(np.float64)) and np.array_equal(V, v.astype(np.float64))
+    assert len(seq.bits) == 3 and seq.ntok == [16, 16, 5]
+    assert PM.bf16_kv_bytes(seq) == L * 4 * Hkv * d
+    qb = C.bf16_encode(rng.standard_normal((Hq, d)).astype(np.float32))
+    O, lse = A.decode_seq(seq, qb, np.float32(0.125))
+    O2, lse2 = A.attend(C.bf16_bits_to_value(qb), k.astype(np.float64), v.astype(np.float64), 0.125)
+    assert np.array_equal(O, O2) and np.array_equal(lse, lse2)
+    # a non-representable row is rounded to nearest even
+    seq2 = PM.Bf16SeqModel(1, 32, 16)
+    x = np.full((1, 1, 32), 1.0 + 2.0 ** -8 + 2.0 ** -12, np.float32)
+    seq2.append(x, x)
+    assert np.all(seq2.dense()[0] == 1.0 + 2.0 ** -7)

@@ -191,3 +191,40 @@ def test_tq3_zero_element_maps_to_code_4():
     x[0] = 3.5
     c, s = C.tq3_encode_groups(x)
     assert s == np.float16(1.0) and c[0] == 7 and np.all(c[1:] == 4)
+
+
+# ----------------------------------------------------------------- bf16 encode
+@pytest.mark.parametrize("x, bits", [
+    (1.0, 0x3F80),
+    (1.0 + 2.0 ** -8, 0x3F80),                 # exact tie, kept part even: down
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),             # exact tie, kept part odd: up to even
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),    # just above the tie: up
+    (1.0 + 2.0 ** -8 - 2.0 ** -20, 0x3F80),    # just below the tie: down
+    (-(1.0 + 3 * 2.0 ** -8), 0xBF82),          # sign-magnitude: same rounding
+    (2.0 - 2.0 ** -23, 0x4000),                # carry out of the significand into the exponent
+    (0.0, 0x0000),
+    (-0.0, 0x8000),
+    (3.0, 0x4040),
+])
+def test_bf16_encode_hand_values(x, bits):
+    assert int(C.bf16_encode(np.float32(x))) == bits
+
+
+def test_bf16_encode_is_nearest_with_ties_to_even():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000)).astype(np.float32)
+    enc = C.bf16_encode(x).astype(np.int64)
+    r = C.bf16_bits_to_value(enc)
+    lo = C.bf16_bits_to_value(enc - 1)        # neighbours in the same binade direction
+    hi = C.bf16_bits_to_value(enc + 1)
+    xd = x.astype(np.float64)
+    assert np.all(np.abs(xd - r) <= np.abs(xd - lo)) and np.all(np.abs(xd - r) <= np.abs(xd - hi))
+    tie = (np.abs(xd - r) == np.abs(xd - lo)) | (np.abs(xd - r) == np.abs(xd - hi))
+    assert np.all(enc[tie] % 2 == 0)
+
+
+def test_bf16_encode_matches_torch_bfloat16():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal(50000) * 10.0 ** rng.integers(-35, 35, 50000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(C.bf16_encode(x), ref)
