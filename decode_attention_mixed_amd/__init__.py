@@ -21,6 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libmkv.so")
 
 FMT_FP8 = 0
 FMT_TQ3 = 1
+FMT_BF16 = 2
+KIND_MIXED = 0
+KIND_BF16 = 1
 
 OK, EINVAL, ENOMEM, ESTATE, ERANGE, EHIP = 0, -1, -2, -3, -4, -5
 
@@ -44,6 +47,7 @@ class PoolDesc(ctypes.Structure):
         ("fp8_pages", ctypes.c_int64),
         ("tq3_pages", ctypes.c_int64),
         ("placement_seed", ctypes.c_uint64),
+        ("kv_kind", ctypes.c_int32),
     ]
 
 
@@ -158,9 +162,10 @@ def _i32_array(values):
 
 # ----------------------------------------------------------------- functions
 def make_desc(*, num_kv_heads, head_dim, page_size, max_seqs, max_pages_per_seq, max_batch,
-              max_q_heads, fp8_pages, tq3_pages, placement_seed=0, max_chunks=0) -> PoolDesc:
+              max_q_heads, fp8_pages, tq3_pages, placement_seed=0, max_chunks=0,
+              kv_kind=KIND_MIXED) -> PoolDesc:
     return PoolDesc(num_kv_heads, head_dim, page_size, max_seqs, max_pages_per_seq, max_batch,
-                    max_q_heads, max_chunks, fp8_pages, tq3_pages, placement_seed)
+                    max_q_heads, max_chunks, fp8_pages, tq3_pages, placement_seed, kv_kind)
 
 
 def pool_bytes(desc: PoolDesc) -> int:

@@ -14,7 +14,7 @@ thread_local std::string g_herr;
 mkv::Desc to_desc(const mkv_pool_desc& d) {
   return mkv::Desc{d.num_kv_heads, d.head_dim, d.page_size, d.max_seqs, d.max_pages_per_seq,
                    d.max_batch,    d.max_q_heads, d.max_chunks, d.fp8_pages, d.tq3_pages,
-                   d.placement_seed};
+                   d.placement_seed, d.kv_kind};
 }
 }  // namespace
 

@@ -67,6 +67,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = kWavesPerWorkgroup;
 constexpr int kThreads = 64 * kWaves;
@@ -1073,6 +1074,169 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
 }
 
 // ---------------------------------------------------------------------------
+// BF16 work item (control pools): the dense single-format cache.  Structure
+// of the FP8 item without scales or widening: a lane's quarter row of keys is
+// the MFMA operand as loaded, value rows go to the LDS tile as loaded.
+// ---------------------------------------------------------------------------
+// P as a bf16 hi + lo pair in one A operand (about 16 significant bits).
+__device__ __forceinline__ bf16x8 pprime_bf16(const float p[4]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 h = __bf16(p[i]);
+    r[i] = h;
+    r[4 + i] = __bf16(p[i] - float(h));
+  }
+  return r;
+}
+
+template <int NG, int NH, int R>
+__device__ __forceinline__ void bf16_item(const DecodeArgs& a, const WorkItem& it, uint8_t* smem) {
+  auto& lds = *reinterpret_cast<Fp8Lds<NG, NH>*>(smem);   // same LDS image as FP8 items
+  constexpr int D = 32 * NG;
+  constexpr int NT = D / 16;
+  constexpr int VROW = Fp8Lds<NG, NH>::VROW;
+  constexpr int LD = D / 4;                     // dims of a row each lane loads
+  constexpr int LW = LD / 2;                    // their dwords
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const PoolView& pv = a.pv;
+  stage_entries(lds.ent, a, it);
+  const int hk0 = blockIdx.y * NH;               // the workgroup's kv-heads
+  if (hk0 >= pv.Hkv) return;
+  const int G = a.Hq / pv.Hkv;
+  const int ncol = NH * G;
+  const int hq0 = hk0 * G;
+  const int jcol = col < ncol ? col / G : 0;
+  auto& W = lds.w[wave];
+  const uint8_t* vbase = W.vt[0] + value_row(4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
+  const uint8_t* vbase2 = vbase + vgpr_opaque_zero();
+
+  // ---- query operand: MFMA r, lane (col, quad), slot s <-> dim quad*LD + 8r + s,
+  // taken as stored (bf16); zero outside the lane's column's kv-head
+  bf16x8 qop[NH][NG];
+  const float F = a.scale * kLog2e;
+  auto prepare = [&]() {
+    const bool live = col < ncol;
+    const uint16_t* qrow = a.q + (int64_t(it.b) * a.Hq + hq0 + (live ? col : 0)) * D;
+#pragma unroll
+    for (int r = 0; r < NG; ++r) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + quad * LD + 8 * r);
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        u32x4 o;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o[x] = live && jcol == j ? w[x] : 0u;
+        qop[j][r] = __builtin_bit_cast(bf16x8, o);
+      }
+    }
+  };
+
+  f32x4 acc[NH * NT];
+#pragma unroll
+  for (int j = 0; j < NH * NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  SoftState st;
+
+  uint32_t row_off[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) row_off[j] = uint32_t((hk0 + j) * 2 * pv.P * D * 2 + col * D * 2 + quad * LD * 2);
+  const int vrow_delta = pv.P * D * 2;                 // V rows follow the K rows
+  struct Raw {
+    uint32_t kw[NH][LW];
+    uint32_t vw[NH][LW];
+  };
+  auto load = [&](const Cursor& c, Raw& r) {
+    const auto rec = record_rsrc(entry_page(pv, lds.ent, c.page), pv.fp8_stride);
+    const int kso = 16 * c.sub * D * 2;                  // the tile's first K row
+    const int vso = kso + vrow_delta;                    // and its first V row
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int x = 0; x < LW / 4; ++x) {
+        const u32x4 kw = rec_load4(rec, row_off[j] + 16 * x, kso);
+        const u32x4 vw = rec_load4(rec, row_off[j] + 16 * x, vso);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          r.kw[j][4 * x + y] = kw[y];
+          r.vw[j][4 * x + y] = vw[y];
+        }
+      }
+  };
+  const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
+
+  auto process = [&](Raw& raw, const Cursor& c, auto refill) {
+    const int nvalid = valid_in_tile(c, tg);
+    // ---- value rows to the LDS tiles (rows past the valid tokens zeroed: an
+    // unwritten slot may hold any bits, and p = 0 times NaN is NaN)
+    const bool vrow_ok = col < nvalid;
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int x = 0; x < LW / 4; ++x) {
+        u32x4 o = {raw.vw[j][4 * x], raw.vw[j][4 * x + 1], raw.vw[j][4 * x + 2], raw.vw[j][4 * x + 3]};
+        if (!vrow_ok) o = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(W.vt[j] + value_row(col) * VROW + 2 * quad * LD + 16 * x) = o;
+      }
+    // ---- QK^T over all dims and both kv-heads into one accumulator (the
+    // query operands are zero outside each lane's own kv-head)
+    f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int r = 0; r < NG; ++r) {
+        const u32x4 ku = {raw.kw[j][4 * r], raw.kw[j][4 * r + 1], raw.kw[j][4 * r + 2], raw.kw[j][4 * r + 3]};
+        dsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ku), qop[j][r], dsum, 0, 0, 0);
+      }
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = dsum[i] * F;
+    refill(raw);
+    wave_lds_sync();
+    if (nvalid < 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * quad + i >= nvalid) s[i] = -INFINITY;
+    }
+    float p[4];
+    softmax_step(st, s, p, acc, W.corr, col, quad);
+
+    const bf16x8 pp = pprime_bf16(p);
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        const half8 bv = value_operand(vbase + j * (16 * VROW) + 32 * jt, vbase2 + j * (16 * VROW) + 32 * jt);
+        acc[j * NT + jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, __builtin_bit_cast(bf16x8, bv),
+                                                                 acc[j * NT + jt], 0, 0, 0);
+      }
+    wave_lds_sync();
+  };
+  run_tiles<R, Raw>(tg, a.pace != 0, load, prepare, process);
+
+  const float lcol = quad_sum(st.l);
+  __syncthreads();
+  auto& M = *reinterpret_cast<MergeLds<D>*>(smem);
+  if (quad == 0) {
+    M.m[wave][col] = st.m;
+    M.l[wave][col] = lcol;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * quad + i;
+    if (c >= ncol) continue;
+    const int jc = c / G;
+    float* dst = M.acc[wave] + c * MergeLds<D>::ROW;
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) dst[16 * jt + col] = pick_head<NH, NT>(acc, jc, jt, i);
+  }
+  __syncthreads();
+  merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
+}
+
+// ---------------------------------------------------------------------------
 // One launch for both formats: workgroup x takes work item x (FP8 or TQ3).
 // ---------------------------------------------------------------------------
 template <int NG, int NH>
@@ -1099,7 +1263,36 @@ __global__ void __launch_bounds__(kThreads, NH == 1 && NG < 8 ? 3 : 2) partial_m
     tq3_item<NG, NH, Cfg::kRingTq3>(a, it, smem);
 }
 
+// Control pools: every work item is BF16.  Two waves per SIMD; one tile in
+// flight (a BF16 tile row share is 4x the TQ3 one).
+template <int NG, int NH>
+__global__ void __launch_bounds__(kThreads, 2) partial_bf16(DecodeArgs a) {
+  constexpr size_t kSmem = PartialCfg<NG, NH>::cmax(sizeof(Fp8Lds<NG, NH>), sizeof(MergeLds<32 * NG>));
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  const WorkItem it = a.items[blockIdx.x];
+  bf16_item<NG, NH, 1>(a, it, smem);
+}
+
 namespace {
+
+template <typename F>
+hipError_t with_bf16_kernel(int d, int nh, F f) {
+  if (nh == 2) {
+    switch (d) {
+      case 32: return f(partial_bf16<1, 2>);
+      case 64: return f(partial_bf16<2, 2>);
+      case 128: return f(partial_bf16<4, 2>);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (d) {
+    case 32: return f(partial_bf16<1, 1>);
+    case 64: return f(partial_bf16<2, 1>);
+    case 128: return f(partial_bf16<4, 1>);
+    case 256: return f(partial_bf16<8, 1>);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 template <typename F>
 hipError_t with_kernel(int d, int nh, F f) {
@@ -1128,24 +1321,26 @@ hipError_t launch_partial(const DecodeArgs& a, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
   const int nh = a.nh;
   const dim3 grid(unsigned(a.n_items), unsigned((a.pv.Hkv + nh - 1) / nh));
-  return with_kernel(a.pv.d, nh, [&](auto kernel) {
+  auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
-  });
+  };
+  return a.pv.kind == kKindBf16 ? with_bf16_kernel(a.pv.d, nh, launch) : with_kernel(a.pv.d, nh, launch);
 }
 
-hipError_t partial_resident_waves(int d, int nh, int* waves) {
+hipError_t partial_resident_waves(int d, int nh, int kind, int* waves) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  return with_kernel(d, nh, [&](auto kernel) {
+  auto query = [&](auto kernel) {
     int blocks = 0;
     const hipError_t r = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kThreads, 0);
     if (r == hipSuccess) *waves = cus * blocks * kWaves;
     return r;
-  });
+  };
+  return kind == kKindBf16 ? with_bf16_kernel(d, nh, query) : with_kernel(d, nh, query);
 }
 
 }  // namespace mkv

@@ -1,5 +1,6 @@
-// Kernels that write the cache: FP8 append, FP8 -> TQ3 demote, and the record
-// gather used to check placement and packing.
+// Kernels that write the cache: FP8 append, FP8 -> TQ3 demote, the BF16
+// append of control pools, and the record gather used to check placement and
+// packing.
 //
 // Every floating-point step here decides a stored code, so this file is built
 // with -ffp-contract=off and relies on IEEE fp32 division and round-to-nearest-
@@ -139,14 +140,54 @@ __global__ void __launch_bounds__(kThreads)
 gather_kernel(PoolView pv, int32_t seq, int32_t first, uint8_t* __restrict__ dst, int64_t slot) {
   const int32_t entry = pv.pt[int64_t(seq) * pv.pt_stride + first + blockIdx.x];
   const uint8_t* src = page_address(pv, entry);
-  const int64_t rec = entry < 0 ? int64_t(pv.Hkv) * pv.P * pv.d * 7 / 8
-                                : 2ll * pv.Hkv * pv.P * pv.d + 16ll * pv.Hkv;
+  const int64_t rec = pv.kind == kKindBf16 ? 4ll * pv.Hkv * pv.P * pv.d
+                     : entry < 0         ? int64_t(pv.Hkv) * pv.P * pv.d * 7 / 8
+                                         : 2ll * pv.Hkv * pv.P * pv.d + 16ll * pv.Hkv;
   const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
   uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + int64_t(blockIdx.x) * slot);
   for (int64_t i = threadIdx.x; i < slot / 4; i += kThreads) d32[i] = i < rec / 4 ? s32[i] : 0u;
 }
 
+// ---------------------------------------------------------------------------
+// Control-pool append: one block per (touched page, kv-head, K-or-V); rows are
+// stored as bf16 at [h][kv][row][d] of the page record.  bf16 is the upper
+// half of the fp32 pattern; adding 0x7FFF plus the kept part's lowest bit
+// carries into the kept half exactly when the dropped half is above one half
+// unit, or equal to it with an odd kept part (round to nearest, ties to
+// even), in integer arithmetic independent of the floating-point mode.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ void __launch_bounds__(kThreads)
+append_bf16_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float* __restrict__ k,
+                   const float* __restrict__ v) {
+  const int per_page = pv.Hkv * 2;
+  const AppendPage ap = plan[blockIdx.x / per_page];
+  const int h = (blockIdx.x / 2) % pv.Hkv;
+  const int kv = blockIdx.x % 2;
+  const int d = pv.d;
+  const float* src = kv ? v : k;
+  uint16_t* rows = reinterpret_cast<uint16_t*>(pv.fp8 + int64_t(ap.phys) * pv.fp8_stride) +
+                   (int64_t(h * 2 + kv) * pv.P + ap.row0) * d;
+  const int n = ap.nrows * d;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int r = i / d, j = i % d;
+    rows[i] = f32_to_bf16_rne(src[(int64_t(ap.src_row + r) * pv.Hkv + h) * d + j]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_bf16(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
+                              const float* k, const float* v, hipStream_t s) {
+  if (n_pages <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_bf16_kernel, dim3(unsigned(n_pages * pv.Hkv * 2)), dim3(kThreads), 0,
+                     s, pv, plan, k, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
                          const float* k, const float* v, hipStream_t s) {

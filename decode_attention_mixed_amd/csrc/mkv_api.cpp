@@ -41,7 +41,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 mkv::Desc to_desc(const mkv_pool_desc& d) {
   return mkv::Desc{d.num_kv_heads, d.head_dim, d.page_size, d.max_seqs, d.max_pages_per_seq,
                    d.max_batch,    d.max_q_heads, d.max_chunks, d.fp8_pages, d.tq3_pages,
-                   d.placement_seed};
+                   d.placement_seed, d.kv_kind};
 }
 
 // Device memory layout of a pool (offsets from the base of its block).
@@ -133,7 +133,7 @@ struct mkv_pool {
     const mkv::Geom& g = meta.geom();
     return mkv::PoolView{mem + lay.fp8, mem + lay.tq3,
                          reinterpret_cast<const int32_t*>(mem + lay.pt), g.fp8_stride,
-                         g.tq3_stride, g.Hkv, g.d, g.P, desc.max_pages_per_seq};
+                         g.tq3_stride, g.Hkv, g.d, g.P, desc.max_pages_per_seq, g.kind};
   }
 
   mkv_status wait_staging() {
@@ -249,6 +249,7 @@ size_t mkv_record_bytes(const mkv_pool_desc* desc, int32_t fmt) {
   if (!desc) return 0;
   mkv::Geom g;
   if (mkv::validate_desc(to_desc(*desc), &g, nullptr) != MKV_S_OK) return 0;
+  if (g.kind == mkv::kKindBf16) return fmt == MKV_FMT_BF16 ? size_t(g.fp8_rec) : 0;
   if (fmt == MKV_FMT_FP8) return size_t(g.fp8_rec);
   if (fmt == MKV_FMT_TQ3) return size_t(g.tq3_rec);
   return 0;
@@ -280,7 +281,7 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
   for (int nh = 1; nh <= 2; ++nh) {
     if (nh == 2 && desc->head_dim > 128) break;
     int waves = 0;
-    e = mkv::partial_resident_waves(desc->head_dim, nh, &waves);
+    e = mkv::partial_resident_waves(desc->head_dim, nh, desc->kv_kind, &waves);
     if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
     if (waves > 0) p->target_waves[nh - 1] = waves;
   }
@@ -350,9 +351,11 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
   if (plan.empty()) return MKV_OK;
   mkv_status r = upload_pt_row_and_plan(p, seq, plan.data(), plan.size() * sizeof(plan[0]), s);
   if (r) return r;
-  MKV_HIP(mkv::launch_append(p->view(),
-                             reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan),
-                             int32_t(plan.size()), k, v, s));
+  const auto* dplan = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
+  if (p->meta.geom().kind == mkv::kKindBf16)
+    MKV_HIP(mkv::launch_append_bf16(p->view(), dplan, int32_t(plan.size()), k, v, s));
+  else
+    MKV_HIP(mkv::launch_append(p->view(), dplan, int32_t(plan.size()), k, v, s));
   return MKV_OK;
 }
 

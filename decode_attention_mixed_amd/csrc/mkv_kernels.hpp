@@ -14,9 +14,10 @@ struct PoolView {
   uint8_t* fp8;        // FP8 slab
   uint8_t* tq3;        // TQ3 slab
   const int32_t* pt;   // page table [max_seqs][pt_stride]
-  int64_t fp8_stride;  // bytes between FP8 records
+  int64_t fp8_stride;  // bytes between FP8 records (BF16 records in a control pool)
   int64_t tq3_stride;  // bytes between TQ3 records
   int32_t Hkv, d, P, pt_stride;
+  int32_t kind;        // kKindMixed or kKindBf16 (control pool: BF16 pages in the FP8 slab)
 };
 
 struct DecodeArgs {
@@ -42,12 +43,16 @@ hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_p
                          const float* k, const float* v, hipStream_t s);
 hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_pages,
                          hipStream_t s);
+// Control pools: store rows as bf16 (round to nearest even).
+hipError_t launch_append_bf16(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
+                              const float* k, const float* v, hipStream_t s);
 hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
                          uint8_t* dst, int64_t slot_bytes, hipStream_t s);
+// Partial kernel of the pool's kind (mixed FP8/TQ3 or BF16 control).
 hipError_t launch_partial(const DecodeArgs& a, hipStream_t s);
-// Waves of the partial kernel (head dim d, nh kv-heads per wave) resident on
-// the current device at once.
-hipError_t partial_resident_waves(int d, int nh, int* waves);
+// Waves of the partial kernel (head dim d, nh kv-heads per wave, pool kind)
+// resident on the current device at once.
+hipError_t partial_resident_waves(int d, int nh, int kind, int* waves);
 // Merge of the partial states; batches with at most narrow_max chunks per
 // entry use the per-lane variant (no cross-lane reduction).
 hipError_t launch_merge(const DecodeArgs& a, int narrow_max, hipStream_t s);

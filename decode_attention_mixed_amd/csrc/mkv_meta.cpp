@@ -43,11 +43,17 @@ int validate_desc(const Desc& d, Geom* g, std::string* err) {
       d.tq3_pages > int64_t(kPtIndexMask))
     return fail(err, MKV_S_EINVAL, "slab page counts must be in 1..2^31-1 (FP8) and 0..2^31-1 (TQ3)");
   if (d.max_chunks < 0) return fail(err, MKV_S_EINVAL, "max_chunks must be >= 0");
+  if (d.kind != kKindMixed && d.kind != kKindBf16)
+    return fail(err, MKV_S_EINVAL, "kv_kind must be MKV_KIND_MIXED or MKV_KIND_BF16");
+  if (d.kind == kKindBf16 && d.tq3_pages != 0)
+    return fail(err, MKV_S_EINVAL, "a BF16 control pool has no TQ3 slab (tq3_pages must be 0)");
   Geom r;
   r.Hkv = d.Hkv;
   r.d = d.d;
   r.P = d.P;
-  r.fp8_rec = 2ll * d.Hkv * d.P * d.d + 16ll * d.Hkv;
+  r.kind = d.kind;
+  // BF16 control record: K and V rows [Hkv][2][P][d] bf16, nothing else
+  r.fp8_rec = d.kind == kKindBf16 ? 4ll * d.Hkv * d.P * d.d : 2ll * d.Hkv * d.P * d.d + 16ll * d.Hkv;
   r.tq3_rec = int64_t(d.Hkv) * d.P * d.d * 7 / 8;
   r.fp8_stride = round_up(r.fp8_rec, kSlabAlign);
   r.tq3_stride = round_up(r.tq3_rec, kSlabAlign);
@@ -132,6 +138,8 @@ int Meta::demote(int32_t s, const int32_t* lps, int32_t n, std::vector<DemotePag
   int st = check_seq(s, err);
   if (st) return st;
   if (n < 0 || (n > 0 && !lps)) return fail(err, MKV_S_EINVAL, "bad page list");
+  if (g_.kind == kKindBf16 && n > 0)
+    return fail(err, MKV_S_ESTATE, "a BF16 control pool holds one format; pages are never converted");
   Seq& q = seqs_[size_t(s)];
   std::vector<char> seen(q.pt.size(), 0);
   for (int32_t i = 0; i < n; ++i) {
@@ -304,7 +312,9 @@ int64_t Meta::seq_kv_bytes(int32_t s) const {
   int64_t t = 0;
   for (int32_t lp = 0; lp < int32_t(q.pt.size()); ++lp) {
     int64_t n = page_tokens(q.len, g_.P, lp);
-    if (pt_is_tq3(q.pt[size_t(lp)]))
+    if (g_.kind == kKindBf16)
+      t += n * 4 * g_.Hkv * g_.d;                  // K and V bf16 rows
+    else if (pt_is_tq3(q.pt[size_t(lp)]))
       t += n * g_.Hkv * g_.d * 7 / 8;
     else
       t += n * 2 * g_.Hkv * g_.d + 8ll * g_.Hkv;

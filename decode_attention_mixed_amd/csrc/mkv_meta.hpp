@@ -27,15 +27,22 @@ inline bool pt_is_tq3(int32_t e) { return e < 0; }
 inline int32_t pt_index(int32_t e) { return e & kPtIndexMask; }
 inline int32_t pt_make(int fmt, int32_t idx) { return fmt ? (idx | kPtTq3Bit) : idx; }
 
+// Pool kinds: the mixed FP8/TQ3 cache, or the dense BF16 control cache (one
+// slab of BF16 pages, held in the FP8 slab's place; no TQ3 slab, no demotion).
+constexpr int32_t kKindMixed = 0;
+constexpr int32_t kKindBf16 = 1;
+
 struct Desc {  // mirror of mkv_pool_desc (kept free of the C header's HIP include)
   int32_t Hkv, d, P, max_seqs, max_pages_per_seq, max_batch, max_q_heads, max_chunks;
   int64_t fp8_pages, tq3_pages;
   uint64_t placement_seed;
+  int32_t kind;
 };
 
 struct Geom {
   int32_t Hkv = 0, d = 0, P = 0;
-  int64_t fp8_rec = 0, tq3_rec = 0;       // record bytes
+  int32_t kind = kKindMixed;
+  int64_t fp8_rec = 0, tq3_rec = 0;       // record bytes (fp8_rec: BF16 record in a control pool)
   int64_t fp8_stride = 0, tq3_stride = 0; // slab strides (records rounded up to 256 B)
   int32_t max_chunks = 0;                 // resolved partial-state capacity
 };

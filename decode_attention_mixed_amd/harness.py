@@ -3,7 +3,9 @@
 For each sequence of a workload: append all of its fp32 K/V rows as FP8 (in
 one call or in the given splits), then demote every non-anchor page to TQ3,
 the lifecycle the Minima-KV summary describes in "Ancoras em FP8, arquivo em
-TQ3".  Pool memory is a torch uint8 tensor, optionally filled with a poison
+TQ3".  The comparison caches of the same summary's "O que foi medido" use the
+same rows: a dense BF16 control pool (append only), and an all-FP8 mixed pool
+(append without demotion).  Pool memory is a torch uint8 tensor, optionally filled with a poison
 byte first so that unwritten slots hold NaN patterns (0x7F is E4M3 NaN and
 0x7F7F is fp16 NaN).
 """
@@ -16,15 +18,28 @@ import decode_attention_mixed_amd as mkv
 
 
 def pool_desc(wl, *, max_seqs=None, max_batch=None, max_chunks=0, placement_seed=None,
-              fp8_pages=None, tq3_pages=None, max_pages_per_seq=None) -> mkv.PoolDesc:
+              fp8_pages=None, tq3_pages=None, max_pages_per_seq=None,
+              kind: str = "mixed") -> mkv.PoolDesc:
+    """kind: "mixed" (FP8/TQ3 slabs of the workload), "bf16" (control pool with
+    one slab holding every page) or "fp8" (mixed pool with an FP8 slab large
+    enough for every page and no TQ3 slab use)."""
     max_pages = max_pages_per_seq or max(wl.n_pages(b) for b in range(wl.B))
+    all_pages = sum(wl.n_pages(b) for b in range(wl.B))
+    if kind == "mixed":
+        f8, t3, kv_kind = fp8_pages or wl.fp8_pages, tq3_pages or wl.tq3_pages, mkv.KIND_MIXED
+    elif kind == "bf16":
+        f8, t3, kv_kind = fp8_pages or all_pages, 0, mkv.KIND_BF16
+    elif kind == "fp8":
+        f8, t3, kv_kind = fp8_pages or all_pages, tq3_pages or 0, mkv.KIND_MIXED
+    else:
+        raise ValueError(kind)
     return mkv.make_desc(
         num_kv_heads=wl.Hkv, head_dim=wl.d, page_size=wl.P,
         max_seqs=max_seqs or wl.B, max_pages_per_seq=max_pages,
         max_batch=max_batch or wl.B, max_q_heads=wl.Hq,
-        fp8_pages=fp8_pages or wl.fp8_pages, tq3_pages=tq3_pages or wl.tq3_pages,
+        fp8_pages=f8, tq3_pages=t3,
         placement_seed=wl.placement_seed if placement_seed is None else placement_seed,
-        max_chunks=max_chunks)
+        max_chunks=max_chunks, kv_kind=kv_kind)
 
 
 class DevicePool:
@@ -55,9 +70,10 @@ class DevicePool:
 
 
 def load_sequence(pool: DevicePool, wl, b: int, seq_id: int | None = None, splits=None,
-                  device="cuda", kv=None) -> None:
-    """Append sequence b of the workload (in `splits` calls if given) and demote
-    its non-anchor pages.  kv: optional (k, v) fp32 arrays or device tensors."""
+                  device="cuda", kv=None, demote: bool = True) -> None:
+    """Append sequence b of the workload (in `splits` calls if given) and, if
+    demote, demote its non-anchor pages.  kv: optional (k, v) fp32 arrays or
+    device tensors."""
     seq_id = b if seq_id is None else seq_id
     if kv is None:
         kv = wl.kv(b)
@@ -76,13 +92,15 @@ def load_sequence(pool: DevicePool, wl, b: int, seq_id: int | None = None, split
         mkv.append(pool.handle, seq_id, k[pos:pos + n], v[pos:pos + n])
         pos += n
     dem = wl.demote_pages(b)
-    if dem.size:
+    if demote and dem.size and pool.desc.kv_kind == mkv.KIND_MIXED:
         mkv.demote(pool.handle, seq_id, dem)
 
 
-def load_cache(pool: DevicePool, wl, splits=None, device="cuda") -> None:
+def load_cache(pool: DevicePool, wl, splits=None, device="cuda", demote: bool = True) -> None:
+    """demote=False: the all-FP8 cache (mixed pool); control pools never demote."""
     for b in range(wl.B):
-        load_sequence(pool, wl, b, splits=None if splits is None else splits[b], device=device)
+        load_sequence(pool, wl, b, splits=None if splits is None else splits[b], device=device,
+                      demote=demote)
 
 
 def q_tensor(wl, device="cuda") -> torch.Tensor:
@@ -92,7 +110,7 @@ def q_tensor(wl, device="cuda") -> torch.Tensor:
 
 def gather_records(pool: DevicePool, seq_id: int, n_pages: int, device="cuda") -> np.ndarray:
     """Records of logical pages 0..n_pages-1 as a uint8 array [n_pages][slot]."""
-    slot = max(mkv.record_bytes(pool.desc, mkv.FMT_FP8), mkv.record_bytes(pool.desc, mkv.FMT_TQ3))
+    slot = max(mkv.record_bytes(pool.desc, f) for f in (mkv.FMT_FP8, mkv.FMT_TQ3, mkv.FMT_BF16))
     dst = torch.empty(n_pages * slot, dtype=torch.uint8, device=device)
     mkv.debug_gather(pool.handle, seq_id, 0, n_pages, dst)
     torch.cuda.synchronize()

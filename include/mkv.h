@@ -28,6 +28,17 @@
  *  - Page-table entry: int32, bit 31 = format (0 FP8, 1 TQ3), bits 0..30 =
  *    physical page index in that format's slab.
  *
+ * Control pools (kv_kind = MKV_KIND_BF16): the dense single-format cache the
+ * summaries measure the mixed cache against (section "O que foi medido":
+ * compression relative to BF16 and to FP8; the canary's throughput relative
+ * to its control).  Every row is stored as bf16, rounded to nearest even;
+ * record [Hkv][2 (K,V)][P][d] bf16, in the slab that holds FP8 pages in a
+ * mixed pool (fp8_pages is its capacity, tq3_pages must be 0); page-table
+ * entries have bit 31 clear.  mkv_append stores bf16 rows, mkv_demote
+ * returns MKV_ESTATE, mkv_decode runs a BF16 partial kernel and the same
+ * merge.  The all-FP8 comparison needs no special pool: a mixed pool whose
+ * pages are never demoted.
+ *
  * Conventions shared by every call:
  *  - All functions are extern "C"; no C++ exception crosses the boundary.
  *  - Device pointers are plain HIP device addresses (e.g. from a torch tensor).
@@ -64,7 +75,8 @@ typedef enum {
   MKV_EHIP = -5
 } mkv_status;
 
-enum { MKV_FMT_FP8 = 0, MKV_FMT_TQ3 = 1 };
+enum { MKV_FMT_FP8 = 0, MKV_FMT_TQ3 = 1, MKV_FMT_BF16 = 2 };
+enum { MKV_KIND_MIXED = 0, MKV_KIND_BF16 = 1 };
 
 typedef struct mkv_pool mkv_pool; /* opaque; owned by the library */
 
@@ -85,6 +97,7 @@ typedef struct {
   int64_t fp8_pages;         /* FP8 slab capacity in pages */
   int64_t tq3_pages;         /* TQ3 slab capacity in pages */
   uint64_t placement_seed;   /* 0: pages handed out in index order; else a seeded shuffle */
+  int32_t kv_kind;           /* MKV_KIND_MIXED (0): FP8/TQ3 cache; MKV_KIND_BF16: control pool */
 } mkv_pool_desc;
 
 typedef struct {
@@ -111,7 +124,9 @@ typedef struct {
  * schedule and partial-state workspace).  Returns 0 for an invalid descriptor. */
 size_t mkv_pool_bytes(const mkv_pool_desc* desc);
 
-/* Bytes of one page record of the given format (layout above); 0 if invalid. */
+/* Bytes of one page record of the given format (layout above): MKV_FMT_FP8
+ * or MKV_FMT_TQ3 for a mixed pool, MKV_FMT_BF16 for a control pool; 0 if the
+ * format does not belong to the descriptor's kind or the descriptor is invalid. */
 size_t mkv_record_bytes(const mkv_pool_desc* desc, int32_t fmt);
 
 /* Create a pool on the current HIP device.  device_mem: NULL to let the
@@ -129,7 +144,9 @@ mkv_status mkv_pool_destroy(mkv_pool* pool);
 mkv_status mkv_seq_reset(mkv_pool* pool, int32_t seq, hipStream_t stream);
 
 /* Append n tokens to sequence `seq` as FP8 ("Ancoras em FP8": new pages start
- * FP8).  k, v: device fp32 [n][Hkv][d], row-major, finite values.  New pages
+ * FP8; in a control pool, as bf16 rows rounded to nearest even, with none of
+ * the scale handling below).  k, v: device fp32 [n][Hkv][d], row-major,
+ * finite values.  New pages
  * come from the FP8 free list.  The FP8 scale of a page-head is recomputed when
  * new rows raise its running amax and the page's earlier rows are re-encoded
  * against it, so a page filled by one call equals one-shot quantisation.
@@ -145,7 +162,8 @@ mkv_status mkv_append(mkv_pool* pool, int32_t seq, int32_t n, const float* k, co
  * page returns to the free list.  Codes: x = fp32(e4m3(c) * sigma) per element,
  * then per 32-group s = fp16(fp32(absmax / 3.5)) (clamped to 65504) and
  * c = #{b in -3..3 : x >= b*s} (c = 4 when s == 0).  Demoting a partially
- * filled last page is allowed; the sequence then accepts no more appends. */
+ * filled last page is allowed; the sequence then accepts no more appends.
+ * MKV_ESTATE in a control pool (n > 0). */
 mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages, int32_t n,
                       hipStream_t stream);
 

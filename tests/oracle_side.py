@@ -21,6 +21,17 @@ def seq_model(wl, b, splits=None, kv=None):
     return seq
 
 
+def bf16_model(wl, b, splits=None, kv=None):
+    """The dense BF16 control cache of sequence b (same rows, never converted)."""
+    k, v = wl.kv(b) if kv is None else kv
+    seq = PM.Bf16SeqModel(wl.Hkv, wl.d, wl.P)
+    pos = 0
+    for n in (splits if splits is not None else [k.shape[0]]):
+        seq.append(k[pos:pos + n], v[pos:pos + n])
+        pos += n
+    return seq
+
+
 def decode_all(wl, models):
     O = np.zeros((wl.B, wl.Hq, wl.d))
     lse = np.zeros((wl.B, wl.Hq))

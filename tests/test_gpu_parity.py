@@ -252,6 +252,63 @@ def test_named_workloads_full_parity(name):
     pool.close()
 
 
+# ------------------------------------------------------------ BF16 control pools
+def _control_splits(wl):
+    """Append each sequence in two calls (the second starting mid-page)."""
+    return [[int(L) // 3, int(L) - int(L) // 3] if L >= 3 else [int(L)] for L in wl.lengths]
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_CASES))
+def test_bf16_control_records_and_decode(name):
+    """Control pools: bf16 records bit for bit (valid rows) and decode against
+    the oracle on the bf16-rounded rows."""
+    wl = W.small(**SMALL_CASES[name])
+    print(f"control case {name}: lengths={list(wl.lengths)}", flush=True)
+    pool = H.DevicePool(H.pool_desc(wl, kind="bf16"))
+    splits = _control_splits(wl)
+    H.load_cache(pool, wl, splits=splits)
+    models = [OS.bf16_model(wl, b, splits[b]) for b in range(wl.B)]
+    for b, m in enumerate(models):
+        n = len(m.bits)
+        recs = H.gather_records(pool, b, n)
+        pt = mkv.page_table(pool.handle, b)
+        assert np.all(np.asarray(pt[:n]) >= 0)
+        for lp in range(n):
+            ref, mask = m.record(lp), m.valid_mask(lp)
+            got = recs[lp, :ref.size]
+            bad = np.nonzero((got != ref) & mask)[0]
+            assert bad.size == 0, f"seq {b} page {lp}: {bad.size} bytes differ, first at {bad[:8]}"
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, *OS.decode_all(wl, models), f"bf16 {name}")
+    st = mkv.pool_stats(pool.handle)
+    from oracle import pool_model as PM
+    assert st["kv_bytes"] == sum(PM.bf16_kv_bytes(m) for m in models)
+    assert st["ratio_vs_bf16"] == pytest.approx(1.0) and st["tq3_pages_live"] == 0
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.demote(pool.handle, 0, np.array([0], np.int32))
+    assert e.value.status == mkv.ESTATE
+    pool.close()
+
+
+def test_bf16_control_long_context_parity():
+    """The 131072-token Hq=48/Hkv=8 shape as a BF16 control cache, decoded in
+    the launch configuration the benchmark times for the control."""
+    wl = W.long()
+    model = OS.bf16_model(wl, 0)
+    O, L = A.decode_seq(model, wl.q_bits[0], wl.tau)
+    pool = H.DevicePool(H.pool_desc(wl, kind="bf16"))
+    H.load_cache(pool, wl)
+    recs = H.gather_records(pool, 0, len(model.bits))
+    for lp in (0, 1, 4000, 8191):
+        ref, mask = model.record(lp), model.valid_mask(lp)
+        assert np.array_equal(recs[lp, :ref.size][mask], ref[mask])
+    out, lse = _run_decode(pool, wl)
+    _check(out[0], lse[0], O, L, "bf16 long")
+    pool.close()
+    del pool
+    torch.cuda.empty_cache()
+
+
 @pytest.fixture(scope="module")
 def long_case():
     wl = W.long()

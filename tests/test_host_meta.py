@@ -304,3 +304,27 @@ def test_host_metadata_under_asan_ubsan(tmp_path, repo_root):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "ok" in r.stdout
+
+
+# ------------------------------------------------------------ BF16 control pools
+def test_bf16_control_pool_metadata(lib):
+    """A control pool (kv_kind = MKV_KIND_BF16) has one slab, counts 4*Hkv*d
+    bytes per token, never converts pages, and schedules every page as one
+    format."""
+    with pytest.raises(ValueError):
+        _host(lib, kv_kind=1)                    # a TQ3 slab is not allowed
+    with pytest.raises(ValueError):
+        _host(lib, kv_kind=2, tq3_pages=0)       # unknown kind
+    h = _host(lib, kv_kind=1, tq3_pages=0, fp8_pages=40)
+    st, plan = h.append(0, 100)
+    assert st == 0 and len(plan) == 7
+    ids = np.array([0], np.int32)
+    assert h.L.mkvh_kv_bytes(h.h, ids.ctypes.data, 1) == 100 * 4 * 2 * 128
+    v0 = h.L.mkvh_version(h.h)
+    st, _ = h.demote(0, [0])
+    assert st == -3                              # MKV_ESTATE
+    assert h.L.mkvh_version(h.h) == v0 and not any(is_tq3(e) for e in h.pt(0))
+    st, sch = h.schedule([0], Hq=8)
+    assert st == 0 and sch["n3"] == 0 and sch["n8"] >= 1
+    assert sorted(sch["pages"].tolist()) == list(range(7))
+    h.close()
