@@ -18,8 +18,13 @@ Prints one JSON line:
                decode stream during a second timed region of the same steps
                (the first, without library events, gives value), against 8 TB/s
   cpu_baseline the CPU oracle on the same workload (bounded repetitions)
+  comparison   the same rows as a dense BF16 control cache and as an all-FP8
+               cache (no demotion), decoded the same way: their us/step, the
+               mixed cache's throughput relative to each (the control ratio
+               of the Minima-KV summary's canary test) and KV bytes per live
+               token (its compression relative to BF16 and FP8)
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-compare]
 """
 from __future__ import annotations
 
@@ -209,6 +214,8 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--replicas", type=int, default=0, help="0: 8, or 1 for multi-GB workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the BF16-control and all-FP8 comparison runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps "
                          "times (reference for the HBM byte counters)")
@@ -245,39 +252,43 @@ def main():
     # R pools, each holding one replica of the batch at its own (seeded, scattered)
     # physical pages, like the per-layer caches of a model; step i decodes pool i % R.
     n_anchor = sum(len(a) for a in wl.anchors)
-    n_tq3 = sum(wl.n_pages(b) for b in range(wl.B)) - n_anchor
+    all_pages = sum(wl.n_pages(b) for b in range(wl.B))
+    n_tq3 = all_pages - n_anchor
     max_pages = max(wl.n_pages(b) for b in range(wl.B))
-    pools = []
-    t0 = time.perf_counter()
     kvs = [wl.kv(b) for b in range(wl.B)] if wl.B * max_pages * wl.P * wl.Hkv * wl.d <= 2**29 else None
-    for r in range(R):
-        if R == 1:
-            desc = H.pool_desc(wl)
-        else:
-            desc = H.pool_desc(wl, fp8_pages=n_anchor + max_pages + 16, tq3_pages=n_tq3 + 16,
-                               placement_seed=wl.placement_seed + r)
-        pools.append(H.DevicePool(desc))
-    for b in range(wl.B):
-        kv = kvs[b] if kvs is not None else wl.kv(b)
-        for r in range(R):
-            H.load_sequence(pools[r], wl, b, kv=kv)
-    del kvs
-    torch.cuda.synchronize()
-    log(f"cache built in {time.perf_counter() - t0:.1f} s: {mkv.pool_stats(pools[0].handle)}")
-
     q = H.q_tensor(wl)
     out = torch.empty(wl.B, wl.Hq, wl.d, device="cuda")
     lse = torch.empty(wl.B, wl.Hq, device="cuda")
     batch = list(range(wl.B))
     tau = float(wl.tau)
-
-    for i in range(max(args.warmup, R)):
-        mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
-    torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
 
-    def timed_steps():
+    def build(kind):
+        """R pools of one kind: "mixed" (anchors FP8, the rest demoted to TQ3),
+        "bf16" (control pool) or "fp8" (mixed pool, nothing demoted)."""
+        t0 = time.perf_counter()
+        pools = []
+        for r in range(R):
+            if kind == "mixed" and R == 1:
+                desc = H.pool_desc(wl)
+            elif kind == "mixed":
+                desc = H.pool_desc(wl, fp8_pages=n_anchor + max_pages + 16, tq3_pages=n_tq3 + 16,
+                                   placement_seed=wl.placement_seed + r)
+            else:
+                desc = H.pool_desc(wl, kind=kind, fp8_pages=all_pages + 16,
+                                   placement_seed=wl.placement_seed + r)
+            pools.append(H.DevicePool(desc))
+        for b in range(wl.B):
+            kv = kvs[b] if kvs is not None else wl.kv(b)
+            for r in range(R):
+                H.load_sequence(pools[r], wl, b, kv=kv, demote=(kind == "mixed"))
+        torch.cuda.synchronize()
+        st = mkv.pool_stats(pools[0].handle)
+        log(f"{kind} cache built in {time.perf_counter() - t0:.1f} s: {st}")
+        return pools, st
+
+    def timed_steps(pools):
         torch.cuda.synchronize()
         ev0.record()
         t0 = time.perf_counter()
@@ -288,14 +299,21 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / args.steps, host_s / args.steps
 
+    def warm(pools):
+        for i in range(max(args.warmup, R)):
+            mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
+        torch.cuda.synchronize()
+
+    pools, mixed_stats = build("mixed")
+    warm(pools)
     # Timed region 1: the step as a caller sees it (no library events).
-    ms, host_s = timed_steps()
+    ms, host_s = timed_steps(pools)
     # Timed region 2: the same steps with the library's per-kernel HIP events
     # recorded on the decode stream (kernel durations for the roofline).
     for p in pools:
         mkv.profile_enable(p.handle, True)
         mkv.profile_read(p.handle)
-    ms_ev, _ = timed_steps()
+    ms_ev, _ = timed_steps(pools)
     prof = {}
     for p in pools:
         for k2, v2 in mkv.profile_read(p.handle).items():
@@ -303,6 +321,34 @@ def main():
         mkv.profile_enable(p.handle, False)
     log(f"step {ms * 1e3:.2f} us (host {host_s * 1e6:.1f} us per call; {ms_ev * 1e3:.2f} us with "
         f"kernel events); kernel profile {prof}")
+    for p in pools:
+        p.close()
+    del pools
+    torch.cuda.empty_cache()
+
+    comparison = None
+    if not args.no_compare:
+        tokens = int(mixed_stats["live_tokens"])
+        comparison = {"mixed": {"us_per_step": round(ms * 1e3, 3),
+                                "kv_bytes_per_token": round(mixed_stats["bytes_per_token"], 2)}}
+        for kind, label in (("bf16", "bf16_control"), ("fp8", "all_fp8")):
+            cpools, cst = build(kind)
+            warm(cpools)
+            cms, _ = timed_steps(cpools)
+            comparison[label] = {
+                "us_per_step": round(cms * 1e3, 3),
+                "kv_bytes_per_token": round(cst["bytes_per_token"], 2),
+                "kv_gbs": round(cst["kv_bytes"] / (cms * 1e-3) / 1e9, 2),
+                "mixed_throughput_ratio": round(cms / ms, 4),
+                "mixed_compression": round(cst["bytes_per_token"] / mixed_stats["bytes_per_token"], 4),
+            }
+            assert int(cst["live_tokens"]) == tokens
+            log(f"{kind}: {comparison[label]}")
+            for p in cpools:
+                p.close()
+            del cpools
+            torch.cuda.empty_cache()
+    del kvs
 
     kernel_ms = {"partial": prof["ms_partial"] / max(1, prof["n_partial"]),
                  "merge": prof["ms_merge"] / max(1, prof["n_merge"])}
@@ -348,10 +394,8 @@ def main():
             "algorithmic_bytes_per_launch": dom_bytes,
         },
     }
-    for p in pools:
-        p.close()
-    del pools
-    torch.cuda.empty_cache()
+    if comparison is not None:
+        result["comparison"] = comparison
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, step_bytes)
     print(json.dumps(result), flush=True)
