@@ -297,6 +297,33 @@ class Bf16SeqModel:
         return m.reshape(-1)
 
 
+def materialise(seq: SeqModel) -> Bf16SeqModel:
+    """The materialising profile of the summary (section "Qualidade em contexto
+    longo": the hybrid pages expanded into dense tensors): every valid row of
+    every page of a mixed-format sequence, dequantised and stored in a dense
+    BF16 control cache with the same page size.  Each element is first the
+    fp32 value the decode kernels work with -- fp32(e4m3(c) * sigma) for FP8
+    (one rounded fp32 product), (c - 3.5) * s for TQ3 (exact) -- then rounded
+    to bf16 (nearest even)."""
+    out = Bf16SeqModel(seq.Hkv, seq.d, seq.P)
+    for page in seq.pages:
+        n = page.ntok
+        if page.fmt == FP8:
+            x = (C.e4m3_decode(page.codes[:, :, :n, :]).astype(np.float32)
+                 * page.scale.astype(np.float32)[:, :, None, None]).astype(np.float32)
+        else:
+            G = seq.d // C.TQ3_GROUP
+            c = page.tcodes[:, :, :n, :].reshape(2, seq.Hkv, n, G, C.TQ3_GROUP)
+            x = C.tq3_decode(c, page.tscale[:, :, :n, :]).reshape(2, seq.Hkv, n, seq.d)
+            x = x.astype(np.float32)                    # exact: 3-bit level times an fp16 scale
+        bits = np.zeros((2, seq.Hkv, seq.P, seq.d), np.uint16)
+        bits[:, :, :n, :] = C.bf16_encode(x)
+        out.bits.append(bits)
+        out.ntok.append(n)
+        out.length += n
+    return out
+
+
 def bf16_kv_bytes(seq: Bf16SeqModel) -> int:
     """Bytes a decode step reads for a control sequence: K and V bf16 rows."""
     return seq.length * 4 * seq.Hkv * seq.d

@@ -370,3 +370,50 @@ def test_bf16_control_dense_and_decode():
     x = np.full((1, 1, 32), 1.0 + 2.0 ** -8 + 2.0 ** -12, np.float32)
     seq2.append(x, x)
     assert np.all(seq2.dense()[0] == 1.0 + 2.0 ** -7)
+
+
+def test_materialise_hand_page_and_properties():
+    """Materialised rows: FP8 elements are fp32(e4m3(c) * sigma) rounded to bf16,
+    TQ3 elements (c - 3.5) * s rounded to bf16; page structure is kept."""
+    Hkv, P, d = 1, 16, 32
+    k = np.zeros((20, Hkv, d), np.float32)
+    v = np.zeros((20, Hkv, d), np.float32)
+    k[0, 0, 0] = 448.0          # amax 448: sigma 1, code 0x7E (448)
+    k[0, 0, 1] = 1.0 + 2.0 ** -3   # e4m3 exact: 1.125
+    v[3, 0, 2] = -3.0
+    k[17, 0, 5] = 7.0           # second page: one of its rows
+    seq = PM.SeqModel(Hkv, d, P)
+    seq.append(k, v)
+    m = PM.materialise(seq)
+    assert m.ntok == [16, 4] and m.length == 20
+    K, V = m.dense()
+    assert K[0, 0, 0] == 448.0 and K[0, 0, 1] == 1.125 and V[3, 0, 2] == -3.0 and K[17, 0, 5] == 7.0
+    assert np.count_nonzero(K) == 3 and np.count_nonzero(V) == 1
+    # demote page 0 to TQ3: the group holding 448 and 1.125 has s = fp16(448/3.5) = 128,
+    # so 448 -> code 7 -> 3.5*128 = 448 and 1.125 -> code 4 -> 0.5*128 = 64, zeros -> 64 too
+    seq.demote(0)
+    K2, _ = PM.materialise(seq).dense()
+    assert K2[0, 0, 0] == 448.0 and K2[0, 0, 1] == 64.0 and K2[1, 0, 0] == 0.0
+    assert np.all(K2[0, 0, 2:] == 64.0)
+
+
+def test_materialise_matches_exact_dequantisation_rounded():
+    """Against the exact fp64 page values: rounding them to fp32 and then to bf16
+    gives the materialised bits (FP8 and TQ3 pages, outlier rows)."""
+    rng = np.random.default_rng(31)
+    Hkv, P, d, L = 2, 16, 64, 70
+    k = rng.standard_normal((L, Hkv, d)).astype(np.float32)
+    v = rng.standard_normal((L, Hkv, d)).astype(np.float32) * np.float32(8.0)
+    seq = PM.SeqModel(Hkv, d, P)
+    seq.append(k, v)
+    for lp in (0, 2):
+        seq.demote(lp)
+    m = PM.materialise(seq)
+    K, V = seq.dense()
+    MK, MV = m.dense()
+    ref_k = C.bf16_bits_to_value(C.bf16_encode(K.astype(np.float32)))
+    ref_v = C.bf16_bits_to_value(C.bf16_encode(V.astype(np.float32)))
+    assert np.array_equal(MK, ref_k) and np.array_equal(MV, ref_v)
+    # TQ3 values carry at most 14 significant bits, so their fp32 rounding is exact
+    tq = K[:16]
+    assert np.array_equal(tq.astype(np.float32).astype(np.float64), tq)
