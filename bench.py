@@ -22,7 +22,9 @@ Prints one JSON line:
                cache (no demotion), decoded the same way: their us/step, the
                mixed cache's throughput relative to each (the control ratio
                of the Minima-KV summary's canary test) and KV bytes per live
-               token (its compression relative to BF16 and FP8)
+               token (its compression relative to BF16 and FP8); and the
+               materialising profile (every step expands the cache into dense
+               bf16 rows of a control pool, then decodes that copy)
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-compare]
 """
@@ -321,6 +323,37 @@ def main():
         mkv.profile_enable(p.handle, False)
     log(f"step {ms * 1e3:.2f} us (host {host_s * 1e6:.1f} us per call; {ms_ev * 1e3:.2f} us with "
         f"kernel events); kernel profile {prof}")
+    materialised = None
+    if not args.no_compare:
+        # Materialising profile: each step expands the whole batch of replica
+        # i % R into dense bf16 rows of a control pool and decodes that copy.
+        dpools = [H.DevicePool(H.pool_desc(wl, kind="bf16", fp8_pages=all_pages + 16,
+                                           placement_seed=wl.placement_seed + r)) for r in range(R)]
+
+        def mat_steps(n, with_decode):
+            torch.cuda.synchronize()
+            ev0.record()
+            for i in range(n):
+                src, dst = pools[i % R], dpools[i % R]
+                for b in batch:
+                    mkv.seq_reset(dst.handle, b)
+                    mkv.materialize(src.handle, b, dst.handle, b)
+                if with_decode:
+                    mkv.decode(dst.handle, batch, q, tau, out, lse)
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / n
+
+        mat_steps(max(args.warmup, R), True)
+        mat_only = mat_steps(args.steps, False)
+        mat_step = mat_steps(args.steps, True)
+        materialised = {"materialise_us": round(mat_only * 1e3, 3),
+                        "us_per_step": round(mat_step * 1e3, 3),
+                        "mixed_throughput_ratio": round(mat_step / ms, 4)}
+        log(f"materialising profile: {materialised}")
+        for p in dpools:
+            p.close()
+        del dpools
     for p in pools:
         p.close()
     del pools
@@ -348,6 +381,7 @@ def main():
                 p.close()
             del cpools
             torch.cuda.empty_cache()
+        comparison["materialising_profile"] = materialised
     del kvs
 
     kernel_ms = {"partial": prof["ms_partial"] / max(1, prof["n_partial"]),

@@ -84,7 +84,7 @@ class Profile(ctypes.Structure):
 
 EXPORTED = [
     "mkv_pool_bytes", "mkv_record_bytes", "mkv_pool_create", "mkv_pool_destroy",
-    "mkv_seq_reset", "mkv_append", "mkv_demote", "mkv_decode", "mkv_seq_info",
+    "mkv_seq_reset", "mkv_append", "mkv_demote", "mkv_materialize", "mkv_decode", "mkv_seq_info",
     "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_profile_enable",
     "mkv_profile_read", "mkv_status_string", "mkv_last_error",
 ]
@@ -110,6 +110,7 @@ def _load():
         "mkv_seq_reset": (I32, [P, I32, P]),
         "mkv_append": (I32, [P, I32, I32, P, P, P]),
         "mkv_demote": (I32, [P, I32, P, I32, P]),
+        "mkv_materialize": (I32, [P, I32, P, I32, P]),
         "mkv_decode": (I32, [P, P, I32, P, I32, F32, P, P, P]),
         "mkv_seq_info": (I32, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "mkv_page_table": (I32, [P, I32, P, I32]),
@@ -210,6 +211,12 @@ def append(pool, seq: int, k, v, stream=None) -> None:
 def demote(pool, seq: int, logical_pages, stream=None) -> None:
     arr, n = _i32_array(logical_pages)
     _check(_load().mkv_demote(pool, seq, arr, n, _stream(stream)))
+
+
+def materialize(src_pool, src_seq: int, dst_pool, dst_seq: int, stream=None) -> None:
+    """Materialising profile: expand sequence src_seq of a mixed pool into the
+    empty sequence dst_seq of a BF16 control pool (a diagnostic)."""
+    _check(_load().mkv_materialize(src_pool, src_seq, dst_pool, dst_seq, _stream(stream)))
 
 
 def decode(pool, seq_ids, q, softmax_scale: float, out, lse, stream=None) -> None:

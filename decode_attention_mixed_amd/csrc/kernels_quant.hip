@@ -179,7 +179,61 @@ append_bf16_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float
   }
 }
 
+// ---------------------------------------------------------------------------
+// Materialising profile (Minima-KV summary, "Qualidade em contexto longo": the
+// hybrid pages expanded into dense tensors; a diagnostic, never on the decode
+// path): one block per (page, kv-head, K-or-V).  Each valid element becomes
+// the fp32 value the decode kernels work with -- fp32(e4m3(c) * sigma) for an
+// FP8 page, (c - 3.5) * s for a TQ3 page (exact) -- rounded to bf16 into the
+// control pool's record [h][kv][row][d].
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+materialise_kernel(PoolView src, PoolView dst, const MaterialisePage* __restrict__ plan) {
+  const int per_page = src.Hkv * 2;
+  const MaterialisePage mp = plan[blockIdx.x / per_page];
+  const int h = (blockIdx.x / 2) % src.Hkv;
+  const int kv = blockIdx.x % 2;
+  const int d = src.d;
+  const uint8_t* rec = page_address(src, mp.src_entry);
+  uint16_t* rows = reinterpret_cast<uint16_t*>(dst.fp8 + int64_t(mp.dst_phys) * dst.fp8_stride) +
+                   int64_t(h * 2 + kv) * dst.P * d;
+  // eight consecutive elements of one row per step (they share a 32-group);
+  // d is a multiple of 32, so a row holds whole steps
+  const int n8 = mp.ntok * d / 8;
+  for (int e = threadIdx.x; e < n8; e += kThreads) {
+    const int i = 8 * e, t = i / d, j = i % d;
+    float x[8];
+    if (mp.src_entry < 0) {
+      // codes j .. j+7 of the group: 24 bits starting at byte 3 (j % 32) / 8
+      const uint8_t* grp = rec + tq3_codes_off(src, h, kv) + t * (3 * d / 8) + 12 * (j / 32) + 3 * (j % 32) / 8;
+      const uint32_t u = uint32_t(grp[0]) | uint32_t(grp[1]) << 8 | uint32_t(grp[2]) << 16;
+      const float s = f16_bits_to_f32(
+          reinterpret_cast<const uint16_t*>(rec + tq3_scale_off(src, h, kv))[t * (d / 32) + j / 32]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = (float((u >> (3 * k)) & 7u) - 3.5f) * s;
+    } else {
+      const uint8_t* c = rec + fp8_codes_off(src, h, kv) + i;
+      const float sigma = *reinterpret_cast<const float*>(rec + fp8_scale_off(src, h, kv));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = e4m3_to_f32(c[k]) * sigma;
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = uint32_t(f32_to_bf16_rne(x[2 * k])) | uint32_t(f32_to_bf16_rne(x[2 * k + 1])) << 16;
+    *reinterpret_cast<uint4*>(rows + i) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_materialise(const PoolView& src, const PoolView& dst, const MaterialisePage* plan,
+                              int32_t n_pages, hipStream_t s) {
+  if (n_pages <= 0) return hipSuccess;
+  hipLaunchKernelGGL(materialise_kernel, dim3(unsigned(n_pages * src.Hkv * 2)), dim3(kThreads), 0, s,
+                     src, dst, plan);
+  return hipGetLastError();
+}
 
 hipError_t launch_append_bf16(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
                               const float* k, const float* v, hipStream_t s) {

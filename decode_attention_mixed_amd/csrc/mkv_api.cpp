@@ -17,7 +17,7 @@ static_assert(MKV_OK == MKV_S_OK && MKV_EINVAL == MKV_S_EINVAL && MKV_ENOMEM == 
                   MKV_EHIP == MKV_S_EHIP,
               "status codes must agree");
 static_assert(sizeof(mkv::WorkItem) == 32 && sizeof(mkv::AppendPage) == 32 &&
-                  sizeof(mkv::DemotePage) == 32,
+                  sizeof(mkv::DemotePage) == 32 && sizeof(mkv::MaterialisePage) == 32,
               "device plan records are 32 bytes");
 
 namespace {
@@ -442,6 +442,38 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   ProfEvent* e = prof_begin(p, 1, s);
   MKV_HIP(mkv::launch_merge(a, p->merge_narrow_max, s));
   prof_end(p, e, s);
+  return MKV_OK;
+}
+
+mkv_status mkv_materialize(mkv_pool* src, int32_t src_seq, mkv_pool* dst, int32_t dst_seq,
+                           hipStream_t s) {
+  if (!src || !dst || src == dst) return set_err(MKV_EINVAL, "two distinct pools are required");
+  const mkv::Geom& gs = src->meta.geom();
+  const mkv::Geom& gd = dst->meta.geom();
+  if (gs.kind != mkv::kKindMixed || gd.kind != mkv::kKindBf16)
+    return set_err(MKV_EINVAL, "source must be a mixed pool and destination a BF16 control pool");
+  if (gs.Hkv != gd.Hkv || gs.d != gd.d || gs.P != gd.P)
+    return set_err(MKV_EINVAL, "pools differ in num_kv_heads, head_dim or page_size");
+  if (src->device != dst->device) return set_err(MKV_EINVAL, "pools live on different devices");
+  if (src_seq < 0 || src_seq >= src->desc.max_seqs || dst_seq < 0 || dst_seq >= dst->desc.max_seqs)
+    return set_err(MKV_EINVAL, "sequence id out of range");
+  const mkv::Seq& sq = src->meta.seq(src_seq);
+  if (sq.len == 0) return set_err(MKV_EINVAL, "empty source sequence");
+  if (dst->meta.seq(dst_seq).len != 0) return set_err(MKV_ESTATE, "destination sequence is not empty");
+  DeviceGuard guard(dst->device);
+  std::vector<mkv::AppendPage> ap;
+  std::string err;
+  int st = dst->meta.append(dst_seq, sq.len, &ap, &err);
+  if (st) return set_err(mkv_status(st), err);
+  std::vector<mkv::MaterialisePage> plan;
+  plan.reserve(ap.size());
+  for (const mkv::AppendPage& a : ap)   // fresh pages: row0 == 0, one per source page
+    plan.push_back(mkv::MaterialisePage{a.lp, sq.pt[size_t(a.lp)], a.phys, a.nrows, 0, 0, 0, 0});
+  mkv_status r = upload_pt_row_and_plan(dst, dst_seq, plan.data(), plan.size() * sizeof(plan[0]), s);
+  if (r) return r;
+  MKV_HIP(mkv::launch_materialise(src->view(), dst->view(),
+                                  reinterpret_cast<const mkv::MaterialisePage*>(dst->mem + dst->lay.plan),
+                                  int32_t(plan.size()), s));
   return MKV_OK;
 }
 

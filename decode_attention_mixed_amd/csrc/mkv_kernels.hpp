@@ -43,6 +43,10 @@ hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_p
                          const float* k, const float* v, hipStream_t s);
 hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_pages,
                          hipStream_t s);
+// Materialising profile: expand pages of a mixed pool (src) into bf16 rows of
+// a control pool (dst).
+hipError_t launch_materialise(const PoolView& src, const PoolView& dst, const MaterialisePage* plan,
+                              int32_t n_pages, hipStream_t s);
 // Control pools: store rows as bf16 (round to nearest even).
 hipError_t launch_append_bf16(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
                               const float* k, const float* v, hipStream_t s);

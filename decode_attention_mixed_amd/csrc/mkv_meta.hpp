@@ -76,6 +76,11 @@ struct AppendPage {
 struct DemotePage {
   int32_t lp, src_phys, dst_phys, ntok, pad0, pad1, pad2, pad3;
 };
+// One page the materialising copy expands: the source page-table entry (either
+// format) and the destination page of a BF16 control pool.
+struct MaterialisePage {
+  int32_t lp, src_entry, dst_phys, ntok, pad0, pad1, pad2, pad3;
+};
 
 // One unit of split-K work: `npages` logical pages of one format of one
 // sequence, listed at pages[list_off ..]; the last listed page holds

@@ -187,6 +187,22 @@ mkv_status mkv_decode(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const v
                       int32_t Hq, float softmax_scale, float* out, float* lse,
                       hipStream_t stream);
 
+/* Materialising profile (Minima-KV summary, "Qualidade em contexto longo":
+ * the hybrid pages expanded into dense tensors, a diagnostic the decode path
+ * never uses).  Appends every token of sequence src_seq of the mixed pool src
+ * to the empty sequence dst_seq of the control pool dst (kv_kind
+ * MKV_KIND_BF16, same num_kv_heads, head_dim and page_size, same device), one
+ * destination page per source page.  Each element is the fp32 value the
+ * decode kernels use -- fp32(e4m3(c) * sigma) for an FP8 page, (c - 3.5) * s
+ * for a TQ3 page -- rounded to bf16 (nearest even).  mkv_decode on dst then
+ * runs dense attention over the materialised rows.  Both pools must be used
+ * on `stream` (or ordered by the caller).
+ * MKV_EINVAL for pools of the wrong kinds or geometries, an empty source, or
+ * bad ids; MKV_ESTATE if dst_seq is not empty; MKV_ENOMEM / MKV_ERANGE if dst
+ * lacks pages. */
+mkv_status mkv_materialize(mkv_pool* src, int32_t src_seq, mkv_pool* dst, int32_t dst_seq,
+                           hipStream_t stream);
+
 /* Introspection (host metadata; no device work). */
 mkv_status mkv_seq_info(mkv_pool* pool, int32_t seq, int32_t* len, int32_t* n_pages);
 /* entries: host int32 [cap] receives the sequence's page-table entries. */

@@ -309,6 +309,41 @@ def test_bf16_control_long_context_parity():
     torch.cuda.empty_cache()
 
 
+def test_materialising_profile_records_and_decode():
+    """mkv_materialize expands every page of a mixed pool (FP8 anchors, TQ3
+    archive, partial tails, a 1-token sequence) into a control pool: records bit
+    for bit against the oracle's materialised rows, then the control pool's
+    decode against the oracle on those rows; the source pool is untouched and
+    a second materialisation into a non-empty sequence is refused."""
+    wl = W.small(seed=41, B=3, Hq=12, Hkv=2, d=128, P=16, lengths=(410, 1, 77),
+                 outliers={"k": (3, 8.0), "v": (3, 8.0)})
+    src = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(src, wl)
+    dst = H.DevicePool(H.pool_desc(wl, kind="bf16"))
+    for b in range(wl.B):
+        mkv.materialize(src.handle, b, dst.handle, b)
+    from oracle import pool_model as PM
+    models = [PM.materialise(OS.seq_model(wl, b)) for b in range(wl.B)]
+    for b, m in enumerate(models):
+        recs = H.gather_records(dst, b, len(m.bits))
+        for lp in range(len(m.bits)):
+            ref, mask = m.record(lp), m.valid_mask(lp)
+            bad = np.nonzero((recs[lp, :ref.size] != ref) & mask)[0]
+            assert bad.size == 0, f"seq {b} page {lp}: {bad.size} bytes differ"
+    out, lse = _run_decode(dst, wl)
+    _check(out, lse, *OS.decode_all(wl, models), "materialised")
+    out_src, lse_src = _run_decode(src, wl)
+    _check(out_src, lse_src, *OS.decode_all(wl, [OS.seq_model(wl, b) for b in range(wl.B)]), "source")
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.materialize(src.handle, 0, dst.handle, 0)
+    assert e.value.status == mkv.ESTATE
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.materialize(dst.handle, 0, src.handle, 1)
+    assert e.value.status == mkv.EINVAL
+    dst.close()
+    src.close()
+
+
 @pytest.fixture(scope="module")
 def long_case():
     wl = W.long()
