@@ -63,6 +63,8 @@ def workload(name):
     from decode_attention_mixed_amd import workloads as W
     if name.startswith("sweep"):
         return W.sweep(int(name[5:]) / 100.0)
+    if name.startswith("canary"):
+        return W.canary(int(name[6:] or 16))
     return getattr(W, name)()
 
 
@@ -218,6 +220,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the BF16-control and all-FP8 comparison runs")
+    ap.add_argument("--layer-calls", type=int, default=0, metavar="N",
+                    help="also time the batch as N calls over consecutive entries (a multi-layer "
+                         "workload decoded layer by layer instead of in one call)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps "
                          "times (reference for the HBM byte counters)")
@@ -323,6 +328,29 @@ def main():
         mkv.profile_enable(p.handle, False)
     log(f"step {ms * 1e3:.2f} us (host {host_s * 1e6:.1f} us per call; {ms_ev * 1e3:.2f} us with "
         f"kernel events); kernel profile {prof}")
+    multi = None
+    if args.layer_calls > 0:
+        assert wl.B % args.layer_calls == 0
+        per = wl.B // args.layer_calls
+        groups = [(batch[i * per:(i + 1) * per], q[i * per:(i + 1) * per].contiguous(),
+                   out[i * per:(i + 1) * per], lse[i * per:(i + 1) * per])
+                  for i in range(args.layer_calls)]
+        def layer_steps(n):
+            torch.cuda.synchronize()
+            ev0.record()
+            for i in range(n):
+                for ids, qg, og, lg in groups:
+                    mkv.decode(pools[i % R].handle, ids, qg, tau, og, lg)
+            ev1.record()
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / n
+        layer_steps(max(args.warmup, R))
+        ms_layers = layer_steps(args.steps)
+        multi = {"calls": args.layer_calls, "entries_per_call": per,
+                 "us_per_step_one_call": round(ms * 1e3, 3),
+                 "us_per_step_per_call": round(ms_layers * 1e3, 3),
+                 "one_call_speedup": round(ms_layers / ms, 4)}
+        log(f"layer by layer: {multi}")
     materialised = None
     if not args.no_compare:
         # Materialising profile: each step expands the whole batch of replica
@@ -430,6 +458,8 @@ def main():
     }
     if comparison is not None:
         result["comparison"] = comparison
+    if multi is not None:
+        result["multi_layer"] = multi
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, step_bytes)
     print(json.dumps(result), flush=True)

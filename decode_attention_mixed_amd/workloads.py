@@ -21,6 +21,12 @@ Named workloads (shapes of the five evaluation cases of this library):
   sweep(f)    B=4, Hq=16, Hkv=4, d=256, P=64, L = {16384, 16384, 16361, 1}; the
               last ceil(f * pages) pages FP8; K has ceil(2% of d) outlier
               channels per kv-head scaled x20.
+  canary(n)   a multi-layer step shaped like the summaries' canary test (two
+              59,008-token requests, n = 16 full-attention layers): batch entry
+              b = layer * 2 + request, Hq=48, Hkv=8, d=128, P=16; each entry has
+              its own K, V and query; anchors = pages overlapping the last 1024
+              tokens; K and V outliers as in long.  One decode call over all
+              entries is one model step's attention over every layer.
 
 Random streams: numpy PCG64 seeded by SeedSequence(seed), spawned in the fixed
 order lengths, placement, anchors, outliers, K, V, Q; K and V streams are split
@@ -33,7 +39,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-NAMED_SEEDS = {"tiny": 1000, "ragged": 1001, "long": 1002, "throughput": 1003, "sweep": 1004}
+NAMED_SEEDS = {"tiny": 1000, "ragged": 1001, "long": 1002, "throughput": 1003, "sweep": 1004,
+               "canary": 1005}
 HBM_BYTES_MI355X = 288 * 10**9
 
 
@@ -207,6 +214,19 @@ def sweep(frac: float) -> Workload:
                 seed=NAMED_SEEDS["sweep"], lengths=[16384, 16384, 16361, 1],
                 anchor_rule=anchor_rule, fp8_pages=1024, tq3_pages=1024,
                 outliers={"k": (c, 20.0)})
+
+
+def canary(layers: int = 16, length: int = 59008, requests: int = 2) -> Workload:
+    """Multi-layer step: entry b = layer * requests + r (layer-major)."""
+    B = layers * requests
+    P = 16
+    pages = -(-length // P)
+    c = math.ceil(0.02 * 128)
+    anchors = len(_tail_pages(length, P, 1024))
+    return make(f"canary{layers}", B=B, Hq=48, Hkv=8, d=128, P=P, seed=NAMED_SEEDS["canary"],
+                lengths=[length] * B, anchor_rule=lambda r, b, L, P: _tail_pages(L, P, 1024),
+                fp8_pages=B * anchors + pages + 16, tq3_pages=B * (pages - anchors) + 16,
+                outliers={"k": (c, 8.0), "v": (c, 8.0)})
 
 
 def small(seed: int, *, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(200, 37, 513),

@@ -344,6 +344,29 @@ def test_materialising_profile_records_and_decode():
     src.close()
 
 
+def test_multi_layer_step_in_one_call():
+    """Per-layer caches as sequences of one pool (entry = layer * 2 + request):
+    one decode call over all layers and layer-by-layer calls both match the
+    oracle for every (layer, request)."""
+    wl = W.canary(layers=3, length=2000)
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    O, L = OS.decode_all(wl, models)
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, O, L, "all layers in one call")
+    q = H.q_tensor(wl)
+    for layer in range(3):
+        ids = [2 * layer, 2 * layer + 1]
+        o = torch.empty(2, wl.Hq, wl.d, device="cuda")
+        l = torch.empty(2, wl.Hq, device="cuda")
+        mkv.decode(pool.handle, ids, q[ids[0]:ids[1] + 1].contiguous(), float(wl.tau), o, l)
+        torch.cuda.synchronize()
+        _check(o.cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64),
+               O[ids[0]:ids[1] + 1], L[ids[0]:ids[1] + 1], f"layer {layer}")
+    pool.close()
+
+
 @pytest.fixture(scope="module")
 def long_case():
     wl = W.long()
