@@ -220,6 +220,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the BF16-control and all-FP8 comparison runs")
+    ap.add_argument("--serve", type=int, default=0, metavar="N",
+                    help="also run N decode steps that each append one token to every sequence "
+                         "(mkv_append_step), demote the pages an anchor policy releases and decode")
     ap.add_argument("--layer-calls", type=int, default=0, metavar="N",
                     help="also time the batch as N calls over consecutive entries (a multi-layer "
                          "workload decoded layer by layer instead of in one call)")
@@ -276,11 +279,16 @@ def main():
         "bf16" (control pool) or "fp8" (mixed pool, nothing demoted)."""
         t0 = time.perf_counter()
         pools = []
+        grow = (args.serve // wl.P + 2) if kind == "mixed" and args.serve > 0 else 0   # serve headroom
         for r in range(R):
             if kind == "mixed" and R == 1:
-                desc = H.pool_desc(wl)
+                desc = H.pool_desc(wl, max_pages_per_seq=max_pages + grow,
+                                   fp8_pages=wl.fp8_pages + wl.B * grow,
+                                   tq3_pages=wl.tq3_pages + wl.B * grow)
             elif kind == "mixed":
-                desc = H.pool_desc(wl, fp8_pages=n_anchor + max_pages + 16, tq3_pages=n_tq3 + 16,
+                desc = H.pool_desc(wl, fp8_pages=n_anchor + max_pages + 16 + wl.B * grow,
+                                   tq3_pages=n_tq3 + 16 + wl.B * grow,
+                                   max_pages_per_seq=max_pages + grow,
                                    placement_seed=wl.placement_seed + r)
             else:
                 desc = H.pool_desc(wl, kind=kind, fp8_pages=all_pages + 16,
@@ -382,6 +390,46 @@ def main():
         for p in dpools:
             p.close()
         del dpools
+    serve = None
+    if args.serve > 0:
+        # Decode-step loop: the recent window is the workload's FP8 tail; anchors
+        # older than it stay protected (FP8) for good.
+        window = {"long": 4096, "throughput": 1024, "ragged": 512}.get(wl.name, 1024)
+        protected, demoted = [], []
+        for b in range(wl.B):
+            L = int(wl.lengths[b])
+            protected.append([a for a in wl.anchors[b] if (a + 1) * wl.P <= L - window])
+            demoted.append(wl.demote_pages(b))
+        policies = [H.AnchorPolicy(wl.P, window, protected, demoted) for _ in range(R)]
+        lens = [[int(x) for x in wl.lengths] for _ in range(R)]
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        rows_k = torch.randn(16, wl.B, wl.Hkv, wl.d, device="cuda", generator=gen)
+        rows_v = torch.randn(16, wl.B, wl.Hkv, wl.d, device="cuda", generator=gen)
+        n_dem = 0
+        torch.cuda.synchronize()
+        ev0.record()
+        t0 = time.perf_counter()
+        for i in range(args.serve):
+            r = i % R
+            h = pools[r].handle
+            mkv.append_step(h, batch, rows_k[i % 16], rows_v[i % 16])
+            for b in batch:
+                lens[r][b] += 1
+                pages = policies[r].step(b, lens[r][b])
+                if pages:
+                    mkv.demote(h, b, np.asarray(pages, np.int32))
+                    n_dem += len(pages)
+            mkv.decode(h, batch, q, tau, out, lse)
+        host = (time.perf_counter() - t0) / args.serve
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_serve = ev0.elapsed_time(ev1) / args.serve
+        serve = {"steps": args.serve, "window_tokens": window,
+                 "us_per_step": round(ms_serve * 1e3, 3),
+                 "host_us_per_step": round(host * 1e6, 2),
+                 "decode_only_us_per_step": round(ms * 1e3, 3),
+                 "pages_demoted": n_dem}
+        log(f"serve: {serve}")
     for p in pools:
         p.close()
     del pools
@@ -460,6 +508,8 @@ def main():
         result["comparison"] = comparison
     if multi is not None:
         result["multi_layer"] = multi
+    if serve is not None:
+        result["serve"] = serve
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, step_bytes)
     print(json.dumps(result), flush=True)

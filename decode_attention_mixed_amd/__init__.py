@@ -84,7 +84,8 @@ class Profile(ctypes.Structure):
 
 EXPORTED = [
     "mkv_pool_bytes", "mkv_record_bytes", "mkv_pool_create", "mkv_pool_destroy",
-    "mkv_seq_reset", "mkv_append", "mkv_demote", "mkv_materialize", "mkv_decode", "mkv_seq_info",
+    "mkv_seq_reset", "mkv_append", "mkv_append_step", "mkv_demote", "mkv_materialize",
+    "mkv_decode", "mkv_seq_info",
     "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_profile_enable",
     "mkv_profile_read", "mkv_status_string", "mkv_last_error",
 ]
@@ -111,6 +112,7 @@ def _load():
         "mkv_append": (I32, [P, I32, I32, P, P, P]),
         "mkv_demote": (I32, [P, I32, P, I32, P]),
         "mkv_materialize": (I32, [P, I32, P, I32, P]),
+        "mkv_append_step": (I32, [P, P, I32, P, P, P]),
         "mkv_decode": (I32, [P, P, I32, P, I32, F32, P, P, P]),
         "mkv_seq_info": (I32, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "mkv_page_table": (I32, [P, I32, P, I32]),
@@ -211,6 +213,17 @@ def append(pool, seq: int, k, v, stream=None) -> None:
 def demote(pool, seq: int, logical_pages, stream=None) -> None:
     arr, n = _i32_array(logical_pages)
     _check(_load().mkv_demote(pool, seq, arr, n, _stream(stream)))
+
+
+def append_step(pool, seq_ids, k, v, stream=None) -> None:
+    """One token per sequence: k, v fp32 device [B][Hkv][d], row b to seq_ids[b]."""
+    import torch
+    ids, B = _i32_array(seq_ids)
+    if k.dim() != 3 or k.shape[0] != B:
+        raise ValueError("k must be [B][Hkv][d] with B = len(seq_ids)")
+    _check(_load().mkv_append_step(pool, ids, B, _dev_ptr(k, torch.float32, name="k"),
+                                   _dev_ptr(v, torch.float32, tuple(k.shape), name="v"),
+                                   _stream(stream)))
 
 
 def materialize(src_pool, src_seq: int, dst_pool, dst_seq: int, stream=None) -> None:

@@ -38,7 +38,17 @@ int mkvh_create(const mkv_pool_desc* desc, mkvh** out) {
 
 void mkvh_destroy(mkvh* h) { delete h; }
 
-// plan_out receives 8 int32 per touched page: lp, phys, row0, nrows, src_row, 0, 0, 0.
+// plan_out receives 8 int32 per touched page: lp, phys, row0, nrows, src_row,
+// pt_slot, pt_entry, 0 (pt_slot -1 for mkvh_append).
+int mkvh_append_step(mkvh* h, const int32_t* ids, int32_t B, int32_t pt_stride, int32_t* plan_out,
+                     int32_t cap, int32_t* n_plan) {
+  std::vector<mkv::AppendPage> plan;
+  int st = h->meta.append_step(ids, B, pt_stride, &plan, &g_herr);
+  *n_plan = int32_t(plan.size());
+  if (!st && int32_t(plan.size()) <= cap) std::memcpy(plan_out, plan.data(), plan.size() * 32);
+  return st;
+}
+
 int mkvh_append(mkvh* h, int32_t seq, int32_t n, int32_t* plan_out, int32_t cap, int32_t* n_plan) {
   std::vector<mkv::AppendPage> plan;
   int st = h->meta.append(seq, n, &plan, &g_herr);

@@ -48,6 +48,8 @@ append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float*
   float* scale_p = reinterpret_cast<float*>(page + fp8_scale_off(pv, h, kv));
   float* amax_p = reinterpret_cast<float*>(page + fp8_amax_off(pv, h, kv));
 
+  if (ap.pt_slot >= 0 && h == 0 && kv == 0 && threadIdx.x == 0)
+    const_cast<int32_t*>(pv.pt)[ap.pt_slot] = ap.pt_entry;   // a page the step opened
   const int n_new = ap.nrows * d;
   float local = 0.0f;
   for (int i = threadIdx.x; i < n_new; i += kThreads) {
@@ -172,6 +174,8 @@ append_bf16_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float
   const float* src = kv ? v : k;
   uint16_t* rows = reinterpret_cast<uint16_t*>(pv.fp8 + int64_t(ap.phys) * pv.fp8_stride) +
                    (int64_t(h * 2 + kv) * pv.P + ap.row0) * d;
+  if (ap.pt_slot >= 0 && h == 0 && kv == 0 && threadIdx.x == 0)
+    const_cast<int32_t*>(pv.pt)[ap.pt_slot] = ap.pt_entry;   // a page the step opened
   const int n = ap.nrows * d;
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const int r = i / d, j = i % d;

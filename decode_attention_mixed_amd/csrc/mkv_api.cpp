@@ -67,7 +67,7 @@ Layout make_layout(const mkv::Desc& d, const mkv::Geom& g) {
   L.sched_bytes = align256(L.base_off + (size_t(d.max_batch) + 1) * 4);
   L.sched = o;
   o += L.sched_bytes;
-  L.plan_bytes = align256(size_t(d.max_pages_per_seq) * 32);
+  L.plan_bytes = align256(size_t(std::max(d.max_pages_per_seq, d.max_batch)) * 32);
   L.plan = o;
   o += L.plan_bytes;
   const size_t slots = size_t(g.max_chunks) * size_t(d.max_q_heads);
@@ -356,6 +356,31 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
     MKV_HIP(mkv::launch_append_bf16(p->view(), dplan, int32_t(plan.size()), k, v, s));
   else
     MKV_HIP(mkv::launch_append(p->view(), dplan, int32_t(plan.size()), k, v, s));
+  return MKV_OK;
+}
+
+mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const float* k,
+                           const float* v, hipStream_t s) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  if (B < 0 || (B > 0 && (!seq_ids || !k || !v))) return set_err(MKV_EINVAL, "null argument");
+  if (B > p->desc.max_batch) return set_err(MKV_ERANGE, "B exceeds max_batch");
+  if (B == 0) return MKV_OK;
+  DeviceGuard guard(p->device);
+  std::vector<mkv::AppendPage> plan;
+  std::string err;
+  int st = p->meta.append_step(seq_ids, B, p->desc.max_pages_per_seq, &plan, &err);
+  if (st) return set_err(mkv_status(st), err);
+  mkv_status r = p->wait_staging();
+  if (r) return r;
+  const size_t bytes = plan.size() * sizeof(plan[0]);
+  std::memcpy(p->staging, plan.data(), bytes);
+  r = flush_uploads(p, {{p->lay.plan, bytes}}, s);
+  if (r) return r;
+  const auto* dplan = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
+  if (p->meta.geom().kind == mkv::kKindBf16)
+    MKV_HIP(mkv::launch_append_bf16(p->view(), dplan, B, k, v, s));
+  else
+    MKV_HIP(mkv::launch_append(p->view(), dplan, B, k, v, s));
   return MKV_OK;
 }
 

@@ -123,12 +123,53 @@ int Meta::append(int32_t s, int32_t n, std::vector<AppendPage>* plan, std::strin
     int32_t lp = pos / P;
     int32_t row0 = pos % P;
     int32_t take = std::min(P - row0, n - src);
-    plan->push_back(AppendPage{lp, pt_index(q.pt[size_t(lp)]), row0, take, src, 0, 0, 0});
+    plan->push_back(AppendPage{lp, pt_index(q.pt[size_t(lp)]), row0, take, src, -1, 0, 0});
     pos += take;
     src += take;
   }
   q.len = int32_t(new_len);
   ++version_;
+  return MKV_S_OK;
+}
+
+int Meta::append_step(const int32_t* ids, int32_t B, int32_t pt_stride,
+                      std::vector<AppendPage>* plan, std::string* err) {
+  plan->clear();
+  if (B < 0 || (B > 0 && !ids)) return fail(err, MKV_S_EINVAL, "bad sequence list");
+  // validate everything first
+  int64_t fresh = 0;
+  std::vector<int32_t> sorted(ids, ids + B);
+  std::sort(sorted.begin(), sorted.end());
+  for (int32_t i = 1; i < B; ++i)
+    if (sorted[size_t(i)] == sorted[size_t(i) - 1]) return fail(err, MKV_S_EINVAL, "sequence listed twice");
+  for (int32_t b = 0; b < B; ++b) {
+    int st = check_seq(ids[b], err);
+    if (st) return st;
+    const Seq& q = seqs_[size_t(ids[b])];
+    if (q.len % g_.P != 0 && pt_is_tq3(q.pt.back()))
+      return fail(err, MKV_S_ESTATE, "last page is TQ3 and partially filled; the sequence is frozen");
+    if (q.len % g_.P == 0) {
+      if (int64_t(q.pt.size()) + 1 > d_.max_pages_per_seq)
+        return fail(err, MKV_S_ERANGE, "sequence would exceed max_pages_per_seq");
+      ++fresh;
+    }
+  }
+  if (fresh > free_[0].size()) return fail(err, MKV_S_ENOMEM, "FP8 slab has too few free pages");
+  // commit
+  for (int32_t b = 0; b < B; ++b) {
+    Seq& q = seqs_[size_t(ids[b])];
+    const int32_t row0 = q.len % g_.P;
+    int32_t slot = -1, entry = 0;
+    if (row0 == 0) {
+      q.pt.push_back(pt_make(0, free_[0].pop()));
+      slot = ids[b] * pt_stride + int32_t(q.pt.size()) - 1;
+      entry = q.pt.back();
+    }
+    const int32_t lp = int32_t(q.pt.size()) - 1;
+    plan->push_back(AppendPage{lp, pt_index(q.pt.back()), row0, 1, b, slot, entry, 0});
+    ++q.len;
+  }
+  if (B) ++version_;
   return MKV_S_OK;
 }
 

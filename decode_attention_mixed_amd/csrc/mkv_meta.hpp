@@ -68,9 +68,11 @@ struct Seq {
 };
 
 // One page an append touches: rows row0 .. row0+nrows-1 of page `phys`
-// receive source rows src_row .. src_row+nrows-1.
+// receive source rows src_row .. src_row+nrows-1.  pt_slot >= 0: the append
+// also writes page-table entry pt_entry at that index of the device page
+// table (a decode step's batched append opens pages this way).
 struct AppendPage {
-  int32_t lp, phys, row0, nrows, src_row, pad0, pad1, pad2;
+  int32_t lp, phys, row0, nrows, src_row, pt_slot, pt_entry, pad0;
 };
 // One page a demote converts.
 struct DemotePage {
@@ -145,6 +147,11 @@ class Meta {
 
   // Each call validates everything first; on failure nothing changes.
   int append(int32_t seq, int32_t n, std::vector<AppendPage>* plan, std::string* err);
+  // One token to each of B distinct sequences (row b to seq_ids[b]), all or
+  // nothing; plan entries take src_row = b, and a page opened by the step
+  // carries its page-table slot (seq * pt_stride + lp) and entry.
+  int append_step(const int32_t* seq_ids, int32_t B, int32_t pt_stride,
+                  std::vector<AppendPage>* plan, std::string* err);
   int demote(int32_t seq, const int32_t* lps, int32_t n, std::vector<DemotePage>* plan,
              std::string* err);
   int reset(int32_t seq, std::string* err);

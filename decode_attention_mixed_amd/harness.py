@@ -115,3 +115,29 @@ def gather_records(pool: DevicePool, seq_id: int, n_pages: int, device="cuda") -
     mkv.debug_gather(pool.handle, seq_id, 0, n_pages, dst)
     torch.cuda.synchronize()
     return dst.cpu().numpy().reshape(n_pages, slot)
+
+
+class AnchorPolicy:
+    """Caller-side anchor policy of a decode loop ("Ancoras em FP8, arquivo em
+    TQ3": recent and protected pages stay FP8, older pages are converted).  A
+    page is demoted once every one of its tokens is older than the last
+    `window` tokens of its sequence, unless it is protected.  The policy keeps
+    its own record of demoted pages, so its decisions depend only on lengths,
+    the window and the protected sets (the same on any implementation).
+
+    protected: per sequence, logical pages that stay FP8 (e.g. attention sinks
+    or pages the caller marks).  demoted: per sequence, pages already TQ3."""
+
+    def __init__(self, P: int, window: int, protected, demoted):
+        self.P = P
+        self.window = window
+        self.protected = [set(int(x) for x in p) for p in protected]
+        self.demoted = [set(int(x) for x in d) for d in demoted]
+
+    def step(self, seq: int, length: int) -> list:
+        """Pages of `seq` to demote now that it holds `length` tokens."""
+        full = max(0, (length - self.window) // self.P)      # pages wholly outside the window
+        new = [lp for lp in range(full)
+               if lp not in self.demoted[seq] and lp not in self.protected[seq]]
+        self.demoted[seq].update(new)
+        return new

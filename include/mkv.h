@@ -155,6 +155,18 @@ mkv_status mkv_seq_reset(mkv_pool* pool, int32_t seq, hipStream_t stream);
 mkv_status mkv_append(mkv_pool* pool, int32_t seq, int32_t n, const float* k, const float* v,
                       hipStream_t stream);
 
+/* One decode step's new rows: append one token to each of B distinct
+ * sequences, row b of k and v (device fp32 [B][Hkv][d]) to seq_ids[b] (host
+ * int32 [B]), with one kernel launch; otherwise as mkv_append (FP8 rows with
+ * rescale-on-grow, or bf16 rows in a control pool).  A sequence whose last
+ * page is full gets a new FP8 page.  All sequences are validated before any
+ * changes (MKV_EINVAL for a repeated or bad id, MKV_ESTATE for a frozen TQ3
+ * tail, MKV_ENOMEM, MKV_ERANGE for B > max_batch or a full page table).  The
+ * caller decides which pages leave the recent window and calls mkv_demote
+ * ("Ancoras em FP8, arquivo em TQ3": recent and protected pages stay FP8). */
+mkv_status mkv_append_step(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const float* k,
+                           const float* v, hipStream_t stream);
+
 /* Convert the listed logical pages of `seq` from FP8 to packed TQ3
  * ("Ancoras em FP8, arquivo em TQ3": older non-anchor pages are converted).
  * logical_pages: host int32 [n], distinct, each an FP8 page of the sequence.

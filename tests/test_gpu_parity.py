@@ -367,6 +367,55 @@ def test_multi_layer_step_in_one_call():
     pool.close()
 
 
+def test_decode_steps_with_appends_and_demotions():
+    """A decode loop: each step appends one token to every sequence with one
+    mkv_append_step call, demotes the pages an anchor policy releases (recency
+    window of 40 tokens, the workload's older anchors protected) and decodes; the
+    oracle replays the same appends and demotions.  Decodes along the way and
+    every record at the end are checked."""
+    wl = W.small(seed=51, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(100, 37, 250),
+                 outliers={"k": (3, 8.0)})
+    pool = H.DevicePool(H.pool_desc(wl, max_pages_per_seq=32))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    # anchors older than the window stay protected; the tail anchors are just
+    # the recent pages and age out
+    protected = [[a for a in wl.anchors[b] if (a + 1) * wl.P <= int(wl.lengths[b]) - 40]
+                 for b in range(wl.B)]
+    policy = H.AnchorPolicy(wl.P, 40, protected=protected,
+                            demoted=[wl.demote_pages(b) for b in range(wl.B)])
+    rng = np.random.default_rng(52)
+    ids = list(range(wl.B))
+    lengths = [int(x) for x in wl.lengths]
+    n_demoted = 0
+    for step in range(40):
+        k = rng.standard_normal((wl.B, wl.Hkv, wl.d)).astype(np.float32)
+        v = (rng.standard_normal((wl.B, wl.Hkv, wl.d)) * (1.0 + step % 3)).astype(np.float32)
+        mkv.append_step(pool.handle, ids, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        for b in ids:
+            models[b].append(k[b:b + 1], v[b:b + 1])
+            lengths[b] += 1
+            pages = policy.step(b, lengths[b])
+            if pages:
+                mkv.demote(pool.handle, b, np.asarray(pages, np.int32))
+                for lp in pages:
+                    models[b].demote(lp)
+                n_demoted += len(pages)
+        if step % 10 == 9:
+            out, lse = _run_decode(pool, wl)
+            _check(out, lse, *OS.decode_all(wl, models), f"step {step}")
+    assert n_demoted >= 3
+    for b in ids:
+        pt = mkv.page_table(pool.handle, b)
+        recs = H.gather_records(pool, b, len(models[b].pages))
+        for lp, page in enumerate(models[b].pages):
+            assert (pt[lp] < 0) == (page.fmt == 1), (b, lp)
+            ref, mask = models[b].record(lp), models[b].valid_mask(lp)
+            bad = np.nonzero((recs[lp, :ref.size] != ref) & mask)[0]
+            assert bad.size == 0, f"seq {b} page {lp}: {bad.size} bytes differ"
+    pool.close()
+
+
 @pytest.fixture(scope="module")
 def long_case():
     wl = W.long()

@@ -22,6 +22,7 @@ def lib():
     L.mkvh_create.argtypes = [ctypes.POINTER(PoolDesc), ctypes.POINTER(P)]
     L.mkvh_destroy.argtypes = [P]
     L.mkvh_append.argtypes = [P, I32, I32, P, I32, ctypes.POINTER(I32)]
+    L.mkvh_append_step.argtypes = [P, P, I32, I32, P, I32, ctypes.POINTER(I32)]
     L.mkvh_demote.argtypes = [P, I32, P, I32, P, I32, ctypes.POINTER(I32)]
     L.mkvh_reset.argtypes = [P, I32]
     L.mkvh_seq_len.argtypes = [P, I32]
@@ -53,6 +54,14 @@ class Host:
         buf = np.zeros((4096, 8), np.int32)
         cnt = ctypes.c_int32()
         st = self.L.mkvh_append(self.h, seq, n, buf.ctypes.data, 4096, ctypes.byref(cnt))
+        return st, buf[:cnt.value]
+
+    def append_step(self, ids, pt_stride=64):
+        arr = np.asarray(ids, np.int32)
+        buf = np.zeros((4096, 8), np.int32)
+        cnt = ctypes.c_int32()
+        st = self.L.mkvh_append_step(self.h, arr.ctypes.data, arr.size, pt_stride, buf.ctypes.data,
+                                     4096, ctypes.byref(cnt))
         return st, buf[:cnt.value]
 
     def demote(self, seq, lps):
@@ -327,4 +336,41 @@ def test_bf16_control_pool_metadata(lib):
     st, sch = h.schedule([0], Hq=8)
     assert st == 0 and sch["n3"] == 0 and sch["n8"] >= 1
     assert sorted(sch["pages"].tolist()) == list(range(7))
+    h.close()
+
+
+# ------------------------------------------------------------ decode-step appends
+def test_append_step_plans_and_page_table_patches(lib):
+    """One token per sequence: row b goes to ids[b]; a sequence whose last page
+    is full (or which is empty) opens a page and its plan carries the device
+    page-table slot seq * pt_stride + lp and the new entry."""
+    h = _host(lib, fp8_pages=40)
+    assert h.append(0, 16)[0] == 0 and h.append(1, 5)[0] == 0
+    st, plan = h.append_step([1, 0, 2], pt_stride=64)
+    assert st == 0 and len(plan) == 3
+    pt0, pt1, pt2 = h.pt(0), h.pt(1), h.pt(2)
+    # seq 1: row 5 of its page 0, no new page
+    assert list(plan[0]) == [0, pt1[0] & 0x7FFFFFFF, 5, 1, 0, -1, 0, 0]
+    # seq 0: page 0 was full -> page 1 opened
+    assert list(plan[1]) == [1, pt0[1], 0, 1, 1, 0 * 64 + 1, pt0[1], 0]
+    # seq 2: empty -> page 0 opened
+    assert list(plan[2]) == [0, pt2[0], 0, 1, 2, 2 * 64 + 0, pt2[0], 0]
+    assert [h.L.mkvh_seq_len(h.h, s) for s in (0, 1, 2)] == [17, 6, 1]
+    h.close()
+
+
+def test_append_step_is_all_or_nothing(lib):
+    h = _host(lib, fp8_pages=3, tq3_pages=4)
+    assert h.append(0, 16)[0] == 0 and h.append(1, 16)[0] == 0
+    v0 = h.L.mkvh_version(h.h)
+    lens = lambda: [h.L.mkvh_seq_len(h.h, s) for s in range(4)]
+    assert h.append_step([0, 2, 0])[0] == -1                 # repeated id: EINVAL
+    assert h.append_step([0, 9])[0] == -1                    # bad id
+    assert h.append_step([0, 1, 2])[0] == -2                 # 3 new pages, 1 free: ENOMEM
+    assert lens() == [16, 16, 0, 0] and h.L.mkvh_version(h.h) == v0 and h.free(0) == 1
+    assert h.append(2, 3)[0] == 0 and h.demote(2, [0])[0] == 0   # seq 2: partial TQ3 tail
+    v1 = h.L.mkvh_version(h.h)
+    assert h.append_step([3, 2])[0] == -3                    # frozen tail: ESTATE
+    assert lens() == [16, 16, 3, 0] and h.L.mkvh_version(h.h) == v1
+    assert h.append_step([3])[0] == 0 and lens()[3] == 1
     h.close()
