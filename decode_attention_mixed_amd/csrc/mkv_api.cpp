@@ -116,6 +116,7 @@ struct mkv_pool {
   // cached decode schedule
   bool sched_valid = false;
   uint64_t sched_version = 0;
+  uint64_t sched_layout = 0;   // page-layout version the schedule was built at
   int32_t sched_Hq = 0;
   std::vector<int32_t> sched_ids;
   mkv::Schedule sched;
@@ -406,9 +407,29 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   if (!q || !out || !lse || !seq_ids) return set_err(MKV_EINVAL, "null argument");
   if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return set_err(MKV_EINVAL, "q must be 16-byte aligned");
   DeviceGuard guard(p->device);
-  const bool same = p->sched_valid && p->sched_version == p->meta.version() && p->sched_Hq == Hq &&
-                    int32_t(p->sched_ids.size()) == B &&
-                    std::memcmp(p->sched_ids.data(), seq_ids, size_t(B) * 4) == 0;
+  const bool same_batch = p->sched_valid && p->sched_Hq == Hq && int32_t(p->sched_ids.size()) == B &&
+                          std::memcmp(p->sched_ids.data(), seq_ids, size_t(B) * 4) == 0;
+  if (same_batch && p->sched_version != p->meta.version() &&
+      p->sched_layout == p->meta.layout_version()) {
+    // Only token counts changed (appends inside existing pages): the page lists
+    // stand; refresh each item's last-page token count and upload the items.
+    mkv_status r = p->wait_staging();
+    if (r) return r;
+    const int32_t P = p->meta.geom().P;
+    size_t off = 0;
+    for (auto& list : p->sched.items)
+      for (mkv::WorkItem& it : list) {
+        it.last_ntok = mkv::page_tokens(p->meta.seq(it.seq).len, P, it.last_lp);
+        std::memcpy(p->staging + off, &it, sizeof(it));
+        off += sizeof(it);
+      }
+    p->sched_valid = false;
+    r = flush_uploads(p, {{p->lay.sched, off}}, s);
+    if (r) return r;
+    p->sched_version = p->meta.version();
+    p->sched_valid = true;
+  }
+  const bool same = same_batch && p->sched_version == p->meta.version();
   if (!same) {
     std::string err;
     mkv::Schedule sc;
@@ -434,6 +455,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     p->sched_ids.assign(seq_ids, seq_ids + B);
     p->sched_Hq = Hq;
     p->sched_version = p->meta.version();
+    p->sched_layout = p->meta.layout_version();
     p->sched_valid = true;
   }
   const mkv::Schedule& sc = p->sched;

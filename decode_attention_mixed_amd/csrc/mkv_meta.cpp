@@ -91,6 +91,7 @@ int Meta::init(const Desc& d, std::string* err) {
   free_[1].init(d.tq3_pages, d.placement_seed ? d.placement_seed ^ 0xA5A5A5A5DEADBEEFull : 0);
   seqs_.assign(size_t(d.max_seqs), Seq{});
   version_ = 1;
+  layout_version_ = 1;
   return MKV_S_OK;
 }
 
@@ -129,6 +130,7 @@ int Meta::append(int32_t s, int32_t n, std::vector<AppendPage>* plan, std::strin
   }
   q.len = int32_t(new_len);
   ++version_;
+  if (fresh > 0) ++layout_version_;
   return MKV_S_OK;
 }
 
@@ -170,6 +172,7 @@ int Meta::append_step(const int32_t* ids, int32_t B, int32_t pt_stride,
     ++q.len;
   }
   if (B) ++version_;
+  if (fresh > 0) ++layout_version_;
   return MKV_S_OK;
 }
 
@@ -200,7 +203,10 @@ int Meta::demote(int32_t s, const int32_t* lps, int32_t n, std::vector<DemotePag
     free_[0].push(src);
     plan->push_back(DemotePage{lp, src, dst, page_tokens(q.len, g_.P, lp), 0, 0, 0, 0});
   }
-  if (n) ++version_;
+  if (n) {
+    ++version_;
+    ++layout_version_;
+  }
   return MKV_S_OK;
 }
 
@@ -212,6 +218,7 @@ int Meta::reset(int32_t s, std::string* err) {
   q.pt.clear();
   q.len = 0;
   ++version_;
+  ++layout_version_;
   return MKV_S_OK;
 }
 
@@ -332,6 +339,7 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
         out->entries.push_back(q.pt[size_t(lp)]);
         items.back().npages++;
         items.back().last_ntok = page_tokens(q.len, g_.P, lp);
+        items.back().last_lp = lp;
         largest = std::max(largest, items.back().npages);
         --left;
       }

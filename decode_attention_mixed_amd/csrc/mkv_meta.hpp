@@ -85,10 +85,10 @@ struct MaterialisePage {
 };
 
 // One unit of split-K work: `npages` logical pages of one format of one
-// sequence, listed at pages[list_off ..]; the last listed page holds
-// last_ntok valid tokens.  `chunk` is the partial-state slot.
+// sequence, listed at pages[list_off ..]; the last listed page (logical page
+// last_lp) holds last_ntok valid tokens.  `chunk` is the partial-state slot.
 struct WorkItem {
-  int32_t b, seq, list_off, npages, last_ntok, chunk, fmt, pad;
+  int32_t b, seq, list_off, npages, last_ntok, chunk, fmt, last_lp;
 };
 
 // Upper bound on WorkItem::npages: the partial kernel stages a work item's
@@ -141,6 +141,10 @@ class Meta {
   const Geom& geom() const { return g_; }
   const Desc& desc() const { return d_; }
   uint64_t version() const { return version_; }
+  // Changes only when pages are added, converted or freed (not when tokens
+  // land in an existing page): a schedule built at one layout version stays
+  // valid up to the items' last_ntok.
+  uint64_t layout_version() const { return layout_version_; }
   const Seq& seq(int32_t s) const { return seqs_[size_t(s)]; }
   int64_t fp8_free() const { return free_[0].size(); }
   int64_t tq3_free() const { return free_[1].size(); }
@@ -173,6 +177,7 @@ class Meta {
   FreeList free_[2];
   std::vector<Seq> seqs_;
   uint64_t version_ = 1;
+  uint64_t layout_version_ = 1;
 };
 
 // Number of tokens held by logical page lp of a sequence of length len.

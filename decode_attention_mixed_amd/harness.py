@@ -133,11 +133,13 @@ class AnchorPolicy:
         self.window = window
         self.protected = [set(int(x) for x in p) for p in protected]
         self.demoted = [set(int(x) for x in d) for d in demoted]
+        self.seen = [0] * len(self.demoted)     # pages below this were already decided
 
     def step(self, seq: int, length: int) -> list:
         """Pages of `seq` to demote now that it holds `length` tokens."""
         full = max(0, (length - self.window) // self.P)      # pages wholly outside the window
-        new = [lp for lp in range(full)
+        new = [lp for lp in range(self.seen[seq], full)
                if lp not in self.demoted[seq] and lp not in self.protected[seq]]
+        self.seen[seq] = max(self.seen[seq], full)
         self.demoted[seq].update(new)
         return new

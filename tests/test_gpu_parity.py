@@ -401,7 +401,7 @@ def test_decode_steps_with_appends_and_demotions():
                 for lp in pages:
                     models[b].demote(lp)
                 n_demoted += len(pages)
-        if step % 10 == 9:
+        if step < 6 or step % 10 == 9:      # early steps mostly fill existing pages
             out, lse = _run_decode(pool, wl)
             _check(out, lse, *OS.decode_all(wl, models), f"step {step}")
     assert n_demoted >= 3
