@@ -83,6 +83,8 @@ int64_t mkvh_kv_bytes(mkvh* h, const int32_t* ids, int32_t B) { return h->meta.k
 
 uint64_t mkvh_version(mkvh* h) { return h->meta.version(); }
 
+uint64_t mkvh_layout_version(mkvh* h) { return h->meta.layout_version(); }
+
 // items_out: 8 int32 per item (b, seq, list_off, npages, last_ntok, chunk, fmt, 0), FP8 items
 // first.  counts_out: n_fp8_items, n_tq3_items, n_pages, n_chunks, chunk_pages.
 int mkvh_schedule(mkvh* h, const int32_t* ids, int32_t B, int32_t Hq, int32_t chunk_pages,

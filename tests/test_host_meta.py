@@ -33,6 +33,8 @@ def lib():
     L.mkvh_kv_bytes.restype = I64
     L.mkvh_version.argtypes = [P]
     L.mkvh_version.restype = ctypes.c_uint64
+    L.mkvh_layout_version.argtypes = [P]
+    L.mkvh_layout_version.restype = ctypes.c_uint64
     L.mkvh_schedule.argtypes = [P, P, I32, I32, I32, I32, P, I32, P, I32, P, P]
     L.mkvh_last_error.restype = ctypes.c_char_p
     return L
@@ -373,4 +375,31 @@ def test_append_step_is_all_or_nothing(lib):
     assert h.append_step([3, 2])[0] == -3                    # frozen tail: ESTATE
     assert lens() == [16, 16, 3, 0] and h.L.mkvh_version(h.h) == v1
     assert h.append_step([3])[0] == 0 and lens()[3] == 1
+    h.close()
+
+
+def test_layout_version_moves_only_when_pages_change(lib):
+    """Decode keeps its schedule while only token counts change; the layout
+    version must move whenever a page opens, converts or is freed."""
+    h = _host(lib, fp8_pages=40)
+    ver = lambda: (h.L.mkvh_version(h.h), h.L.mkvh_layout_version(h.h))
+    v0, l0 = ver()
+    assert h.append(0, 10)[0] == 0                 # opens page 0
+    v1, l1 = ver()
+    assert v1 > v0 and l1 > l0
+    assert h.append(0, 6)[0] == 0                  # fills page 0: lengths only
+    v2, l2 = ver()
+    assert v2 > v1 and l2 == l1
+    assert h.append_step([0])[0] == 0              # opens page 1
+    v3, l3 = ver()
+    assert v3 > v2 and l3 > l2
+    assert h.append_step([0])[0] == 0              # inside page 1
+    v4, l4 = ver()
+    assert v4 > v3 and l4 == l3
+    assert h.demote(0, [0])[0] == 0                # converts page 0
+    v5, l5 = ver()
+    assert v5 > v4 and l5 > l4
+    assert h.L.mkvh_reset(h.h, 0) == 0             # frees pages
+    v6, l6 = ver()
+    assert v6 > v5 and l6 > l5
     h.close()
