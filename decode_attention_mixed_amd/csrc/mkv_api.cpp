@@ -108,11 +108,17 @@ struct mkv_pool {
   int device = 0;
   uint8_t* mem = nullptr;
   bool owns_mem = false;
-  // pinned staging for host -> device metadata uploads
-  uint8_t* staging = nullptr;
-  size_t staging_bytes = 0;
-  hipEvent_t staging_ev = nullptr;
-  bool staging_pending = false;
+  // pinned staging ring for host -> device metadata uploads: an upload takes
+  // the next slot, waiting only for that slot's previous copy, so the host can
+  // run several calls ahead of the device (the copies themselves are stream-
+  // ordered behind the kernels that read the previous contents)
+  static constexpr int kStagingSlots = 4;
+  uint8_t* staging_mem = nullptr;
+  uint8_t* staging = nullptr;            // the slot being filled
+  size_t staging_bytes = 0;              // bytes per slot
+  hipEvent_t staging_ev[kStagingSlots] = {};
+  bool staging_pending[kStagingSlots] = {};
+  int staging_slot = 0;
   // cached decode schedule
   bool sched_valid = false;
   uint64_t sched_version = 0;
@@ -137,11 +143,14 @@ struct mkv_pool {
                          g.tq3_stride, g.Hkv, g.d, g.P, desc.max_pages_per_seq, g.kind};
   }
 
+  // Selects the next staging slot, once its previous upload has completed.
   mkv_status wait_staging() {
-    if (staging_pending) {
-      MKV_HIP(hipEventSynchronize(staging_ev));
-      staging_pending = false;
+    staging_slot = (staging_slot + 1) % kStagingSlots;
+    if (staging_pending[staging_slot]) {
+      MKV_HIP(hipEventSynchronize(staging_ev[staging_slot]));
+      staging_pending[staging_slot] = false;
     }
+    staging = staging_mem + size_t(staging_slot) * staging_bytes;
     return MKV_OK;
   }
 };
@@ -162,8 +171,8 @@ mkv_status flush_uploads(mkv_pool* p, const std::vector<Upload>& ups, hipStream_
                              hipMemcpyHostToDevice, s));
     src += u.bytes;
   }
-  MKV_HIP(hipEventRecord(p->staging_ev, s));
-  p->staging_pending = true;
+  MKV_HIP(hipEventRecord(p->staging_ev[p->staging_slot], s));
+  p->staging_pending[p->staging_slot] = true;
   return MKV_OK;
 }
 
@@ -271,8 +280,9 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
   p->desc = *desc;
   p->lay = make_layout(to_desc(*desc), p->meta.geom());
   auto cleanup = [&](mkv_status s, const std::string& msg) {
-    if (p->staging) (void)hipHostFree(p->staging);
-    if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
+    if (p->staging_mem) (void)hipHostFree(p->staging_mem);
+    for (hipEvent_t ev : p->staging_ev)
+      if (ev) (void)hipEventDestroy(ev);
     if (p->owns_mem && p->mem) (void)hipFree(p->mem);
     delete p;
     return set_err(s, msg);
@@ -302,12 +312,16 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
   }
   p->staging_bytes = std::max(p->lay.sched_bytes, p->lay.plan_bytes +
                                                       size_t(desc->max_pages_per_seq) * 4);
+  p->staging_bytes = align256(p->staging_bytes);
   void* h = nullptr;
-  e = hipHostMalloc(&h, p->staging_bytes, hipHostMallocDefault);
+  e = hipHostMalloc(&h, p->staging_bytes * mkv_pool::kStagingSlots, hipHostMallocDefault);
   if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("hipHostMalloc: ") + hipGetErrorString(e));
-  p->staging = static_cast<uint8_t*>(h);
-  e = hipEventCreateWithFlags(&p->staging_ev, hipEventDisableTiming);
-  if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
+  p->staging_mem = static_cast<uint8_t*>(h);
+  p->staging = p->staging_mem;
+  for (hipEvent_t& ev : p->staging_ev) {
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
+  }
   *out = p;
   return MKV_OK;
 }
@@ -324,8 +338,9 @@ mkv_status mkv_pool_destroy(mkv_pool* p) {
     (void)hipEventDestroy(ev.a);
     (void)hipEventDestroy(ev.b);
   }
-  if (p->staging_ev) (void)hipEventDestroy(p->staging_ev);
-  if (p->staging) (void)hipHostFree(p->staging);
+  for (hipEvent_t ev : p->staging_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  if (p->staging_mem) (void)hipHostFree(p->staging_mem);
   if (p->owns_mem && p->mem) (void)hipFree(p->mem);
   delete p;
   if (e != hipSuccess) return set_err(MKV_EHIP, hipGetErrorString(e));
