@@ -285,6 +285,27 @@ __device__ __forceinline__ half8 value_operand(const uint8_t* p, const uint8_t* 
   return __builtin_bit_cast(half8, d);
 }
 
+// Two kv-heads per wave: the PV MFMA's K dimension holds head 0's four tokens
+// of the lane quad in k-slots 0..3 and head 1's in 4..7.  The B operand is
+// V_0 | V_1 of the lane's column (one transposing read from each head's tile);
+// the A operand carries the lane's P' (its column belongs to one head) in that
+// head's slots and zeros in the other's, split into a hi and a lo MFMA.  Both
+// heads then accumulate into one accumulator per N-tile, each output row
+// receiving only its own head's values.
+__device__ __forceinline__ void split_pprime(half8 pp, bool head1, half8& a_hi, half8& a_lo) {
+  const u32x4 w = __builtin_bit_cast(u32x4, pp);     // hi 0-1, hi 2-3, lo 0-1, lo 2-3
+  const u32x4 h = {head1 ? 0u : w[0], head1 ? 0u : w[1], head1 ? w[0] : 0u, head1 ? w[1] : 0u};
+  const u32x4 l = {head1 ? 0u : w[2], head1 ? 0u : w[3], head1 ? w[2] : 0u, head1 ? w[3] : 0u};
+  a_hi = __builtin_bit_cast(half8, h);
+  a_lo = __builtin_bit_cast(half8, l);
+}
+__device__ __forceinline__ half8 value_operand_heads(const uint8_t* p0, const uint8_t* p1) {
+  const u32x2 a = __builtin_bit_cast(u32x2, read_tr(p0));
+  const u32x2 b = __builtin_bit_cast(u32x2, read_tr(p1));
+  const u32x4 d = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(half8, d);
+}
+
 // ---- cross-lane helpers -----------------------------------------------------
 
 // Orders one wave's LDS accesses around this point (writes before later reads
@@ -722,9 +743,9 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
   };
 
-  f32x4 acc[NH * NT];
+  f32x4 acc[NT];                                // one per N-tile, both kv-heads' rows
 #pragma unroll
-  for (int j = 0; j < NH * NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
 
   // Per-lane byte offsets inside a record (the tile's first token is added per
@@ -861,13 +882,20 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 #pragma unroll
       for (int i = 0; i < 4; ++i) sv[i] = f16_half(vsd[(i * NG + g) >> 1], (i * NG + g) & 1);
       const half8 pp = pprime(p, sv);
-#pragma unroll
-      for (int j = 0; j < NH; ++j)
+      if constexpr (NH == 2) {
+        half8 a_hi, a_lo;
+        split_pprime(pp, jcol == 1, a_hi, a_lo);
 #pragma unroll
         for (int jt = 2 * g; jt < 2 * g + 2; ++jt) {
-          const half8 bv = value_operand(vbase + j * (16 * VROW) + 32 * jt, vbase2 + j * (16 * VROW) + 32 * jt);
-          acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
+          const half8 bv = value_operand_heads(vbase + 32 * jt, vbase + 16 * VROW + 32 * jt);
+          acc[jt] = pv_mfma(a_hi, bv, acc[jt]);
+          acc[jt] = pv_mfma(a_lo, bv, acc[jt]);
         }
+      } else {
+#pragma unroll
+        for (int jt = 2 * g; jt < 2 * g + 2; ++jt)
+          acc[jt] = pv_mfma(pp, value_operand(vbase + 32 * jt, vbase2 + 32 * jt), acc[jt]);
+      }
     }
     wave_lds_sync();
   };
@@ -893,12 +921,10 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
     if (c >= ncol) continue;
-    const int jc = c / G;
     float* dst = M.acc[wave] + c * MergeLds<D>::ROW;
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt)
-      dst[32 * (jt >> 1) + ((jt & 1) ? (eo & 31) : (ee & 31))] =
-          pick_head<NH, NT>(acc, jc, jt, i) * ((jt & 1) ? up_o : up_e);
+      dst[32 * (jt >> 1) + ((jt & 1) ? (eo & 31) : (ee & 31))] = acc[jt][i] * ((jt & 1) ? up_o : up_e);
   }
   __syncthreads();
   merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
@@ -948,9 +974,9 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
     F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
   };
 
-  f32x4 acc[NH * NT];
+  f32x4 acc[NT];                                // one per N-tile, both kv-heads' rows
 #pragma unroll
-  for (int j = 0; j < NH * NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
 
   uint32_t code_off[NH], ks_off[NH], vs_off[NH];
@@ -1042,13 +1068,20 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
     softmax_step(st, s, p, acc, W.corr, col, quad);
 
     const half8 pp = pprime_uniform(p, sv);
-#pragma unroll
-    for (int j = 0; j < NH; ++j)
+    if constexpr (NH == 2) {
+      half8 a_hi, a_lo;
+      split_pprime(pp, jcol == 1, a_hi, a_lo);
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        const half8 bv = value_operand(vbase + j * (16 * VROW) + 32 * jt, vbase2 + j * (16 * VROW) + 32 * jt);
-        acc[j * NT + jt] = pv_mfma(pp, bv, acc[j * NT + jt]);
+        const half8 bv = value_operand_heads(vbase + 32 * jt, vbase + 16 * VROW + 32 * jt);
+        acc[jt] = pv_mfma(a_hi, bv, acc[jt]);
+        acc[jt] = pv_mfma(a_lo, bv, acc[jt]);
       }
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+        acc[jt] = pv_mfma(pp, value_operand(vbase + 32 * jt, vbase2 + 32 * jt), acc[jt]);
+    }
     wave_lds_sync();
   };
   run_tiles<R, Raw>(tg, a.pace != 0, load, prepare, process);
@@ -1064,10 +1097,9 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
     if (c >= ncol) continue;
-    const int jc = c / G;
     float* dst = M.acc[wave] + c * MergeLds<D>::ROW;
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) dst[16 * jt + col] = pick_head<NH, NT>(acc, jc, jt, i);
+    for (int jt = 0; jt < NT; ++jt) dst[16 * jt + col] = acc[jt][i];
   }
   __syncthreads();
   merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
@@ -1243,17 +1275,17 @@ template <int NG, int NH>
 struct PartialCfg {
   static constexpr int kRingTq3 = 2;                 // TQ3 tiles in flight per wave
   // FP8 rows are 4x the TQ3 bytes: one tile in flight with two kv-heads or
-  // head dim 256, so the kernel keeps two waves per SIMD
+  // head dim 256, within the register budget of the waves per SIMD
   static constexpr int kRingFp8 = NH == 1 && NG < 8 ? 2 : 1;
   static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
   static constexpr size_t kSmem =
       cmax(cmax(sizeof(Tq3Lds<NG, NH>), sizeof(Fp8Lds<NG, NH>)), sizeof(MergeLds<32 * NG>));
 };
 
-// Two waves per SIMD (256 VGPRs); three for one kv-head per wave at head
-// dim <= 128.
+// Three waves per SIMD (168 VGPRs) at head dim <= 128 -- two kv-heads per
+// wave fit because they share one accumulator per N-tile; two waves at 256.
 template <int NG, int NH>
-__global__ void __launch_bounds__(kThreads, NH == 1 && NG < 8 ? 3 : 2) partial_mixed(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, NG < 8 ? 3 : 2) partial_mixed(DecodeArgs a) {
   using Cfg = PartialCfg<NG, NH>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
   const WorkItem it = a.items[blockIdx.x];
