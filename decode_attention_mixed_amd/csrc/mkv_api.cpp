@@ -205,7 +205,7 @@ ProfEvent* prof_begin(mkv_pool* p, int kind, hipStream_t s) {
   return &p->prof_events.back();
 }
 
-void prof_end(mkv_pool* p, ProfEvent* e, hipStream_t s) {
+void prof_end(mkv_pool*, ProfEvent* e, hipStream_t s) {
   if (e) (void)hipEventRecord(e->b, s);
 }
 
