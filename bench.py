@@ -11,7 +11,10 @@ a step from the previous one.  Workloads whose live KV already exceeds a few GB
 use one pool with their own slab sizes.
 
 Prints one JSON line:
-  value        KV GB/s = algorithmic bytes per step / step time
+  value        KV GB/s = algorithmic bytes per step / step time (mean over the
+               timed steps; config adds per-step p10 / p50 / p90 from a pass
+               with an event pair around every step, and the KV GB/s as a share
+               of a plain 1 GiB device copy's read + write rate)
   roofline     the dominant kernel (the partial kernel, which reads every KV
                byte of the step in one launch): its algorithmic bytes per
                launch / its mean launch time from HIP events recorded on the
@@ -334,6 +337,17 @@ def main():
         for k2, v2 in mkv.profile_read(p.handle).items():
             prof[k2] = prof.get(k2, 0) + v2
         mkv.profile_enable(p.handle, False)
+    # Timed region 3 (library events off again): one event pair around every
+    # step, for the per-step distribution.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
+    pct = {f"p{k}": round(float(np.percentile(per_step, k)), 3) for k in (10, 50, 90)}
     log(f"step {ms * 1e3:.2f} us (host {host_s * 1e6:.1f} us per call; {ms_ev * 1e3:.2f} us with "
         f"kernel events); kernel profile {prof}")
     multi = None
@@ -460,6 +474,22 @@ def main():
         comparison["materialising_profile"] = materialised
     del kvs
 
+    # Practical HBM ceiling on this device: a 1 GiB device-to-device copy,
+    # counting the bytes read and written (context for the KV GB/s).
+    src = torch.empty(2**30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_ceiling = 2.0 * 2**30 * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
     kernel_ms = {"partial": prof["ms_partial"] / max(1, prof["n_partial"]),
                  "merge": prof["ms_merge"] / max(1, prof["n_merge"])}
     # the dominant kernel: the partial kernel, one launch reads every KV byte
@@ -492,6 +522,9 @@ def main():
             "kernel_us": {k: round(v * 1e3, 3) for k, v in kernel_ms.items()},
             "host_us_per_call": round(host_s * 1e6, 2),
             "us_per_step_with_kernel_events": round(ms_ev * 1e3, 3),
+            "us_per_step_percentiles": pct,
+            "copy_ceiling_gbs": round(copy_ceiling, 1),
+            "pct_of_copy_ceiling": round(100.0 * value / copy_ceiling, 2) if copy_ceiling else None,
         },
         "roofline": {
             "kernel": dom,
