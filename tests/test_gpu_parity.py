@@ -290,6 +290,32 @@ def test_bf16_control_records_and_decode(name):
     pool.close()
 
 
+def test_bf16_control_decode_steps():
+    """One-token appends to every sequence of a control pool (mkv_append_step,
+    pages opened on the way), decoded and gathered against the oracle."""
+    wl = W.small(seed=71, B=3, Hq=8, Hkv=2, d=64, P=16, lengths=(30, 16, 1))
+    pool = H.DevicePool(H.pool_desc(wl, kind="bf16", max_pages_per_seq=8, fp8_pages=40))
+    H.load_cache(pool, wl)
+    models = [OS.bf16_model(wl, b) for b in range(wl.B)]
+    rng = np.random.default_rng(72)
+    ids = [2, 0, 1]                                   # any order of distinct sequences
+    for step in range(20):
+        k = rng.standard_normal((3, wl.Hkv, wl.d)).astype(np.float32)
+        v = rng.standard_normal((3, wl.Hkv, wl.d)).astype(np.float32)
+        mkv.append_step(pool.handle, ids, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        for row, b in enumerate(ids):
+            models[b].append(k[row:row + 1], v[row:row + 1])
+        if step in (0, 1, 14, 19):
+            out, lse = _run_decode(pool, wl)
+            _check(out, lse, *OS.decode_all(wl, models), f"control step {step}")
+    for b in range(wl.B):
+        recs = H.gather_records(pool, b, len(models[b].bits))
+        for lp in range(len(models[b].bits)):
+            ref, mask = models[b].record(lp), models[b].valid_mask(lp)
+            assert np.array_equal(recs[lp, :ref.size][mask], ref[mask]), (b, lp)
+    pool.close()
+
+
 def test_bf16_control_long_context_parity():
     """The 131072-token Hq=48/Hkv=8 shape as a BF16 control cache, decoded in
     the launch configuration the benchmark times for the control."""
