@@ -10,9 +10,10 @@
 //
 // Two variants.  Wide (many chunks per sequence): one wave per (b, h, 16-dim
 // slice).  Lane (j, k) owns dims 4j..4j+3 of the slice for chunks k, k+16,
-// ...; it loads a batch of up to kUnroll of them (max, denominator and a
-// float4 of the accumulator) at once, so a batch of 16 * kUnroll chunks costs
-// one memory round trip.  The batch maximum is reduced over the wave, the lane
+// ...; it loads a batch of up to U of them (max, denominator and a float4 of
+// the accumulator) at once, so a batch of 16 * U chunks costs one memory
+// round trip (U = 16 when a sequence has more than 128 chunks, else 8, so
+// short lists do not pay for redundant loads).  The batch maximum is reduced over the wave, the lane
 // accumulates its chunks with weights 2^(m_i - M) (rescaling earlier batches
 // if M rose), and the 16 chunk lanes are summed with shuffles at the end (no
 // LDS, no workgroup barrier).  Narrow (few chunks per sequence, as
@@ -38,6 +39,7 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+template <int U>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   const int d = a.pv.d;
   const int nslices = d / kSlice;
@@ -51,11 +53,11 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   float M = -INFINITY;                 // running maximum over live chunks
   float L = 0.0f;                      // this thread's share of the denominator
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int cb = c0; cb < c1; cb += kChunkLanes * kUnroll) {
-    float m[kUnroll], l[kUnroll];
-    float4 v[kUnroll];
+  for (int cb = c0; cb < c1; cb += kChunkLanes * U) {
+    float m[U], l[U];
+    float4 v[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int c = cb + k + kChunkLanes * u;
       const bool ok = c < c1;
       const int64_t i = int64_t(ok ? c : c0) * a.Hq + h;
@@ -65,7 +67,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
     }
     float bm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
       if (l[u] > 0.0f) bm = fmaxf(bm, m[u]);
     bm = wave_max(bm);
     if (bm > M) {                      // rescale what earlier batches accumulated
@@ -78,7 +80,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
       M = bm;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (!(l[u] > 0.0f)) continue;
       const float w = exp2f(m[u] - M);
       L += l[u] * w;
@@ -166,8 +168,11 @@ hipError_t launch_merge(const DecodeArgs& a, int narrow_max, hipStream_t s) {
     return hipGetLastError();
   }
   const int nslices = a.pv.d / kSlice;
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(a.B * a.Hq * nslices)), dim3(kMergeThreads), 0,
-                     s, a);
+  const dim3 grid(unsigned(a.B * a.Hq * nslices));
+  if (a.max_seq_chunks > kChunkLanes * 8)
+    hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(kMergeThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -519,7 +519,7 @@ __device__ __forceinline__ void merge_waves_and_store(MergeLds<D>& M, const Deco
   // (the global stores come after the barrier: a barrier's release fence
   // would otherwise wait for them to reach memory)
   __syncthreads();
-  if (threadIdx.x < ncol) {
+  if (int(threadIdx.x) < ncol) {
     a.pm[base + threadIdx.x] = mx;
     a.pl[base + threadIdx.x] = lsum;
   }
