@@ -192,8 +192,8 @@ mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages,
  * wave-reduced one).  The split-K schedule is rebuilt only when page
  * metadata, the batch or Hq changed since the previous decode; the result of
  * a given schedule is bit-reproducible.
- * MKV_EINVAL for an empty sequence, Hq not a multiple of Hkv, Hq / Hkv > 16,
- * or a misaligned q;
+ * MKV_EINVAL for B < 1, an id outside [0, max_seqs), an empty sequence, Hq
+ * not a multiple of Hkv, Hq / Hkv > 16, or a misaligned q;
  * MKV_ERANGE for B > max_batch or Hq > max_q_heads. */
 mkv_status mkv_decode(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const void* q,
                       int32_t Hq, float softmax_scale, float* out, float* lse,

@@ -176,6 +176,8 @@ def test_invalid_arguments_and_states(lib):
     assert h.schedule([0], 5)[0] == EINVAL    # Hq not a multiple of Hkv
     assert h.schedule([0], 10)[0] == ERANGE   # Hq > max_q_heads
     assert h.schedule([0, 0, 0, 0, 0], 8)[0] == ERANGE  # B > max_batch
+    assert h.schedule([], 8)[0] == EINVAL     # empty batch
+    assert h.schedule([5], 8)[0] == EINVAL    # id past max_seqs
     h.close()
 
 
