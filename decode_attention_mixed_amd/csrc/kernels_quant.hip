@@ -33,12 +33,10 @@ __device__ float block_max(float v, float* red) {
 // the running amax the earlier rows of the page are re-encoded from their
 // dequantised values, so a page filled in one call equals one-shot encoding.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads)
-append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float* __restrict__ k,
-                  const float* __restrict__ v) {
+__device__ __forceinline__ void append_fp8_block(const PoolView& pv, const AppendPage& ap,
+                                                 const float* __restrict__ k,
+                                                 const float* __restrict__ v) {
   __shared__ float red[kThreads / 64];
-  const int per_page = pv.Hkv * 2;
-  const AppendPage ap = plan[blockIdx.x / per_page];
   const int h = (blockIdx.x / 2) % pv.Hkv;
   const int kv = blockIdx.x % 2;
   const int d = pv.d;
@@ -79,6 +77,12 @@ append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float*
     *scale_p = sigma;
     *amax_p = amax;
   }
+}
+
+__global__ void __launch_bounds__(kThreads)
+append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float* __restrict__ k,
+                  const float* __restrict__ v) {
+  append_fp8_block(pv, plan[blockIdx.x / (pv.Hkv * 2)], k, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -163,11 +167,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-__global__ void __launch_bounds__(kThreads)
-append_bf16_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float* __restrict__ k,
-                   const float* __restrict__ v) {
-  const int per_page = pv.Hkv * 2;
-  const AppendPage ap = plan[blockIdx.x / per_page];
+__device__ __forceinline__ void append_bf16_block(const PoolView& pv, const AppendPage& ap,
+                                                  const float* __restrict__ k,
+                                                  const float* __restrict__ v) {
   const int h = (blockIdx.x / 2) % pv.Hkv;
   const int kv = blockIdx.x % 2;
   const int d = pv.d;
@@ -181,6 +183,27 @@ append_bf16_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float
     const int r = i / d, j = i % d;
     rows[i] = f32_to_bf16_rne(src[(int64_t(ap.src_row + r) * pv.Hkv + h) * d + j]);
   }
+}
+
+__global__ void __launch_bounds__(kThreads)
+append_bf16_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float* __restrict__ k,
+                   const float* __restrict__ v) {
+  append_bf16_block(pv, plan[blockIdx.x / (pv.Hkv * 2)], k, v);
+}
+
+// Append with the plan in the kernel arguments (one block per (page, kv-head,
+// K-or-V) as above); the first block also applies the plan's patches.
+template <bool kBf16>
+__global__ void __launch_bounds__(kThreads)
+append_inline_kernel(PoolView pv, InlinePlan plan, const float* __restrict__ k,
+                     const float* __restrict__ v) {
+  if (blockIdx.x == 0 && int(threadIdx.x) < plan.n_patch)
+    plan.patch_base[plan.patch_off[threadIdx.x]] = plan.patch_val[threadIdx.x];
+  const AppendPage ap = plan.pages[blockIdx.x / (pv.Hkv * 2)];
+  if constexpr (kBf16)
+    append_bf16_block(pv, ap, k, v);
+  else
+    append_fp8_block(pv, ap, k, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -252,6 +275,18 @@ hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_p
   if (n_pages <= 0) return hipSuccess;
   hipLaunchKernelGGL(append_fp8_kernel, dim3(unsigned(n_pages * pv.Hkv * 2)), dim3(kThreads), 0,
                      s, pv, plan, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_inline(const PoolView& pv, const InlinePlan& plan, int32_t n_pages,
+                                const float* k, const float* v, hipStream_t s) {
+  if (n_pages <= 0 || n_pages > kInlinePages || plan.n_patch < 0 || plan.n_patch > kInlinePages)
+    return hipErrorInvalidValue;
+  const dim3 grid(unsigned(n_pages * pv.Hkv * 2));
+  if (pv.kind == kKindBf16)
+    hipLaunchKernelGGL(append_inline_kernel<true>, grid, dim3(kThreads), 0, s, pv, plan, k, v);
+  else
+    hipLaunchKernelGGL(append_inline_kernel<false>, grid, dim3(kThreads), 0, s, pv, plan, k, v);
   return hipGetLastError();
 }
 

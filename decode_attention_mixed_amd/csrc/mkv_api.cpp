@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -386,6 +387,41 @@ mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
   std::string err;
   int st = p->meta.append_step(seq_ids, B, p->desc.max_pages_per_seq, &plan, &err);
   if (st) return set_err(mkv_status(st), err);
+  if (plan.size() <= size_t(mkv::kInlinePages)) {
+    // Small step: the plan travels in the kernel arguments.  When the step
+    // opened no page and the cached decode schedule predates it only in token
+    // counts, the same launch brings the device items' last-page counts up to
+    // date, so the next decode of that batch uploads nothing.
+    mkv::InlinePlan ip{};
+    std::memcpy(ip.pages, plan.data(), plan.size() * sizeof(plan[0]));
+    std::vector<std::pair<mkv::WorkItem*, int32_t>> fixes;
+    bool patch = p->sched_valid && p->sched_layout == p->meta.layout_version();
+    if (patch) {
+      const int32_t P = p->meta.geom().P;
+      int32_t idx = 0;
+      for (auto& list : p->sched.items)
+        for (mkv::WorkItem& it : list) {
+          const int32_t n = mkv::page_tokens(p->meta.seq(it.seq).len, P, it.last_lp);
+          if (n != it.last_ntok) {
+            if (ip.n_patch == mkv::kInlinePages) patch = false;
+            if (!patch) break;
+            ip.patch_off[ip.n_patch] = idx * int32_t(sizeof(mkv::WorkItem) / 4) +
+                                       int32_t(offsetof(mkv::WorkItem, last_ntok) / 4);
+            ip.patch_val[ip.n_patch++] = n;
+            fixes.emplace_back(&it, n);
+          }
+          ++idx;
+        }
+    }
+    if (!patch) ip.n_patch = 0;
+    ip.patch_base = reinterpret_cast<int32_t*>(p->mem + p->lay.sched);
+    MKV_HIP(mkv::launch_append_inline(p->view(), ip, int32_t(plan.size()), k, v, s));
+    if (patch) {
+      for (auto& f : fixes) f.first->last_ntok = f.second;
+      p->sched_version = p->meta.version();
+    }
+    return MKV_OK;
+  }
   mkv_status r = p->wait_staging();
   if (r) return r;
   const size_t bytes = plan.size() * sizeof(plan[0]);

@@ -50,6 +50,22 @@ hipError_t launch_materialise(const PoolView& src, const PoolView& dst, const Ma
 // Control pools: store rows as bf16 (round to nearest even).
 hipError_t launch_append_bf16(const PoolView& pv, const AppendPage* plan, int32_t n_pages,
                               const float* k, const float* v, hipStream_t s);
+// A small append plan carried in the kernel arguments, so a decode step's
+// append needs no upload: up to kInlinePages pages, and up to kInlinePages
+// 32-bit stores into device memory (patch_base[patch_off[i]] = patch_val[i],
+// done by the first block; a step uses them to bring a cached decode
+// schedule's last-page token counts up to date).
+constexpr int kInlinePages = 32;
+struct InlinePlan {
+  int32_t* patch_base;
+  int32_t n_patch, pad0;
+  AppendPage pages[kInlinePages];
+  int32_t patch_off[kInlinePages];
+  int32_t patch_val[kInlinePages];
+};
+// The pool's kind picks the FP8 or the BF16 append.
+hipError_t launch_append_inline(const PoolView& pv, const InlinePlan& plan, int32_t n_pages,
+                                const float* k, const float* v, hipStream_t s);
 hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
                          uint8_t* dst, int64_t slot_bytes, hipStream_t s);
 // Partial kernel of the pool's kind (mixed FP8/TQ3 or BF16 control).

@@ -163,7 +163,11 @@ mkv_status mkv_append(mkv_pool* pool, int32_t seq, int32_t n, const float* k, co
  * changes (MKV_EINVAL for a repeated or bad id, MKV_ESTATE for a frozen TQ3
  * tail, MKV_ENOMEM, MKV_ERANGE for B > max_batch or a full page table).  The
  * caller decides which pages leave the recent window and calls mkv_demote
- * ("Ancoras em FP8, arquivo em TQ3": recent and protected pages stay FP8). */
+ * ("Ancoras em FP8, arquivo em TQ3": recent and protected pages stay FP8).
+ * With B <= 32 the step copies nothing to the device: the plan goes in the
+ * kernel arguments, and when no page opens the same launch refreshes the
+ * token counts of the pool's cached decode schedule, so the next mkv_decode
+ * of that batch (on the same stream) uploads nothing either. */
 mkv_status mkv_append_step(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const float* k,
                            const float* v, hipStream_t stream);
 

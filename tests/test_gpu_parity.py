@@ -442,6 +442,49 @@ def test_decode_steps_with_appends_and_demotions():
     pool.close()
 
 
+@pytest.mark.parametrize("B", [3, 40])
+def test_append_steps_keep_the_cached_schedule_current(B):
+    """Decode after every mkv_append_step.  A step of at most 32 pages carries
+    its plan in the kernel arguments and, when it opens no page, brings the
+    cached schedule's last-page token counts up to date in the same launch (a
+    step that opens a page leaves the rebuild to the decode); larger steps take
+    the uploaded plan.  The batch repeats sequence 0 and leaves out the last
+    one, and a plain mkv_append between two steps must be picked up too."""
+    rng = np.random.default_rng(60 + B)
+    lengths = tuple(int(x) for x in rng.integers(1, 60, B))
+    wl = W.small(seed=61 + B, B=B, Hq=4, Hkv=2, d=64, P=16, lengths=lengths)
+    n_pages = sum(wl.n_pages(b) for b in range(B))
+    pool = H.DevicePool(H.pool_desc(wl, max_pages_per_seq=16, fp8_pages=n_pages + 4 * B + 16))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(B)]
+    ids = list(range(B))
+    batch = [0] + ids[:-1]
+    q = H.q_tensor(wl)
+    out = torch.empty(B, wl.Hq, wl.d, device="cuda")
+    lse = torch.empty(B, wl.Hq, device="cuda")
+    for step in range(24):
+        k = rng.standard_normal((B, wl.Hkv, wl.d)).astype(np.float32)
+        v = rng.standard_normal((B, wl.Hkv, wl.d)).astype(np.float32)
+        mkv.append_step(pool.handle, ids, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        for b in ids:
+            models[b].append(k[b:b + 1], v[b:b + 1])
+        if step == 7:
+            x = rng.standard_normal((1, wl.Hkv, wl.d)).astype(np.float32)
+            mkv.append(pool.handle, 1, torch.from_numpy(x).cuda(), torch.from_numpy(x).cuda())
+            models[1].append(x, x)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        mkv.decode(pool.handle, batch, q, float(wl.tau), out, lse)
+        torch.cuda.synchronize()
+        O = np.zeros((B, wl.Hq, wl.d))
+        L = np.zeros((B, wl.Hq))
+        for b, sid in enumerate(batch):
+            O[b], L[b] = A.decode_seq(models[sid], wl.q_bits[b], wl.tau)
+        _check(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), O, L,
+               f"B={B} step {step}")
+    pool.close()
+
+
 @pytest.fixture(scope="module")
 def long_case():
     wl = W.long()
