@@ -141,6 +141,11 @@ def _check(status: int):
 def _stream(stream):
     import torch
     if stream is None:
+        # the raw handle of the current stream, without building a Stream
+        # object (that costs a few microseconds per call)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return ctypes.c_void_p(raw(torch.cuda.current_device()))
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 

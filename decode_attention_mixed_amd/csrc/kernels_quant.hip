@@ -278,6 +278,26 @@ hipError_t launch_append(const PoolView& pv, const AppendPage* plan, int32_t n_p
   return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(kThreads) upload_kernel(UploadSet u) {
+  const uint32_t stride = gridDim.x * kThreads;
+  for (int g = 0; g < u.nseg; ++g) {
+    const uint32_t* __restrict__ src = u.src + u.src_word[g];
+    uint32_t* __restrict__ dst = u.dst[g];
+    for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < u.words[g]; i += stride) dst[i] = src[i];
+  }
+}
+
+hipError_t launch_upload(const UploadSet& u, hipStream_t s) {
+  if (u.nseg <= 0) return hipSuccess;
+  if (u.nseg > kUploadSegs) return hipErrorInvalidValue;
+  uint32_t most = 0;
+  for (int g = 0; g < u.nseg; ++g) most = u.words[g] > most ? u.words[g] : most;
+  if (most == 0) return hipSuccess;
+  const uint32_t blocks = (most + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(upload_kernel, dim3(blocks < 128 ? blocks : 128), dim3(kThreads), 0, s, u);
+  return hipGetLastError();
+}
+
 hipError_t launch_append_inline(const PoolView& pv, const InlinePlan& plan, int32_t n_pages,
                                 const float* k, const float* v, hipStream_t s) {
   if (n_pages <= 0 || n_pages > kInlinePages || plan.n_patch < 0 || plan.n_patch > kInlinePages)

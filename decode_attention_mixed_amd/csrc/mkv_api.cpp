@@ -48,10 +48,17 @@ mkv::Desc to_desc(const mkv_pool_desc& d) {
 // Device memory layout of a pool (offsets from the base of its block).
 struct Layout {
   size_t fp8, tq3, pt, sched, sched_bytes, plan, plan_bytes, pm, pl, pacc, total;
+  // The schedule region holds chunk_base, then the work items, then (at the
+  // next 256-byte boundary after the items) the page-list entries, so a
+  // rebuilt schedule is one contiguous upload.
   size_t items_cap;  // work items that fit the schedule region
-  size_t pages_off;  // page-list offset inside the schedule region
-  size_t base_off;   // chunk_base offset inside the schedule region
+  size_t items_off;  // offset of the items inside the region (chunk_base is at 0)
 };
+
+// Offset of the page-list entries of a schedule with n_items items.
+inline size_t entries_off(const Layout& L, size_t n_items) {
+  return L.items_off + align256(n_items * sizeof(mkv::WorkItem));
+}
 
 Layout make_layout(const mkv::Desc& d, const mkv::Geom& g) {
   Layout L{};
@@ -63,9 +70,9 @@ Layout make_layout(const mkv::Desc& d, const mkv::Geom& g) {
   L.pt = o;
   o = align256(o + size_t(d.max_seqs) * size_t(d.max_pages_per_seq) * 4);
   L.items_cap = size_t(g.max_chunks);
-  L.pages_off = align256(L.items_cap * sizeof(mkv::WorkItem));
-  L.base_off = align256(L.pages_off + size_t(d.max_batch) * size_t(d.max_pages_per_seq) * 4);
-  L.sched_bytes = align256(L.base_off + (size_t(d.max_batch) + 1) * 4);
+  L.items_off = align256((size_t(d.max_batch) + 1) * 4);
+  L.sched_bytes = align256(entries_off(L, L.items_cap) +
+                           size_t(d.max_batch) * size_t(d.max_pages_per_seq) * 4);
   L.sched = o;
   o += L.sched_bytes;
   L.plan_bytes = align256(size_t(std::max(d.max_pages_per_seq, d.max_batch)) * 32);
@@ -114,7 +121,8 @@ struct mkv_pool {
   // run several calls ahead of the device (the copies themselves are stream-
   // ordered behind the kernels that read the previous contents)
   static constexpr int kStagingSlots = 4;
-  uint8_t* staging_mem = nullptr;
+  uint8_t* staging_mem = nullptr;        // coherent pinned host memory
+  const uint32_t* staging_dev = nullptr; // the same memory as the device reads it
   uint8_t* staging = nullptr;            // the slot being filled
   size_t staging_bytes = 0;              // bytes per slot
   hipEvent_t staging_ev[kStagingSlots] = {};
@@ -163,15 +171,24 @@ struct Upload {
   size_t bytes;
 };
 
-// Copy the staged bytes (laid out back to back) to their device offsets.
+// Copy the staged bytes (laid out back to back, whole 32-bit words) to their
+// device offsets: one upload-kernel launch reading the staging slot.
 mkv_status flush_uploads(mkv_pool* p, const std::vector<Upload>& ups, hipStream_t s) {
+  if (ups.size() > size_t(mkv::kUploadSegs)) return set_err(MKV_EINVAL, "too many upload segments");
+  mkv::UploadSet u{};
+  u.src = p->staging_dev + (p->staging - p->staging_mem) / 4;
   size_t src = 0;
-  for (const Upload& u : ups) {
-    if (u.bytes)
-      MKV_HIP(hipMemcpyAsync(p->mem + u.dst_off, p->staging + src, u.bytes,
-                             hipMemcpyHostToDevice, s));
-    src += u.bytes;
+  for (const Upload& up : ups) {
+    if (up.bytes % 4 || up.dst_off % 4) return set_err(MKV_EINVAL, "upload not in whole words");
+    if (up.bytes) {
+      u.dst[u.nseg] = reinterpret_cast<uint32_t*>(p->mem + up.dst_off);
+      u.src_word[u.nseg] = uint32_t(src / 4);
+      u.words[u.nseg] = uint32_t(up.bytes / 4);
+      ++u.nseg;
+    }
+    src += up.bytes;
   }
+  MKV_HIP(mkv::launch_upload(u, s));
   MKV_HIP(hipEventRecord(p->staging_ev[p->staging_slot], s));
   p->staging_pending[p->staging_slot] = true;
   return MKV_OK;
@@ -315,9 +332,17 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
                                                       size_t(desc->max_pages_per_seq) * 4);
   p->staging_bytes = align256(p->staging_bytes);
   void* h = nullptr;
-  e = hipHostMalloc(&h, p->staging_bytes * mkv_pool::kStagingSlots, hipHostMallocDefault);
+  // coherent: the upload kernel reads it directly, so no GPU cache may keep
+  // an older copy of a slot
+  e = hipHostMalloc(&h, p->staging_bytes * mkv_pool::kStagingSlots,
+                    hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("hipHostMalloc: ") + hipGetErrorString(e));
   p->staging_mem = static_cast<uint8_t*>(h);
+  void* hd = nullptr;
+  e = hipHostGetDevicePointer(&hd, h, 0);
+  if (e != hipSuccess)
+    return cleanup(MKV_EHIP, std::string("hipHostGetDevicePointer: ") + hipGetErrorString(e));
+  p->staging_dev = static_cast<const uint32_t*>(hd);
   p->staging = p->staging_mem;
   for (hipEvent_t& ev : p->staging_ev) {
     e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
@@ -414,7 +439,7 @@ mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
         }
     }
     if (!patch) ip.n_patch = 0;
-    ip.patch_base = reinterpret_cast<int32_t*>(p->mem + p->lay.sched);
+    ip.patch_base = reinterpret_cast<int32_t*>(p->mem + p->lay.sched + p->lay.items_off);
     MKV_HIP(mkv::launch_append_inline(p->view(), ip, int32_t(plan.size()), k, v, s));
     if (patch) {
       for (auto& f : fixes) f.first->last_ntok = f.second;
@@ -475,7 +500,7 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
         off += sizeof(it);
       }
     p->sched_valid = false;
-    r = flush_uploads(p, {{p->lay.sched, off}}, s);
+    r = flush_uploads(p, {{p->lay.sched + p->lay.items_off, off}}, s);
     if (r) return r;
     p->sched_version = p->meta.version();
     p->sched_valid = true;
@@ -488,19 +513,16 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     if (st) return set_err(mkv_status(st), err);
     mkv_status r = p->wait_staging();
     if (r) return r;
+    // the staging slot mirrors the schedule region: one copy
     const size_t n8 = sc.items[0].size(), n3 = sc.items[1].size();
+    const size_t eoff = entries_off(p->lay, n8 + n3);
     uint8_t* st8 = p->staging;
-    std::memcpy(st8, sc.items[0].data(), n8 * 32);
-    std::memcpy(st8 + n8 * 32, sc.items[1].data(), n3 * 32);
-    const size_t items_bytes = (n8 + n3) * 32;
-    std::memcpy(st8 + items_bytes, sc.entries.data(), sc.entries.size() * 4);
-    std::memcpy(st8 + items_bytes + sc.entries.size() * 4, sc.chunk_base.data(),
-                sc.chunk_base.size() * 4);
-    std::vector<Upload> ups{{p->lay.sched, items_bytes},
-                            {p->lay.sched + p->lay.pages_off, sc.entries.size() * 4},
-                            {p->lay.sched + p->lay.base_off, sc.chunk_base.size() * 4}};
+    std::memcpy(st8, sc.chunk_base.data(), sc.chunk_base.size() * 4);
+    std::memcpy(st8 + p->lay.items_off, sc.items[0].data(), n8 * 32);
+    std::memcpy(st8 + p->lay.items_off + n8 * 32, sc.items[1].data(), n3 * 32);
+    std::memcpy(st8 + eoff, sc.entries.data(), sc.entries.size() * 4);
     p->sched_valid = false;
-    r = flush_uploads(p, ups, s);
+    r = flush_uploads(p, {{p->lay.sched, eoff + sc.entries.size() * 4}}, s);
     if (r) return r;
     p->sched = std::move(sc);
     p->sched_ids.assign(seq_ids, seq_ids + B);
@@ -510,11 +532,13 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     p->sched_valid = true;
   }
   const mkv::Schedule& sc = p->sched;
-  const mkv::WorkItem* items = reinterpret_cast<const mkv::WorkItem*>(p->mem + p->lay.sched);
+  uint8_t* region = p->mem + p->lay.sched;
+  const mkv::WorkItem* items = reinterpret_cast<const mkv::WorkItem*>(region + p->lay.items_off);
   mkv::DecodeArgs a{};
   a.pv = p->view();
-  a.entries = reinterpret_cast<const int32_t*>(p->mem + p->lay.sched + p->lay.pages_off);
-  a.chunk_base = reinterpret_cast<const int32_t*>(p->mem + p->lay.sched + p->lay.base_off);
+  a.entries = reinterpret_cast<const int32_t*>(
+      region + entries_off(p->lay, sc.items[0].size() + sc.items[1].size()));
+  a.chunk_base = reinterpret_cast<const int32_t*>(region);
   a.q = static_cast<const uint16_t*>(q);
   a.B = B;
   a.Hq = Hq;

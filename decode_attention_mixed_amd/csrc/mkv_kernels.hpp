@@ -63,6 +63,19 @@ struct InlinePlan {
   int32_t patch_off[kInlinePages];
   int32_t patch_val[kInlinePages];
 };
+// Metadata upload: up to kUploadSegs runs of 32-bit words copied from a
+// device-mapped, coherent pinned host buffer (src, word offsets src_word) to
+// device memory, in one launch (a copy-engine transfer of the same bytes adds
+// more latency to the stream than this kernel takes).
+constexpr int kUploadSegs = 4;
+struct UploadSet {
+  const uint32_t* src;
+  int32_t nseg, pad0;
+  uint32_t* dst[kUploadSegs];
+  uint32_t src_word[kUploadSegs];
+  uint32_t words[kUploadSegs];
+};
+hipError_t launch_upload(const UploadSet& u, hipStream_t s);
 // The pool's kind picks the FP8 or the BF16 append.
 hipError_t launch_append_inline(const PoolView& pv, const InlinePlan& plan, int32_t n_pages,
                                 const float* k, const float* v, hipStream_t s);
