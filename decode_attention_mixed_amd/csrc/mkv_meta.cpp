@@ -2,6 +2,8 @@
 #include "mkv_meta.hpp"
 
 #include <algorithm>
+#include <queue>
+#include <utility>
 
 namespace mkv {
 
@@ -277,26 +279,34 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     }
     // Balanced chunks are counted down (floor); hand the spare slots up to the
     // target, one at a time, to the lists whose chunks cost the most.
+    // (A heap ordered by chunk cost, ties to the lowest list index 2b + f.)
     if (fixed == 0 && attempt == 0) {
       const int64_t cap = std::min<int64_t>(target_items, g_.max_chunks);
-      while (count < cap) {
-        double worst = 0.0;
-        int32_t wb = -1, wf = 0;
-        for (int32_t b = 0; b < B; ++b)
-          for (int f = 0; f < 2; ++f) {
-            const int32_t n = f ? n3[size_t(b)] : n8[size_t(b)];
-            const int64_t k = f ? k3[size_t(b)] : k8[size_t(b)];
-            if (n == 0 || k >= n || (n + k) / (k + 1) < pol.min_chunk_pages) continue;
-            const double per = double(n) * (f ? 1.0 : c8) / double(k);
-            if (per > worst) {
-              worst = per;
-              wb = b;
-              wf = f;
-            }
-          }
-        if (wb < 0) break;
-        ++(wf ? k3 : k8)[size_t(wb)];
+      auto cost_of = [&](int32_t list, double* per) {
+        const int32_t b = list >> 1, f = list & 1;
+        const int32_t n = f ? n3[size_t(b)] : n8[size_t(b)];
+        const int64_t k = f ? k3[size_t(b)] : k8[size_t(b)];
+        if (n == 0 || k >= n || (n + k) / (k + 1) < pol.min_chunk_pages) return false;
+        *per = double(n) * (f ? 1.0 : c8) / double(k);
+        return *per > 0.0;
+      };
+      using Entry = std::pair<double, int32_t>;   // (cost per chunk, list)
+      auto lower = [](const Entry& x, const Entry& y) {
+        return x.first < y.first || (x.first == y.first && x.second > y.second);
+      };
+      std::priority_queue<Entry, std::vector<Entry>, decltype(lower)> heap(lower);
+      if (count < cap)
+        for (int32_t list = 0; list < 2 * B; ++list) {
+          double per;
+          if (cost_of(list, &per)) heap.emplace(per, list);
+        }
+      while (count < cap && !heap.empty()) {
+        const int32_t list = heap.top().second;
+        heap.pop();
+        ++((list & 1) ? k3 : k8)[size_t(list >> 1)];
         ++count;
+        double per;
+        if (cost_of(list, &per)) heap.emplace(per, list);
       }
     }
     if (count <= g_.max_chunks) break;
