@@ -102,6 +102,20 @@ def test_small_records_and_decode(name):
     pool.close()
 
 
+@pytest.mark.parametrize("name", sorted(n for n in SMALL_CASES if n != "d128_all_fp8"))
+def test_batches_without_tq3_pages(name):
+    """Every page anchored (FP8): a batch with no TQ3 item, for each head dim
+    and kv-heads-per-wave case of the partial kernel."""
+    wl = W.small(**{**SMALL_CASES[name], "anchor_frac": 1.0})
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    assert all(p.fmt == 0 for m in models for p in m.pages)
+    out, lse = _run_decode(pool, wl)
+    _check(out, lse, *OS.decode_all(wl, models), f"{name} all FP8")
+    pool.close()
+
+
 def test_all_tq3_with_partial_tail_and_single_token():
     wl = W.small(seed=21, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(77, 1, 16), anchor_frac=0.0)
     wl.anchors = [np.zeros(0, np.int64) for _ in range(wl.B)]       # every page TQ3
