@@ -401,6 +401,77 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
   return MKV_OK;
 }
 
+namespace {
+
+// A decode step opened pages: extend the cached schedule instead of leaving a
+// rebuild to the next decode.  For each batch entry of a sequence that got a
+// new page, that entry's last FP8 item (the one ending at the highest logical
+// page) takes the page: its page list is copied, one longer, to the end of
+// the list array, and the items plus the new tail go up in one upload.
+// Returns false, changing nothing, where that does not apply (an entry with
+// no FP8 item, a full chunk, no room left in the list array).
+bool extend_schedule(mkv_pool* p, const int32_t* seq_ids, const std::vector<mkv::AppendPage>& plan,
+                     hipStream_t s, mkv_status* err) {
+  mkv::Schedule& sc = p->sched;
+  const size_t cap = size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
+  std::vector<mkv::WorkItem> fp8 = sc.items[0];
+  std::vector<int32_t> entries = sc.entries, pages = sc.pages;
+  const size_t old_size = entries.size();
+  int32_t chunk_pages = sc.chunk_pages;
+  for (const mkv::AppendPage& ap : plan) {
+    if (ap.pt_slot < 0) continue;
+    const int32_t seq = seq_ids[ap.src_row];
+    for (size_t b = 0; b < p->sched_ids.size(); ++b) {
+      if (p->sched_ids[b] != seq) continue;
+      mkv::WorkItem* last = nullptr;
+      for (mkv::WorkItem& it : fp8)
+        if (it.b == int32_t(b) && (!last || it.last_lp > last->last_lp)) last = &it;
+      if (!last || last->npages >= mkv::kMaxChunkPages || entries.size() + last->npages + 1 > cap)
+        return false;
+      const int32_t off = int32_t(entries.size());
+      for (int32_t i = 0; i < last->npages; ++i) {
+        const int32_t e = entries[size_t(last->list_off + i)], lp = pages[size_t(last->list_off + i)];
+        entries.push_back(e);
+        pages.push_back(lp);
+      }
+      entries.push_back(ap.pt_entry);
+      pages.push_back(ap.lp);
+      last->list_off = off;
+      last->npages += 1;
+      last->last_lp = ap.lp;
+      chunk_pages = std::max(chunk_pages, last->npages);
+    }
+  }
+  // commit: token counts of every item, then one upload of items and tail
+  *err = p->wait_staging();
+  if (*err) return false;
+  sc.items[0] = std::move(fp8);
+  sc.entries = std::move(entries);
+  sc.pages = std::move(pages);
+  sc.chunk_pages = chunk_pages;
+  const int32_t P = p->meta.geom().P;
+  size_t off = 0;
+  for (auto& list : sc.items)
+    for (mkv::WorkItem& it : list) {
+      it.last_ntok = mkv::page_tokens(p->meta.seq(it.seq).len, P, it.last_lp);
+      std::memcpy(p->staging + off, &it, sizeof(it));
+      off += sizeof(it);
+    }
+  const size_t n_items = sc.items[0].size() + sc.items[1].size();
+  const size_t tail = (sc.entries.size() - old_size) * 4;
+  std::memcpy(p->staging + off, sc.entries.data() + old_size, tail);
+  p->sched_valid = false;
+  *err = flush_uploads(p, {{p->lay.sched + p->lay.items_off, off},
+                           {p->lay.sched + entries_off(p->lay, n_items) + old_size * 4, tail}}, s);
+  if (*err) return false;
+  p->sched_version = p->meta.version();
+  p->sched_layout = p->meta.layout_version();
+  p->sched_valid = true;
+  return true;
+}
+
+}  // namespace
+
 mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const float* k,
                            const float* v, hipStream_t s) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
@@ -410,8 +481,13 @@ mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
   DeviceGuard guard(p->device);
   std::vector<mkv::AppendPage> plan;
   std::string err;
+  const bool lists_current = p->sched_valid && p->sched_layout == p->meta.layout_version();
   int st = p->meta.append_step(seq_ids, B, p->desc.max_pages_per_seq, &plan, &err);
   if (st) return set_err(mkv_status(st), err);
+  if (lists_current && p->meta.layout_version() != p->sched_layout) {
+    mkv_status e = MKV_OK;
+    if (!extend_schedule(p, seq_ids, plan, s, &e) && e) return e;
+  }
   if (plan.size() <= size_t(mkv::kInlinePages)) {
     // Small step: the plan travels in the kernel arguments.  When the step
     // opened no page and the cached decode schedule predates it only in token
