@@ -403,6 +403,11 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
 
 namespace {
 
+mkv_status commit_schedule(mkv_pool* p, std::vector<mkv::WorkItem>&& fp8,
+                           std::vector<mkv::WorkItem>&& tq3, std::vector<int32_t>&& entries,
+                           std::vector<int32_t>&& pages, int32_t chunk_pages, size_t from,
+                           hipStream_t s);
+
 // A decode step opened pages: extend the cached schedule instead of leaving a
 // rebuild to the next decode.  For each batch entry of a sequence that got a
 // new page, that entry's last FP8 item (the one ending at the highest logical
@@ -412,7 +417,7 @@ namespace {
 // no FP8 item, a full chunk, no room left in the list array).
 bool extend_schedule(mkv_pool* p, const int32_t* seq_ids, const std::vector<mkv::AppendPage>& plan,
                      hipStream_t s, mkv_status* err) {
-  mkv::Schedule& sc = p->sched;
+  const mkv::Schedule& sc = p->sched;
   const size_t cap = size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
   std::vector<mkv::WorkItem> fp8 = sc.items[0];
   std::vector<int32_t> entries = sc.entries, pages = sc.pages;
@@ -442,10 +447,23 @@ bool extend_schedule(mkv_pool* p, const int32_t* seq_ids, const std::vector<mkv:
       chunk_pages = std::max(chunk_pages, last->npages);
     }
   }
-  // commit: token counts of every item, then one upload of items and tail
-  *err = p->wait_staging();
-  if (*err) return false;
+  std::vector<mkv::WorkItem> tq3 = sc.items[1];
+  *err = commit_schedule(p, std::move(fp8), std::move(tq3), std::move(entries), std::move(pages),
+                         chunk_pages, old_size, s);
+  return *err == MKV_OK;
+}
+
+// Commits an edited copy of the cached schedule: token counts of every item,
+// then one upload of the items and of the page list from word `from` on.
+mkv_status commit_schedule(mkv_pool* p, std::vector<mkv::WorkItem>&& fp8,
+                           std::vector<mkv::WorkItem>&& tq3, std::vector<int32_t>&& entries,
+                           std::vector<int32_t>&& pages, int32_t chunk_pages, size_t from,
+                           hipStream_t s) {
+  mkv_status err = p->wait_staging();
+  if (err) return err;
+  mkv::Schedule& sc = p->sched;
   sc.items[0] = std::move(fp8);
+  sc.items[1] = std::move(tq3);
   sc.entries = std::move(entries);
   sc.pages = std::move(pages);
   sc.chunk_pages = chunk_pages;
@@ -458,16 +476,78 @@ bool extend_schedule(mkv_pool* p, const int32_t* seq_ids, const std::vector<mkv:
       off += sizeof(it);
     }
   const size_t n_items = sc.items[0].size() + sc.items[1].size();
-  const size_t tail = (sc.entries.size() - old_size) * 4;
-  std::memcpy(p->staging + off, sc.entries.data() + old_size, tail);
+  const size_t tail = (sc.entries.size() - from) * 4;
+  std::memcpy(p->staging + off, sc.entries.data() + from, tail);
   p->sched_valid = false;
-  *err = flush_uploads(p, {{p->lay.sched + p->lay.items_off, off},
-                           {p->lay.sched + entries_off(p->lay, n_items) + old_size * 4, tail}}, s);
-  if (*err) return false;
+  err = flush_uploads(p, {{p->lay.sched + p->lay.items_off, off},
+                          {p->lay.sched + entries_off(p->lay, n_items) + from * 4, tail}}, s);
+  if (err) return err;
   p->sched_version = p->meta.version();
   p->sched_layout = p->meta.layout_version();
   p->sched_valid = true;
-  return true;
+  return MKV_OK;
+}
+
+// Pages of sequence `seq` were demoted: in the cached schedule, each batch
+// entry of the sequence drops every such page from the FP8 item listing it
+// (in place) and its last TQ3 item (highest last page) takes it, its list
+// copied one longer to the end of the list array.  The TQ3 item's previous
+// last page must be full, since only an item's last page may hold fewer
+// tokens.  Returns false, changing nothing, where that does not apply (an FP8
+// item would become empty, an entry with no TQ3 item, a full chunk, no room).
+bool demote_in_schedule(mkv_pool* p, int32_t seq, const std::vector<mkv::DemotePage>& plan,
+                        hipStream_t s, mkv_status* err) {
+  const mkv::Schedule& sc = p->sched;
+  const size_t cap = size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
+  std::vector<mkv::WorkItem> fp8 = sc.items[0], tq3 = sc.items[1];
+  std::vector<int32_t> entries = sc.entries, pages = sc.pages;
+  int32_t chunk_pages = sc.chunk_pages;
+  const mkv::Seq& q = p->meta.seq(seq);
+  const int32_t P = p->meta.geom().P;
+  for (size_t b = 0; b < p->sched_ids.size(); ++b) {
+    if (p->sched_ids[b] != seq) continue;
+    for (const mkv::DemotePage& dp : plan) {
+      mkv::WorkItem* src = nullptr;
+      int32_t at = -1;
+      for (mkv::WorkItem& it : fp8) {
+        if (it.b != int32_t(b)) continue;
+        for (int32_t i = 0; i < it.npages && at < 0; ++i)
+          if (pages[size_t(it.list_off + i)] == dp.lp) at = i;
+        if (at >= 0) {
+          src = &it;
+          break;
+        }
+      }
+      if (!src || src->npages < 2) return false;
+      for (int32_t i = at; i + 1 < src->npages; ++i) {
+        entries[size_t(src->list_off + i)] = entries[size_t(src->list_off + i + 1)];
+        pages[size_t(src->list_off + i)] = pages[size_t(src->list_off + i + 1)];
+      }
+      --src->npages;
+      src->last_lp = pages[size_t(src->list_off + src->npages - 1)];
+      mkv::WorkItem* dst = nullptr;
+      for (mkv::WorkItem& it : tq3)
+        if (it.b == int32_t(b) && (!dst || it.last_lp > dst->last_lp)) dst = &it;
+      if (!dst || dst->npages >= mkv::kMaxChunkPages ||
+          mkv::page_tokens(q.len, P, dst->last_lp) != P || entries.size() + dst->npages + 1 > cap)
+        return false;
+      const int32_t off = int32_t(entries.size());
+      for (int32_t i = 0; i < dst->npages; ++i) {
+        const int32_t e = entries[size_t(dst->list_off + i)], lp = pages[size_t(dst->list_off + i)];
+        entries.push_back(e);
+        pages.push_back(lp);
+      }
+      entries.push_back(q.pt[size_t(dp.lp)]);
+      pages.push_back(dp.lp);
+      dst->list_off = off;
+      dst->npages += 1;
+      dst->last_lp = dp.lp;
+      chunk_pages = std::max(chunk_pages, dst->npages);
+    }
+  }
+  *err = commit_schedule(p, std::move(fp8), std::move(tq3), std::move(entries), std::move(pages),
+                         chunk_pages, 0, s);
+  return *err == MKV_OK;
 }
 
 }  // namespace
@@ -542,6 +622,7 @@ mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, h
   DeviceGuard guard(p->device);
   std::vector<mkv::DemotePage> plan;
   std::string err;
+  const bool lists_current = p->sched_valid && p->sched_layout == p->meta.layout_version();
   int st = p->meta.demote(seq, lps, n, &plan, &err);
   if (st) return set_err(mkv_status(st), err);
   if (plan.empty()) return MKV_OK;
@@ -550,6 +631,8 @@ mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, h
   MKV_HIP(mkv::launch_demote(p->view(),
                              reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan),
                              int32_t(plan.size()), s));
+  // keep the cached schedule current where the moved pages fit it
+  if (lists_current && !demote_in_schedule(p, seq, plan, s, &r) && r) return r;
   return MKV_OK;
 }
 

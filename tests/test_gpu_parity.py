@@ -463,7 +463,9 @@ def test_append_steps_keep_the_cached_schedule_current(B):
     cached schedule's last-page token counts up to date in the same launch (a
     step that opens a page leaves the rebuild to the decode); larger steps take
     the uploaded plan.  The batch repeats sequence 0 and leaves out the last
-    one, and a plain mkv_append between two steps must be picked up too."""
+    one, and a plain mkv_append between two steps must be picked up too.
+    Every fifth step demotes an older FP8 page of sequences 0 and 1, which the
+    cached schedule takes in place where it can."""
     rng = np.random.default_rng(60 + B)
     lengths = tuple(int(x) for x in rng.integers(1, 60, B))
     wl = W.small(seed=61 + B, B=B, Hq=4, Hkv=2, d=64, P=16, lengths=lengths)
@@ -473,6 +475,7 @@ def test_append_steps_keep_the_cached_schedule_current(B):
     models = [OS.seq_model(wl, b) for b in range(B)]
     ids = list(range(B))
     batch = [0] + ids[:-1]
+    n_demoted = 0
     q = H.q_tensor(wl)
     out = torch.empty(B, wl.Hq, wl.d, device="cuda")
     lse = torch.empty(B, wl.Hq, device="cuda")
@@ -486,6 +489,15 @@ def test_append_steps_keep_the_cached_schedule_current(B):
             x = rng.standard_normal((1, wl.Hkv, wl.d)).astype(np.float32)
             mkv.append(pool.handle, 1, torch.from_numpy(x).cuda(), torch.from_numpy(x).cuda())
             models[1].append(x, x)
+        if step % 5 == 3:
+            # demote the oldest FP8 page outside the last two of sequences 0 and 1
+            for sid in (0, 1):
+                pages = models[sid].pages
+                old = [lp for lp, pg in enumerate(pages[:-2]) if pg.fmt == 0]
+                if old:
+                    mkv.demote(pool.handle, sid, np.asarray(old[:1], np.int32))
+                    models[sid].demote(old[0])
+                    n_demoted += 1
         out.fill_(float("nan"))
         lse.fill_(float("nan"))
         mkv.decode(pool.handle, batch, q, float(wl.tau), out, lse)
@@ -496,6 +508,7 @@ def test_append_steps_keep_the_cached_schedule_current(B):
             O[b], L[b] = A.decode_seq(models[sid], wl.q_bits[b], wl.tau)
         _check(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), O, L,
                f"B={B} step {step}")
+    assert n_demoted >= 3
     pool.close()
 
 
