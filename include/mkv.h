@@ -179,6 +179,8 @@ mkv_status mkv_append_step(mkv_pool* pool, const int32_t* seq_ids, int32_t B, co
  * then per 32-group s = fp16(fp32(absmax / 3.5)) (clamped to 65504) and
  * c = #{b in -3..3 : x >= b*s} (c = 4 when s == 0).  Demoting a partially
  * filled last page is allowed; the sequence then accepts no more appends.
+ * The pool's cached decode schedule moves the converted pages from FP8 to
+ * TQ3 work items where it can (else the next decode rebuilds it).
  * MKV_ESTATE in a control pool (n > 0). */
 mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages, int32_t n,
                       hipStream_t stream);
@@ -193,9 +195,11 @@ mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages,
  * each chunk in its own format (FP8 and TQ3 code paths), and a merge kernel
  * combines their (max, denominator, unnormalised accumulator) states (a
  * per-lane merge when no sequence has more than 16 chunks, else a
- * wave-reduced one).  The split-K schedule is rebuilt only when page
- * metadata, the batch or Hq changed since the previous decode; the result of
- * a given schedule is bit-reproducible.
+ * wave-reduced one).  The split-K schedule is cached per pool and rebuilt
+ * only when the batch or Hq changed, or pages changed in a way the pool could
+ * not fold into it (mkv_append_step and mkv_demote edit the cached schedule
+ * for the pages they open or convert where they can; token counts are
+ * patched); the result of a given schedule is bit-reproducible.
  * MKV_EINVAL for B < 1, an id outside [0, max_seqs), an empty sequence, Hq
  * not a multiple of Hkv, Hq / Hkv > 16, or a misaligned q;
  * MKV_ERANGE for B > max_batch or Hq > max_q_heads. */
