@@ -62,27 +62,6 @@ def decode_seq(seq, q_bits, tau32):
     return attend(q, K, V, tau)
 
 
-def decode_heads(seq, q_bits, tau32, heads):
-    """Oracle O, LSE for selected query heads only (for sampled checks at full size)."""
-    q = C.bf16_bits_to_value(q_bits)
-    tau = float(np.float32(tau32))
-    Hq = q.shape[0]
-    G = Hq // seq.Hkv
-    kv_heads = sorted({h // G for h in heads})
-    K, V = seq.dense(heads=kv_heads)
-    O = {}
-    lse = {}
-    for h in heads:
-        j = kv_heads.index(h // G)
-        s = tau * (K[:, j, :] @ q[h])
-        m = np.max(s)
-        w = np.exp(s - m)
-        Ls = np.sum(w)
-        O[h] = (w @ V[:, j, :]) / Ls
-        lse[h] = m + math.log(Ls)
-    return O, lse
-
-
 # --------------------------------------------------------------------------
 # Partial states and the merge
 # --------------------------------------------------------------------------

@@ -360,7 +360,10 @@ def test_bf16_control_dense_and_decode():
     K, V = seq.dense()
     assert np.array_equal(K, k.astype(np.float64)) and np.array_equal(V, v.astype(np.float64))
     assert len(seq.bits) == 3 and seq.ntok == [16, 16, 5]
-    assert PM.bf16_kv_bytes(seq) == L * 4 * Hkv * d
+    # bytes a decode reads: a hand count (37 tokens x 2 kv-heads x K and V x 64
+    # dims x 2 bytes) and the valid bytes of the page records
+    assert PM.bf16_kv_bytes(seq) == 18944
+    assert PM.bf16_kv_bytes(seq) == sum(int(seq.valid_mask(lp).sum()) for lp in range(len(seq.bits)))
     qb = C.bf16_encode(rng.standard_normal((Hq, d)).astype(np.float32))
     O, lse = A.decode_seq(seq, qb, np.float32(0.125))
     O2, lse2 = A.attend(C.bf16_bits_to_value(qb), k.astype(np.float64), v.astype(np.float64), 0.125)
