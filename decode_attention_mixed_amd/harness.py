@@ -3,10 +3,11 @@
 For each sequence of a workload: append all of its fp32 K/V rows as FP8 (in
 one call or in the given splits), then demote every non-anchor page to TQ3,
 the lifecycle the Minima-KV summary describes in "Ancoras em FP8, arquivo em
-TQ3".  The comparison caches of the same summary's "O que foi medido" use the
-same rows: a dense BF16 control pool (append only), and an all-FP8 mixed pool
-(append without demotion).  Pool memory is a torch uint8 tensor, optionally filled with a poison
-byte first so that unwritten slots hold NaN patterns (0x7F is E4M3 NaN and
+TQ3".  The comparison caches of the same summary (section "O que as medicoes
+mostram", subsection "Memoria e compressao") use the same rows: a dense BF16
+control pool (append only), and an all-FP8 mixed pool (append without
+demotion).  Pool memory is a torch uint8 tensor, optionally filled with a
+poison byte first so that unwritten slots hold NaN patterns (0x7F is E4M3 NaN and
 0x7F7F is fp16 NaN).
 """
 from __future__ import annotations

@@ -29,8 +29,9 @@
  *    physical page index in that format's slab.
  *
  * Control pools (kv_kind = MKV_KIND_BF16): the dense single-format cache the
- * summaries measure the mixed cache against (section "O que foi medido":
- * compression relative to BF16 and to FP8; the canary's throughput relative
+ * summaries measure the mixed cache against (section "O que as medicoes
+ * mostram", subsection "Memoria e compressao": compression relative to BF16
+ * and to FP8; section "Verificacao canario": the canary's throughput relative
  * to its control).  Every row is stored as bf16, rounded to nearest even;
  * record [Hkv][2 (K,V)][P][d] bf16, in the slab that holds FP8 pages in a
  * mixed pool (fp8_pages is its capacity, tq3_pages must be 0); page-table
@@ -48,7 +49,13 @@
  *    calls documented as synchronous.  All calls on one pool must be issued
  *    from one host thread, on one stream (or the caller orders the streams).
  *  - A call validates all of its arguments and capacity before it enqueues any
- *    work or changes any metadata: a non-OK status leaves the pool unchanged.
+ *    work or changes any metadata: a non-OK status leaves the pool's metadata
+ *    (lengths, page tables, free pages) unchanged.  When a HIP call fails after
+ *    the metadata was changed (MKV_EHIP from mkv_append, mkv_append_step,
+ *    mkv_demote or mkv_materialize), the change is rolled back; work already
+ *    enqueued before the failing HIP call may still run, but it only writes
+ *    pages and page-table slots the restored metadata does not reference, and
+ *    the cached decode schedule is rebuilt by the next mkv_decode.
  *  - Errors: MKV_EINVAL bad argument, MKV_ENOMEM a slab has too few free
  *    pages, MKV_ESTATE an operation the sequence's state forbids, MKV_ERANGE a
  *    capacity of the pool descriptor is exceeded, MKV_EHIP a HIP runtime

@@ -33,7 +33,8 @@ records in logical order).  With Hkv kv-heads, head dim d and P tokens per page:
 Rows at or beyond the page's valid-token count are unspecified in both formats.
 
 The dense BF16 control cache (Bf16SeqModel) is the single-format baseline of the
-same summary, section "O que foi medido" (compression "em relacao ao BF16"):
+same summary, section "O que as medicoes mostram", subsection "Memoria e
+compressao" (the compression is stated relative to BF16 and to FP8):
 every row stored as bf16, record [Hkv][2 (K, V)][P][d] bf16.
 """
 from __future__ import annotations
@@ -245,8 +246,9 @@ def bf16_record_bytes(Hkv: int, P: int, d: int) -> int:
 @dataclass
 class Bf16SeqModel:
     """A sequence of the dense BF16 control cache: the single-format baseline the
-    summaries compare the mixed cache against ("3,50x de compressao em relacao
-    ao BF16", section "O que foi medido").  Every row is stored as bf16
+    summaries compare the mixed cache against (its compression is given relative
+    to BF16 in section "O que as medicoes mostram", subsection "Memoria e
+    compressao").  Every row is stored as bf16
     (round to nearest even); pages are never converted.
     Record of a page: [Hkv][2 (K, V)][P][d] bf16, little-endian."""
     Hkv: int
