@@ -112,6 +112,46 @@ int mkvh_schedule(mkvh* h, const int32_t* ids, int32_t B, int32_t Hq, int32_t ch
   return 0;
 }
 
+// Builds a schedule (as mkvh_schedule) and checks it with check_schedule.
+int mkvh_check_schedule(mkvh* h, const int32_t* ids, int32_t B, int32_t Hq, int32_t chunk_pages,
+                        int32_t target_waves, int32_t min_items, int32_t* n_chunks) {
+  mkv::SchedPolicy pol;
+  pol.fixed_chunk_pages = chunk_pages > 0 ? chunk_pages : 0;
+  if (target_waves > 0) pol.target_waves = target_waves;
+  pol.min_items = min_items;
+  mkv::Schedule sc;
+  int st = h->meta.build_schedule(ids, B, Hq, pol, &sc, &g_herr);
+  if (st) return st;
+  *n_chunks = sc.n_chunks;
+  return mkv::check_schedule(h->meta, ids, B, sc, &g_herr);
+}
+
+// An append (or demote) that is taken back with its undo record, as the
+// C-ABI does when the device work of the call cannot be enqueued.
+int mkvh_append_rollback(mkvh* h, int32_t seq, int32_t n) {
+  std::vector<mkv::AppendPage> plan;
+  mkv::Undo undo;
+  int st = h->meta.append(seq, n, &plan, &g_herr, &undo);
+  if (!st) h->meta.rollback(undo);
+  return st;
+}
+
+int mkvh_demote_rollback(mkvh* h, int32_t seq, const int32_t* lps, int32_t n) {
+  std::vector<mkv::DemotePage> plan;
+  mkv::Undo undo;
+  int st = h->meta.demote(seq, lps, n, &plan, &g_herr, &undo);
+  if (!st) h->meta.rollback(undo);
+  return st;
+}
+
+int mkvh_append_step_rollback(mkvh* h, const int32_t* ids, int32_t B, int32_t pt_stride) {
+  std::vector<mkv::AppendPage> plan;
+  mkv::Undo undo;
+  int st = h->meta.append_step(ids, B, pt_stride, &plan, &g_herr, &undo);
+  if (!st) h->meta.rollback(undo);
+  return st;
+}
+
 const char* mkvh_last_error(void) { return g_herr.c_str(); }
 
 }  // extern "C"

@@ -388,186 +388,65 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
   DeviceGuard guard(p->device);
   std::vector<mkv::AppendPage> plan;
   std::string err;
-  int st = p->meta.append(seq, n, &plan, &err);
+  mkv::Undo undo;
+  int st = p->meta.append(seq, n, &plan, &err, &undo);
   if (st) return set_err(mkv_status(st), err);
   if (plan.empty()) return MKV_OK;
   mkv_status r = upload_pt_row_and_plan(p, seq, plan.data(), plan.size() * sizeof(plan[0]), s);
-  if (r) return r;
-  const auto* dplan = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
-  if (p->meta.geom().kind == mkv::kKindBf16)
-    MKV_HIP(mkv::launch_append_bf16(p->view(), dplan, int32_t(plan.size()), k, v, s));
-  else
-    MKV_HIP(mkv::launch_append(p->view(), dplan, int32_t(plan.size()), k, v, s));
-  return MKV_OK;
+  if (r == MKV_OK) {
+    const auto* dplan = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
+    const hipError_t e = p->meta.geom().kind == mkv::kKindBf16
+                             ? mkv::launch_append_bf16(p->view(), dplan, int32_t(plan.size()), k, v, s)
+                             : mkv::launch_append(p->view(), dplan, int32_t(plan.size()), k, v, s);
+    if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("append launch: ") + hipGetErrorString(e));
+  }
+  if (r) p->meta.rollback(undo);   // nothing of the append stays in the metadata
+  return r;
 }
 
 namespace {
 
-mkv_status commit_schedule(mkv_pool* p, std::vector<mkv::WorkItem>&& fp8,
-                           std::vector<mkv::WorkItem>&& tq3, std::vector<int32_t>&& entries,
-                           std::vector<int32_t>&& pages, int32_t chunk_pages, size_t from,
-                           hipStream_t s);
-
-// A decode step opened pages: extend the cached schedule instead of leaving a
-// rebuild to the next decode.  For each batch entry of a sequence that got a
-// new page, that entry's last FP8 item (the one ending at the highest logical
-// page) takes the page: its page list is copied, one longer, to the end of
-// the list array, and the items plus the new tail go up in one upload.
-// Returns false, changing nothing, where that does not apply (an entry with
-// no FP8 item, a full chunk, no room left in the list array).
-bool extend_schedule(mkv_pool* p, const int32_t* seq_ids, const std::vector<mkv::AppendPage>& plan,
-                     hipStream_t s, mkv_status* err) {
-  const mkv::Schedule& sc = p->sched;
-  const size_t cap = size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
-  std::vector<mkv::WorkItem> fp8 = sc.items[0];
-  std::vector<int32_t> entries = sc.entries, pages = sc.pages;
-  const size_t old_size = entries.size();
-  int32_t chunk_pages = sc.chunk_pages;
-  for (const mkv::AppendPage& ap : plan) {
-    if (ap.pt_slot < 0) continue;
-    const int32_t seq = seq_ids[ap.src_row];
-    for (size_t b = 0; b < p->sched_ids.size(); ++b) {
-      if (p->sched_ids[b] != seq) continue;
-      mkv::WorkItem* last = nullptr;
-      for (mkv::WorkItem& it : fp8)
-        if (it.b == int32_t(b) && (!last || it.last_lp > last->last_lp)) last = &it;
-      if (!last || last->npages >= mkv::kMaxChunkPages || entries.size() + last->npages + 1 > cap)
-        return false;
-      const int32_t off = int32_t(entries.size());
-      for (int32_t i = 0; i < last->npages; ++i) {
-        const int32_t e = entries[size_t(last->list_off + i)], lp = pages[size_t(last->list_off + i)];
-        entries.push_back(e);
-        pages.push_back(lp);
-      }
-      entries.push_back(ap.pt_entry);
-      pages.push_back(ap.lp);
-      last->list_off = off;
-      last->npages += 1;
-      last->last_lp = ap.lp;
-      chunk_pages = std::max(chunk_pages, last->npages);
-    }
-  }
-  std::vector<mkv::WorkItem> tq3 = sc.items[1];
-  *err = commit_schedule(p, std::move(fp8), std::move(tq3), std::move(entries), std::move(pages),
-                         chunk_pages, old_size, s);
-  return *err == MKV_OK;
-}
-
-// Commits an edited copy of the cached schedule: token counts of every item,
-// then one upload of the items and of the page list from word `from` on.
-mkv_status commit_schedule(mkv_pool* p, std::vector<mkv::WorkItem>&& fp8,
-                           std::vector<mkv::WorkItem>&& tq3, std::vector<int32_t>&& entries,
-                           std::vector<int32_t>&& pages, int32_t chunk_pages, size_t from,
-                           hipStream_t s) {
+// Uploads an edited copy of the cached schedule (the items, and the page list
+// from word `from` on) and makes it the cached one.  On failure the cached
+// schedule is dropped, so the next decode rebuilds it.
+mkv_status commit_schedule(mkv_pool* p, mkv::Schedule&& sc, size_t from, hipStream_t s) {
+  p->sched_valid = false;
   mkv_status err = p->wait_staging();
   if (err) return err;
-  mkv::Schedule& sc = p->sched;
-  sc.items[0] = std::move(fp8);
-  sc.items[1] = std::move(tq3);
-  sc.entries = std::move(entries);
-  sc.pages = std::move(pages);
-  sc.chunk_pages = chunk_pages;
-  const int32_t P = p->meta.geom().P;
   size_t off = 0;
-  for (auto& list : sc.items)
-    for (mkv::WorkItem& it : list) {
-      it.last_ntok = mkv::page_tokens(p->meta.seq(it.seq).len, P, it.last_lp);
+  for (const auto& list : sc.items)
+    for (const mkv::WorkItem& it : list) {
       std::memcpy(p->staging + off, &it, sizeof(it));
       off += sizeof(it);
     }
   const size_t n_items = sc.items[0].size() + sc.items[1].size();
   const size_t tail = (sc.entries.size() - from) * 4;
   std::memcpy(p->staging + off, sc.entries.data() + from, tail);
-  p->sched_valid = false;
   err = flush_uploads(p, {{p->lay.sched + p->lay.items_off, off},
                           {p->lay.sched + entries_off(p->lay, n_items) + from * 4, tail}}, s);
   if (err) return err;
+  p->sched = std::move(sc);
   p->sched_version = p->meta.version();
   p->sched_layout = p->meta.layout_version();
   p->sched_valid = true;
   return MKV_OK;
 }
 
-// Pages of sequence `seq` were demoted: in the cached schedule, each batch
-// entry of the sequence drops every such page from the FP8 item listing it
-// (in place) and its last TQ3 item (highest last page) takes it, its list
-// copied one longer to the end of the list array.  The TQ3 item's previous
-// last page must be full, since only an item's last page may hold fewer
-// tokens.  Returns false, changing nothing, where that does not apply (an FP8
-// item would become empty, an entry with no TQ3 item, a full chunk, no room).
-bool demote_in_schedule(mkv_pool* p, int32_t seq, const std::vector<mkv::DemotePage>& plan,
-                        hipStream_t s, mkv_status* err) {
-  const mkv::Schedule& sc = p->sched;
-  const size_t cap = size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
-  std::vector<mkv::WorkItem> fp8 = sc.items[0], tq3 = sc.items[1];
-  std::vector<int32_t> entries = sc.entries, pages = sc.pages;
-  int32_t chunk_pages = sc.chunk_pages;
-  const mkv::Seq& q = p->meta.seq(seq);
-  const int32_t P = p->meta.geom().P;
-  for (size_t b = 0; b < p->sched_ids.size(); ++b) {
-    if (p->sched_ids[b] != seq) continue;
-    for (const mkv::DemotePage& dp : plan) {
-      mkv::WorkItem* src = nullptr;
-      int32_t at = -1;
-      for (mkv::WorkItem& it : fp8) {
-        if (it.b != int32_t(b)) continue;
-        for (int32_t i = 0; i < it.npages && at < 0; ++i)
-          if (pages[size_t(it.list_off + i)] == dp.lp) at = i;
-        if (at >= 0) {
-          src = &it;
-          break;
-        }
-      }
-      if (!src || src->npages < 2) return false;
-      for (int32_t i = at; i + 1 < src->npages; ++i) {
-        entries[size_t(src->list_off + i)] = entries[size_t(src->list_off + i + 1)];
-        pages[size_t(src->list_off + i)] = pages[size_t(src->list_off + i + 1)];
-      }
-      --src->npages;
-      src->last_lp = pages[size_t(src->list_off + src->npages - 1)];
-      mkv::WorkItem* dst = nullptr;
-      for (mkv::WorkItem& it : tq3)
-        if (it.b == int32_t(b) && (!dst || it.last_lp > dst->last_lp)) dst = &it;
-      if (!dst || dst->npages >= mkv::kMaxChunkPages ||
-          mkv::page_tokens(q.len, P, dst->last_lp) != P || entries.size() + dst->npages + 1 > cap)
-        return false;
-      const int32_t off = int32_t(entries.size());
-      for (int32_t i = 0; i < dst->npages; ++i) {
-        const int32_t e = entries[size_t(dst->list_off + i)], lp = pages[size_t(dst->list_off + i)];
-        entries.push_back(e);
-        pages.push_back(lp);
-      }
-      entries.push_back(q.pt[size_t(dp.lp)]);
-      pages.push_back(dp.lp);
-      dst->list_off = off;
-      dst->npages += 1;
-      dst->last_lp = dp.lp;
-      chunk_pages = std::max(chunk_pages, dst->npages);
-    }
-  }
-  *err = commit_schedule(p, std::move(fp8), std::move(tq3), std::move(entries), std::move(pages),
-                         chunk_pages, 0, s);
-  return *err == MKV_OK;
+size_t list_cap(const mkv_pool* p) {
+  return size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
 }
 
 }  // namespace
 
-mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const float* k,
-                           const float* v, hipStream_t s) {
-  if (!p) return set_err(MKV_EINVAL, "null pool");
-  if (B < 0 || (B > 0 && (!seq_ids || !k || !v))) return set_err(MKV_EINVAL, "null argument");
-  if (B > p->desc.max_batch) return set_err(MKV_ERANGE, "B exceeds max_batch");
-  if (B == 0) return MKV_OK;
-  DeviceGuard guard(p->device);
-  std::vector<mkv::AppendPage> plan;
-  std::string err;
-  const bool lists_current = p->sched_valid && p->sched_layout == p->meta.layout_version();
-  int st = p->meta.append_step(seq_ids, B, p->desc.max_pages_per_seq, &plan, &err);
-  if (st) return set_err(mkv_status(st), err);
-  if (lists_current && p->meta.layout_version() != p->sched_layout) {
-    mkv_status e = MKV_OK;
-    if (!extend_schedule(p, seq_ids, plan, s, &e) && e) return e;
-  }
+namespace {
+
+// The device side of an append step whose metadata is already committed: the
+// append kernel (with the plan in its arguments for small steps, else an
+// uploaded plan).  A small step that opened no page also brings the cached
+// schedule's last-page token counts up to date in the same launch.
+mkv_status append_step_device(mkv_pool* p, const int32_t*, int32_t B,
+                              const std::vector<mkv::AppendPage>& plan, const float* k,
+                              const float* v, hipStream_t s) {
   if (plan.size() <= size_t(mkv::kInlinePages)) {
     // Small step: the plan travels in the kernel arguments.  When the step
     // opened no page and the cached decode schedule predates it only in token
@@ -617,22 +496,70 @@ mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
   return MKV_OK;
 }
 
+}  // namespace
+
+mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const float* k,
+                           const float* v, hipStream_t s) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  if (B < 0 || (B > 0 && (!seq_ids || !k || !v))) return set_err(MKV_EINVAL, "null argument");
+  if (B > p->desc.max_batch) return set_err(MKV_ERANGE, "B exceeds max_batch");
+  if (B == 0) return MKV_OK;
+  DeviceGuard guard(p->device);
+  std::vector<mkv::AppendPage> plan;
+  std::string err;
+  const bool lists_current = p->sched_valid && p->sched_layout == p->meta.layout_version();
+  mkv::Undo undo;
+  int st = p->meta.append_step(seq_ids, B, p->desc.max_pages_per_seq, &plan, &err, &undo);
+  if (st) return set_err(mkv_status(st), err);
+  mkv_status r = append_step_device(p, seq_ids, B, plan, k, v, s);
+  if (r) {
+    p->meta.rollback(undo);
+    return r;
+  }
+  if (lists_current && p->meta.layout_version() != p->sched_layout) {
+    // pages opened: extend the cached schedule where it applies; otherwise
+    // (or if its upload fails) the next decode rebuilds it
+    mkv::Schedule sc = p->sched;
+    if (mkv::schedule_extend(p->meta, p->sched_ids, seq_ids, plan, list_cap(p), &sc)) {
+      const size_t from = p->sched.entries.size();
+      (void)commit_schedule(p, std::move(sc), from, s);
+    } else {
+      p->sched_valid = false;
+    }
+  }
+  return MKV_OK;
+}
+
+
 mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, hipStream_t s) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
   DeviceGuard guard(p->device);
   std::vector<mkv::DemotePage> plan;
   std::string err;
   const bool lists_current = p->sched_valid && p->sched_layout == p->meta.layout_version();
-  int st = p->meta.demote(seq, lps, n, &plan, &err);
+  mkv::Undo undo;
+  int st = p->meta.demote(seq, lps, n, &plan, &err, &undo);
   if (st) return set_err(mkv_status(st), err);
   if (plan.empty()) return MKV_OK;
   mkv_status r = upload_pt_row_and_plan(p, seq, plan.data(), plan.size() * sizeof(plan[0]), s);
-  if (r) return r;
-  MKV_HIP(mkv::launch_demote(p->view(),
-                             reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan),
-                             int32_t(plan.size()), s));
-  // keep the cached schedule current where the moved pages fit it
-  if (lists_current && !demote_in_schedule(p, seq, plan, s, &r) && r) return r;
+  if (r == MKV_OK) {
+    const hipError_t e = mkv::launch_demote(
+        p->view(), reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan), int32_t(plan.size()), s);
+    if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("demote launch: ") + hipGetErrorString(e));
+  }
+  if (r) {
+    p->meta.rollback(undo);
+    return r;
+  }
+  // keep the cached schedule current where the moved pages fit it; otherwise
+  // (or if its upload fails) the next decode rebuilds it
+  if (lists_current) {
+    mkv::Schedule sc = p->sched;
+    if (mkv::schedule_demote(p->meta, p->sched_ids, seq, plan, list_cap(p), &sc))
+      (void)commit_schedule(p, std::move(sc), 0, s);
+    else
+      p->sched_valid = false;
+  }
   return MKV_OK;
 }
 
@@ -650,11 +577,10 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     // stand; refresh each item's last-page token count and upload the items.
     mkv_status r = p->wait_staging();
     if (r) return r;
-    const int32_t P = p->meta.geom().P;
+    mkv::schedule_refresh_tokens(p->meta, &p->sched);
     size_t off = 0;
-    for (auto& list : p->sched.items)
-      for (mkv::WorkItem& it : list) {
-        it.last_ntok = mkv::page_tokens(p->meta.seq(it.seq).len, P, it.last_lp);
+    for (const auto& list : p->sched.items)
+      for (const mkv::WorkItem& it : list) {
         std::memcpy(p->staging + off, &it, sizeof(it));
         off += sizeof(it);
       }
@@ -744,18 +670,22 @@ mkv_status mkv_materialize(mkv_pool* src, int32_t src_seq, mkv_pool* dst, int32_
   DeviceGuard guard(dst->device);
   std::vector<mkv::AppendPage> ap;
   std::string err;
-  int st = dst->meta.append(dst_seq, sq.len, &ap, &err);
+  mkv::Undo undo;
+  int st = dst->meta.append(dst_seq, sq.len, &ap, &err, &undo);
   if (st) return set_err(mkv_status(st), err);
   std::vector<mkv::MaterialisePage> plan;
   plan.reserve(ap.size());
   for (const mkv::AppendPage& a : ap)   // fresh pages: row0 == 0, one per source page
     plan.push_back(mkv::MaterialisePage{a.lp, sq.pt[size_t(a.lp)], a.phys, a.nrows, 0, 0, 0, 0});
   mkv_status r = upload_pt_row_and_plan(dst, dst_seq, plan.data(), plan.size() * sizeof(plan[0]), s);
-  if (r) return r;
-  MKV_HIP(mkv::launch_materialise(src->view(), dst->view(),
-                                  reinterpret_cast<const mkv::MaterialisePage*>(dst->mem + dst->lay.plan),
-                                  int32_t(plan.size()), s));
-  return MKV_OK;
+  if (r == MKV_OK) {
+    const hipError_t e = mkv::launch_materialise(
+        src->view(), dst->view(), reinterpret_cast<const mkv::MaterialisePage*>(dst->mem + dst->lay.plan),
+        int32_t(plan.size()), s);
+    if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("materialise launch: ") + hipGetErrorString(e));
+  }
+  if (r) dst->meta.rollback(undo);
+  return r;
 }
 
 mkv_status mkv_seq_info(mkv_pool* p, int32_t seq, int32_t* len, int32_t* n_pages) {

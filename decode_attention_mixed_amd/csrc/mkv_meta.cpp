@@ -102,7 +102,54 @@ int Meta::check_seq(int32_t s, std::string* err) const {
   return MKV_S_OK;
 }
 
-int Meta::append(int32_t s, int32_t n, std::vector<AppendPage>* plan, std::string* err) {
+void Meta::arm(Undo* u) const {
+  if (!u) return;
+  u->version = version_;
+  u->layout_version = layout_version_;
+  for (int f = 0; f < 2; ++f) {
+    u->free_size[f] = free_[f].size();
+    u->popped[f].clear();
+  }
+  u->lens.clear();
+  u->entries.clear();
+  u->armed = true;
+}
+
+int32_t Meta::take(int f, Undo* u) {
+  const int32_t v = free_[f].pop();
+  if (u) u->popped[f].push_back(v);
+  return v;
+}
+
+void Meta::note_seq(Undo* u, int32_t s, const Seq& q) {
+  if (!u) return;
+  for (const Undo::SeqLen& x : u->lens)
+    if (x.seq == s) return;
+  u->lens.push_back(Undo::SeqLen{s, q.len, int32_t(q.pt.size())});
+}
+
+void Meta::rollback(const Undo& u) {
+  if (!u.armed) return;
+  for (size_t i = u.entries.size(); i-- > 0;) {
+    const Undo::Entry& e = u.entries[i];
+    seqs_[size_t(e.seq)].pt[size_t(e.lp)] = e.entry;
+  }
+  for (const Undo::SeqLen& x : u.lens) {
+    Seq& q = seqs_[size_t(x.seq)];
+    q.len = x.len;
+    q.pt.resize(size_t(x.npages));
+  }
+  for (int f = 0; f < 2; ++f) {
+    // the untouched bottom of the stack, then the taken pages in reverse pop order
+    free_[f].truncate(u.free_size[f] - int64_t(u.popped[f].size()));
+    for (size_t i = u.popped[f].size(); i-- > 0;) free_[f].push(u.popped[f][i]);
+  }
+  version_ = u.version;
+  layout_version_ = u.layout_version;
+}
+
+int Meta::append(int32_t s, int32_t n, std::vector<AppendPage>* plan, std::string* err,
+                 Undo* undo) {
   plan->clear();
   int st = check_seq(s, err);
   if (st) return st;
@@ -119,7 +166,9 @@ int Meta::append(int32_t s, int32_t n, std::vector<AppendPage>* plan, std::strin
   int64_t fresh = need - int64_t(q.pt.size());
   if (fresh > free_[0].size()) return fail(err, MKV_S_ENOMEM, "FP8 slab has too few free pages");
   // Commit.
-  for (int64_t i = 0; i < fresh; ++i) q.pt.push_back(pt_make(0, free_[0].pop()));
+  arm(undo);
+  note_seq(undo, s, q);
+  for (int64_t i = 0; i < fresh; ++i) q.pt.push_back(pt_make(0, take(0, undo)));
   int32_t pos = q.len;
   int32_t src = 0;
   while (src < n) {
@@ -137,7 +186,7 @@ int Meta::append(int32_t s, int32_t n, std::vector<AppendPage>* plan, std::strin
 }
 
 int Meta::append_step(const int32_t* ids, int32_t B, int32_t pt_stride,
-                      std::vector<AppendPage>* plan, std::string* err) {
+                      std::vector<AppendPage>* plan, std::string* err, Undo* undo) {
   plan->clear();
   if (B < 0 || (B > 0 && !ids)) return fail(err, MKV_S_EINVAL, "bad sequence list");
   // validate everything first
@@ -160,12 +209,14 @@ int Meta::append_step(const int32_t* ids, int32_t B, int32_t pt_stride,
   }
   if (fresh > free_[0].size()) return fail(err, MKV_S_ENOMEM, "FP8 slab has too few free pages");
   // commit
+  arm(undo);
   for (int32_t b = 0; b < B; ++b) {
     Seq& q = seqs_[size_t(ids[b])];
+    note_seq(undo, ids[b], q);
     const int32_t row0 = q.len % g_.P;
     int32_t slot = -1, entry = 0;
     if (row0 == 0) {
-      q.pt.push_back(pt_make(0, free_[0].pop()));
+      q.pt.push_back(pt_make(0, take(0, undo)));
       slot = ids[b] * pt_stride + int32_t(q.pt.size()) - 1;
       entry = q.pt.back();
     }
@@ -179,7 +230,7 @@ int Meta::append_step(const int32_t* ids, int32_t B, int32_t pt_stride,
 }
 
 int Meta::demote(int32_t s, const int32_t* lps, int32_t n, std::vector<DemotePage>* plan,
-                 std::string* err) {
+                 std::string* err, Undo* undo) {
   plan->clear();
   int st = check_seq(s, err);
   if (st) return st;
@@ -197,10 +248,12 @@ int Meta::demote(int32_t s, const int32_t* lps, int32_t n, std::vector<DemotePag
     if (pt_is_tq3(q.pt[size_t(lp)])) return fail(err, MKV_S_ESTATE, "page is already TQ3");
   }
   if (n > free_[1].size()) return fail(err, MKV_S_ENOMEM, "TQ3 slab has too few free pages");
+  arm(undo);
   for (int32_t i = 0; i < n; ++i) {
     int32_t lp = lps[i];
     int32_t src = pt_index(q.pt[size_t(lp)]);
-    int32_t dst = free_[1].pop();
+    int32_t dst = take(1, undo);
+    if (undo) undo->entries.push_back(Undo::Entry{s, lp, q.pt[size_t(lp)]});
     q.pt[size_t(lp)] = pt_make(1, dst);
     free_[0].push(src);
     plan->push_back(DemotePage{lp, src, dst, page_tokens(q.len, g_.P, lp), 0, 0, 0, 0});
@@ -266,7 +319,8 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     return fail(err, MKV_S_EINVAL, "unsupported kv-heads per wave");
   const int64_t waves_per_item =
       int64_t(kWavesPerWorkgroup) * ((g_.Hkv + heads_per_block - 1) / heads_per_block);
-  const int64_t target_items = std::max<int64_t>(1, pol.target_waves / waves_per_item);
+  const int64_t target_items =
+      std::max<int64_t>({int64_t(1), pol.target_waves / waves_per_item, int64_t(pol.min_items)});
   double budget = std::max(1.0, total_cost / double(target_items));
   std::vector<int64_t> k8(static_cast<size_t>(B)), k3(static_cast<size_t>(B));
   int64_t count = 0;
@@ -398,6 +452,156 @@ int64_t Meta::live_pages(int fmt) const {
   for (const Seq& q : seqs_)
     for (int32_t e : q.pt) t += (int(pt_is_tq3(e)) == fmt);
   return t;
+}
+
+
+// ---- edits of a cached decode schedule ----------------------------------------
+
+void schedule_refresh_tokens(const Meta& m, Schedule* sc) {
+  const int32_t P = m.geom().P;
+  for (auto& list : sc->items)
+    for (WorkItem& it : list) it.last_ntok = page_tokens(m.seq(it.seq).len, P, it.last_lp);
+}
+
+namespace {
+
+// Copies item `it`'s page list to the end of the list arrays, one page longer
+// (the new last page is (lp, entry)).
+void grow_item(Schedule& sc, WorkItem& it, int32_t lp, int32_t entry) {
+  const int32_t off = int32_t(sc.entries.size());
+  for (int32_t i = 0; i < it.npages; ++i) {
+    const int32_t e = sc.entries[size_t(it.list_off + i)], p = sc.pages[size_t(it.list_off + i)];
+    sc.entries.push_back(e);
+    sc.pages.push_back(p);
+  }
+  sc.entries.push_back(entry);
+  sc.pages.push_back(lp);
+  it.list_off = off;
+  it.npages += 1;
+  it.last_lp = lp;
+  sc.chunk_pages = std::max(sc.chunk_pages, it.npages);
+}
+
+}  // namespace
+
+bool schedule_extend(const Meta& m, const std::vector<int32_t>& ids, const int32_t* ids_of_rows,
+                     const std::vector<AppendPage>& plan, size_t list_cap, Schedule* out) {
+  Schedule sc = *out;
+  for (const AppendPage& ap : plan) {
+    if (ap.pt_slot < 0) continue;
+    const int32_t seq = ids_of_rows[ap.src_row];
+    for (size_t b = 0; b < ids.size(); ++b) {
+      if (ids[b] != seq) continue;
+      WorkItem* last = nullptr;
+      for (WorkItem& it : sc.items[0])
+        if (it.b == int32_t(b) && (!last || it.last_lp > last->last_lp)) last = &it;
+      if (!last || last->npages >= kMaxChunkPages || sc.entries.size() + size_t(last->npages) + 1 > list_cap)
+        return false;
+      grow_item(sc, *last, ap.lp, ap.pt_entry);
+    }
+  }
+  schedule_refresh_tokens(m, &sc);
+  *out = std::move(sc);
+  return true;
+}
+
+bool schedule_demote(const Meta& m, const std::vector<int32_t>& ids, int32_t seq,
+                     const std::vector<DemotePage>& plan, size_t list_cap, Schedule* out) {
+  Schedule sc = *out;
+  const Seq& q = m.seq(seq);
+  const int32_t P = m.geom().P;
+  for (size_t b = 0; b < ids.size(); ++b) {
+    if (ids[b] != seq) continue;
+    for (const DemotePage& dp : plan) {
+      WorkItem* src = nullptr;
+      int32_t at = -1;
+      for (WorkItem& it : sc.items[0]) {
+        if (it.b != int32_t(b)) continue;
+        for (int32_t i = 0; i < it.npages && at < 0; ++i)
+          if (sc.pages[size_t(it.list_off + i)] == dp.lp) at = i;
+        if (at >= 0) {
+          src = &it;
+          break;
+        }
+      }
+      if (!src || src->npages < 2) return false;
+      for (int32_t i = at; i + 1 < src->npages; ++i) {
+        sc.entries[size_t(src->list_off + i)] = sc.entries[size_t(src->list_off + i + 1)];
+        sc.pages[size_t(src->list_off + i)] = sc.pages[size_t(src->list_off + i + 1)];
+      }
+      --src->npages;
+      src->last_lp = sc.pages[size_t(src->list_off + src->npages - 1)];
+      WorkItem* dst = nullptr;
+      for (WorkItem& it : sc.items[1])
+        if (it.b == int32_t(b) && (!dst || it.last_lp > dst->last_lp)) dst = &it;
+      if (!dst || dst->npages >= kMaxChunkPages || page_tokens(q.len, P, dst->last_lp) != P ||
+          sc.entries.size() + size_t(dst->npages) + 1 > list_cap)
+        return false;
+      grow_item(sc, *dst, dp.lp, q.pt[size_t(dp.lp)]);
+    }
+  }
+  schedule_refresh_tokens(m, &sc);
+  *out = std::move(sc);
+  return true;
+}
+
+int check_schedule(const Meta& m, const int32_t* ids, int32_t B, const Schedule& sc,
+                   std::string* why) {
+  auto bad = [&](const std::string& msg) { return fail(why, MKV_S_EINVAL, msg.c_str()); };
+  if (B < 1 || int32_t(sc.chunk_base.size()) != B + 1 || sc.chunk_base[0] != 0)
+    return bad("chunk_base must hold B + 1 offsets starting at 0");
+  for (int32_t b = 0; b < B; ++b)
+    if (sc.chunk_base[size_t(b) + 1] < sc.chunk_base[size_t(b)]) return bad("chunk_base decreases");
+  if (sc.chunk_base[size_t(B)] != sc.n_chunks) return bad("chunk_base does not end at n_chunks");
+  if (sc.entries.size() != sc.pages.size()) return bad("entries and pages differ in length");
+  const int32_t P = m.geom().P;
+  std::vector<char> slot_seen(size_t(std::max(0, sc.n_chunks)), 0);
+  std::vector<std::vector<int32_t>> seen(static_cast<size_t>(B));   // per entry: times each page is listed
+  std::vector<int32_t> items_of(size_t(B), 0);
+  for (int32_t b = 0; b < B; ++b) seen[size_t(b)].assign(m.seq(ids[b]).pt.size(), 0);
+  int32_t largest = 0;
+  for (int f = 0; f < 2; ++f) {
+    for (const WorkItem& it : sc.items[f]) {
+      const std::string at = "item of entry " + std::to_string(it.b) + " chunk " + std::to_string(it.chunk);
+      if (it.b < 0 || it.b >= B || it.seq != ids[it.b]) return bad(at + ": wrong batch entry or sequence");
+      if (it.fmt != f) return bad(at + ": format differs from its list");
+      if (it.npages < 1 || it.npages > kMaxChunkPages) return bad(at + ": page count out of range");
+      if (it.list_off < 0 || size_t(it.list_off) + size_t(it.npages) > sc.pages.size())
+        return bad(at + ": page list outside the arrays");
+      if (it.chunk < sc.chunk_base[size_t(it.b)] || it.chunk >= sc.chunk_base[size_t(it.b) + 1])
+        return bad(at + ": partial-state slot outside its entry's range");
+      if (slot_seen[size_t(it.chunk)]++) return bad(at + ": partial-state slot used twice");
+      items_of[size_t(it.b)]++;
+      largest = std::max(largest, it.npages);
+      const Seq& q = m.seq(it.seq);
+      for (int32_t i = 0; i < it.npages; ++i) {
+        const int32_t lp = sc.pages[size_t(it.list_off + i)];
+        if (lp < 0 || size_t(lp) >= q.pt.size()) return bad(at + ": logical page out of range");
+        if (sc.entries[size_t(it.list_off + i)] != q.pt[size_t(lp)])
+          return bad(at + ": entry differs from the page table at page " + std::to_string(lp));
+        if (int(pt_is_tq3(q.pt[size_t(lp)])) != f) return bad(at + ": page of the other format");
+        if (i + 1 < it.npages && page_tokens(q.len, P, lp) != P)
+          return bad(at + ": a page before the item's last is not full");
+        seen[size_t(it.b)][size_t(lp)]++;
+      }
+      const int32_t last = sc.pages[size_t(it.list_off + it.npages - 1)];
+      if (last != it.last_lp) return bad(at + ": last_lp is not the last listed page");
+      if (it.last_ntok != page_tokens(q.len, P, last)) return bad(at + ": last_ntok is stale");
+    }
+  }
+  int32_t most = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    for (size_t lp = 0; lp < seen[size_t(b)].size(); ++lp)
+      if (seen[size_t(b)][lp] != 1)
+        return bad("entry " + std::to_string(b) + " lists page " + std::to_string(lp) + " " +
+                   std::to_string(seen[size_t(b)][lp]) + " times");
+    const int32_t n = sc.chunk_base[size_t(b) + 1] - sc.chunk_base[size_t(b)];
+    if (n != items_of[size_t(b)]) return bad("entry " + std::to_string(b) + " has slots without items");
+    most = std::max(most, n);
+  }
+  if (sc.max_seq_chunks != most) return bad("max_seq_chunks is wrong");
+  if (sc.chunk_pages < largest) return bad("chunk_pages is below the largest item");
+  return MKV_S_OK;
 }
 
 }  // namespace mkv

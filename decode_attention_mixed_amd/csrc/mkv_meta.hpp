@@ -58,6 +58,9 @@ class FreeList {
   int64_t size() const { return int64_t(stack_.size()); }
   int32_t pop() { int32_t v = stack_.back(); stack_.pop_back(); return v; }
   void push(int32_t v) { stack_.push_back(v); }
+  // The page pop() would return k calls from now (k < size()).
+  int32_t peek(int64_t k) const { return stack_[stack_.size() - 1 - size_t(k)]; }
+  void truncate(int64_t n) { stack_.resize(size_t(n)); }
  private:
   std::vector<int32_t> stack_;
 };
@@ -111,12 +114,14 @@ inline int32_t heads_per_wave(int32_t d, int32_t Hkv, int32_t G) {
 // into near-equal chunks so that all items of a batch cost about the same and
 // together they fill the partial kernel's resident waves once (an item takes
 // ceil(Hkv / kWavesPerWorkgroup) workgroups); an FP8 page counts
-// fp8_page_cost TQ3 pages.  A
+// fp8_page_cost TQ3 pages.  min_items raises that count (a split-K floor:
+// more, shorter chunks) as far as min_chunk_pages allows.  A
 // nonzero fixed_chunk_pages cuts every list into chunks of exactly that many
 // pages instead (the last one shorter).  Chunks grow when a batch would need
 // more than max_chunks of them; no chunk exceeds kMaxChunkPages.
 struct SchedPolicy {
   int32_t target_waves = 2048;   // resident partial-kernel waves on the device
+  int32_t min_items = 0;         // at least this many items per batch when the pages allow
   int32_t min_chunk_pages = 4;   // smallest balanced chunk (shorter lists stay whole)
   int32_t fixed_chunk_pages = 0; // 0: balanced chunks
   int32_t heads_per_wave = 0;    // kv-heads per partial-kernel workgroup; 0: heads_per_wave()
@@ -134,6 +139,25 @@ struct Schedule {
   int32_t max_seq_chunks = 0;       // most chunks of one batch entry
 };
 
+// What a mutating Meta call changed, recorded so that the caller can take the
+// call back when the device work that goes with it cannot be enqueued (the
+// C-ABI promises that a failed call leaves the pool unchanged).  Within one
+// call a free list is either only popped or only pushed.
+struct Undo {
+  struct SeqLen {
+    int32_t seq, len, npages;
+  };
+  struct Entry {
+    int32_t seq, lp, entry;
+  };
+  uint64_t version = 0, layout_version = 0;
+  int64_t free_size[2] = {0, 0};
+  std::vector<int32_t> popped[2];   // pages taken from each free list, in pop order
+  std::vector<SeqLen> lens;         // first recorded state of each touched sequence
+  std::vector<Entry> entries;       // page-table entries overwritten, in order
+  bool armed = false;
+};
+
 class Meta {
  public:
   int init(const Desc& d, std::string* err);
@@ -146,19 +170,25 @@ class Meta {
   // valid up to the items' last_ntok.
   uint64_t layout_version() const { return layout_version_; }
   const Seq& seq(int32_t s) const { return seqs_[size_t(s)]; }
+  const FreeList& free_list(int fmt) const { return free_[fmt ? 1 : 0]; }
   int64_t fp8_free() const { return free_[0].size(); }
   int64_t tq3_free() const { return free_[1].size(); }
 
-  // Each call validates everything first; on failure nothing changes.
-  int append(int32_t seq, int32_t n, std::vector<AppendPage>* plan, std::string* err);
+  // Each call validates everything first; on failure nothing changes.  With
+  // an Undo record, a successful call also records what it changed, and
+  // rollback() restores the state before the call (valid only while no other
+  // mutating call has run since).
+  int append(int32_t seq, int32_t n, std::vector<AppendPage>* plan, std::string* err,
+             Undo* undo = nullptr);
   // One token to each of B distinct sequences (row b to seq_ids[b]), all or
   // nothing; plan entries take src_row = b, and a page opened by the step
   // carries its page-table slot (seq * pt_stride + lp) and entry.
   int append_step(const int32_t* seq_ids, int32_t B, int32_t pt_stride,
-                  std::vector<AppendPage>* plan, std::string* err);
+                  std::vector<AppendPage>* plan, std::string* err, Undo* undo = nullptr);
   int demote(int32_t seq, const int32_t* lps, int32_t n, std::vector<DemotePage>* plan,
-             std::string* err);
+             std::string* err, Undo* undo = nullptr);
   int reset(int32_t seq, std::string* err);
+  void rollback(const Undo& u);
 
   int build_schedule(const int32_t* seq_ids, int32_t B, int32_t Hq, const SchedPolicy& pol,
                      Schedule* out, std::string* err) const;
@@ -172,6 +202,9 @@ class Meta {
 
  private:
   int check_seq(int32_t s, std::string* err) const;
+  void arm(Undo* u) const;
+  int32_t take(int f, Undo* u);
+  static void note_seq(Undo* u, int32_t s, const Seq& q);
   Desc d_{};
   Geom g_{};
   FreeList free_[2];
@@ -185,5 +218,43 @@ inline int32_t page_tokens(int32_t len, int32_t P, int32_t lp) {
   int32_t rest = len - lp * P;
   return rest < P ? rest : P;
 }
+
+// ---- edits of a cached decode schedule ------------------------------------
+// A schedule built for batch `ids` stays usable across calls that change the
+// cache, when it is brought up to date instead of rebuilt.  Each function
+// edits *sc in place and returns true, or returns false and leaves *sc as it
+// was when the edit does not apply (the caller then rebuilds).  list_cap is
+// the room of the device copy's page-list array (entries).
+
+// Every item's last-page token count from the sequences' current lengths.
+void schedule_refresh_tokens(const Meta& m, Schedule* sc);
+
+// Pages were opened by an append step (plan rows src_row -> ids_of_rows):
+// for each batch entry of a sequence that got a page, its last FP8 item (the
+// one ending at the highest logical page) takes the page; its list is copied,
+// one longer, to the end of the list array.  Does not apply to an entry with
+// no FP8 item, a full chunk, or no room left.
+bool schedule_extend(const Meta& m, const std::vector<int32_t>& ids, const int32_t* ids_of_rows,
+                     const std::vector<AppendPage>& plan, size_t list_cap, Schedule* sc);
+
+// Pages of sequence seq were demoted: in each batch entry of the sequence the
+// FP8 item listing a page drops it in place, and the entry's last TQ3 item
+// (highest last page) takes it, its list copied one longer to the end of the
+// list array.  That TQ3 item's previous last page must be full (only an
+// item's last page may hold fewer tokens).  Does not apply when an FP8 item
+// would become empty, an entry has no TQ3 item, a chunk is full or there is no
+// room.
+bool schedule_demote(const Meta& m, const std::vector<int32_t>& ids, int32_t seq,
+                     const std::vector<DemotePage>& plan, size_t list_cap, Schedule* sc);
+
+// Checks that sc is a valid decode schedule of batch ids for the current
+// metadata: chunk_base partitions the partial-state slots by batch entry;
+// every item lists 1..kMaxChunkPages pages of its sequence in its format, with
+// their current page-table entries, ends at last_lp with last_ntok tokens and
+// has full pages before that; every live page of each batch entry appears in
+// exactly one of the entry's items.  Returns MKV_OK or MKV_EINVAL with the
+// first violation in *why.
+int check_schedule(const Meta& m, const int32_t* ids, int32_t B, const Schedule& sc,
+                   std::string* why);
 
 }  // namespace mkv

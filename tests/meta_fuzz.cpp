@@ -1,45 +1,98 @@
 // Randomised exercise of the host metadata layer, built with ASan/UBSan by
-// tests/test_host_meta.py.  Checks invariants after every operation: every
-// physical page is either free or owned by exactly one live logical page, and
-// every schedule covers every live page exactly once.
+// tests/test_host_meta.py.  After every operation it checks that every
+// physical page is either free or owned by exactly one live logical page.
+// It also checks schedules:
+//  * every schedule the builder returns passes check_schedule: each live page
+//    of each batch entry is listed once, with its current page-table entry;
+//  * a cached schedule kept current by the edit functions passes as well,
+//    after append steps that open pages and after demotions.
+// It also takes random calls back with their undo record and compares the
+// whole state with a copy taken before the call.
 #include <cstdio>
 #include <cstdlib>
 #include <random>
+#include <string>
 #include <vector>
 
 #include "mkv_meta.hpp"
 
 using namespace mkv;
 
-static void die(const char* m) {
-  std::printf("FAIL: %s\n", m);
+static void die(const char* m, const std::string& why = "") {
+  std::printf("FAIL: %s %s\n", m, why.c_str());
   std::exit(1);
+}
+
+static bool same_state(const Meta& a, const Meta& b, int max_seqs) {
+  if (a.version() != b.version() || a.layout_version() != b.layout_version()) return false;
+  for (int f = 0; f < 2; ++f) {
+    const FreeList& x = a.free_list(f);
+    const FreeList& y = b.free_list(f);
+    if (x.size() != y.size()) return false;
+    for (int64_t k = 0; k < x.size(); ++k)
+      if (x.peek(k) != y.peek(k)) return false;
+  }
+  for (int s = 0; s < max_seqs; ++s)
+    if (a.seq(s).len != b.seq(s).len || a.seq(s).pt != b.seq(s).pt) return false;
+  return true;
 }
 
 int main() {
   std::mt19937_64 rng(12345);
-  Desc d{4, 64, 16, 6, 40, 6, 16, 0, 60, 50, 99};
+  Desc d{4, 64, 16, 6, 40, 6, 16, 0, 60, 50, 99, 0};
   Meta m;
   std::string err;
   if (m.init(d, &err)) die(err.c_str());
-  for (int step = 0; step < 20000; ++step) {
-    int op = int(rng() % 10);
-    int s = int(rng() % 7) - (rng() % 20 == 0 ? 1 : 0);  // occasionally invalid ids
-    if (op < 5) {
+  const size_t list_cap = size_t(d.max_batch) * size_t(d.max_pages_per_seq);
+  // a cached schedule for a batch, kept current by the edit functions
+  std::vector<int32_t> cached_ids;
+  Schedule cached;
+  bool cached_ok = false;
+  int edits_applied = 0, rollbacks = 0;
+  for (int step = 0; step < 100000; ++step) {
+    const int op = int(rng() % 12);
+    const int s = int(rng() % 7) - (rng() % 20 == 0 ? 1 : 0);  // occasionally invalid ids
+    const bool take_back = rng() % 4 == 0;
+    Meta before = take_back ? m : Meta();
+    Undo undo;
+    int st = -1;
+    if (op < 4) {
       std::vector<AppendPage> plan;
-      int n = int(rng() % 70) - 2;
-      m.append(s, n, &plan, &err);
-    } else if (op < 8) {
+      st = m.append(s, int(rng() % 70) - 2, &plan, &err, &undo);
+      if (st == 0 && !undo.popped[0].empty()) cached_ok = false;   // pages opened: rebuild
+      if (cached_ok) schedule_refresh_tokens(m, &cached);
+    } else if (op < 6) {
+      // one token to each of a few distinct sequences
+      std::vector<int32_t> ids;
+      for (int q = 0; q < d.max_seqs; ++q)
+        if (rng() % 2) ids.push_back(q);
+      if (ids.empty()) continue;
+      const uint64_t lay0 = m.layout_version();
+      std::vector<AppendPage> plan;
+      st = m.append_step(ids.data(), int32_t(ids.size()), d.max_pages_per_seq, &plan, &err, &undo);
+      if (st == 0 && cached_ok && m.layout_version() != lay0) {
+        cached_ok = schedule_extend(m, cached_ids, ids.data(), plan, list_cap, &cached);
+        edits_applied += cached_ok;
+      } else if (st == 0 && cached_ok) {
+        schedule_refresh_tokens(m, &cached);
+      }
+    } else if (op < 9) {
       if (s < 0 || s >= d.max_seqs) continue;
-      int np = int(m.seq(s).pt.size());
+      const int np = int(m.seq(s).pt.size());
       std::vector<int32_t> lps;
       for (int i = 0; i < np; ++i)
         if (rng() % 3 == 0) lps.push_back(i);
       if (rng() % 10 == 0) lps.push_back(np + 1);
       std::vector<DemotePage> plan;
-      m.demote(s, lps.data(), int32_t(lps.size()), &plan, &err);
-    } else if (op == 8) {
+      st = m.demote(s, lps.data(), int32_t(lps.size()), &plan, &err, &undo);
+      if (st == 0 && cached_ok && !plan.empty()) {
+        cached_ok = schedule_demote(m, cached_ids, s, plan, list_cap, &cached);
+        edits_applied += cached_ok;
+      }
+    } else if (op == 9) {
       m.reset(s, &err);
+      cached_ok = false;
+      continue;
     } else {
       std::vector<int32_t> ids;
       for (int i = 0; i < 1 + int(rng() % 6); ++i) ids.push_back(int32_t(rng() % 6));
@@ -47,16 +100,25 @@ int main() {
       SchedPolicy pol;
       pol.fixed_chunk_pages = int(rng() % 9);          // 0: balanced chunks
       pol.target_waves = 1 + int(rng() % 4096);
+      pol.min_items = int(rng() % 300);
       pol.fp8_page_cost = 0.25f + float(rng() % 8);
       if (m.build_schedule(ids.data(), int32_t(ids.size()), 16, pol, &sc, &err) == 0) {
-        size_t total = 0;
-        for (int32_t id : ids) total += m.seq(id).pt.size();
-        size_t covered = 0;
-        for (int f = 0; f < 2; ++f)
-          for (const WorkItem& it : sc.items[f]) covered += size_t(it.npages);
-        if (covered != total) die("schedule coverage");
+        if (check_schedule(m, ids.data(), int32_t(ids.size()), sc, &err)) die("built schedule", err);
+        cached_ids = ids;
+        cached = sc;
+        cached_ok = true;
       }
+      continue;
     }
+    if (take_back && st == 0) {
+      m.rollback(undo);
+      ++rollbacks;
+      if (!same_state(m, before, d.max_seqs)) die("rollback did not restore the state");
+      cached_ok = false;
+    }
+    if (cached_ok &&
+        check_schedule(m, cached_ids.data(), int32_t(cached_ids.size()), cached, &err))
+      die("edited schedule", err);
     // ownership invariant
     std::vector<int> own8(size_t(d.fp8_pages), 0), own3(size_t(d.tq3_pages), 0);
     for (int q = 0; q < d.max_seqs; ++q)
@@ -73,6 +135,7 @@ int main() {
     if (used8 + m.fp8_free() != d.fp8_pages) die("fp8 page leak");
     if (used3 + m.tq3_free() != d.tq3_pages) die("tq3 page leak");
   }
-  std::printf("ok\n");
+  if (edits_applied < 50 || rollbacks < 100) die("too few schedule edits or rollbacks exercised");
+  std::printf("ok (%d schedule edits, %d rollbacks)\n", edits_applied, rollbacks);
   return 0;
 }

@@ -36,6 +36,10 @@ def lib():
     L.mkvh_layout_version.argtypes = [P]
     L.mkvh_layout_version.restype = ctypes.c_uint64
     L.mkvh_schedule.argtypes = [P, P, I32, I32, I32, I32, P, I32, P, I32, P, P]
+    L.mkvh_check_schedule.argtypes = [P, P, I32, I32, I32, I32, I32, ctypes.POINTER(I32)]
+    L.mkvh_append_rollback.argtypes = [P, I32, I32]
+    L.mkvh_demote_rollback.argtypes = [P, I32, P, I32]
+    L.mkvh_append_step_rollback.argtypes = [P, P, I32, I32]
     L.mkvh_last_error.restype = ctypes.c_char_p
     return L
 
@@ -405,3 +409,52 @@ def test_layout_version_moves_only_when_pages_change(lib):
     v6, l6 = ver()
     assert v6 > v5 and l6 > l5
     h.close()
+
+
+# ------------------------------------------------------------ schedule checks and rollback
+def test_built_schedules_pass_the_checker(lib):
+    """check_schedule (the invariant the sanitizer fuzz also applies to edited
+    schedules) accepts every schedule the builder makes: ragged batches,
+    repeated sequences, fixed and balanced chunks, split-K floors."""
+    rng = np.random.default_rng(3)
+    h = _host(lib, num_kv_heads=8, max_seqs=8, max_pages_per_seq=600, max_batch=8,
+              max_q_heads=32, fp8_pages=4096, tq3_pages=4096, placement_seed=11)
+    for s in range(6):
+        L = int(rng.integers(1, 9000))
+        assert h.append(s, L)[0] == OK
+        n = -(-L // 16)
+        assert h.demote(s, [p for p in range(n) if rng.random() < 0.7])[0] == OK
+    n = ctypes.c_int32()
+    for ids in ([0], [1, 2, 3], [5, 5, 0], [0, 1, 2, 3, 4, 5]):
+        arr = np.asarray(ids, np.int32)
+        for cp, waves, floor in ((0, 2048, 0), (0, 4096, 256), (3, 0, 0), (0, 64, 1000), (0, 100000, 0)):
+            st = h.L.mkvh_check_schedule(h.h, arr.ctypes.data, arr.size, 32, cp, waves, floor, ctypes.byref(n))
+            assert st == OK, h.L.mkvh_last_error()
+    h.close()
+
+
+def test_rolled_back_calls_leave_no_trace(lib):
+    """A call taken back with its undo record (what the C-ABI does when the
+    call's device work cannot be enqueued) leaves page tables, lengths and free
+    lists as they were: the next call hands out the very same pages."""
+    def state(h):
+        return ([h.pt(s).tolist() for s in range(4)], [h.L.mkvh_seq_len(h.h, s) for s in range(4)],
+                h.free(0), h.free(1), h.L.mkvh_version(h.h), h.L.mkvh_layout_version(h.h))
+    a = _host(lib, fp8_pages=60, tq3_pages=60, placement_seed=9, max_seqs=4)
+    b = _host(lib, fp8_pages=60, tq3_pages=60, placement_seed=9, max_seqs=4)
+    for h in (a, b):
+        assert h.append(0, 40)[0] == OK and h.append(1, 3)[0] == OK
+    s0 = state(a)
+    assert a.L.mkvh_append_rollback(a.h, 0, 100) == OK
+    assert a.L.mkvh_append_step_rollback(a.h, np.asarray([1, 2, 0], np.int32).ctypes.data, 3, 64) == OK
+    lps = np.asarray([0, 2], np.int32)
+    assert a.L.mkvh_demote_rollback(a.h, 0, lps.ctypes.data, 2) == OK
+    assert state(a) == s0
+    # the same calls made for real on both pools now give identical results
+    for h in (a, b):
+        assert h.append(0, 100)[0] == OK
+        assert h.demote(0, [0, 2])[0] == OK
+        assert h.append_step([1, 2, 0])[0] == OK
+    assert state(a) == state(b)
+    a.close()
+    b.close()
