@@ -324,6 +324,8 @@ def main():
 
     pools, mixed_stats = build("mixed")
     warm(pools)
+    sched = mkv.debug_schedule(pools[0].handle, arrays=False)
+    log(f"decode schedule: {sched}")
     # Timed region 1: the step as a caller sees it (no library events).
     ms, host_s = timed_steps(pools)
     # Timed region 2: the same steps with the library's per-kernel HIP events
@@ -518,6 +520,10 @@ def main():
             "kv_bytes_per_step": step_bytes,
             "kv_bytes_fp8": fp8_b,
             "kv_bytes_tq3": tq3_b,
+            "split_k": {"chunks": sched["n_chunks"], "work_items": sched["n_items"],
+                        "most_chunks_per_entry": sched["max_seq_chunks"],
+                        "kv_heads_per_workgroup": sched["heads_per_wave"],
+                        "resident_waves": sched["resident_waves"]},
             "replicas_rotated": R,
             "kernel_us": {k: round(v * 1e3, 3) for k, v in kernel_ms.items()},
             "host_us_per_call": round(host_s * 1e6, 2),

@@ -9,7 +9,7 @@ to torch's current stream.
 Function names match the C-ABI in include/mkv.h without the ``mkv_`` prefix:
 pool_bytes, record_bytes, pool_create, pool_destroy, seq_reset, append,
 demote, decode, seq_info, page_table, pool_stats, debug_gather,
-profile_enable, profile_read, status_string, last_error.
+debug_schedule, profile_enable, profile_read, status_string, last_error.
 """
 from __future__ import annotations
 
@@ -82,11 +82,27 @@ class Profile(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class ScheduleInfo(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_items", ctypes.c_int32),
+        ("n_list", ctypes.c_int32),
+        ("n_chunks", ctypes.c_int32),
+        ("max_seq_chunks", ctypes.c_int32),
+        ("heads_per_wave", ctypes.c_int32),
+        ("resident_waves", ctypes.c_int32),
+        ("pad0", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "pad0"}
+
+
 EXPORTED = [
     "mkv_pool_bytes", "mkv_record_bytes", "mkv_pool_create", "mkv_pool_destroy",
     "mkv_seq_reset", "mkv_append", "mkv_append_step", "mkv_demote", "mkv_materialize",
     "mkv_decode", "mkv_seq_info",
-    "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_profile_enable",
+    "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_debug_schedule", "mkv_profile_enable",
     "mkv_profile_read", "mkv_status_string", "mkv_last_error",
 ]
 
@@ -118,6 +134,7 @@ def _load():
         "mkv_page_table": (I32, [P, I32, P, I32]),
         "mkv_pool_stats": (I32, [P, ctypes.POINTER(Stats)]),
         "mkv_debug_gather": (I32, [P, I32, I32, I32, P, P]),
+        "mkv_debug_schedule": (I32, [P, ctypes.POINTER(ScheduleInfo), P, I32, P, I32, P, I32]),
         "mkv_profile_enable": (I32, [P, I32]),
         "mkv_profile_read": (I32, [P, ctypes.POINTER(Profile)]),
         "mkv_status_string": (ctypes.c_char_p, [I32]),
@@ -276,6 +293,26 @@ def debug_gather(pool, seq: int, first: int, n: int, dst, stream=None) -> None:
     """dst: uint8 device tensor of n * max(record bytes) bytes."""
     _check(_load().mkv_debug_gather(pool, seq, first, n, _dev_ptr(dst, name="dst"),
                                     _stream(stream)))
+
+
+def debug_schedule(pool, arrays: bool = True):
+    """The device's copy of the cached decode schedule (synchronous): a dict of
+    counts, plus (arrays=True) items int32 [n][8], entries int32 [n_list] and
+    chunk_base int32 [B + 1] as numpy arrays."""
+    import numpy as np
+    lib = _load()
+    info = ScheduleInfo()
+    _check(lib.mkv_debug_schedule(pool, ctypes.byref(info), None, 0, None, 0, None, 0))
+    out = info.as_dict()
+    if arrays:
+        items = np.zeros((max(1, info.n_items), 8), np.int32)
+        ent = np.zeros(max(1, info.n_list), np.int32)
+        base = np.zeros(info.batch + 1, np.int32)
+        _check(lib.mkv_debug_schedule(pool, ctypes.byref(info), items.ctypes.data_as(ctypes.c_void_p),
+                                      items.shape[0], ent.ctypes.data_as(ctypes.c_void_p), ent.size,
+                                      base.ctypes.data_as(ctypes.c_void_p), base.size))
+        out.update(items=items[:info.n_items], entries=ent[:info.n_list], chunk_base=base)
+    return out
 
 
 def profile_enable(pool, on: bool) -> None:

@@ -648,24 +648,6 @@ __device__ __forceinline__ void load_scale_dwords(const uint32_t* p, uint32_t (&
 
 // LDS images of the two work-item kinds (one of them per workgroup).
 template <int NG, int NH>
-struct Tq3Lds {
-  static constexpr int D = 32 * NG;
-  static constexpr int VROW = value_row_bytes(D);
-  // key units as [group][token][unit]: a lane stores its group's four units
-  // with one 16-byte write, and the 64 lanes reading one unit each for a
-  // group hit the 64 banks once
-  static constexpr int SD = 16 * NG;            // scale dwords of a tile (K then V)
-  struct Wave {
-    alignas(16) uint32_t kst[NH][64 * NG];      // key units, [group][token][unit]
-    alignas(16) uint8_t vt[NH][16 * VROW];      // value tiles, [token][D] f16
-    alignas(16) uint32_t sc[NH][SD + 4];        // tile scales as f16 [K, V][token][group] (padded)
-    float corr[16];
-  };
-  int32_t ent[kMaxChunkPages];                  // page-table entries of the work item
-  Wave w[kWaves];
-};
-
-template <int NG, int NH>
 struct Fp8Lds {
   static constexpr int D = 32 * NG;
   static constexpr int VROW = value_row_bytes(D);
@@ -689,220 +671,386 @@ __device__ __forceinline__ float pick_head(const f32x4 (&acc)[NH * NT], int jc, 
 
 }  // namespace
 
-// ---------------------------------------------------------------------------
-// TQ3 work item: the workgroup owns NH kv-heads; each wave a quarter of the tiles
-// ---------------------------------------------------------------------------
-template <int NG, int NH, int R>
-__device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it, uint8_t* smem) {
-  auto& lds = *reinterpret_cast<Tq3Lds<NG, NH>*>(smem);
-  constexpr int D = 32 * NG;
-  constexpr int GPL = NG > 4 ? NG / 4 : 1;      // groups each lane loads per head
-  constexpr int NT = D / 16;                    // PV N-tiles per head
-  constexpr int VROW = Tq3Lds<NG, NH>::VROW;
-  constexpr int ROWB = 3 * D / 8;               // code bytes per token row
-  constexpr int SD = Tq3Lds<NG, NH>::SD;
-  constexpr int SPL = (SD + 63) / 64;           // scale dwords each lane loads per head
+namespace {
 
+// ---------------------------------------------------------------------------
+// Mixed FP8/TQ3 work items.
+//
+// One workgroup of four wave64 per (work item, block of NH kv-heads); each
+// wave takes a contiguous quarter of the item's 16-token tiles.  A tile's
+// bytes are copied from the page record into the wave's own LDS by 16-byte
+// loads that write LDS directly (no register holds raw page bytes).  A tile
+// travels as two halves, the key half (key codes and scales of its heads) and
+// the value half, through a ring of three half-slots: while tile i is
+// computed, the key half and then the value half of tile i + 1 are in flight
+// (the key half of tile i + 1 is issued once tile i's values are consumed,
+// its value half once tile i's keys are consumed).  An FP8 tile is processed
+// as NH one-head tiles, whose key half fills one slot.
+// ---------------------------------------------------------------------------
+template <int NG, int NH>
+struct Mix {
+  static constexpr int D = 32 * NG;
+  static constexpr int NT = D / 16;                     // PV N-tiles
+  static constexpr int ROWB = 12 * NG;                  // TQ3 code bytes of a token row
+  static constexpr int SCB = 2 * NG;                    // TQ3 scale bytes of a token
+  static constexpr int THALF = 16 * (ROWB + SCB);       // TQ3 key (or value) half of one head
+  static constexpr int FHALF = 16 * D;                  // FP8 key (or value) half of one head
+  static constexpr int SLOT = NG == 8 ? 4096 : 2048;    // bytes of a half-slot
+  static constexpr int NSLOT = 3;
+  static constexpr int PASS = NG < 2 ? NG : 2;          // 32-dim groups per value pass
+  static constexpr int NPASS = NG / PASS;
+  static constexpr int VROWB = 64 * PASS;               // bytes of a value-tile row
+  static constexpr int VBUF = NH * 16 * VROWB;          // value tile of the NH heads
+  static constexpr int WAVE = NSLOT * SLOT + VBUF;      // LDS bytes of one wave
+  static constexpr int CPH = (12 * NG + 63) / 64;      // code loads per head of a TQ3 half
+  static constexpr int TNI = NH * CPH + 1;              // load instructions of a TQ3 half
+  static constexpr int SCOFF = NH * 16 * ROWB;          // scales of a TQ3 half-slot
+  static_assert(NH * 2 * NG <= 64, "one scale load per half");
+  static constexpr int FVEC = FHALF / 16;
+  static constexpr int FNI = (FVEC + 63) / 64;
+  static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+  static constexpr size_t SMEM = cmax(size_t(kWaves) * WAVE, sizeof(MergeLds<D>));
+  static_assert(NH * THALF <= SLOT && FHALF <= SLOT, "a half-tile fits a slot");
+  static_assert(TNI <= 4 && FNI <= 4, "load instructions per half");
+};
+
+// Position of 32-byte segment `seg` of value-tile row r.  The transposing
+// reads of a half-wave touch 8 rows at one segment; XOR-ing the segment index
+// with bits of the row spreads those 8 reads over all 64 banks.
+template <int VROWB>
+__device__ __forceinline__ int vseg(int r, int seg) {
+  if constexpr (VROWB == 128) return seg ^ ((r >> 1) & 3);
+  else return seg ^ ((r >> 2) & 1);
+}
+
+// LDS byte address of a pointer into this workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((const __attribute__((address_space(3))) uint8_t*)(p)));
+}
+
+// Value operands of the PV MFMAs of one group: for N-tiles n0 and n0 + 1 of
+// the pass, the transposing reads from the value tiles of heads 0 and 1 (NH =
+// 2) or twice from the one tile (NH = 1).  Written as one asm block that waits
+// for its reads: the compiler would otherwise make such a read wait for every
+// load into LDS still in flight (the next tiles' halves), since it cannot tell
+// that they write other slots.
+template <int NH>
+__device__ __forceinline__ void value_operands2(uint32_t a0, uint32_t a1, uint32_t head1_off,
+                                                half8& v0, half8& v1) {
+  u32x2 x0, x1, y0, y1;
+  if constexpr (NH == 2) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %6\n\t"
+        "ds_read_b64_tr_b16 %2, %5\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
+        : "v"(a0), "v"(a1), "v"(a0 + head1_off), "v"(a1 + head1_off)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4\n\t"
+        "ds_read_b64_tr_b16 %2, %5\n\t"
+        "ds_read_b64_tr_b16 %3, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
+        : "v"(a0), "v"(a1)
+        : "memory");
+  }
+  v0 = __builtin_bit_cast(half8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+  v1 = __builtin_bit_cast(half8, u32x4{y0[0], y0[1], y1[0], y1[1]});
+}
+
+// max without the quieting the compiler adds to fmaxf (the values here are
+// never signalling NaNs)
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float quad_max2(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 16 bytes from the record (voff: this lane's byte offset) into LDS at
+// dst + 16 * lane (dst is the same for the whole wave).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* dst, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
+// Four E4M3 bytes -> two dwords of f16 pairs (the hardware conversion with
+// scale 1 is exact: every E4M3 value is an f16 normal number).
+__device__ __forceinline__ u32x2 fp8x4_to_f16_s(uint32_t w) {
+  u32x2 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  return o;
+}
+
+// Softmax step of one tile for the lane's column (as softmax_step, with the
+// accumulator rows' correction factors read from the lanes of their columns;
+// `live` false: the column takes no token of this tile).
+template <int NACC>
+__device__ __forceinline__ void softmax_live(SoftState& st, float s[4], float p[4], f32x4 (&acc)[NACC],
+                                             int quad, bool live) {
+  float tmax = vmax(vmax(s[0], s[1]), vmax(s[2], s[3]));
+  tmax = quad_max2(tmax);
+  if (__any(tmax > st.m)) {
+    // a column whose maximum does not rise keeps a factor of exactly 1 (its
+    // maximum may still be -inf: no live token of it seen yet)
+    const bool rise = tmax > st.m;
+    const float m_new = rise ? tmax + kHeadroom : st.m;
+    const float corr = rise ? exp2f(st.m - m_new) : 1.0f;   // 0 on the column's first tile
+    st.m = m_new;
+    st.l *= corr;
+    // accumulator row i of this lane is column 4quad + i, whose factor lane
+    // 4quad + i (column 4quad + i, quad 0) holds
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float c = __shfl(corr, 4 * quad + i, 64);
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) acc[j][i] *= c;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float e = __builtin_amdgcn_exp2f(s[i] - st.m);
+    p[i] = live ? e : 0.0f;
+    st.l += p[i];
+  }
+}
+
+// Page-table entries of a wave's pages, one per lane (a wave's tiles span at
+// most 64 pages), read per tile with readlane.
+struct WavePages {
+  int32_t ent;
+  int first;
+  __device__ __forceinline__ const uint8_t* page(const PoolView& pv, int pg) const {
+    return page_address(pv, __builtin_amdgcn_readlane(ent, pg - first));
+  }
+};
+__device__ __forceinline__ WavePages wave_pages(const DecodeArgs& a, const WorkItem& it, const TileGeom& g) {
+  const int lane = threadIdx.x & 63;
+  WavePages w;
+  w.first = g.first.page;
+  const int n = g.stop_page - g.first.page + 1;
+  w.ent = lane < n ? a.entries[it.list_off + w.first + lane] : 0;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// TQ3 work item
+// ---------------------------------------------------------------------------
+template <int NG, int NH>
+__device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it, uint8_t* smem) {
+  using C = Mix<NG, NH>;
+  constexpr int D = C::D, NT = C::NT, ROWB = C::ROWB, TNI = C::TNI;
+  constexpr int VROWB = C::VROWB, PASS = C::PASS;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15;                    // token (loads) / head column (outputs)
+  const int col = lane & 15;                    // token (keys) / head column (outputs)
   const int quad = lane >> 4;
   const PoolView& pv = a.pv;
-  stage_entries(lds.ent, a, it);
   const int hk0 = blockIdx.y * NH;               // the workgroup's kv-heads
-  if (hk0 >= pv.Hkv) return;
   const int G = a.Hq / pv.Hkv;
   const int ncol = NH * G;
   const int hq0 = hk0 * G;
-  const int jcol = col < ncol ? col / G : 0;    // kv-head (within the wave) of column col
-  auto& W = lds.w[wave];
+  const int jcol = col < ncol ? col / G : 0;    // kv-head (within the workgroup) of column col
+  uint8_t* wl = smem + wave * C::WAVE;          // this wave's slots and value tile
+  uint8_t* vt = wl + C::NSLOT * C::SLOT;
   const uint32_t one = vgpr_one_pair();
-  // the lane's value-tile reads (head 0, N-tile 0): row 4quad + col/4, dims
-  // 4(col & 3) .. +3; a second base for the duplicate read
-  const uint8_t* vbase = W.vt[0] + value_row(4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
-  const uint8_t* vbase2 = vbase + vgpr_opaque_zero();
-
-  // ---- query operands: slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s],
-  // scaled by 2^(E + 7 - kSlotShift[s]) against the key slot's 2^(k-10)
-  // (prepared once the first tiles' loads are in flight)
-  half8 qop[NH][NG];
-  float F;
-  auto prepare = [&]() {
-    half8 qh[NG];
-    const int E = load_query<NG, NH>(
-        a, it.b, hq0, col, ncol, jcol, qop, qh,
-        [&](const uint16_t* qrow, int g, float (&v)[8]) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const int e = kSlotCode[s];
-            v[s] = bf16_to_f32(uint16_t(w[e >> 1] >> (16 * (e & 1))));
-          }
-        },
-        [](float x, int E, int s) { return _Float16(__builtin_amdgcn_ldexpf(x, E + 7 - kSlotShift[s])); });
-    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
-  };
+  const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
 
   f32x4 acc[NT];                                // one per N-tile, both kv-heads' rows
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
 
-  // Per-lane byte offsets inside a record (the tile's first token is added per
-  // tile).  Lane (token col, quad) loads group quad (+4i) of that token; with
-  // fewer than 4 groups the spare quads repeat a real group's load, and spare
-  // lanes of the scale load repeat a real scale dword (results unused).
-  // (unsigned 32-bit lane offsets added to a wave-uniform base address map
-  // to loads with a scalar base and a vector offset)
-  uint32_t code_off[NH][GPL], sc_off[NH][SPL];
+  if (tg.ntiles > 0) {
+    const WavePages wp = wave_pages(a, it, tg);
+    // query rows of the lane's column: fetched now, converted once the first
+    // tile's loads are in flight
+    const bool qlive = col < ncol;
+    const uint16_t* qrow = a.q + (int64_t(it.b) * a.Hq + hq0 + (qlive ? col : 0)) * D;
+    u32x4 qraw[NG];
 #pragma unroll
-  for (int j = 0; j < NH; ++j) {
-    const uint32_t cb = uint32_t(tq3_codes_off(pv, hk0 + j, 0));
-    const uint32_t kb = uint32_t(tq3_scale_off(pv, hk0 + j, 0));
-    const uint32_t vb = uint32_t(tq3_scale_off(pv, hk0 + j, 1));
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) code_off[j][i] = cb + col * ROWB + 12 * ((quad + 4 * i) % NG);
-#pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      const int e = (lane + 64 * i) & (SD - 1);
-      sc_off[j][i] = e < 8 * NG ? kb + 4 * e : vb + 4 * (e - 8 * NG);
-    }
-  }
-  const int vcode_delta = pv.P * ROWB;                  // V codes follow the K codes
+    for (int g = 0; g < NG; ++g) qraw[g] = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
 
-  struct Raw {
-    uint32_t kc[NH][GPL][3];                    // K codes: one 12-byte group of token col
-    uint32_t vc[NH][GPL][3];                    // V codes, same group and token
-    uint32_t sc[NH][SPL];                       // the lane's share of the tile's scales
-  };
-  auto load = [&](const Cursor& c, Raw& r) {
-    const auto rec = record_rsrc(entry_page(pv, lds.ent, c.page), pv.tq3_stride);
-    const int kso = 16 * c.sub * ROWB;                   // the tile's first K row
-    const int vso = kso + vcode_delta;                   // and its first V row
-    const int sso = 32 * c.sub * NG;                     // and its scales
+    // A half-slot holds the key (value) codes of the NH heads, 16 token rows
+    // each, then their scales.  Each code load copies up to 64 16-byte vectors
+    // of one head's rows (lane l: bytes 16l..), the scale load the scale
+    // vectors of all NH heads; the tile and head positions are scalar offsets.
+    const int BLK = pv.P * 28 * NG;              // TQ3 bytes of one kv-head of a page
+    const uint32_t voff_c = 16u * uint32_t(lane);
+    const uint32_t voff_s = uint32_t((lane / (2 * NG)) * BLK + 2 * pv.P * ROWB + 16 * (lane % (2 * NG)));
+    Cursor lc = tg.first;                        // next tile whose halves are loaded
+    int ls = 0;                                  // next slot to fill
+    auto issue = [&](bool value_half) {
+      const auto rsrc = record_rsrc(wp.page(pv, lc.page), pv.tq3_stride);
+      uint8_t* dst = wl + ls * C::SLOT;
+      const int code0 = hk0 * BLK + (value_half ? pv.P * ROWB : 0) + lc.sub * 16 * ROWB;
 #pragma unroll
-    for (int j = 0; j < NH; ++j) {
+      for (int j = 0; j < NH; ++j)
 #pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const u32x3 kw = rec_load3(rec, code_off[j][i], kso);
-        const u32x3 vw = rec_load3(rec, code_off[j][i], vso);
+        for (int x = 0; x < C::CPH; ++x)
+          if (64 * x + lane < 12 * NG)
+            lds_load16(rsrc, dst + j * 16 * ROWB + 1024 * x, voff_c, code0 + j * BLK + 1024 * x);
+      if (lane < NH * 2 * NG)
+        lds_load16(rsrc, dst + NH * 16 * ROWB, voff_s,
+                   hk0 * BLK + (value_half ? pv.P * C::SCB : 0) + lc.sub * 16 * C::SCB);
+      ls = ls == C::NSLOT - 1 ? 0 : ls + 1;
+      if (value_half) advance_clamped(lc, tg);   // past the end, the last tile is loaded again
+    };
+    issue(false);
+    issue(true);
+    issue(false);
+
+    // query operands: slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s],
+    // scaled by 2^(E + 7 - kSlotShift[s]) against the key slot's 2^(k-10)
+    half8 qop[NH][NG];
+    float F;
+    {
+      half8 qh[NG];
+      const int E = load_query<NG, NH>(
+          a, it.b, hq0, col, ncol, jcol, qop, qh,
+          [&](const uint16_t*, int g, float (&v)[8]) {
 #pragma unroll
-        for (int x = 0; x < 3; ++x) {
-          r.kc[j][i][x] = kw[x];
-          r.vc[j][i][x] = vw[x];
+            for (int s = 0; s < 8; ++s) {
+              const int e = kSlotCode[s];
+              v[s] = bf16_to_f32(uint16_t(qraw[g][e >> 1] >> (16 * (e & 1))));
+            }
+          },
+          [](float x, int E, int s) { return _Float16(__builtin_amdgcn_ldexpf(x, E + 7 - kSlotShift[s])); });
+      F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
+    }
+
+    // lane constants: the unit of a key group a lane reads (dword offset and
+    // funnel shift of unit `quad`, bytes 3quad .. 3quad+2 of the group)
+    const int uoff = quad == 0 ? 0 : quad - 1;
+    const uint32_t ush = uint32_t(32 - 8 * quad) & 31u;
+    // value-tile addresses of the transposing reads (row 4quad + col/4,
+    // 8 bytes at column 4(col & 3) of N-tile n of the pass)
+    const int vr = 4 * quad + (col >> 2);
+    uint32_t vrd[2 * PASS];
+#pragma unroll
+    for (int n = 0; n < 2 * PASS; ++n) vrd[n] = uint32_t(vr * VROWB + 32 * vseg<VROWB>(vr, n) + 8 * (col & 3));
+    const uint32_t vt_addr = lds_addr(vt);
+    // value unpack: lane -> (token ut, head uj, group ug of the pass); spare
+    // lanes repeat a real one's work
+    const int ci = lane % (16 * NH * PASS);
+    const int ut = ci & 15, uj = (ci >> 4) % NH, ug = ci / (16 * NH);
+
+    Cursor pc = tg.first;
+    int ks = 0;                                  // slot of this tile's key half
+    for (int ti = 0; ti < tg.ntiles; ++ti) {
+      if (a.pace) pace_priority(ti, tg.ntiles);
+      const int vs = ks == C::NSLOT - 1 ? 0 : ks + 1;
+      const int nvalid = valid_in_tile(pc, tg);
+      const uint8_t* kb = wl + ks * C::SLOT;
+      const uint8_t* vb = wl + vs * C::SLOT;
+
+      // ---- keys: QK^T per group, both kv-heads into one D, scaled per token
+      wait_vm<2 * TNI>();                        // this tile's key half has landed
+      uint32_t ksd[2 * NG];
+      load_scale_dwords<NG>(reinterpret_cast<const uint32_t*>(kb + C::SCOFF + jcol * 16 * C::SCB + 8 * NG * quad), ksd);
+      float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const uint32_t* u = reinterpret_cast<const uint32_t*>(kb + j * 16 * ROWB + col * ROWB + 12 * g) + uoff;
+          const uint32_t x = __builtin_amdgcn_alignbit(u[1], u[0], ush);
+          dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tq3_unit_to_f16(x, one)),
+                                                      qop[j][g], dg, 0, 0, 0);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[i] = __builtin_fmaf(dg[i], f16_half(ksd[(i * NG + g) >> 1], (i * NG + g) & 1), s[i]);
+      }
+      wait_lds();                                // the key half is consumed: its slot takes
+      issue(true);                               // the next tile's value half
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] *= F;
+      if (nvalid < 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * quad + i >= nvalid) s[i] = -INFINITY;
+      }
+      float p[4];
+      softmax_live(st, s, p, acc, quad, true);
+
+      // ---- values: per pass of PASS groups, unpack into the value tile, then
+      // P' = p * value scale (hi/lo f16) and acc += P' * V
+      wait_vm<2 * TNI>();                        // this tile's value half has landed
+      uint32_t vsd[2 * NG];
+      load_scale_dwords<NG>(reinterpret_cast<const uint32_t*>(vb + C::SCOFF + jcol * 16 * C::SCB + 8 * NG * quad), vsd);
+      if (nvalid < 16) {
+        // an unwritten slot's scale may be NaN, and p = 0 times NaN is NaN
+#pragma unroll
+        for (int e = 0; e < 4 * NG; ++e)
+          if (4 * quad + e / NG >= nvalid) vsd[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
       }
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) r.sc[j][i] = rec_load1(rec, sc_off[j][i], sso);
-    }
-  };
-  const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
-
-  // Tile body: the raw buffer is consumed into LDS, refilled with a later
-  // tile, and the tile is computed from LDS.
-  auto process = [&](Raw& raw, const Cursor& c, auto refill) {
-    const int nvalid = valid_in_tile(c, tg);
-#pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      // scales: the lane's dword holds f16 k0 = 2e' and k0 + 1 of the tile's
-      // K (e < 8NG) or V block, f16 k being (token k / NG, group k % NG), and
-      // is stored in place ([K, V][token][group]).  Value scales of masked
-      // tokens become 0 (an unwritten slot may hold NaN, and p = 0 times NaN
-      // is NaN).
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < SD) {
-          const bool is_v = e >= 8 * NG;
-          const int k0 = 2 * (is_v ? e - 8 * NG : e);
-          const int t0 = k0 / NG, t1 = (k0 + 1) / NG;
-          uint32_t w = raw.sc[j][i];
-          if (is_v && t0 >= nvalid) w &= 0xFFFF0000u;
-          if (is_v && t1 >= nvalid) w &= 0x0000FFFFu;
-          W.sc[j][e] = w;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const int g = quad + 4 * i;
-        if (g < NG) {
-          uint32_t u[4];
-          tq3_split_units(raw.kc[j][i], u);
-          *reinterpret_cast<u32x4*>(&W.kst[j][64 * g + 4 * col]) = u32x4{u[0], u[1], u[2], u[3]};
+      for (int ps = 0; ps < C::NPASS; ++ps) {
+        {
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(vb + uj * 16 * ROWB + ut * ROWB + 12 * (ps * PASS + ug));
+          const uint32_t w[3] = {src[0], src[1], src[2]};
           uint32_t o[16];
-          tq3_value_group(raw.vc[j][i], one, o);
-          uint8_t* vd = W.vt[j] + value_row(col) * VROW + 64 * g;
+          tq3_value_group(w, one, o);
+          uint8_t* row = vt + (uj * 16 + ut) * VROWB;
 #pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4)
-            *reinterpret_cast<u32x4*>(vd + 16 * c4) = u32x4{o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]};
+          for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<u32x4*>(row + 32 * vseg<VROWB>(ut, 2 * ug + (k >> 1)) + 16 * (k & 1)) =
+                u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
         }
-      }
-    }
-    refill(raw);
-    wave_lds_sync();
-
-    // ---- QK^T per group (the NH kv-heads into one D), scaled per token by
-    // the group's key scale of the lane's column's kv-head
-    // the lane's tokens 4quad .. 4quad+3 hold 2NG consecutive scale dwords of
-    // each block: token 4quad+i, group g is half (i NG + g) & 1 of dword
-    // (i NG + g) >> 1
-    const uint32_t* scl = W.sc[jcol] + 2 * NG * quad;   // + 8NG: V scales
-    uint32_t ksd[2 * NG];
-    load_scale_dwords<NG>(scl, ksd);
-    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        wave_lds_sync();
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int gs = 0; gs < PASS; ++gs) {
+          const int g = ps * PASS + gs;
+          float sv[4];
 #pragma unroll
-      for (int j = 0; j < NH; ++j) {
-        const half8 kop =
-            __builtin_bit_cast(half8, tq3_unit_to_f16(W.kst[j][64 * g + 4 * col + quad], one));
-        dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[j][g], dg, 0, 0, 0);
-      }
+          for (int i = 0; i < 4; ++i) sv[i] = f16_half(vsd[(i * NG + g) >> 1], (i * NG + g) & 1);
+          const half8 pp = pprime(p, sv);
+          half8 bv[2];
+          value_operands2<NH>(vt_addr + vrd[2 * gs], vt_addr + vrd[2 * gs + 1], 16 * VROWB, bv[0], bv[1]);
+          if constexpr (NH == 2) {
+            half8 a_hi, a_lo;
+            split_pprime(pp, jcol == 1, a_hi, a_lo);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s[i] = __builtin_fmaf(dg[i], f16_half(ksd[(i * NG + g) >> 1], (i * NG + g) & 1), s[i]);
-    }
+            for (int h = 0; h < 2; ++h) {
+              acc[2 * g + h] = pv_mfma(a_hi, bv[h], acc[2 * g + h]);
+              acc[2 * g + h] = pv_mfma(a_lo, bv[h], acc[2 * g + h]);
+            }
+          } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] *= F;
-    if (nvalid < 16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * quad + i >= nvalid) s[i] = -INFINITY;
-    }
-    float p[4];
-    softmax_step(st, s, p, acc, W.corr, col, quad);
-
-    // ---- per group: P' = p * value scale (hi/lo f16), acc_j += P' * V_j
-    uint32_t vsd[2 * NG];
-    load_scale_dwords<NG>(scl + 8 * NG, vsd);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      float sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = f16_half(vsd[(i * NG + g) >> 1], (i * NG + g) & 1);
-      const half8 pp = pprime(p, sv);
-      if constexpr (NH == 2) {
-        half8 a_hi, a_lo;
-        split_pprime(pp, jcol == 1, a_hi, a_lo);
-#pragma unroll
-        for (int jt = 2 * g; jt < 2 * g + 2; ++jt) {
-          const half8 bv = value_operand_heads(vbase + 32 * jt, vbase + 16 * VROW + 32 * jt);
-          acc[jt] = pv_mfma(a_hi, bv, acc[jt]);
-          acc[jt] = pv_mfma(a_lo, bv, acc[jt]);
+            for (int h = 0; h < 2; ++h) acc[2 * g + h] = pv_mfma(pp, bv[h], acc[2 * g + h]);
+          }
         }
-      } else {
-#pragma unroll
-        for (int jt = 2 * g; jt < 2 * g + 2; ++jt)
-          acc[jt] = pv_mfma(pp, value_operand(vbase + 32 * jt, vbase2 + 32 * jt), acc[jt]);
+        wave_lds_sync();
       }
+      wait_lds();                                // the value half is consumed: its slot takes
+      issue(false);                              // the tile after next's key half
+      advance(pc, tg);
+      ks = ks >= C::NSLOT - 2 ? ks - (C::NSLOT - 2) : ks + 2;
     }
-    wave_lds_sync();
-  };
-  run_tiles<R, Raw>(tg, a.pace != 0, load, prepare, process);
+    if (a.pace) __builtin_amdgcn_s_setprio(0);
+    wait_vm<0>();                                // no load into LDS outlives the loop
+  }
 
-  // ---- combine the four waves' states through LDS (the tile staging is
-  // reused once every wave is past its last tile) and write the item's state
+  // ---- combine the four waves' states through LDS (the slots are reused once
+  // every wave is past its last tile) and write the item's state
   const float lcol = quad_sum(st.l);
   __syncthreads();
   auto& M = *reinterpret_cast<MergeLds<D>*>(smem);
@@ -931,160 +1079,182 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 }
 
 // ---------------------------------------------------------------------------
-// FP8 work item: the workgroup owns NH kv-heads; each wave a quarter of the tiles
+// FP8 work item: each 16-token tile is NH one-head tiles
 // ---------------------------------------------------------------------------
-template <int NG, int NH, int R>
+template <int NG, int NH>
 __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it, uint8_t* smem) {
-  auto& lds = *reinterpret_cast<Fp8Lds<NG, NH>*>(smem);
-  constexpr int D = 32 * NG;
-  constexpr int NT = D / 16;
-  constexpr int VROW = Fp8Lds<NG, NH>::VROW;
-  constexpr int LB = D / 4;                     // bytes of a row each lane loads
-
+  using C = Mix<NG, NH>;
+  constexpr int D = C::D, NT = C::NT, FNI = C::FNI, VROWB = C::VROWB, PASS = C::PASS;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
   const int quad = lane >> 4;
   const PoolView& pv = a.pv;
-  stage_entries(lds.ent, a, it);
-  const int hk0 = blockIdx.y * NH;               // the workgroup's kv-heads
-  if (hk0 >= pv.Hkv) return;
+  const int hk0 = blockIdx.y * NH;
   const int G = a.Hq / pv.Hkv;
   const int ncol = NH * G;
   const int hq0 = hk0 * G;
   const int jcol = col < ncol ? col / G : 0;
-  auto& W = lds.w[wave];
-  const uint8_t* vbase = W.vt[0] + value_row(4 * quad + (col >> 2)) * VROW + 8 * (col & 3);
-  const uint8_t* vbase2 = vbase + vgpr_opaque_zero();
+  uint8_t* wl = smem + wave * C::WAVE;
+  uint8_t* vt = wl + C::NSLOT * C::SLOT;
+  const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
 
-  // ---- query operand: MFMA r, lane (col, quad), slot s <-> dim quad*LB + 8r + s
-  // (prepared once the first tiles' loads are in flight)
-  half8 qop[NH][NG];
-  float F;
-  auto prepare = [&]() {
-    half8 qh[NG];
-    const int E = load_query<NG, NH>(
-        a, it.b, hq0, col, ncol, jcol, qop, qh,
-        [&](const uint16_t* qrow, int r, float (&v)[8]) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + quad * LB + 8 * r);
-#pragma unroll
-          for (int s = 0; s < 8; ++s) v[s] = bf16_to_f32(uint16_t(w[s >> 1] >> (16 * (s & 1))));
-        },
-        [](float x, int E, int) { return _Float16(__builtin_amdgcn_ldexpf(x, E)); });
-    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
-  };
-
-  f32x4 acc[NT];                                // one per N-tile, both kv-heads' rows
+  f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
 
-  uint32_t code_off[NH], ks_off[NH], vs_off[NH];
+  if (tg.ntiles > 0) {
+    const WavePages wp = wave_pages(a, it, tg);
+    const bool qlive = col < ncol;
+    const uint16_t* qrow = a.q + (int64_t(it.b) * a.Hq + hq0 + (qlive ? col : 0)) * D;
+    u32x4 qraw[NG];
 #pragma unroll
-  for (int j = 0; j < NH; ++j) {
-    code_off[j] = uint32_t(fp8_codes_off(pv, hk0 + j, 0)) + col * D + quad * LB;
-    ks_off[j] = uint32_t(fp8_scale_off(pv, hk0 + j, 0));
-    vs_off[j] = uint32_t(fp8_scale_off(pv, hk0 + j, 1));
-  }
-  const int vcode_delta = pv.P * D;
-  struct Raw {
-    uint32_t kw[NH][LB / 4];
-    uint32_t vw[NH][LB / 4];
-    float sigk[NH], sigv[NH];
-  };
-  auto load = [&](const Cursor& c, Raw& r) {
-    const auto rec = record_rsrc(entry_page(pv, lds.ent, c.page), pv.fp8_stride);
-    const int kso = 16 * c.sub * D;                      // the tile's first K row
-    const int vso = kso + vcode_delta;                   // and its first V row
+    for (int g = 0; g < NG; ++g) qraw[g] = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
+
+    // a one-head half is 16 consecutive token rows of that head's key (or
+    // value) block: vector v of the slot is bytes 16v.. of it
+    const int PD = pv.P * D;
+    const uint32_t voff_c = 16u * uint32_t(lane);
+    Cursor lc = tg.first;
+    int lj = 0;                                  // head of the next one-head tile to load
+    int ls = 0;
+    auto issue = [&](bool value_half) {
+      const auto rsrc = record_rsrc(wp.page(pv, lc.page), pv.fp8_stride);
+      uint8_t* dst = wl + ls * C::SLOT;
+      const int so = ((hk0 + lj) * 2 + (value_half ? 1 : 0)) * PD + lc.sub * 16 * D;
 #pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      if constexpr (LB % 16 == 0) {
-#pragma unroll
-        for (int x = 0; x < LB / 16; ++x) {
-          const u32x4 kw = rec_load4(rec, code_off[j] + 16 * x, kso);
-          const u32x4 vw = rec_load4(rec, code_off[j] + 16 * x, vso);
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            r.kw[j][4 * x + y] = kw[y];
-            r.vw[j][4 * x + y] = vw[y];
-          }
+      for (int x = 0; x < FNI; ++x)
+        if (64 * x + lane < C::FVEC) lds_load16(rsrc, dst + 1024 * x, voff_c, so + 1024 * x);
+      ls = ls == C::NSLOT - 1 ? 0 : ls + 1;
+      if (value_half) {
+        if (++lj == NH) {
+          lj = 0;
+          advance_clamped(lc, tg);
         }
-      } else {
-        static_assert(LB == 8, "an FP8 lane row share is 8 or a multiple of 16 bytes");
-        const u32x2 kw = rec_load2(rec, code_off[j], kso);
-        const u32x2 vw = rec_load2(rec, code_off[j], vso);
-        r.kw[j][0] = kw[0];
-        r.kw[j][1] = kw[1];
-        r.vw[j][0] = vw[0];
-        r.vw[j][1] = vw[1];
       }
-      r.sigk[j] = __builtin_bit_cast(float, rec_load1(rec, 0, ks_off[j]));
-      r.sigv[j] = __builtin_bit_cast(float, rec_load1(rec, 0, vs_off[j]));
-    }
-  };
-  const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
+    };
+    issue(false);
+    issue(true);
+    issue(false);
 
-  auto process = [&](Raw& raw, const Cursor& c, auto refill) {
-    const int nvalid = valid_in_tile(c, tg);
-    // ---- values: f16 rows of the LDS tiles (rows past the valid tokens zeroed)
-    const bool vrow_ok = col < nvalid;
+    half8 qop[NH][NG];
+    float F;
+    {
+      half8 qh[NG];
+      const int E = load_query<NG, NH>(
+          a, it.b, hq0, col, ncol, jcol, qop, qh,
+          [&](const uint16_t*, int r, float (&v)[8]) {
 #pragma unroll
-    for (int j = 0; j < NH; ++j)
-#pragma unroll
-      for (int i = 0; i < LB / 4; i += 2) {
-        const u32x2 a0 = fp8x4_to_f16(raw.vw[j][i]);
-        const u32x2 a1 = fp8x4_to_f16(raw.vw[j][i + 1]);
-        u32x4 o = {a0[0], a0[1], a1[0], a1[1]};
-        if (!vrow_ok) o = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(W.vt[j] + value_row(col) * VROW + 2 * (quad * LB + 4 * i)) = o;
-      }
-    // ---- QK^T over all dims, per kv-head, keys widened to f16 operands from
-    // the raw words (page-head scale applied per column)
-    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float sv = raw.sigv[0];
-#pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int r = 0; r < NG; ++r) {
-        const u32x2 k0 = fp8x4_to_f16(raw.kw[j][2 * r]);
-        const u32x2 k1 = fp8x4_to_f16(raw.kw[j][2 * r + 1]);
-        const u32x4 ku = {k0[0], k0[1], k1[0], k1[1]};
-        dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ku), qop[j][r], dsum, 0, 0, 0);
-      }
-      const float fk = jcol == j ? F * raw.sigk[j] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(dsum[i], fk, s[i]);
-      if (j > 0) sv = jcol == j ? raw.sigv[j] : sv;
+            for (int s = 0; s < 8; ++s) v[s] = bf16_to_f32(uint16_t(qraw[r][s >> 1] >> (16 * (s & 1))));
+          },
+          [](float x, int E, int) { return _Float16(__builtin_amdgcn_ldexpf(x, E)); });
+      F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, -E);
     }
-    refill(raw);
-    wave_lds_sync();
-    if (nvalid < 16) {
+    const int vr = 4 * quad + (col >> 2);
+    uint32_t vrd[2 * PASS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * quad + i >= nvalid) s[i] = -INFINITY;
-    }
-    float p[4];
-    softmax_step(st, s, p, acc, W.corr, col, quad);
+    for (int n = 0; n < 2 * PASS; ++n) vrd[n] = uint32_t(vr * VROWB + 32 * vseg<VROWB>(vr, n) + 8 * (col & 3));
+    const uint32_t vt_addr = lds_addr(vt);
+    // value conversion: lane -> (token ut, quarter uq of the pass's 32 PASS dims)
+    const int ut = lane & 15, uq = lane >> 4;
 
-    const half8 pp = pprime_uniform(p, sv);
-    if constexpr (NH == 2) {
-      half8 a_hi, a_lo;
-      split_pprime(pp, jcol == 1, a_hi, a_lo);
+    Cursor pc = tg.first;
+    int ks = 0;
+    for (int ti = 0; ti < tg.ntiles; ++ti) {
+      if (a.pace) pace_priority(ti, tg.ntiles);
+      const int nvalid = valid_in_tile(pc, tg);
+      const uint8_t* page = wp.page(pv, pc.page);
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt) {
-        const half8 bv = value_operand_heads(vbase + 32 * jt, vbase + 16 * VROW + 32 * jt);
-        acc[jt] = pv_mfma(a_hi, bv, acc[jt]);
-        acc[jt] = pv_mfma(a_lo, bv, acc[jt]);
+      for (int j = 0; j < NH; ++j) {
+        const int vs = ks == C::NSLOT - 1 ? 0 : ks + 1;
+        const uint8_t* kb = wl + ks * C::SLOT;
+        const uint8_t* vb = wl + vs * C::SLOT;
+        const bool live = jcol == j && col < ncol;
+        // page-head scales of head hk0 + j (wave-uniform)
+        const float sk = *reinterpret_cast<const float*>(page + fp8_scale_off(pv, hk0 + j, 0));
+        const float sv = *reinterpret_cast<const float*>(page + fp8_scale_off(pv, hk0 + j, 1));
+
+        wait_vm<2 * FNI>();
+        f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < NG; ++r) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(kb + col * D + 32 * r + 8 * quad);
+          const u32x2 k0 = fp8x4_to_f16_s(w[0]);
+          const u32x2 k1 = fp8x4_to_f16_s(w[1]);
+          const u32x4 ku = {k0[0], k0[1], k1[0], k1[1]};
+          dsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ku), qop[j][r], dsum, 0, 0, 0);
+        }
+        wait_lds();
+        issue(true);
+        const float fk = F * sk;
+        float s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = live && 4 * quad + i < nvalid ? dsum[i] * fk : -INFINITY;
+        float p[4];
+        softmax_live(st, s, p, acc, quad, live);
+        const half8 pp = pprime_uniform(p, sv);
+
+        wait_vm<2 * FNI>();
+#pragma unroll
+        for (int ps = 0; ps < C::NPASS; ++ps) {
+          {
+            // token ut's dims 32 PASS ps + 8 PASS uq .. +8 PASS, widened to f16
+            // (rows past the valid tokens are zeroed: an unwritten byte may be NaN)
+            constexpr int NB = 8 * PASS;                     // bytes (dims) per lane
+            const uint8_t* src = vb + ut * D + 32 * PASS * ps + NB * uq;
+            uint32_t o[NB / 2];
+            if constexpr (NB == 16) {
+              const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                const u32x2 h = fp8x4_to_f16_s(w[x]);
+                o[2 * x] = h[0];
+                o[2 * x + 1] = h[1];
+              }
+            } else {
+              const u32x2 w = *reinterpret_cast<const u32x2*>(src);
+#pragma unroll
+              for (int x = 0; x < 2; ++x) {
+                const u32x2 h = fp8x4_to_f16_s(w[x]);
+                o[2 * x] = h[0];
+                o[2 * x + 1] = h[1];
+              }
+            }
+            if (ut >= nvalid) {
+#pragma unroll
+              for (int x = 0; x < NB / 2; ++x) o[x] = 0u;
+            }
+            uint8_t* row = vt + ut * VROWB;
+#pragma unroll
+            for (int k = 0; k < NB / 8; ++k) {
+              const int byte = 2 * NB * uq + 16 * k;           // f16 bytes within the row
+              *reinterpret_cast<u32x4*>(row + 32 * vseg<VROWB>(ut, byte >> 5) + (byte & 31)) =
+                  u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+            }
+          }
+          wave_lds_sync();
+#pragma unroll
+          for (int n = 0; n < 2 * PASS; n += 2) {
+            half8 bv[2];
+            value_operands2<1>(vt_addr + vrd[n], vt_addr + vrd[n + 1], 0, bv[0], bv[1]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int jt = 2 * PASS * ps + n + h;
+              acc[jt] = pv_mfma(pp, bv[h], acc[jt]);
+            }
+          }
+          wave_lds_sync();
+        }
+        wait_lds();
+        issue(false);
+        ks = ks >= C::NSLOT - 2 ? ks - (C::NSLOT - 2) : ks + 2;
       }
-    } else {
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt)
-        acc[jt] = pv_mfma(pp, value_operand(vbase + 32 * jt, vbase2 + 32 * jt), acc[jt]);
+      advance(pc, tg);
     }
-    wave_lds_sync();
-  };
-  run_tiles<R, Raw>(tg, a.pace != 0, load, prepare, process);
+    if (a.pace) __builtin_amdgcn_s_setprio(0);
+    wait_vm<0>();
+  }
 
   const float lcol = quad_sum(st.l);
   __syncthreads();
@@ -1104,6 +1274,8 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   __syncthreads();
   merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
 }
+
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // BF16 work item (control pools): the dense single-format cache.  Structure
@@ -1270,36 +1442,25 @@ __device__ __forceinline__ void bf16_item(const DecodeArgs& a, const WorkItem& i
 
 // ---------------------------------------------------------------------------
 // One launch for both formats: workgroup x takes work item x (FP8 or TQ3).
+// Four waves per SIMD at head dim <= 128 (at most 128 VGPRs and 10 KB of LDS
+// per wave); two at head dim 256.
 // ---------------------------------------------------------------------------
 template <int NG, int NH>
-struct PartialCfg {
-  static constexpr int kRingTq3 = 2;                 // TQ3 tiles in flight per wave
-  // FP8 rows are 4x the TQ3 bytes: one tile in flight with two kv-heads or
-  // head dim 256, within the register budget of the waves per SIMD
-  static constexpr int kRingFp8 = NH == 1 && NG < 8 ? 2 : 1;
-  static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
-  static constexpr size_t kSmem =
-      cmax(cmax(sizeof(Tq3Lds<NG, NH>), sizeof(Fp8Lds<NG, NH>)), sizeof(MergeLds<32 * NG>));
-};
-
-// Three waves per SIMD (168 VGPRs) at head dim <= 128 -- two kv-heads per
-// wave fit because they share one accumulator per N-tile; two waves at 256.
-template <int NG, int NH>
-__global__ void __launch_bounds__(kThreads, NG < 8 ? 3 : 2) partial_mixed(DecodeArgs a) {
-  using Cfg = PartialCfg<NG, NH>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmem];
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NG < 8 ? 4 : 2)))
+partial_mixed(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Mix<NG, NH>::SMEM];
   const WorkItem it = a.items[blockIdx.x];
   if (it.fmt == 0)
-    fp8_item<NG, NH, Cfg::kRingFp8>(a, it, smem);
+    fp8_item<NG, NH>(a, it, smem);
   else
-    tq3_item<NG, NH, Cfg::kRingTq3>(a, it, smem);
+    tq3_item<NG, NH>(a, it, smem);
 }
 
 // Control pools: every work item is BF16.  Two waves per SIMD; one tile in
 // flight (a BF16 tile row share is 4x the TQ3 one).
 template <int NG, int NH>
 __global__ void __launch_bounds__(kThreads, 2) partial_bf16(DecodeArgs a) {
-  constexpr size_t kSmem = PartialCfg<NG, NH>::cmax(sizeof(Fp8Lds<NG, NH>), sizeof(MergeLds<32 * NG>));
+  constexpr size_t kSmem = Mix<NG, NH>::cmax(sizeof(Fp8Lds<NG, NH>), sizeof(MergeLds<32 * NG>));
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   const WorkItem it = a.items[blockIdx.x];
   bf16_item<NG, NH, 1>(a, it, smem);

@@ -742,6 +742,39 @@ mkv_status mkv_debug_gather(mkv_pool* p, int32_t seq, int32_t first, int32_t n, 
   return MKV_OK;
 }
 
+mkv_status mkv_debug_schedule(mkv_pool* p, mkv_schedule_info* info, int32_t* items_host,
+                              int32_t items_cap, int32_t* entries_host, int32_t entries_cap,
+                              int32_t* chunk_base_host, int32_t base_cap) {
+  if (!p || !info) return set_err(MKV_EINVAL, "null argument");
+  if (!p->sched_valid) return set_err(MKV_ESTATE, "no current decode schedule");
+  const mkv::Schedule& sc = p->sched;
+  const int32_t n_items = int32_t(sc.items[0].size() + sc.items[1].size());
+  const int32_t n_list = int32_t(sc.entries.size());
+  const int32_t B = int32_t(p->sched_ids.size());
+  if ((items_host && items_cap < n_items) || (entries_host && entries_cap < n_list) ||
+      (chunk_base_host && base_cap < B + 1))
+    return set_err(MKV_ERANGE, "output buffer smaller than the schedule");
+  DeviceGuard guard(p->device);
+  MKV_HIP(hipDeviceSynchronize());
+  const uint8_t* region = p->mem + p->lay.sched;
+  if (items_host && n_items)
+    MKV_HIP(hipMemcpy(items_host, region + p->lay.items_off, size_t(n_items) * sizeof(mkv::WorkItem),
+                      hipMemcpyDeviceToHost));
+  if (entries_host && n_list)
+    MKV_HIP(hipMemcpy(entries_host, region + entries_off(p->lay, size_t(n_items)), size_t(n_list) * 4,
+                      hipMemcpyDeviceToHost));
+  if (chunk_base_host) MKV_HIP(hipMemcpy(chunk_base_host, region, size_t(B + 1) * 4, hipMemcpyDeviceToHost));
+  info->batch = B;
+  info->n_items = n_items;
+  info->n_list = n_list;
+  info->n_chunks = sc.n_chunks;
+  info->max_seq_chunks = sc.max_seq_chunks;
+  info->heads_per_wave = sc.heads_per_wave;
+  info->resident_waves = p->target_waves[sc.heads_per_wave - 1];
+  info->pad0 = 0;
+  return MKV_OK;
+}
+
 mkv_status mkv_profile_enable(mkv_pool* p, int32_t on) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
   p->prof = on != 0;

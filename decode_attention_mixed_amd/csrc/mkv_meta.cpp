@@ -66,7 +66,7 @@ int validate_desc(const Desc& d, Geom* g, std::string* err) {
   const int64_t mc = d.max_chunks ? int64_t(d.max_chunks) : std::max<int64_t>(4096 + 2 * int64_t(d.max_batch), need);
   if (mc < need || mc > (int64_t(1) << 30))
     return fail(err, MKV_S_EINVAL,
-                "max_chunks must be at least max_batch * (2 + ceil(max_pages_per_seq / 256))");
+                "max_chunks must be at least max_batch * (2 + ceil(max_pages_per_seq / 240))");
   r.max_chunks = int32_t(mc);
   if (g) *g = r;
   return MKV_S_OK;
@@ -288,11 +288,17 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     if (check_seq(ids[b], err)) return MKV_S_EINVAL;
     if (seqs_[size_t(ids[b])].len == 0) return fail(err, MKV_S_EINVAL, "empty sequence in batch");
   }
-  // Per-format page counts of each batch entry.
+  const int32_t heads_per_block =
+      pol.heads_per_wave > 0 ? pol.heads_per_wave : heads_per_wave(g_.d, g_.Hkv, Hq / g_.Hkv);
+  if (heads_per_block != 1 && (heads_per_block != 2 || g_.Hkv % 2 || 2 * (Hq / g_.Hkv) > 16 || g_.d > 128))
+    return fail(err, MKV_S_EINVAL, "unsupported kv-heads per wave");
+  // Per-format page counts of each batch entry.  A wave walks an FP8 page one
+  // kv-head at a time and a TQ3 page heads_per_block kv-heads at a time, so by
+  // default an FP8 page costs heads_per_block TQ3 pages.
   std::vector<int32_t> n8(size_t(B), 0), n3(size_t(B), 0);
   int64_t total_pages = 0;
   double total_cost = 0.0;
-  const double c8 = pol.fp8_page_cost > 0.0f ? double(pol.fp8_page_cost) : 1.0;
+  const double c8 = pol.fp8_page_cost > 0.0f ? double(pol.fp8_page_cost) : double(heads_per_block);
   for (int32_t b = 0; b < B; ++b) {
     for (int32_t e : seqs_[size_t(ids[b])].pt) (pt_is_tq3(e) ? n3 : n8)[size_t(b)]++;
     total_pages += int64_t(seqs_[size_t(ids[b])].pt.size());
@@ -313,10 +319,6 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     per = std::min<int64_t>(per, kMaxChunkPages);
     return (n + per - 1) / per;
   };
-  const int32_t heads_per_block =
-      pol.heads_per_wave > 0 ? pol.heads_per_wave : heads_per_wave(g_.d, g_.Hkv, Hq / g_.Hkv);
-  if (heads_per_block != 1 && (heads_per_block != 2 || g_.Hkv % 2 || 2 * (Hq / g_.Hkv) > 16 || g_.d > 128))
-    return fail(err, MKV_S_EINVAL, "unsupported kv-heads per wave");
   const int64_t waves_per_item =
       int64_t(kWavesPerWorkgroup) * ((g_.Hkv + heads_per_block - 1) / heads_per_block);
   const int64_t target_items =

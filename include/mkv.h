@@ -243,6 +243,31 @@ mkv_status mkv_pool_stats(mkv_pool* pool, mkv_stats* out);
 mkv_status mkv_debug_gather(mkv_pool* pool, int32_t seq, int32_t first, int32_t n, void* dst,
                             hipStream_t stream);
 
+/* The decode schedule the device holds: the one the pool's last mkv_decode
+ * used, with the edits later mkv_append_step and mkv_demote calls made to it.
+ * Synchronous (waits for the device, then copies).  `info` receives the
+ * counts.  items_host (8 int32 per work item, FP8 items first: batch entry,
+ * sequence, page-list offset, pages, valid tokens of the last page, partial-
+ * state slot, format 0 FP8 / 1 TQ3, last logical page), entries_host (the
+ * page-table entries of the items' page lists, in list order) and
+ * chunk_base_host (B + 1 partial-slot offsets by batch entry) may be NULL; a
+ * non-NULL buffer smaller than its part gives MKV_ERANGE.  MKV_ESTATE when the
+ * pool holds no current schedule (no decode since the last change that the
+ * cached schedule could not absorb). */
+typedef struct {
+  int32_t batch;           /* B of the decoded batch */
+  int32_t n_items;         /* work items */
+  int32_t n_list;          /* page-list entries in use */
+  int32_t n_chunks;        /* partial-state slots */
+  int32_t max_seq_chunks;  /* most slots of one batch entry */
+  int32_t heads_per_wave;  /* kv-heads per partial-kernel workgroup */
+  int32_t resident_waves;  /* partial-kernel waves the device holds at once (the schedule's target) */
+  int32_t pad0;
+} mkv_schedule_info;
+mkv_status mkv_debug_schedule(mkv_pool* pool, mkv_schedule_info* info, int32_t* items_host,
+                              int32_t items_cap, int32_t* entries_host, int32_t entries_cap,
+                              int32_t* chunk_base_host, int32_t base_cap);
+
 /* Profiling: when enabled, decode brackets each kernel with HIP events;
  * mkv_profile_read waits for the device and returns the accumulated times
  * (then clears them). */

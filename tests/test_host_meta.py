@@ -261,19 +261,21 @@ def test_schedule_covers_every_page_once_ragged_and_scattered(lib):
 
 def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
     # 131072 tokens, last 4096 FP8.  G = 6 puts two kv-heads on a workgroup,
-    # so an item takes four 4-wave workgroups for its 8 kv-heads: 2048
-    # resident waves give 128 items at most, of near-equal cost (an FP8 page
-    # costs as much as a TQ3 page by default).
+    # so an item takes four 4-wave workgroups for its 8 kv-heads.  The split-K
+    # floor keeps at least 256 chunks even where the resident waves (2048
+    # here) would give 128; 4096 resident waves (four per SIMD) give 256 too.
+    # An FP8 page costs two TQ3 pages (a wave walks it one kv-head at a time).
     h = _host(lib, num_kv_heads=8, max_seqs=1, max_pages_per_seq=8192, max_batch=1,
               max_q_heads=48, fp8_pages=8192, tq3_pages=8192, placement_seed=5)
     assert h.append(0, 131072)[0] == OK
     assert h.demote(0, list(range(8192 - 256)))[0] == OK
-    st, sc = h.schedule([0], 48, target_waves=2048)
-    assert st == OK
-    assert 120 <= sc["n_chunks"] <= 128 and sc["n8"] >= 1 and sc["n3"] >= 1
-    _check_coverage(h, [0], sc, 16)
-    cost = np.array([float(it[3]) for it in sc["items"]])
-    assert cost.max() <= 1.15 * (7936 + 256) / 128
+    for waves in (2048, 4096):
+        st, sc = h.schedule([0], 48, target_waves=waves)
+        assert st == OK
+        assert 256 <= sc["n_chunks"] <= 264 and sc["n8"] >= 1 and sc["n3"] >= 1
+        _check_coverage(h, [0], sc, 16)
+        cost = np.array([float(it[3]) * (2 if i < sc["n8"] else 1) for i, it in enumerate(sc["items"])])
+        assert cost.max() <= 1.15 * (7936 + 2 * 256) / 256
     sizes3 = sc["items"][sc["n8"]:, 3]
     assert sizes3.max() - sizes3.min() <= 1
     # algorithmic bytes: 126976 TQ3 tokens * 896 B + 4096 FP8 tokens * 2048 B + 256 pages * 64 B
@@ -283,26 +285,28 @@ def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
 
 
 def test_schedule_respects_chunk_capacity(lib):
-    # 4 * (2 + ceil(512 / 256)) = 16 is the smallest max_chunks this descriptor accepts
+    # chunks hold at most 240 pages: 4 * (2 + ceil(512 / 240)) = 20 is the
+    # smallest max_chunks this descriptor accepts
     with pytest.raises(ValueError):
-        _host(lib, max_pages_per_seq=512, fp8_pages=2048, max_chunks=15)
-    h = _host(lib, max_pages_per_seq=512, fp8_pages=2048, tq3_pages=2048, max_chunks=16)
+        _host(lib, max_pages_per_seq=512, fp8_pages=2048, max_chunks=19)
+    h = _host(lib, max_pages_per_seq=512, fp8_pages=2048, tq3_pages=2048, max_chunks=20)
     for s in range(4):
         h.append(s, 512 * 16)
     st, sc = h.schedule([0, 1, 2, 3], 8, chunk_pages=1)
-    assert st == OK and sc["n_chunks"] <= 16
+    assert st == OK and sc["n_chunks"] <= 20
     _check_coverage(h, [0, 1, 2, 3], sc, 16)
     h.close()
 
 
-def test_chunks_never_exceed_256_pages(lib):
+def test_chunks_never_exceed_240_pages(lib):
+    # (a wave of the partial kernel then spans at most 64 pages)
     h = _host(lib, max_pages_per_seq=1024, fp8_pages=1024, tq3_pages=1024, max_seqs=2)
     h.append(0, 1000 * 16 + 3)
     assert h.demote(0, list(range(0, 900)))[0] == OK
     st, sc = h.schedule([0], 8, chunk_pages=4096)
-    assert st == OK and sc["chunk_pages"] <= 256
-    assert sc["n3"] == 4 and sc["n8"] == 1          # ceil(900 / 256), ceil(101 / 256)
-    assert sc["items"][:, 3].max() <= 256
+    assert st == OK and sc["chunk_pages"] <= 240
+    assert sc["n3"] == 4 and sc["n8"] == 1          # ceil(900 / 240), ceil(101 / 240)
+    assert sc["items"][:, 3].max() <= 240
     _check_coverage(h, [0], sc, 16)
     h.close()
 
