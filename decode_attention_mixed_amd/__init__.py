@@ -101,7 +101,7 @@ class ScheduleInfo(ctypes.Structure):
 EXPORTED = [
     "mkv_pool_bytes", "mkv_record_bytes", "mkv_pool_create", "mkv_pool_destroy",
     "mkv_seq_reset", "mkv_append", "mkv_append_step", "mkv_demote", "mkv_materialize",
-    "mkv_decode", "mkv_seq_info",
+    "mkv_decode", "mkv_decode_static", "mkv_seq_info",
     "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_debug_schedule", "mkv_profile_enable",
     "mkv_profile_read", "mkv_status_string", "mkv_last_error",
 ]
@@ -130,6 +130,7 @@ def _load():
         "mkv_materialize": (I32, [P, I32, P, I32, P]),
         "mkv_append_step": (I32, [P, P, I32, P, P, P]),
         "mkv_decode": (I32, [P, P, I32, P, I32, F32, P, P, P]),
+        "mkv_decode_static": (I32, [P, P, I32, P, I32, F32, P, P, P]),
         "mkv_seq_info": (I32, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "mkv_page_table": (I32, [P, I32, P, I32]),
         "mkv_pool_stats": (I32, [P, ctypes.POINTER(Stats)]),
@@ -254,18 +255,28 @@ def materialize(src_pool, src_seq: int, dst_pool, dst_seq: int, stream=None) -> 
     _check(_load().mkv_materialize(src_pool, src_seq, dst_pool, dst_seq, _stream(stream)))
 
 
-def decode(pool, seq_ids, q, softmax_scale: float, out, lse, stream=None) -> None:
-    """q: bf16 [B][Hq][d]; out: fp32 [B][Hq][d]; lse: fp32 [B][Hq] (all device)."""
+def _decode(fn, pool, seq_ids, q, softmax_scale, out, lse, stream):
     import torch
     ids, B = _i32_array(seq_ids)
     if q.dim() != 3 or q.shape[0] != B:
         raise ValueError("q must be [B][Hq][d] with B = len(seq_ids)")
     Hq = q.shape[1]
-    _check(_load().mkv_decode(pool, ids, B, _dev_ptr(q, torch.bfloat16, name="q"), Hq,
-                              ctypes.c_float(softmax_scale),
-                              _dev_ptr(out, torch.float32, tuple(q.shape), name="out"),
-                              _dev_ptr(lse, torch.float32, tuple(q.shape[:2]), name="lse"),
-                              _stream(stream)))
+    _check(fn(pool, ids, B, _dev_ptr(q, torch.bfloat16, name="q"), Hq,
+              ctypes.c_float(softmax_scale),
+              _dev_ptr(out, torch.float32, tuple(q.shape), name="out"),
+              _dev_ptr(lse, torch.float32, tuple(q.shape[:2]), name="lse"),
+              _stream(stream)))
+
+
+def decode(pool, seq_ids, q, softmax_scale: float, out, lse, stream=None) -> None:
+    """q: bf16 [B][Hq][d]; out: fp32 [B][Hq][d]; lse: fp32 [B][Hq] (all device)."""
+    _decode(_load().mkv_decode, pool, seq_ids, q, softmax_scale, out, lse, stream)
+
+
+def decode_static(pool, seq_ids, q, softmax_scale: float, out, lse, stream=None) -> None:
+    """decode() with the partial states in the library's fixed per-GPU
+    workspace: allocates no device memory (calls on one GPU must not overlap)."""
+    _decode(_load().mkv_decode_static, pool, seq_ids, q, softmax_scale, out, lse, stream)
 
 
 def seq_info(pool, seq: int):

@@ -37,6 +37,7 @@ LIB_SOURCES = [
     ("kernels_quant.hip", ["-ffp-contract=off"]),
     ("kernels_partial.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("kernels_merge.hip", []),
+    ("workspace.hip", []),
 ]
 
 

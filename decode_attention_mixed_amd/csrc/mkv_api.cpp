@@ -138,6 +138,7 @@ struct mkv_pool {
   int32_t target_waves[2] = {2048, 1024};   // resident partial-kernel waves, 1 or 2 heads per wave
   int32_t merge_narrow_max = 16;            // per-lane merge up to this many chunks per entry
   bool pace = true;                         // progress-paced wave priorities (one-round launches)
+  void* static_ws = nullptr;                // the device's fixed workspace (mkv_decode_static)
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
@@ -307,6 +308,8 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
   };
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
+  e = mkv::static_workspace(p->device, &p->static_ws);
+  if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("static workspace: ") + hipGetErrorString(e));
   for (int nh = 1; nh <= 2; ++nh) {
     if (nh == 2 && desc->head_dim > 128) break;
     int waves = 0;
@@ -563,14 +566,41 @@ mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, h
   return MKV_OK;
 }
 
-mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void* q, int32_t Hq,
-                      float softmax_scale, float* out, float* lse, hipStream_t s) {
+namespace {
+
+// Where a decode keeps its partial states: the pool's workspace, or the
+// device's fixed one (mkv_decode_static), which bounds the chunk count.
+enum class StateHome { kPool, kStatic };
+
+// Bytes of the partial states of n_chunks chunks of Hq heads (m, l, acc).
+size_t state_bytes(int64_t n_chunks, int32_t Hq, int32_t d) {
+  const size_t slots = size_t(n_chunks) * size_t(Hq);
+  return 2 * align256(slots * 4) + slots * size_t(d) * 4;
+}
+
+mkv_status decode_impl(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void* q, int32_t Hq,
+                       float softmax_scale, float* out, float* lse, hipStream_t s, StateHome home) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
   if (!q || !out || !lse || !seq_ids) return set_err(MKV_EINVAL, "null argument");
   if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return set_err(MKV_EINVAL, "q must be 16-byte aligned");
+  const int32_t d = p->meta.geom().d;
+  auto fits = [&](int64_t n_chunks) {
+    if (home != StateHome::kStatic || state_bytes(n_chunks, Hq, d) <= mkv::kStaticWorkspaceBytes)
+      return MKV_OK;
+    return set_err(MKV_ERANGE, "partial states of " + std::to_string(n_chunks) + " chunks x " +
+                                   std::to_string(Hq) + " heads need " +
+                                   std::to_string(state_bytes(n_chunks, Hq, d)) +
+                                   " bytes; the static workspace holds " +
+                                   std::to_string(mkv::kStaticWorkspaceBytes));
+  };
+  if (home == StateHome::kStatic && !p->static_ws) return set_err(MKV_EHIP, "no static workspace");
   DeviceGuard guard(p->device);
   const bool same_batch = p->sched_valid && p->sched_Hq == Hq && int32_t(p->sched_ids.size()) == B &&
                           std::memcmp(p->sched_ids.data(), seq_ids, size_t(B) * 4) == 0;
+  if (same_batch) {
+    mkv_status r = fits(p->sched.n_chunks);
+    if (r) return r;
+  }
   if (same_batch && p->sched_version != p->meta.version() &&
       p->sched_layout == p->meta.layout_version()) {
     // Only token counts changed (appends inside existing pages): the page lists
@@ -596,7 +626,9 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     mkv::Schedule sc;
     int st = p->meta.build_schedule(seq_ids, B, Hq, pool_policy(p, Hq), &sc, &err);
     if (st) return set_err(mkv_status(st), err);
-    mkv_status r = p->wait_staging();
+    mkv_status r = fits(sc.n_chunks);
+    if (r) return r;
+    r = p->wait_staging();
     if (r) return r;
     // the staging slot mirrors the schedule region: one copy
     const size_t n8 = sc.items[0].size(), n3 = sc.items[1].size();
@@ -628,9 +660,17 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
   a.B = B;
   a.Hq = Hq;
   a.scale = softmax_scale;
-  a.pm = reinterpret_cast<float*>(p->mem + p->lay.pm);
-  a.pl = reinterpret_cast<float*>(p->mem + p->lay.pl);
-  a.pacc = reinterpret_cast<float*>(p->mem + p->lay.pacc);
+  if (home == StateHome::kStatic) {
+    const size_t slots = size_t(sc.n_chunks) * size_t(Hq);
+    uint8_t* ws = static_cast<uint8_t*>(p->static_ws);
+    a.pm = reinterpret_cast<float*>(ws);
+    a.pl = reinterpret_cast<float*>(ws + align256(slots * 4));
+    a.pacc = reinterpret_cast<float*>(ws + 2 * align256(slots * 4));
+  } else {
+    a.pm = reinterpret_cast<float*>(p->mem + p->lay.pm);
+    a.pl = reinterpret_cast<float*>(p->mem + p->lay.pl);
+    a.pacc = reinterpret_cast<float*>(p->mem + p->lay.pacc);
+  }
   a.out = out;
   a.lse = lse;
   a.nh = sc.heads_per_wave;
@@ -641,15 +681,29 @@ mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void
     const int64_t waves = int64_t(a.n_items) * ((a.pv.Hkv + a.nh - 1) / a.nh) * mkv::kWavesPerWorkgroup;
     a.pace = p->pace && waves <= p->target_waves[a.nh - 1] ? 1 : 0;
   }
+  // (profiling events are taken only on the pool-workspace path)
+  const bool prof = home == StateHome::kPool;
   {
-    ProfEvent* e = prof_begin(p, 0, s);
+    ProfEvent* e = prof ? prof_begin(p, 0, s) : nullptr;
     MKV_HIP(mkv::launch_partial(a, s));
-    prof_end(p, e, s);
+    if (prof) prof_end(p, e, s);
   }
-  ProfEvent* e = prof_begin(p, 1, s);
+  ProfEvent* e = prof ? prof_begin(p, 1, s) : nullptr;
   MKV_HIP(mkv::launch_merge(a, p->merge_narrow_max, s));
-  prof_end(p, e, s);
+  if (prof) prof_end(p, e, s);
   return MKV_OK;
+}
+
+}  // namespace
+
+mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void* q, int32_t Hq,
+                      float softmax_scale, float* out, float* lse, hipStream_t s) {
+  return decode_impl(p, seq_ids, B, q, Hq, softmax_scale, out, lse, s, StateHome::kPool);
+}
+
+mkv_status mkv_decode_static(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void* q, int32_t Hq,
+                             float softmax_scale, float* out, float* lse, hipStream_t s) {
+  return decode_impl(p, seq_ids, B, q, Hq, softmax_scale, out, lse, s, StateHome::kStatic);
 }
 
 mkv_status mkv_materialize(mkv_pool* src, int32_t src_seq, mkv_pool* dst, int32_t dst_seq,

@@ -90,4 +90,11 @@ hipError_t partial_resident_waves(int d, int nh, int kind, int* waves);
 // entry use the per-lane variant (no cross-lane reduction).
 hipError_t launch_merge(const DecodeArgs& a, int narrow_max, hipStream_t s);
 
+// Fixed per-device workspace for the partial states of an allocation-free
+// decode (m, l and acc regions of chunks x Hq slots, each 256-byte aligned).
+constexpr size_t kStaticWorkspaceBytes = size_t(16) << 20;
+// Device address of that workspace on `device`, which must be the current
+// device; looked up on the first call per device and cached.
+hipError_t static_workspace(int device, void** out);
+
 }  // namespace mkv

@@ -214,6 +214,23 @@ mkv_status mkv_decode(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const v
                       int32_t Hq, float softmax_scale, float* out, float* lse,
                       hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mkv_decode
+ * with the same arguments, kernels, results and errors, except that the
+ * partial states live in a fixed workspace of 16 MiB that the library holds on
+ * every GPU it runs on (from module load until the process ends) instead of in
+ * the pool.  No call allocates or frees device memory, and nothing is
+ * cleared: every state the merge reads is written by the same call first.
+ * Capacity: n_chunks * Hq * (d + 2) * 4 bytes (plus alignment) of partial
+ * states, where n_chunks is the split-K chunk count of the batch; a batch over
+ * that limit returns MKV_ERANGE before any work is enqueued.  All calls on one
+ * GPU share its workspace, which keeps the last call's contents: calls that
+ * overlap on one GPU (concurrent streams, or pools of one device used from
+ * several threads) race and must be ordered by the caller. */
+mkv_status mkv_decode_static(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const void* q,
+                             int32_t Hq, float softmax_scale, float* out, float* lse,
+                             hipStream_t stream);
+
 /* Materialising profile (Minima-KV summary, "Qualidade em contexto longo":
  * the hybrid pages expanded into dense tensors, a diagnostic the decode path
  * never uses).  Appends every token of sequence src_seq of the mixed pool src
