@@ -202,6 +202,26 @@ def record_bytes(desc: PoolDesc, fmt: int) -> int:
     return int(_load().mkv_record_bytes(ctypes.byref(desc), fmt))
 
 
+# (Hkv, d) of each live pool, keyed by handle value: the shape checks below
+_POOL_GEOM: dict = {}
+
+
+def _geom(pool):
+    key = pool.value if isinstance(pool, ctypes.c_void_p) else int(pool)
+    g = _POOL_GEOM.get(key)
+    if g is None:
+        raise ValueError("unknown pool handle (not created by pool_create, or destroyed)")
+    return g
+
+
+def _check_rows(name, t, lead, pool):
+    """t must be [lead][Hkv][d] for the pool's geometry (lead=None: any)."""
+    Hkv, d = _geom(pool)
+    if t.dim() != 3 or tuple(t.shape[1:]) != (Hkv, d) or (lead is not None and t.shape[0] != lead):
+        want = f"[{'n' if lead is None else lead}][{Hkv}][{d}]"
+        raise ValueError(f"{name} must be {want}, got {tuple(t.shape)}")
+
+
 def pool_create(desc: PoolDesc, device_mem=None):
     """Create a pool.  device_mem: None (library allocates) or a torch uint8
     device tensor of at least pool_bytes(desc) bytes that outlives the pool."""
@@ -213,11 +233,13 @@ def pool_create(desc: PoolDesc, device_mem=None):
         ptr = _dev_ptr(device_mem, name="device_mem")
         nbytes = device_mem.numel() * device_mem.element_size()
         _check(lib.mkv_pool_create(ctypes.byref(desc), ptr, nbytes, ctypes.byref(out)))
+    _POOL_GEOM[out.value] = (int(desc.num_kv_heads), int(desc.head_dim))
     return out
 
 
 def pool_destroy(pool) -> None:
     _check(_load().mkv_pool_destroy(pool))
+    _POOL_GEOM.pop(pool.value if isinstance(pool, ctypes.c_void_p) else int(pool), None)
 
 
 def seq_reset(pool, seq: int, stream=None) -> None:
@@ -227,6 +249,7 @@ def seq_reset(pool, seq: int, stream=None) -> None:
 def append(pool, seq: int, k, v, stream=None) -> None:
     """Append fp32 rows k, v [n][Hkv][d] (device) to sequence seq as FP8."""
     import torch
+    _check_rows("k", k, None, pool)
     n = k.shape[0]
     _check(_load().mkv_append(pool, seq, n, _dev_ptr(k, torch.float32, name="k"),
                               _dev_ptr(v, torch.float32, tuple(k.shape), name="v"),
@@ -242,8 +265,7 @@ def append_step(pool, seq_ids, k, v, stream=None) -> None:
     """One token per sequence: k, v fp32 device [B][Hkv][d], row b to seq_ids[b]."""
     import torch
     ids, B = _i32_array(seq_ids)
-    if k.dim() != 3 or k.shape[0] != B:
-        raise ValueError("k must be [B][Hkv][d] with B = len(seq_ids)")
+    _check_rows("k", k, B, pool)
     _check(_load().mkv_append_step(pool, ids, B, _dev_ptr(k, torch.float32, name="k"),
                                    _dev_ptr(v, torch.float32, tuple(k.shape), name="v"),
                                    _stream(stream)))
@@ -258,8 +280,9 @@ def materialize(src_pool, src_seq: int, dst_pool, dst_seq: int, stream=None) -> 
 def _decode(fn, pool, seq_ids, q, softmax_scale, out, lse, stream):
     import torch
     ids, B = _i32_array(seq_ids)
-    if q.dim() != 3 or q.shape[0] != B:
-        raise ValueError("q must be [B][Hq][d] with B = len(seq_ids)")
+    d = _geom(pool)[1]
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != d:
+        raise ValueError(f"q must be [B][Hq][{d}] with B = len(seq_ids) = {B}, got {tuple(q.shape)}")
     Hq = q.shape[1]
     _check(fn(pool, ids, B, _dev_ptr(q, torch.bfloat16, name="q"), Hq,
               ctypes.c_float(softmax_scale),

@@ -46,3 +46,33 @@ def test_library_loads_and_answers_host_only_queries():
     bad = mkv.make_desc(num_kv_heads=8, head_dim=100, page_size=16, max_seqs=1,
                         max_pages_per_seq=8, max_batch=1, max_q_heads=8, fp8_pages=8, tq3_pages=8)
     assert mkv.pool_bytes(bad) == 0
+
+
+def test_binding_rejects_tensors_of_the_wrong_geometry():
+    # shape checks run before any library call or device-pointer check, so a
+    # handle that is only registered (never passed to the library) serves
+    import torch
+    h = ctypes.c_void_p(0x1000)
+    mkv._POOL_GEOM[h.value] = (8, 128)
+    try:
+        bad_q = [torch.zeros(2, 48, 64), torch.zeros(3, 48, 128), torch.zeros(2, 128)]
+        for q in bad_q:
+            with pytest.raises(ValueError):
+                mkv.decode(h, [0, 1], q, 0.1, None, None)
+            with pytest.raises(ValueError):
+                mkv.decode_static(h, [0, 1], q, 0.1, None, None)
+        for k in [torch.zeros(5, 4, 128), torch.zeros(5, 8, 64), torch.zeros(5, 1024)]:
+            with pytest.raises(ValueError):
+                mkv.append(h, 0, k, k)
+        for k in [torch.zeros(2, 8, 64), torch.zeros(3, 8, 128), torch.zeros(2, 4, 128)]:
+            with pytest.raises(ValueError):
+                mkv.append_step(h, [0, 1], k, k)
+        # right shapes pass the shape check and stop at the device-pointer check
+        with pytest.raises(TypeError):
+            mkv.decode(h, [0, 1], torch.zeros(2, 48, 128, dtype=torch.bfloat16), 0.1, None, None)
+        with pytest.raises(TypeError):
+            mkv.append(h, 0, torch.zeros(5, 8, 128), torch.zeros(5, 8, 128))
+    finally:
+        del mkv._POOL_GEOM[h.value]
+    with pytest.raises(ValueError):
+        mkv.decode(h, [0], torch.zeros(1, 8, 128), 0.1, None, None)
