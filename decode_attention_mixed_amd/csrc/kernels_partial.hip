@@ -90,10 +90,10 @@ __device__ __forceinline__ uint32_t vgpr_opaque_zero() {
   return r;
 }
 
-// A VGPR holding the f16 pair (1.0, 1.0), opaque to constant folding.
-__device__ __forceinline__ uint32_t vgpr_one_pair() {
+// Per-half unsigned 16-bit maximum.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   uint32_t r;
-  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(r));
+  asm("v_pk_max_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
 
@@ -102,97 +102,85 @@ __device__ __forceinline__ float f16_half(uint32_t w, int h) {
   return float(__builtin_bit_cast(_Float16, uint16_t(w >> (16 * h))));
 }
 
-// f16 pair subtraction (x - c) with c given as the bits of two f16 values.
-__device__ __forceinline__ uint32_t sub_f16x2(uint32_t x, uint32_t c) {
-  const half2v h = __builtin_bit_cast(half2v, x) - __builtin_bit_cast(half2v, c);
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// f16 bits of 1 + 3.5 * 2^(k-10) = 1 + 7 * 2^(k-11)
-constexpr uint32_t center_bits(int k) { return 0x3C00u + (7u << (k - 1)); }
-
-// ---- TQ3 key unit unpack ---------------------------------------------------
-// A unit is 8 consecutive codes (24 bits, code i at bit 3i; bits 24..31 are
-// ignored).  It becomes four dwords of f16 pairs holding (c - 3.5) * 2^(k-10):
+// ---- TQ3 codes as f16 MFMA operands -------------------------------------------
+// A 3-bit code c placed at bits k .. k+2 (k <= 7) of an f16 half whose other
+// bits are zero is the subnormal number c * 2^(k-24): exact, and the MFMA
+// multiplies it exactly (the f16 matrix instructions of this architecture
+// keep subnormal inputs).  One AND of a 32-bit window of a code stream with
+// a mask thus yields two codes as operands, each carrying a power of two that
+// the other operand (or the result) takes back.  The centring (c - 3.5) is
+// applied outside the MFMA: for keys through the accumulator's initial value,
+// for values through the probability mass of the tile.
+//
+// Key operands.  Quad q of the MFMA's A operand takes codes 8q .. 8q+7 of the
+// group (bits 24q .. 24q+23 of its 96-bit stream), from two windows starting
+// at bits 24q - 4 and 24q + 2.  Each window gives two operand dwords through
+// the masks below; the 8 k-slots of the lane then hold
 //   slot:        0   1   2   3   4   5   6   7
-//   code index:  2   6   3   7   4   0   5   1     (kSlotCode)
-//   bit pos k:   6   2   7   3   3   7   3   7     (kSlotShift)
-// Dword j takes the unit rotated right by 0, 2, 9 or 12 bits, which puts two
-// codes inside the two 10-bit mantissa fields at positions k >= 1; the codes
-// are AND-ed into the mantissas of (1.0, 1.0) and (1 + 3.5 * 2^(k-10)) is
-// subtracted.  Both operands of the subtraction lie in [1, 2) and the
-// constant has at most 10 fraction bits because k >= 1, so the result is
-// exact and, as |c - 3.5| >= 1/2, an f16 normal number.
-constexpr int kSlotCode[8] = {2, 6, 3, 7, 4, 0, 5, 1};
-constexpr int kSlotShift[8] = {6, 2, 7, 3, 3, 7, 3, 7};
-constexpr uint32_t center_pair(int slot) {
-  return center_bits(kSlotShift[slot]) | (center_bits(kSlotShift[slot + 1]) << 16);
+//   code 8q + :  0   4   1   5   2   6   3   7     (kSlotCode)
+//   bit pos k:   4   0   7   3   4   0   7   3     (kSlotShift)
+// The first window is the funnel shift by 28 - 8q of the dwords q - 1 and q
+// of the group (for quad 0 the dword before the group, for quad 3 the one
+// after it: their bits land only where the masks clear them); the second is
+// the first shifted right by 6 (the masks use its bits 0..21 only).
+constexpr int kSlotCode[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+constexpr int kSlotShift[8] = {4, 0, 7, 3, 4, 0, 7, 3};
+constexpr uint32_t kKeyMaskA = (7u << 4) | (7u << 16);    // codes at k = 4 (low), 0 (high)
+constexpr uint32_t kKeyMaskB = (7u << 7) | (7u << 19);    // codes at k = 7 (low), 3 (high)
+// Checks the table against the windows: quad 0, window start ws, mask m.
+constexpr bool key_slot_ok(int slot) {
+  const int code = kSlotCode[slot], k = kSlotShift[slot];
+  const int ws = slot < 4 ? -4 : 2;                        // window of this slot
+  const int half = slot & 1;                               // operand half
+  const uint32_t m = ((slot >> 1) & 1) ? kKeyMaskB : kKeyMaskA;
+  const int pos = 3 * code - ws;                           // code position in the window
+  return pos == 16 * half + k && ((m >> pos) & 7u) == 7u && k >= 0 && k <= 7;
 }
-static_assert(center_pair(0) == 0x3C0E3CE0u && center_pair(2) == 0x3C1C3DC0u &&
-                  center_pair(4) == 0x3DC03C1Cu && center_pair(6) == 0x3DC03C1Cu,
-              "centering constants");
+static_assert(key_slot_ok(0) && key_slot_ok(1) && key_slot_ok(2) && key_slot_ok(3) && key_slot_ok(4) &&
+                  key_slot_ok(5) && key_slot_ok(6) && key_slot_ok(7),
+              "key operand slots");
 
-__device__ __forceinline__ u32x4 tq3_unit_to_f16(uint32_t x, uint32_t one) {
-  const uint32_t r2 = __builtin_amdgcn_alignbit(x, x, 2);
-  const uint32_t r9 = __builtin_amdgcn_alignbit(x, x, 9);
-  const uint32_t r12 = __builtin_amdgcn_alignbit(x, x, 12);
-  u32x4 o;
-  o[0] = sub_f16x2(and_or(x, 0x001C01C0u, one), center_pair(0));     // c2 -> bits 6..8, c6 -> 18..20
-  o[1] = sub_f16x2(and_or(r2, 0x00380380u, one), center_pair(2));    // c3 -> bits 7..9, c7 -> 19..21
-  o[2] = sub_f16x2(and_or(r9, 0x03800038u, one), center_pair(4));    // c4 -> bits 3..5, c0 -> 23..25
-  o[3] = sub_f16x2(and_or(r12, 0x03800038u, one), center_pair(6));   // c5 -> bits 3..5, c1 -> 23..25
-  return o;
-}
-
-// The four 24-bit units of a 12-byte group held as three little-endian dwords.
-__device__ __forceinline__ void tq3_split_units(const uint32_t d[3], uint32_t u[4]) {
-  u[0] = d[0];
-  u[1] = __builtin_amdgcn_alignbit(d[1], d[0], 24);
-  u[2] = __builtin_amdgcn_alignbit(d[2], d[1], 16);
-  u[3] = d[2] >> 8;
+// Operand of one key unit from dwords q - 1 and q of the group (see above).
+__device__ __forceinline__ u32x4 tq3_key_operand(uint32_t lo, uint32_t hi, uint32_t s1) {
+  const uint32_t w1 = __builtin_amdgcn_alignbit(hi, lo, s1);
+  const uint32_t w2 = w1 >> 6;
+  return u32x4{w1 & kKeyMaskA, w1 & kKeyMaskB, w2 & kKeyMaskA, w2 & kKeyMaskB};
 }
 
 // ---- TQ3 value group unpack ------------------------------------------------
 // A group is 32 codes held as three little-endian dwords, code i at bits
 // 3i .. 3i+2.  Read as a ring of 96 bits, any 32-bit window starting at bit b
 // is one funnel shift of two of the dwords (no shift for b = 0, 32, 64).  One
-// AND-OR of a window keeps two codes, code lo at bits k_lo .. k_lo+2 of the
-// low half and code hi at bits 16+k_hi .. 18+k_hi (1 <= k <= 7, inside the
-// f16 mantissa field), on top of the exponent of 1.0; subtracting
-// 1 + 3.5 * 2^(k-10) leaves (c - 3.5) * 2^(k-10).  Both operands lie in
-// [1, 2) and the constant has at most 10 fraction bits because k >= 1, so the
-// difference is exact and, as |c - 3.5| >= 1/2, an f16 normal number.  The
-// sixteen pairs below, (window start, lo, hi), cover the group with six
-// shifted windows; the bit offsets follow from them.  (Value tiles are
-// unpacked once per tile by the lane that loads the group, so the whole group
-// is at hand; key operands are unpacked per MFMA chunk from units instead.)
+// AND of a window keeps two codes, code lo at bits k_lo .. k_lo+2 of the low
+// half and code hi at bits 16+k_hi .. 18+k_hi (0 <= k <= 7), which are the
+// subnormal f16 values c * 2^(k-24).  The sixteen pairs below, (window start,
+// lo, hi), cover the group with four shifted windows (no cover with three
+// exists); the bit offsets follow from them.  (Value tiles are unpacked once
+// per tile by the lane that loads the group, so the whole group is at hand.)
 struct Tq3Pair {
   int win, lo, hi;
 };
 constexpr Tq3Pair kValuePairs[16] = {
-    {0, 2, 7},    {6, 3, 8},    {6, 4, 9},    {13, 5, 10},  {13, 6, 12},  {32, 11, 17},
-    {32, 13, 18}, {40, 14, 19}, {41, 15, 20}, {41, 16, 21}, {64, 22, 28}, {64, 23, 29},
-    {70, 24, 30}, {70, 25, 31}, {77, 26, 0},  {77, 27, 1}};
+    {0, 0, 6},    {0, 1, 7},    {4, 2, 8},    {4, 3, 9},    {10, 4, 10},  {10, 5, 11},
+    {32, 12, 17}, {32, 13, 18}, {41, 14, 19}, {41, 15, 20}, {41, 16, 21}, {64, 22, 27},
+    {64, 23, 28}, {71, 24, 29}, {71, 25, 30}, {71, 26, 31}};
 constexpr int kappa_lo(const Tq3Pair& p) { return (3 * p.lo - p.win + 96) % 96; }
 constexpr int kappa_hi(const Tq3Pair& p) { return (3 * p.hi - p.win + 96) % 96 - 16; }
 constexpr uint32_t pair_mask(const Tq3Pair& p) {
   return (7u << kappa_lo(p)) | (7u << (16 + kappa_hi(p)));
 }
-constexpr bool is_cover(const Tq3Pair (&t)[16], int kmin) {
+constexpr bool is_cover(const Tq3Pair (&t)[16]) {
   uint32_t seen = 0;
   for (const Tq3Pair& p : t) {
     const int a = kappa_lo(p), b = kappa_hi(p);
-    if (a < kmin || a > 7 || b < kmin || b > 7 || p.win < 0 || p.win >= 96) return false;
+    if (a < 0 || a > 7 || b < 0 || b > 7 || p.win < 0 || p.win >= 96) return false;
     const uint32_t bits = (1u << p.lo) | (1u << p.hi);
     if ((seen & bits) != 0 || p.lo == p.hi) return false;
     seen |= bits;
   }
   return seen == 0xFFFFFFFFu;
 }
-static_assert(is_cover(kValuePairs, 1), "TQ3 value pair cover");
-constexpr uint32_t value_center(const Tq3Pair& p) {
-  return center_bits(kappa_lo(p)) | (center_bits(kappa_hi(p)) << 16);
-}
+static_assert(is_cover(kValuePairs), "TQ3 value pair cover");
 
 // Value position 2p + h (half h of pair p) as a byte (dim-in-group | k << 5),
 // 8 per 64-bit word, for run-time lookups.
@@ -215,13 +203,10 @@ __device__ __forceinline__ uint32_t group_window(const uint32_t (&w)[3], int b) 
   return (b & 31) == 0 ? lo : __builtin_amdgcn_alignbit(hi, lo, b & 31);
 }
 
-// Value group -> 16 dwords of centred f16 pairs, pair p in dword p.
-__device__ __forceinline__ void tq3_value_group(const uint32_t (&w)[3], uint32_t one,
-                                                uint32_t (&o)[16]) {
+// Value group -> 16 dwords of f16 pairs c * 2^(k-24), pair p in dword p.
+__device__ __forceinline__ void tq3_value_group(const uint32_t (&w)[3], uint32_t (&o)[16]) {
 #pragma unroll
-  for (int p = 0; p < 16; ++p)
-    o[p] = sub_f16x2(and_or(group_window(w, kValuePairs[p].win), pair_mask(kValuePairs[p]), one),
-                     value_center(kValuePairs[p]));
+  for (int p = 0; p < 16; ++p) o[p] = group_window(w, kValuePairs[p].win) & pair_mask(kValuePairs[p]);
 }
 
 // ---- FP8 -> f16 -------------------------------------------------------------
@@ -256,6 +241,88 @@ __device__ __forceinline__ half8 pprime(const float p[4], const float sv[4]) {
     r[4 + i] = _Float16(__builtin_fmaf(p[i], sv[i], -float(h)));
   }
   return r;
+}
+
+// The same from f16 scales held in halves of dwords, written as explicit
+// mixed-precision FMAs (the compiler widens the scales first otherwise):
+// pair word of f16(p_a * s_a) | f16(p_b * s_b) << 16, s_a half HA of wa,
+// s_b half HB of wb; and the pair word of the remainders f16(p * s - hi).
+#define MKV_MIX_HI(HA, HB)                                                              \
+  "v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0," #HA ",0] op_sel_hi:[0,1,0]\n\t"            \
+  "v_fma_mixhi_f16 %0, %3, %4, 0 op_sel:[0," #HB ",0] op_sel_hi:[0,1,0]"
+#define MKV_MIX_LO(HA, HB)                                                              \
+  "v_fma_mixlo_f16 %0, %1, %2, -%5 op_sel:[0," #HA ",0] op_sel_hi:[0,1,1]\n\t"                \
+  "v_fma_mixhi_f16 %0, %3, %4, -%5 op_sel:[0," #HB ",1] op_sel_hi:[0,1,1]"
+template <int HA, int HB>
+__device__ __forceinline__ uint32_t mix_hi(float pa, uint32_t wa, float pb, uint32_t wb) {
+  uint32_t d;
+  if constexpr (HA == 0 && HB == 0) asm(MKV_MIX_HI(0, 0) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb));
+  else if constexpr (HA == 0 && HB == 1) asm(MKV_MIX_HI(0, 1) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb));
+  else if constexpr (HA == 1 && HB == 0) asm(MKV_MIX_HI(1, 0) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb));
+  else asm(MKV_MIX_HI(1, 1) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb));
+  return d;
+}
+template <int HA, int HB>
+__device__ __forceinline__ uint32_t mix_lo(float pa, uint32_t wa, float pb, uint32_t wb, uint32_t hi) {
+  uint32_t d;
+  if constexpr (HA == 0 && HB == 0) asm(MKV_MIX_LO(0, 0) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb), "v"(hi));
+  else if constexpr (HA == 0 && HB == 1) asm(MKV_MIX_LO(0, 1) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb), "v"(hi));
+  else if constexpr (HA == 1 && HB == 0) asm(MKV_MIX_LO(1, 0) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb), "v"(hi));
+  else asm(MKV_MIX_LO(1, 1) : "=&v"(d) : "v"(pa), "v"(wa), "v"(pb), "v"(wb), "v"(hi));
+  return d;
+}
+#undef MKV_MIX_HI
+#undef MKV_MIX_LO
+// p * (f16 half H of w) + c in fp32
+template <int H>
+__device__ __forceinline__ float fma_mix_f32(float p, uint32_t w, float c) {
+  float r;
+  if constexpr (H == 0) asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(p), "v"(w), "v"(c));
+  else asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(p), "v"(w), "v"(c));
+  return r;
+}
+
+// Value scales of pass ps for the lane's 4 tokens, from the slot's scale rows
+// sp (token t: NG f16): NG >= 2: sw[i] = the scales of groups 2ps, 2ps + 1 of
+// token i; NG = 1: sw[0], sw[1] = tokens (0, 1) and (2, 3).  Tokens i >= nv
+// get 0.
+template <int NG>
+__device__ __forceinline__ void tq3_pass_scales(const uint32_t* sp, int ps, int nv, uint32_t (&sw)[4]) {
+  if constexpr (NG >= 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sw[i] = sp[i * (NG / 2) + ps];
+    if (nv < 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i >= nv) sw[i] = 0u;
+    }
+  } else {
+    sw[0] = sp[0];
+    sw[1] = sp[1];
+    sw[2] = sw[3] = 0u;
+    if (nv < 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i >= nv) sw[i >> 1] &= (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    }
+  }
+}
+
+// P' of the lane's 4 tokens for group 2ps + H of a pass (scales as
+// tq3_pass_scales gives them; NG = 1: H = 0).  hi = pair words of tokens
+// (0, 1), (2, 3); lo = their remainders; mass += sum of p * s.
+template <int NG, int H>
+__device__ __forceinline__ void pprime_tq3(const float p[4], const uint32_t (&sw)[4], uint32_t (&hi)[2],
+                                           uint32_t (&lo)[2], float& mass) {
+  constexpr int HA = NG >= 2 ? H : 0, HB = NG >= 2 ? H : 1;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t wa = NG >= 2 ? sw[2 * k] : sw[k], wb = NG >= 2 ? sw[2 * k + 1] : sw[k];
+    hi[k] = mix_hi<HA, HB>(p[2 * k], wa, p[2 * k + 1], wb);
+    lo[k] = mix_lo<HA, HB>(p[2 * k], wa, p[2 * k + 1], wb, hi[k]);
+    mass = fma_mix_f32<HA>(p[2 * k], wa, mass);
+    mass = fma_mix_f32<HB>(p[2 * k + 1], wb, mass);
+  }
 }
 
 // FP8: one scale for all four tokens (page-head scale).
@@ -703,20 +770,39 @@ struct Mix {
   static constexpr int VBUF = NH * 16 * VROWB;          // value tile of the NH heads
   static constexpr int WAVE = NSLOT * SLOT + VBUF;      // LDS bytes of one wave
   static constexpr int CPH = (12 * NG + 63) / 64;      // code loads per head of a TQ3 half
-  static constexpr int TNI = NH * CPH + 1;              // load instructions of a TQ3 half
+  static constexpr int TNI = NH * (CPH + 1);            // load instructions of a TQ3 half
   static constexpr int SCOFF = NH * 16 * ROWB;          // scales of a TQ3 half-slot
-  static_assert(NH * 2 * NG <= 64, "one scale load per half");
+  // TQ3 mode leaves the end of each half-slot unwritten: it holds the key
+  // centring values of the wave's columns, 8 bytes (the value twice) per
+  // column and group, KPS groups per slot
+  static constexpr int KIOFF = (NH * THALF + 15) / 16 * 16;
+  static constexpr int KPS = (SLOT - KIOFF) / 128;
+  static constexpr int kinit_off(int g) { return (g / KPS) * SLOT + KIOFF + (g % KPS) * 128; }
+  // the workgroup's shared copies: centring values of group g in wave
+  // g mod 4's half-slot tails; the query operands of (kv-head j, group g),
+  // 1 KB each, in the value tiles (free until the tile loop)
+  static __device__ uint8_t* kinit_addr(uint8_t* smem, int g) {
+    return smem + (g % kWaves) * WAVE + VBUF + kinit_off(g / kWaves);
+  }
+  static constexpr int QPW = VBUF / 1024;               // operand blocks per value tile
+  static __device__ uint8_t* qop_addr(uint8_t* smem, int j, int g) {
+    const int k = j * NG + g;
+    return smem + (k / QPW) * WAVE + (k % QPW) * 1024;
+  }
+  static_assert(2 * NG <= 64, "one scale load per head and half");
   static constexpr int FVEC = FHALF / 16;
   static constexpr int FNI = (FVEC + 63) / 64;
   static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
   static constexpr size_t SMEM = cmax(size_t(kWaves) * WAVE, sizeof(MergeLds<D>));
   static_assert(NH * THALF <= SLOT && FHALF <= SLOT, "a half-tile fits a slot");
+  static_assert(KPS * NSLOT >= (NG + kWaves - 1) / kWaves, "key centring values fit the slots' tails");
+  static_assert(QPW * kWaves >= NH * NG, "query operands fit the value tiles");
   static_assert(TNI <= 4 && FNI <= 4, "load instructions per half");
 };
 
 // Position of 32-byte segment `seg` of value-tile row r.  The transposing
 // reads of a half-wave touch 8 rows at one segment; XOR-ing the segment index
-// with bits of the row spreads those 8 reads over all 64 banks.
+// with bits of the row spreads those 8 reads over the banks.
 template <int VROWB>
 __device__ __forceinline__ int vseg(int r, int seg) {
   if constexpr (VROWB == 128) return seg ^ ((r >> 1) & 3);
@@ -734,19 +820,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // for its reads: the compiler would otherwise make such a read wait for every
 // load into LDS still in flight (the next tiles' halves), since it cannot tell
 // that they write other slots.
-template <int NH>
-__device__ __forceinline__ void value_operands2(uint32_t a0, uint32_t a1, uint32_t head1_off,
-                                                half8& v0, half8& v1) {
+template <int NH, int HEAD1_OFF = 0>
+__device__ __forceinline__ void value_operands2(uint32_t a0, uint32_t a1, half8& v0, half8& v1) {
   u32x2 x0, x1, y0, y1;
   if constexpr (NH == 2) {
+    // the second kv-head's rows sit HEAD1_OFF bytes on
     asm volatile(
         "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %6\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
         "ds_read_b64_tr_b16 %2, %5\n\t"
-        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
-        : "v"(a0), "v"(a1), "v"(a0 + head1_off), "v"(a1 + head1_off)
+        : "v"(a0), "v"(a1), "n"(HEAD1_OFF)
         : "memory");
   } else {
     asm volatile(
@@ -801,9 +887,9 @@ __device__ __forceinline__ u32x2 fp8x4_to_f16_s(uint32_t w) {
 // Softmax step of one tile for the lane's column (as softmax_step, with the
 // accumulator rows' correction factors read from the lanes of their columns;
 // `live` false: the column takes no token of this tile).
-template <int NACC>
+template <int NACC, typename OnRescale>
 __device__ __forceinline__ void softmax_live(SoftState& st, float s[4], float p[4], f32x4 (&acc)[NACC],
-                                             int quad, bool live) {
+                                             int quad, bool live, OnRescale on_rescale) {
   float tmax = vmax(vmax(s[0], s[1]), vmax(s[2], s[3]));
   tmax = quad_max2(tmax);
   if (__any(tmax > st.m)) {
@@ -814,6 +900,7 @@ __device__ __forceinline__ void softmax_live(SoftState& st, float s[4], float p[
     const float corr = rise ? exp2f(st.m - m_new) : 1.0f;   // 0 on the column's first tile
     st.m = m_new;
     st.l *= corr;
+    on_rescale(corr);
     // accumulator row i of this lane is column 4quad + i, whose factor lane
     // 4quad + i (column 4quad + i, quad 0) holds
 #pragma unroll
@@ -867,85 +954,135 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   const int ncol = NH * G;
   const int hq0 = hk0 * G;
   const int jcol = col < ncol ? col / G : 0;    // kv-head (within the workgroup) of column col
-  uint8_t* wl = smem + wave * C::WAVE;          // this wave's slots and value tile
-  uint8_t* vt = wl + C::NSLOT * C::SLOT;
-  const uint32_t one = vgpr_one_pair();
+  uint8_t* vt = smem + wave * C::WAVE;          // this wave's value tile, then its slots
+  uint8_t* wl = vt + C::VBUF;
   const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
 
   f32x4 acc[NT];                                // one per N-tile, both kv-heads' rows
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   SoftState st;
-
-  if (tg.ntiles > 0) {
-    const WavePages wp = wave_pages(a, it, tg);
-    // query rows of the lane's column: fetched now, converted once the first
-    // tile's loads are in flight
-    const bool qlive = col < ncol;
-    const uint16_t* qrow = a.q + (int64_t(it.b) * a.Hq + hq0 + (qlive ? col : 0)) * D;
-    u32x4 qraw[NG];
+  // probability mass of the lane's column times the value scale, per group
+  // (this lane's tokens): the value codes enter the MFMA uncentred, so the
+  // accumulator of group g misses -3.5 times this sum
+  float vmass[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) qraw[g] = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
+  for (int g = 0; g < NG; ++g) vmass[g] = 0.0f;
 
-    // A half-slot holds the key (value) codes of the NH heads, 16 token rows
-    // each, then their scales.  Each code load copies up to 64 16-byte vectors
-    // of one head's rows (lane l: bytes 16l..), the scale load the scale
-    // vectors of all NH heads; the tile and head positions are scalar offsets.
-    const int BLK = pv.P * 28 * NG;              // TQ3 bytes of one kv-head of a page
-    const uint32_t voff_c = 16u * uint32_t(lane);
-    const uint32_t voff_s = uint32_t((lane / (2 * NG)) * BLK + 2 * pv.P * ROWB + 16 * (lane % (2 * NG)));
-    Cursor lc = tg.first;                        // next tile whose halves are loaded
-    int ls = 0;                                  // next slot to fill
-    auto issue = [&](bool value_half) {
-      const auto rsrc = record_rsrc(wp.page(pv, lc.page), pv.tq3_stride);
-      uint8_t* dst = wl + ls * C::SLOT;
-      const int code0 = hk0 * BLK + (value_half ? pv.P * ROWB : 0) + lc.sub * 16 * ROWB;
+  const WavePages wp = wave_pages(a, it, tg);
+  // query rows of the lane's column: fetched now, converted once the first
+  // tile's loads are in flight
+  const bool qlive = col < ncol;
+  const uint16_t* qrow = a.q + (int64_t(it.b) * a.Hq + hq0 + (qlive ? col : 0)) * D;
+  u32x4 qraw[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) qraw[g] = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
+
+  // A half-slot holds the key (value) codes of the NH heads, 16 token rows
+  // each, then their scales.  Each code load copies up to 64 16-byte vectors
+  // of one head's rows (lane l: bytes 16l..), each scale load the 2NG scale
+  // vectors of one head; the tile and head positions are scalar offsets.
+  const int BLK = pv.P * 28 * NG;                // TQ3 bytes of one kv-head of a page
+  const uint32_t voff_c = 16u * uint32_t(lane);
+  Cursor lc = tg.first;                          // next tile whose halves are loaded
+  int ls = 0;                                    // next slot to fill
+  auto issue = [&](bool value_half) {
+    const auto rsrc = record_rsrc(wp.page(pv, lc.page), pv.tq3_stride);
+    uint8_t* dst = wl + ls * C::SLOT;
+    const int code0 = hk0 * BLK + (value_half ? pv.P * ROWB : 0) + lc.sub * 16 * ROWB;
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int x = 0; x < C::CPH; ++x)
+        if (64 * x + lane < 12 * NG)
+          lds_load16(rsrc, dst + j * 16 * ROWB + 1024 * x, voff_c, code0 + j * BLK + 1024 * x);
+    if (lane < 2 * NG)
 #pragma unroll
       for (int j = 0; j < NH; ++j)
-#pragma unroll
-        for (int x = 0; x < C::CPH; ++x)
-          if (64 * x + lane < 12 * NG)
-            lds_load16(rsrc, dst + j * 16 * ROWB + 1024 * x, voff_c, code0 + j * BLK + 1024 * x);
-      if (lane < NH * 2 * NG)
-        lds_load16(rsrc, dst + NH * 16 * ROWB, voff_s,
-                   hk0 * BLK + (value_half ? pv.P * C::SCB : 0) + lc.sub * 16 * C::SCB);
-      ls = ls == C::NSLOT - 1 ? 0 : ls + 1;
-      if (value_half) advance_clamped(lc, tg);   // past the end, the last tile is loaded again
-    };
+        lds_load16(rsrc, dst + NH * 16 * ROWB + j * 16 * C::SCB, voff_c,
+                   (hk0 + j) * BLK + 2 * pv.P * ROWB + (value_half ? pv.P * C::SCB : 0) +
+                       lc.sub * 16 * C::SCB);
+    ls = ls == C::NSLOT - 1 ? 0 : ls + 1;
+    if (value_half) advance_clamped(lc, tg);     // past the end, the last tile is loaded again
+  };
+  if (tg.ntiles > 0) {
     issue(false);
     issue(true);
     issue(false);
+  }
 
-    // query operands: slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s],
-    // scaled by 2^(E + 7 - kSlotShift[s]) against the key slot's 2^(k-10)
-    half8 qop[NH][NG];
-    float F;
-    {
-      half8 qh[NG];
-      const int E = load_query<NG, NH>(
-          a, it.b, hq0, col, ncol, jcol, qop, qh,
-          [&](const uint16_t*, int g, float (&v)[8]) {
+  // Query operands, shared by the workgroup's waves (same sequence and
+  // kv-heads): slot s of MFMA g holds dim 32g + 8quad + kSlotCode[s], scaled
+  // by 2^(E + 7 - kSlotShift[s]) against the key slot's 2^(k-24), so each
+  // product is c * q * 2^(E-17); E is the column's exponent (max|q| * 2^E in
+  // [64, 128)).  Wave w converts the groups g = w mod 4 and publishes their
+  // operands for each kv-head of the wave (zero outside that head's columns)
+  // through the value tiles, which no wave uses before its first tile's
+  // values, and the key centring -3.5 * sum of q * 2^(E-17) over the group's
+  // dims as the pair (v, v) per column in a half-slot tail, where the tile
+  // loop reads it as the groups' accumulator initial value.
+  half8 qop[NH][NG];
+  float F;
+  {
+    // max |q| of the column: the magnitude bits of bf16 values order like
+    // unsigned integers (no NaN in a query), so packed 16-bit maxima do
+    uint32_t mbits = 0u;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              const int e = kSlotCode[s];
-              v[s] = bf16_to_f32(uint16_t(qraw[g][e >> 1] >> (16 * (e & 1))));
-            }
-          },
-          [](float x, int E, int s) { return _Float16(__builtin_amdgcn_ldexpf(x, E + 7 - kSlotShift[s])); });
-      F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 3 - E);
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) mbits = pk_max_u16(mbits, qraw[g][x] & 0x7FFF7FFFu);
+    float amax = __uint_as_float(max(mbits & 0xFFFFu, mbits >> 16) << 16);
+    amax = qlive ? quad_max(amax) : 0.0f;
+    const int E = q_shift(amax);
+    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 17 - E);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g % kWaves != wave) continue;
+      half8 qh;
+      float part = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int e = kSlotCode[sl];
+        const float x = qlive ? bf16_to_f32(uint16_t(qraw[g][e >> 1] >> (16 * (e & 1)))) : 0.0f;
+        qh[sl] = _Float16(__builtin_amdgcn_ldexpf(x, E + 7 - kSlotShift[sl]));
+        part = __builtin_fmaf(float(qh[sl]), __builtin_amdgcn_ldexpf(1.0f, kSlotShift[sl] - 24), part);
+      }
+      const float kinit = -3.5f * quad_sum(part);
+      if (quad == 0) *reinterpret_cast<f32x2*>(C::kinit_addr(smem, g) + 8 * col) = f32x2{kinit, kinit};
+      const u32x4 w = __builtin_bit_cast(u32x4, qh);
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const u32x4 o = {jcol == j ? w[0] : 0u, jcol == j ? w[1] : 0u, jcol == j ? w[2] : 0u, jcol == j ? w[3] : 0u};
+        *reinterpret_cast<u32x4*>(C::qop_addr(smem, j, g) + 16 * lane) = o;
+      }
     }
-
-    // lane constants: the unit of a key group a lane reads (dword offset and
-    // funnel shift of unit `quad`, bytes 3quad .. 3quad+2 of the group)
-    const int uoff = quad == 0 ? 0 : quad - 1;
-    const uint32_t ush = uint32_t(32 - 8 * quad) & 31u;
-    // value-tile addresses of the transposing reads (row 4quad + col/4,
-    // 8 bytes at column 4(col & 3) of N-tile n of the pass)
-    const int vr = 4 * quad + (col >> 2);
-    uint32_t vrd[2 * PASS];
+    __syncthreads();
 #pragma unroll
-    for (int n = 0; n < 2 * PASS; ++n) vrd[n] = uint32_t(vr * VROWB + 32 * vseg<VROWB>(vr, n) + 8 * (col & 3));
-    const uint32_t vt_addr = lds_addr(vt);
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        qop[j][g] = *reinterpret_cast<const half8*>(C::qop_addr(smem, j, g) + 16 * lane);
+    __syncthreads();                             // the value tiles are free again
+  }
+
+  if (tg.ntiles > 0) {
+    // lane constant: the funnel shift of the first key window (dwords
+    // quad - 1 and quad of the group; quad 0 reads the dword before the
+    // group, which the value tile in front of the slots keeps inside this
+    // workgroup's LDS)
+    const uint32_t ks1 = uint32_t(28 - 8 * quad);
+    // byte offset of the lane's key dwords in a slot (kept opaque so that the
+    // slot's constant part stays in the scalar base and the per-MFMA offsets
+    // fit the LDS instructions' immediate fields)
+    uint32_t klane = uint32_t(C::VBUF + col * ROWB + 4 * (quad - 1));
+    asm volatile("" : "+v"(klane));
+    // value-tile addresses of the transposing reads (row 4quad + col/4,
+    // 8 bytes at column 4(col & 3) of N-tile n of the pass): segment n of a
+    // row is segment 0 with n XOR-ed into bits 5.. of the address (the tile
+    // sits at a multiple of 1 KB and a row's offset has those bits clear)
+    const int vr = 4 * quad + (col >> 2);
+    const uint32_t va0 = lds_addr(vt) + uint32_t(vr * VROWB + 32 * vseg<VROWB>(vr, 0) + 8 * (col & 3));
+    const uint32_t va1 = va0 ^ 32u;
     // value unpack: lane -> (token ut, head uj, group ug of the pass); spare
     // lanes repeat a real one's work
     const int ci = lane % (16 * NH * PASS);
@@ -959,6 +1096,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       const int nvalid = valid_in_tile(pc, tg);
       const uint8_t* kb = wl + ks * C::SLOT;
       const uint8_t* vb = wl + vs * C::SLOT;
+      const uint8_t* kq = vt + ks * C::SLOT + klane;    // = kb + lane's row and dword
 
       // ---- keys: QK^T per group, both kv-heads into one D, scaled per token
       wait_vm<2 * TNI>();                        // this tile's key half has landed
@@ -967,13 +1105,13 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        f32x4 dg = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x2 k0 = *reinterpret_cast<const f32x2*>(C::kinit_addr(smem, g) + 8 * col);
+        f32x4 dg = {k0[0], k0[1], k0[0], k0[1]};
 #pragma unroll
         for (int j = 0; j < NH; ++j) {
-          const uint32_t* u = reinterpret_cast<const uint32_t*>(kb + j * 16 * ROWB + col * ROWB + 12 * g) + uoff;
-          const uint32_t x = __builtin_amdgcn_alignbit(u[1], u[0], ush);
-          dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tq3_unit_to_f16(x, one)),
-                                                      qop[j][g], dg, 0, 0, 0);
+          const uint32_t* u = reinterpret_cast<const uint32_t*>(kq + j * 16 * ROWB + 12 * g);
+          dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(half8, tq3_key_operand(u[0], u[1], ks1)), qop[j][g], dg, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -989,45 +1127,47 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
           if (4 * quad + i >= nvalid) s[i] = -INFINITY;
       }
       float p[4];
-      softmax_live(st, s, p, acc, quad, true);
+      softmax_live(st, s, p, acc, quad, true, [&](float c) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) vmass[g] *= c;
+      });
 
       // ---- values: per pass of PASS groups, unpack into the value tile, then
       // P' = p * value scale (hi/lo f16) and acc += P' * V
       wait_vm<2 * TNI>();                        // this tile's value half has landed
-      uint32_t vsd[2 * NG];
-      load_scale_dwords<NG>(reinterpret_cast<const uint32_t*>(vb + C::SCOFF + jcol * 16 * C::SCB + 8 * NG * quad), vsd);
-      if (nvalid < 16) {
-        // an unwritten slot's scale may be NaN, and p = 0 times NaN is NaN
-#pragma unroll
-        for (int e = 0; e < 4 * NG; ++e)
-          if (4 * quad + e / NG >= nvalid) vsd[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      }
+      const uint32_t* vsp = reinterpret_cast<const uint32_t*>(vb + C::SCOFF + jcol * 16 * C::SCB + 8 * NG * quad);
 #pragma unroll
       for (int ps = 0; ps < C::NPASS; ++ps) {
+        // value scales of the pass for the lane's 4 tokens (an unwritten
+        // row's scale may be NaN, and p = 0 times NaN is NaN: invalid rows
+        // get 0)
+        uint32_t sw[4];
+        tq3_pass_scales<NG>(vsp, ps, nvalid - 4 * quad, sw);
         {
           const uint32_t* src = reinterpret_cast<const uint32_t*>(vb + uj * 16 * ROWB + ut * ROWB + 12 * (ps * PASS + ug));
           const uint32_t w[3] = {src[0], src[1], src[2]};
           uint32_t o[16];
-          tq3_value_group(w, one, o);
+          tq3_value_group(w, o);
           uint8_t* row = vt + (uj * 16 + ut) * VROWB;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            *reinterpret_cast<u32x4*>(row + 32 * vseg<VROWB>(ut, 2 * ug + (k >> 1)) + 16 * (k & 1)) =
-                u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+          for (int h = 0; h < 2; ++h) {
+            uint8_t* c0 = row + 32 * vseg<VROWB>(ut, 2 * ug + h);
+            *reinterpret_cast<u32x4*>(c0) = u32x4{o[8 * h], o[8 * h + 1], o[8 * h + 2], o[8 * h + 3]};
+            *reinterpret_cast<u32x4*>(c0 + 16) = u32x4{o[8 * h + 4], o[8 * h + 5], o[8 * h + 6], o[8 * h + 7]};
+          }
         }
         wave_lds_sync();
 #pragma unroll
         for (int gs = 0; gs < PASS; ++gs) {
           const int g = ps * PASS + gs;
-          float sv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[i] = f16_half(vsd[(i * NG + g) >> 1], (i * NG + g) & 1);
-          const half8 pp = pprime(p, sv);
+          uint32_t phi[2], plo[2];
+          if (gs == 0) pprime_tq3<NG, 0>(p, sw, phi, plo, vmass[g]);
+          else pprime_tq3<NG, 1>(p, sw, phi, plo, vmass[g]);
           half8 bv[2];
-          value_operands2<NH>(vt_addr + vrd[2 * gs], vt_addr + vrd[2 * gs + 1], 16 * VROWB, bv[0], bv[1]);
+          value_operands2<NH, 16 * VROWB>(va0 ^ uint32_t(64 * gs), va1 ^ uint32_t(64 * gs), bv[0], bv[1]);
           if constexpr (NH == 2) {
             half8 a_hi, a_lo;
-            split_pprime(pp, jcol == 1, a_hi, a_lo);
+            split_pprime(__builtin_bit_cast(half8, u32x4{phi[0], phi[1], plo[0], plo[1]}), jcol == 1, a_hi, a_lo);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               acc[2 * g + h] = pv_mfma(a_hi, bv[h], acc[2 * g + h]);
@@ -1035,7 +1175,9 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
             }
           } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) acc[2 * g + h] = pv_mfma(pp, bv[h], acc[2 * g + h]);
+            for (int h = 0; h < 2; ++h)
+              acc[2 * g + h] = pv_mfma(__builtin_bit_cast(half8, u32x4{phi[0], phi[1], plo[0], plo[1]}), bv[h],
+                                       acc[2 * g + h]);
           }
         }
         wave_lds_sync();
@@ -1052,6 +1194,14 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   // ---- combine the four waves' states through LDS (the slots are reused once
   // every wave is past its last tile) and write the item's state
   const float lcol = quad_sum(st.l);
+  // centring term of each accumulator row (column 4quad + i) and group
+  float cent[NG][4];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const float m = -3.5f * quad_sum(vmass[g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cent[g][i] = __shfl(m, 4 * quad + i, 64);
+  }
   __syncthreads();
   auto& M = *reinterpret_cast<MergeLds<D>*>(smem);
   if (quad == 0) {
@@ -1059,12 +1209,12 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     M.l[wave][col] = lcol;
   }
   // accumulator column col of N-tile jt holds value position 16 (jt & 1) + col
-  // of group jt / 2 (half pos & 1 of value pair pos / 2), scaled by 2^(k-10)
+  // of group jt / 2 (half pos & 1 of value pair pos / 2), scaled by 2^(k-24)
   const uint64_t we = (col & 8) ? kValuePos[1] : kValuePos[0];
   const uint64_t wo = (col & 8) ? kValuePos[3] : kValuePos[2];
   const int ee = int(we >> (8 * (col & 7))) & 255, eo = int(wo >> (8 * (col & 7))) & 255;
-  const float up_e = __builtin_amdgcn_ldexpf(1.0f, 10 - (ee >> 5));
-  const float up_o = __builtin_amdgcn_ldexpf(1.0f, 10 - (eo >> 5));
+  const float up_e = __builtin_amdgcn_ldexpf(1.0f, 24 - (ee >> 5));
+  const float up_o = __builtin_amdgcn_ldexpf(1.0f, 24 - (eo >> 5));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
@@ -1072,7 +1222,8 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     float* dst = M.acc[wave] + c * MergeLds<D>::ROW;
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt)
-      dst[32 * (jt >> 1) + ((jt & 1) ? (eo & 31) : (ee & 31))] = acc[jt][i] * ((jt & 1) ? up_o : up_e);
+      dst[32 * (jt >> 1) + ((jt & 1) ? (eo & 31) : (ee & 31))] =
+          __builtin_fmaf(acc[jt][i], (jt & 1) ? up_o : up_e, cent[jt >> 1][i]);
   }
   __syncthreads();
   merge_waves_and_store<D>(M, a, it.chunk, hq0, ncol);
@@ -1095,8 +1246,8 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
   const int ncol = NH * G;
   const int hq0 = hk0 * G;
   const int jcol = col < ncol ? col / G : 0;
-  uint8_t* wl = smem + wave * C::WAVE;
-  uint8_t* vt = wl + C::NSLOT * C::SLOT;
+  uint8_t* vt = smem + wave * C::WAVE;
+  uint8_t* wl = vt + C::VBUF;
   const TileGeom tg = wave_tiles(it, pv.P / 16, wave);
 
   f32x4 acc[NT];
@@ -1192,7 +1343,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = live && 4 * quad + i < nvalid ? dsum[i] * fk : -INFINITY;
         float p[4];
-        softmax_live(st, s, p, acc, quad, live);
+        softmax_live(st, s, p, acc, quad, live, [](float) {});
         const half8 pp = pprime_uniform(p, sv);
 
         wait_vm<2 * FNI>();
@@ -1237,7 +1388,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
 #pragma unroll
           for (int n = 0; n < 2 * PASS; n += 2) {
             half8 bv[2];
-            value_operands2<1>(vt_addr + vrd[n], vt_addr + vrd[n + 1], 0, bv[0], bv[1]);
+            value_operands2<1>(vt_addr + vrd[n], vt_addr + vrd[n + 1], bv[0], bv[1]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int jt = 2 * PASS * ps + n + h;
