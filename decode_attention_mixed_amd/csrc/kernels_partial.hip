@@ -808,6 +808,23 @@ __device__ __forceinline__ int vseg(int r, int seg) {
   if constexpr (VROWB == 128) return seg ^ ((r >> 1) & 3);
   else return seg ^ ((r >> 2) & 1);
 }
+// Byte offset (0 or 16) of the first 16-byte half of a segment in value-tile
+// row r.  16-byte writes are served 8 lanes at a time: with 128-byte rows the
+// segment swizzle alone leaves pairs of rows on the same banks, and swapping
+// the halves in odd rows separates them (the transposing reads, which only
+// permute within a segment, are unaffected).
+template <int VROWB>
+__device__ __forceinline__ int vhalf(int r) {
+  return VROWB == 128 ? 16 * (r & 1) : 0;
+}
+
+// p with address bit 4 flipped (an asm statement: the result is formed where
+// it is used instead of being kept live).
+__device__ __forceinline__ uint8_t* flip16(uint8_t* p) {
+  uint32_t a = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(p)));
+  asm volatile("v_xor_b32 %0, 16, %0" : "+v"(a));
+  return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t(a));
+}
 
 // LDS byte address of a pointer into this workgroup's LDS.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -1081,7 +1098,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     // row is segment 0 with n XOR-ed into bits 5.. of the address (the tile
     // sits at a multiple of 1 KB and a row's offset has those bits clear)
     const int vr = 4 * quad + (col >> 2);
-    const uint32_t va0 = lds_addr(vt) + uint32_t(vr * VROWB + 32 * vseg<VROWB>(vr, 0) + 8 * (col & 3));
+    const uint32_t va0 = lds_addr(vt) + uint32_t(vr * VROWB + 32 * vseg<VROWB>(vr, 0) + ((8 * (col & 3)) ^ vhalf<VROWB>(vr)));
     const uint32_t va1 = va0 ^ 32u;
     // value unpack: lane -> (token ut, head uj, group ug of the pass); spare
     // lanes repeat a real one's work
@@ -1148,12 +1165,13 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
           const uint32_t w[3] = {src[0], src[1], src[2]};
           uint32_t o[16];
           tq3_value_group(w, o);
-          uint8_t* row = vt + (uj * 16 + ut) * VROWB;
+          uint8_t* row = vt + (uj * 16 + ut) * VROWB + vhalf<VROWB>(ut);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             uint8_t* c0 = row + 32 * vseg<VROWB>(ut, 2 * ug + h);
             *reinterpret_cast<u32x4*>(c0) = u32x4{o[8 * h], o[8 * h + 1], o[8 * h + 2], o[8 * h + 3]};
-            *reinterpret_cast<u32x4*>(c0 + 16) = u32x4{o[8 * h + 4], o[8 * h + 5], o[8 * h + 6], o[8 * h + 7]};
+            *reinterpret_cast<u32x4*>(vhalf<VROWB>(1) ? flip16(c0) : c0 + 16) =
+                u32x4{o[8 * h + 4], o[8 * h + 5], o[8 * h + 6], o[8 * h + 7]};
           }
         }
         wave_lds_sync();
