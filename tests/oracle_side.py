@@ -38,3 +38,23 @@ def decode_all(wl, models):
     for b in range(wl.B):
         O[b], lse[b] = A.decode_seq(models[b], wl.q_bits[b], wl.tau)
     return O, lse
+
+
+def _decode_one(spec, b):
+    """Oracle output of sequence b of the named workload (run in a worker)."""
+    from decode_attention_mixed_amd import workloads as W
+    wl = getattr(W, spec[0])(**spec[1])
+    return b, A.decode_seq(seq_model(wl, b), wl.q_bits[b], wl.tau)
+
+
+def decode_parallel(spec, indices, workers=16):
+    """{b: (O, lse)} for the listed sequences of workload spec = (factory name,
+    kwargs), each built and decoded by the oracle in a separate process (fresh
+    interpreters: the workers import no GPU code)."""
+    import multiprocessing as mp
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+    indices = list(indices)
+    n = max(1, min(workers, len(indices), os.cpu_count() or 1))
+    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
+        return dict(ex.map(_decode_one, [spec] * len(indices), indices))

@@ -538,12 +538,11 @@ def test_long_context_full_parity(long_case):
     pool.close()
 
 
-def test_throughput_batch_sampled_parity():
+def test_throughput_batch_full_parity():
     """The B=64 throughput batch at full size: 16K-32K-token sequences whose
     pages scatter over slabs holding 60% of HBM, decoded in one call over the
-    whole batch as the benchmark times it.  Every output is finite; a seeded
-    sample of sequences (the shortest, the longest and two others) is checked
-    element by element against the oracle."""
+    whole batch as the benchmark times it; every sequence is compared element
+    by element with the oracle (computed in worker processes)."""
     wl = W.throughput()
     print(f"throughput: B={wl.B} tokens={int(np.sum(wl.lengths))} "
           f"slabs fp8={wl.fp8_pages} tq3={wl.tq3_pages} pages", flush=True)
@@ -551,14 +550,139 @@ def test_throughput_batch_sampled_parity():
     H.load_cache(pool, wl)
     print("throughput: cache built", flush=True)
     out, lse = _run_decode(pool, wl)
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
-    lengths = np.asarray(wl.lengths)
-    picks = {int(lengths.argmin()), int(lengths.argmax())}
-    picks |= set(int(x) for x in np.random.default_rng(7).choice(wl.B, 2, replace=False))
-    for b in sorted(picks):
-        model = OS.seq_model(wl, b)
-        Ob, Lb = A.decode_seq(model, wl.q_bits[b], wl.tau)
-        _check(out[b], lse[b], Ob, Lb, f"throughput[{b}] L={int(lengths[b])}")
     pool.close()
     del pool
     torch.cuda.empty_cache()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ref = OS.decode_parallel(("throughput", {}), range(wl.B))
+    print("throughput: oracle done", flush=True)
+    for b in range(wl.B):
+        _check(out[b], lse[b], *ref[b], f"throughput[{b}] L={int(wl.lengths[b])}")
+
+
+def test_canary16_full_parity():
+    """The 16-layer canary step at full size (32 entries of 59008 tokens, each
+    layer's cache a sequence of one pool) in one decode call, every entry
+    compared with the oracle."""
+    wl = W.canary(16)
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    print(f"canary16: B={wl.B} cache built", flush=True)
+    out, lse = _run_decode(pool, wl)
+    pool.close()
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ref = OS.decode_parallel(("canary", {"layers": 16}), range(wl.B))
+    for b in range(wl.B):
+        _check(out[b], lse[b], *ref[b], f"canary16[{b}]")
+
+
+def _check_schedule_export(pool, ids):
+    """The device copy of the cached schedule names every page of the batch's
+    sequences exactly once, each by its page-table entry (bit-exact), in items
+    of one format whose last page and token count match the sequence."""
+    sc = mkv.debug_schedule(pool.handle)
+    items, ent = sc["items"], sc["entries"]
+    seen = {s: [] for s in ids}
+    for it in items:
+        b, seq, off, npg, last_ntok, chunk, fmt, last_lp = (int(x) for x in it)
+        assert seq == ids[b]
+        e = ent[off:off + npg]
+        assert npg >= 1 and all((x < 0) == (fmt == 1) for x in e), it
+        pt = mkv.page_table(pool.handle, seq)
+        assert pt[last_lp] == e[-1], it
+        L, n = mkv.seq_info(pool.handle, seq)
+        assert last_ntok == (L - pool.desc.page_size * (n - 1) if last_lp == n - 1 else pool.desc.page_size), it
+        seen[seq] += [int(x) for x in e]
+    for s in ids:
+        pt = mkv.page_table(pool.handle, s)
+        assert sorted(seen[s]) == sorted(int(x) for x in pt), s
+    return sc
+
+
+def test_schedule_export_matches_page_tables():
+    """Schedule built by decode, then edited in place by one-token appends (which
+    open pages) and by demotions: after each change the device's schedule
+    region agrees with mkv_page_table bit for bit."""
+    wl = W.small(seed=41, B=4, Hq=8, Hkv=2, d=128, P=16, lengths=(150, 31, 400, 16), anchor_frac=0.4)
+    pool = H.DevicePool(H.pool_desc(wl, max_pages_per_seq=64, fp8_pages=128, tq3_pages=128))
+    H.load_cache(pool, wl)
+    ids = list(range(wl.B))
+    q = H.q_tensor(wl)
+    out = torch.empty(wl.B, wl.Hq, wl.d, device="cuda")
+    lse = torch.empty(wl.B, wl.Hq, device="cuda")
+    mkv.decode(pool.handle, ids, q, float(wl.tau), out, lse)
+    torch.cuda.synchronize()
+    _check_schedule_export(pool, ids)
+    rng = np.random.default_rng(3)
+    edits = 0
+    for step in range(40):
+        k = torch.from_numpy(rng.standard_normal((wl.B, wl.Hkv, wl.d), dtype=np.float32)).cuda()
+        mkv.append_step(pool.handle, ids, k, k)
+        if step % 10 == 9:
+            for s in (0, 2):
+                pt = mkv.page_table(pool.handle, s)
+                fp8 = [lp for lp in range(len(pt) - 1) if pt[lp] >= 0]
+                if fp8:
+                    mkv.demote(pool.handle, s, fp8[:2])
+        torch.cuda.synchronize()
+        try:
+            _check_schedule_export(pool, ids)          # the edited schedule, before any rebuild
+            edits += 1
+        except mkv.MkvError as e:
+            assert e.status == mkv.ESTATE               # no schedule cached: the next decode builds one
+        mkv.decode(pool.handle, ids, q, float(wl.tau), out, lse)
+        torch.cuda.synchronize()
+        _check_schedule_export(pool, ids)
+    print(f"schedule checked after {edits} in-place edits", flush=True)
+    assert edits >= 30
+    pool.close()
+
+
+def test_edge_values_records_and_decode():
+    """Edge values through append, demote and decode: a kv-head whose rows are
+    zero on whole pages (FP8 scale 1, TQ3 scale 0), zero groups, groups so small
+    that the TQ3 scale is an fp16 subnormal, groups so large that it clamps to
+    65504 (records only: their attention outputs exceed what fp32 can hold to
+    the absolute tolerance), and queries scaled by 16 and by 1/256."""
+    wl = W.small(seed=43, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(160, 96, 120), anchor_frac=0.3)
+    kvs = [wl.kv(b) for b in range(wl.B)]
+    k0, v0 = kvs[0]
+    k0[16:48, 1, :] = 0.0                          # kv-head 1: pages 1, 2 (TQ3) and the
+    v0[16:48, 1, :] = 0.0                          # last page (FP8 anchor) all zero
+    k0[144:160, 1, :] = 0.0
+    v0[144:160, 1, :] = 0.0
+    k0[:, 0, 32:64] = 0.0                          # a zero group in every page of kv-head 0
+    v0[64:112, 0, 96:128] = 0.0
+    k1, v1 = kvs[1]
+    k1[:, 0, 0:32] *= np.float32(3e-6)            # TQ3 scales ~1e-6: fp16 subnormals
+    v1[:, 1, 64:96] *= np.float32(2e-7)
+    k2, v2 = kvs[2]
+    k2[:, 1, 32:64] *= np.float32(4e5)            # TQ3 scales clamp to 65504
+    v2[:, 0, 0:32] *= np.float32(5e5)
+    pool = H.DevicePool(H.pool_desc(wl))
+    for b in range(wl.B):
+        H.load_sequence(pool, wl, b, kv=kvs[b])
+    models = [OS.seq_model(wl, b, kv=kvs[b]) for b in range(wl.B)]
+    _check_records(pool, wl, models)
+    # the clamp and subnormal cases really occur in the records
+    from oracle import codecs as CD
+    from oracle import attention as OA
+    scales = np.concatenate([m.pages[lp].tscale[:, :, :m.pages[lp].ntok].astype(np.float64).ravel()
+                             for m in models for lp in range(len(m.pages)) if m.pages[lp].fmt == 1])
+    assert np.any(scales == 65504.0) and np.any((scales > 0) & (scales < 2.0 ** -14)) and np.any(scales == 0)
+    assert any(np.any(m.pages[lp].scale == 1.0) for m in models for lp in range(len(m.pages))
+               if m.pages[lp].fmt == 0)            # an all-zero FP8 page-head: sigma = 1
+    qf = CD.bf16_bits_to_value(wl.q_bits).astype(np.float32)
+    qf[0, :4] *= 16.0                              # sharper softmax on the first 4 query heads
+    qf[1, 4:] *= 1.0 / 256.0                       # nearly flat on the others
+    qb = CD.bf16_encode(qf)
+    q = torch.from_numpy(qb[:2].view(np.int16).copy()).view(torch.bfloat16).cuda()
+    out = torch.empty(2, wl.Hq, wl.d, device="cuda")
+    lse = torch.empty(2, wl.Hq, device="cuda")
+    mkv.decode(pool.handle, [0, 1], q, float(wl.tau), out, lse)
+    torch.cuda.synchronize()
+    for b in range(2):
+        Ob, Lb = OA.decode_seq(models[b], qb[b], wl.tau)
+        _check(out[b].cpu().numpy().astype(np.float64), lse[b].cpu().numpy().astype(np.float64), Ob, Lb,
+               f"edge values [{b}]")
+    pool.close()
