@@ -34,13 +34,11 @@
 //    f16 rounding of P' costs up to 2^-12 * |v| per weight, too much for
 //    values with outlier channels.
 //
-// Operand encodings (all exact, all in the f16 normal range: MFMA products
-// with subnormal f16 operands are not accumulated to full fp32 precision):
-//  * TQ3: a 3-bit code c is masked into mantissa bits k..k+2 (1 <= k <= 7)
-//    of an f16 whose exponent encodes 1.0 (one AND-OR per two elements), then
-//    1 + 3.5 * 2^(k-10) is subtracted (one packed add): the operand is the
-//    centred code (c - 3.5) * 2^(k-10), exact and finite for any bit pattern,
-//    including unwritten poisoned slots.
+// Operand encodings (all exact):
+//  * TQ3: a 3-bit code c is masked into bits k..k+2 of an f16 whose other
+//    bits are zero, the number c * 2^(k-24) (see the TQ3 operand section
+//    below); the centring (c - 3.5) is applied outside the MFMA.  Any bit
+//    pattern, including unwritten poisoned slots, gives a finite operand.
 //  * FP8 E4M3 codes are widened by the hardware conversion to fp32 and packed
 //    to f16 (every E4M3 value is an f16 normal number).  Value rows past the
 //    valid tokens are zeroed because a poisoned byte may decode to NaN.
@@ -103,38 +101,51 @@ __device__ __forceinline__ float f16_half(uint32_t w, int h) {
 }
 
 // ---- TQ3 codes as f16 MFMA operands -------------------------------------------
-// A 3-bit code c placed at bits k .. k+2 (k <= 7) of an f16 half whose other
-// bits are zero is the subnormal number c * 2^(k-24): exact, and the MFMA
-// multiplies it exactly (the f16 matrix instructions of this architecture
-// keep subnormal inputs).  One AND of a 32-bit window of a code stream with
-// a mask thus yields two codes as operands, each carrying a power of two that
-// the other operand (or the result) takes back.  The centring (c - 3.5) is
-// applied outside the MFMA: for keys through the accumulator's initial value,
-// for values through the probability mass of the tile.
+// A 3-bit code c placed at bits k .. k+2 (k <= 8) of an f16 half whose other
+// bits are zero is the number c * 2^(k-24): for k <= 7 a subnormal, for
+// k = 8 the code's top bit is the exponent's lowest bit, and the encodings
+// with exponent field 1 continue the subnormal grid (value = bits * 2^-24).
+// The MFMA multiplies such inputs exactly, so one AND of a 32-bit window of a
+// code stream with a mask yields two codes as operands, each carrying a power
+// of two that the other operand (or the result) takes back.  The centring
+// (c - 3.5) is applied outside the MFMA: for keys through the accumulator's
+// initial value, for values through the probability mass of the tile.
+//
+// Precision: the f16 MFMA sums its products in a fixed-width window placed
+// by the operands' exponent fields, and these operands all read as exponent
+// -14, whatever c and k.  A product c * 2^(k-24) * b thus counts as large as
+// 2^-14 * b, and the sum's rounding grain follows the largest such nominal
+// product: about 2^(10-k) / c times coarser than for normal operands of the
+// same values.  (Measured on 16x16x32 tiles with C = 0 and slots down to
+// k = 0: errors near 2^-24 absolute on sums near 2^-5.)  The codes are
+// therefore placed as high in the half as the bit stream allows.
 //
 // Key operands.  Quad q of the MFMA's A operand takes codes 8q .. 8q+7 of the
-// group (bits 24q .. 24q+23 of its 96-bit stream), from two windows starting
-// at bits 24q - 4 and 24q + 2.  Each window gives two operand dwords through
-// the masks below; the 8 k-slots of the lane then hold
+// group (bits 24q .. 24q+23 of its 96-bit stream).  Window W starts at bit
+// 24q - 8, so code e sits at bits 8 + 3e of W; dword j of the operand is
+// (W >> 3j) & kKeyMask, which keeps code j at k = 8 in the low half and code
+// j + 4 at k = 4 in the high half.  The 8 k-slots of the lane hold
 //   slot:        0   1   2   3   4   5   6   7
 //   code 8q + :  0   4   1   5   2   6   3   7     (kSlotCode)
-//   bit pos k:   4   0   7   3   4   0   7   3     (kSlotShift)
-// The first window is the funnel shift by 28 - 8q of the dwords q - 1 and q
-// of the group (for quad 0 the dword before the group, for quad 3 the one
-// after it: their bits land only where the masks clear them); the second is
-// the first shifted right by 6 (the masks use its bits 0..21 only).
+//   bit pos k:   8   4   8   4   8   4   8   4     (kSlotShift)
+// (No cover of the 8 codes by 4 dwords keeps every k above 4: a dword's two
+// codes sit 16 + k_hi - k_lo bits apart, a multiple of 3, so with all k >= 3
+// they are 4, 5 or 6 codes apart; codes 3 and 4 then pair only as (3, 7) and
+// (0, 4), the rest as (1, 5) and (2, 6), and distance 4 means k_hi = k_lo - 4
+// <= 4.)  W is the funnel shift by 24 - 8q of
+// the dwords q - 1 and q of the group (for quad 0 the dword before the group:
+// its bits land only where the mask clears them).
 constexpr int kSlotCode[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-constexpr int kSlotShift[8] = {4, 0, 7, 3, 4, 0, 7, 3};
-constexpr uint32_t kKeyMaskA = (7u << 4) | (7u << 16);    // codes at k = 4 (low), 0 (high)
-constexpr uint32_t kKeyMaskB = (7u << 7) | (7u << 19);    // codes at k = 7 (low), 3 (high)
-// Checks the table against the windows: quad 0, window start ws, mask m.
+constexpr int kSlotShift[8] = {8, 4, 8, 4, 8, 4, 8, 4};
+constexpr uint32_t kKeyMask = (7u << 8) | (7u << 20);    // codes at k = 8 (low), 4 (high)
+// Checks the table against the windows: W starts 8 bits before the quad's
+// first code; dword j is W shifted right by 3j.
 constexpr bool key_slot_ok(int slot) {
   const int code = kSlotCode[slot], k = kSlotShift[slot];
-  const int ws = slot < 4 ? -4 : 2;                        // window of this slot
-  const int half = slot & 1;                               // operand half
-  const uint32_t m = ((slot >> 1) & 1) ? kKeyMaskB : kKeyMaskA;
-  const int pos = 3 * code - ws;                           // code position in the window
-  return pos == 16 * half + k && ((m >> pos) & 7u) == 7u && k >= 0 && k <= 7;
+  const int j = slot >> 1, half = slot & 1;
+  const int pos = 3 * code + 8 - 3 * j;                    // code position in W >> 3j
+  return pos == 16 * half + k && ((kKeyMask >> pos) & 7u) == 7u && pos + 2 <= 31 - 3 * j && k >= 0 &&
+         k <= 8;
 }
 static_assert(key_slot_ok(0) && key_slot_ok(1) && key_slot_ok(2) && key_slot_ok(3) && key_slot_ok(4) &&
                   key_slot_ok(5) && key_slot_ok(6) && key_slot_ok(7),
@@ -142,9 +153,8 @@ static_assert(key_slot_ok(0) && key_slot_ok(1) && key_slot_ok(2) && key_slot_ok(
 
 // Operand of one key unit from dwords q - 1 and q of the group (see above).
 __device__ __forceinline__ u32x4 tq3_key_operand(uint32_t lo, uint32_t hi, uint32_t s1) {
-  const uint32_t w1 = __builtin_amdgcn_alignbit(hi, lo, s1);
-  const uint32_t w2 = w1 >> 6;
-  return u32x4{w1 & kKeyMaskA, w1 & kKeyMaskB, w2 & kKeyMaskA, w2 & kKeyMaskB};
+  const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, s1);
+  return u32x4{w & kKeyMask, (w >> 3) & kKeyMask, (w >> 6) & kKeyMask, (w >> 9) & kKeyMask};
 }
 
 // ---- TQ3 value group unpack ------------------------------------------------
@@ -152,18 +162,23 @@ __device__ __forceinline__ u32x4 tq3_key_operand(uint32_t lo, uint32_t hi, uint3
 // 3i .. 3i+2.  Read as a ring of 96 bits, any 32-bit window starting at bit b
 // is one funnel shift of two of the dwords (no shift for b = 0, 32, 64).  One
 // AND of a window keeps two codes, code lo at bits k_lo .. k_lo+2 of the low
-// half and code hi at bits 16+k_hi .. 18+k_hi (0 <= k <= 7), which are the
-// subnormal f16 values c * 2^(k-24).  The sixteen pairs below, (window start,
-// lo, hi), cover the group with four shifted windows (no cover with three
-// exists); the bit offsets follow from them.  (Value tiles are unpacked once
-// per tile by the lane that loads the group, so the whole group is at hand.)
+// half and code hi at bits 16+k_hi .. 18+k_hi, the numbers c * 2^(k-24)
+// (k <= 8, see the operand section above).  The sixteen pairs below,
+// (window start, lo, hi), put every code at k >= 4, which bounds the MFMA's
+// rounding grain for these operands to 2^6 times that of normal operands
+// (as for the keys).  They take eight shifted windows; an exact-cover search
+// over all window starts finds none with fewer at k >= 4 (k >= 3 takes six,
+// any k three).  The bit offsets follow from the table.  (Value tiles are
+// unpacked once per tile by the lane that loads the group, so the whole group
+// is at hand.)
 struct Tq3Pair {
   int win, lo, hi;
 };
 constexpr Tq3Pair kValuePairs[16] = {
-    {0, 0, 6},    {0, 1, 7},    {4, 2, 8},    {4, 3, 9},    {10, 4, 10},  {10, 5, 11},
-    {32, 12, 17}, {32, 13, 18}, {41, 14, 19}, {41, 15, 20}, {41, 16, 21}, {64, 22, 27},
-    {64, 23, 28}, {71, 24, 29}, {71, 25, 30}, {71, 26, 31}};
+    {0, 2, 8},    {13, 6, 11},  {13, 7, 12},  {22, 9, 14},  {22, 10, 15}, {32, 13, 18},
+    {43, 16, 21}, {43, 17, 22}, {51, 19, 25}, {54, 20, 26}, {64, 23, 28}, {64, 24, 29},
+    {75, 27, 1},  {82, 30, 3},  {88, 0, 5},   {88, 31, 4}};
+constexpr int kValueMinK = 4;
 constexpr int kappa_lo(const Tq3Pair& p) { return (3 * p.lo - p.win + 96) % 96; }
 constexpr int kappa_hi(const Tq3Pair& p) { return (3 * p.hi - p.win + 96) % 96 - 16; }
 constexpr uint32_t pair_mask(const Tq3Pair& p) {
@@ -173,7 +188,7 @@ constexpr bool is_cover(const Tq3Pair (&t)[16]) {
   uint32_t seen = 0;
   for (const Tq3Pair& p : t) {
     const int a = kappa_lo(p), b = kappa_hi(p);
-    if (a < 0 || a > 7 || b < 0 || b > 7 || p.win < 0 || p.win >= 96) return false;
+    if (a < kValueMinK || a > 8 || b < kValueMinK || b > 8 || p.win < 0 || p.win >= 96) return false;
     const uint32_t bits = (1u << p.lo) | (1u << p.hi);
     if ((seen & bits) != 0 || p.lo == p.hi) return false;
     seen |= bits;
@@ -182,14 +197,14 @@ constexpr bool is_cover(const Tq3Pair (&t)[16]) {
 }
 static_assert(is_cover(kValuePairs), "TQ3 value pair cover");
 
-// Value position 2p + h (half h of pair p) as a byte (dim-in-group | k << 5),
-// 8 per 64-bit word, for run-time lookups.
+// Value position 2p + h (half h of pair p) as a byte (dim-in-group |
+// (8 - k) << 5), 8 per 64-bit word, for run-time lookups.
 constexpr uint64_t value_pos_word(int w) {
   uint64_t r = 0;
   for (int i = 0; i < 8; ++i) {
     const int pos = 8 * w + i;
     const Tq3Pair& p = kValuePairs[pos / 2];
-    const int e = (pos & 1) ? (p.hi | (kappa_hi(p) << 5)) : (p.lo | (kappa_lo(p) << 5));
+    const int e = (pos & 1) ? (p.hi | ((8 - kappa_hi(p)) << 5)) : (p.lo | ((8 - kappa_lo(p)) << 5));
     r |= uint64_t(e) << (8 * i);
   }
   return r;
@@ -892,13 +907,26 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* ds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
-// Four E4M3 bytes -> two dwords of f16 pairs (the hardware conversion with
-// scale 1 is exact: every E4M3 value is an f16 normal number).
-__device__ __forceinline__ u32x2 fp8x4_to_f16_s(uint32_t w) {
+// Four E4M3 bytes -> two dwords of f16 pairs, each value times sc (a power
+// of two 2^j, -5 <= j <= 7): exact, since every E4M3 value times such a power
+// is an f16 normal number (the smallest, 2^-9, stays at or above 2^-14, the
+// largest, 448, at or below 57344).
+__device__ __forceinline__ u32x2 fp8x4_to_f16_s(uint32_t w, float sc = 1.0f) {
   u32x2 o;
-  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, sc, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, sc, true));
   return o;
+}
+
+// Power-of-two split of an FP8 value scale sv between P' and the value codes:
+// P' = p * sv * 2^k with codes times 2^-k leaves every product P' * code
+// unchanged.  k is chosen so that sv * 2^k < 2^10 sits high in the f16 range:
+// then P' and its f16 remainder stay normal for all but negligible p, where
+// P' = p * sv alone (sv = amax / 448, often below 2^-6) would put the
+// remainder on the subnormal grid, an absolute error that codes up to 448
+// magnify.  (Wave-uniform; clamped to the exact range of fp8x4_to_f16_s.)
+__device__ __forceinline__ int fp8_value_shift(float sv) {
+  return min(5, max(-7, 10 - __builtin_amdgcn_frexp_expf(sv)));
 }
 
 // Softmax step of one tile for the lane's column (as softmax_step, with the
@@ -1083,11 +1111,10 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   }
 
   if (tg.ntiles > 0) {
-    // lane constant: the funnel shift of the first key window (dwords
-    // quad - 1 and quad of the group; quad 0 reads the dword before the
-    // group, which the value tile in front of the slots keeps inside this
-    // workgroup's LDS)
-    const uint32_t ks1 = uint32_t(28 - 8 * quad);
+    // lane constant: the funnel shift of the key window (dwords quad - 1 and
+    // quad of the group; quad 0 reads the dword before the group, which the
+    // value tile in front of the slots keeps inside this workgroup's LDS)
+    const uint32_t ks1 = uint32_t(24 - 8 * quad);
     // byte offset of the lane's key dwords in a slot (kept opaque so that the
     // slot's constant part stays in the scalar base and the per-MFMA offsets
     // fit the LDS instructions' immediate fields)
@@ -1231,8 +1258,8 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   const uint64_t we = (col & 8) ? kValuePos[1] : kValuePos[0];
   const uint64_t wo = (col & 8) ? kValuePos[3] : kValuePos[2];
   const int ee = int(we >> (8 * (col & 7))) & 255, eo = int(wo >> (8 * (col & 7))) & 255;
-  const float up_e = __builtin_amdgcn_ldexpf(1.0f, 24 - (ee >> 5));
-  const float up_o = __builtin_amdgcn_ldexpf(1.0f, 24 - (eo >> 5));
+  const float up_e = __builtin_amdgcn_ldexpf(1.0f, 16 + (ee >> 5));      // 2^(24 - k)
+  const float up_o = __builtin_amdgcn_ldexpf(1.0f, 16 + (eo >> 5));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * quad + i;
@@ -1342,7 +1369,10 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
         const bool live = jcol == j && col < ncol;
         // page-head scales of head hk0 + j (wave-uniform)
         const float sk = *reinterpret_cast<const float*>(page + fp8_scale_off(pv, hk0 + j, 0));
-        const float sv = *reinterpret_cast<const float*>(page + fp8_scale_off(pv, hk0 + j, 1));
+        const float sv0 = *reinterpret_cast<const float*>(page + fp8_scale_off(pv, hk0 + j, 1));
+        const int kv = fp8_value_shift(sv0);
+        const float sv = __builtin_amdgcn_ldexpf(sv0, kv);             // P' scale
+        const float vsc = __builtin_amdgcn_ldexpf(1.0f, -kv);          // code scale
 
         wait_vm<2 * FNI>();
         f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1377,7 +1407,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
               const u32x4 w = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
               for (int x = 0; x < 4; ++x) {
-                const u32x2 h = fp8x4_to_f16_s(w[x]);
+                const u32x2 h = fp8x4_to_f16_s(w[x], vsc);
                 o[2 * x] = h[0];
                 o[2 * x + 1] = h[1];
               }
@@ -1385,7 +1415,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
               const u32x2 w = *reinterpret_cast<const u32x2*>(src);
 #pragma unroll
               for (int x = 0; x < 2; ++x) {
-                const u32x2 h = fp8x4_to_f16_s(w[x]);
+                const u32x2 h = fp8x4_to_f16_s(w[x], vsc);
                 o[2 * x] = h[0];
                 o[2 * x + 1] = h[1];
               }
