@@ -788,11 +788,12 @@ struct Mix {
   static constexpr int TNI = NH * (CPH + 1);            // load instructions of a TQ3 half
   static constexpr int SCOFF = NH * 16 * ROWB;          // scales of a TQ3 half-slot
   // TQ3 mode leaves the end of each half-slot unwritten: it holds the key
-  // centring values of the wave's columns, 8 bytes (the value twice) per
-  // column and group, KPS groups per slot
+  // centring values of the wave's columns, 16 bytes (the value four times,
+  // an MFMA accumulator's initial value as read) per column and group, KPS
+  // groups per slot
   static constexpr int KIOFF = (NH * THALF + 15) / 16 * 16;
-  static constexpr int KPS = (SLOT - KIOFF) / 128;
-  static constexpr int kinit_off(int g) { return (g / KPS) * SLOT + KIOFF + (g % KPS) * 128; }
+  static constexpr int KPS = (SLOT - KIOFF) / 256;
+  static constexpr int kinit_off(int g) { return (g / KPS) * SLOT + KIOFF + (g % KPS) * 256; }
   // the workgroup's shared copies: centring values of group g in wave
   // g mod 4's half-slot tails; the query operands of (kv-head j, group g),
   // 1 KB each, in the value tiles (free until the tile loop)
@@ -1064,7 +1065,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
   // operands for each kv-head of the wave (zero outside that head's columns)
   // through the value tiles, which no wave uses before its first tile's
   // values, and the key centring -3.5 * sum of q * 2^(E-17) over the group's
-  // dims as the pair (v, v) per column in a half-slot tail, where the tile
+  // dims as (v, v, v, v) per column in a half-slot tail, where the tile
   // loop reads it as the groups' accumulator initial value.
   half8 qop[NH][NG];
   float F;
@@ -1093,7 +1094,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
         part = __builtin_fmaf(float(qh[sl]), __builtin_amdgcn_ldexpf(1.0f, kSlotShift[sl] - 24), part);
       }
       const float kinit = -3.5f * quad_sum(part);
-      if (quad == 0) *reinterpret_cast<f32x2*>(C::kinit_addr(smem, g) + 8 * col) = f32x2{kinit, kinit};
+      if (quad == 0) *reinterpret_cast<f32x4*>(C::kinit_addr(smem, g) + 16 * col) = f32x4{kinit, kinit, kinit, kinit};
       const u32x4 w = __builtin_bit_cast(u32x4, qh);
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
@@ -1149,8 +1150,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const f32x2 k0 = *reinterpret_cast<const f32x2*>(C::kinit_addr(smem, g) + 8 * col);
-        f32x4 dg = {k0[0], k0[1], k0[0], k0[1]};
+        f32x4 dg = *reinterpret_cast<const f32x4*>(C::kinit_addr(smem, g) + 16 * col);
 #pragma unroll
         for (int j = 0; j < NH; ++j) {
           const uint32_t* u = reinterpret_cast<const uint32_t*>(kq + j * 16 * ROWB + 12 * g);
