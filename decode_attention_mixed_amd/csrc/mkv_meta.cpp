@@ -321,8 +321,12 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
   };
   const int64_t waves_per_item =
       int64_t(kWavesPerWorkgroup) * ((g_.Hkv + heads_per_block - 1) / heads_per_block);
+  // the split-K floor holds for batches long enough to give each of its chunks
+  // kFloorChunkPages pages; shorter ones fill the resident waves once
+  const int64_t floor_items =
+      total_pages >= int64_t(pol.min_items) * kFloorChunkPages ? int64_t(pol.min_items) : int64_t(0);
   const int64_t target_items =
-      std::max<int64_t>({int64_t(1), pol.target_waves / waves_per_item, int64_t(pol.min_items)});
+      std::max<int64_t>({int64_t(1), pol.target_waves / waves_per_item, floor_items});
   double budget = std::max(1.0, total_cost / double(target_items));
   std::vector<int64_t> k8(static_cast<size_t>(B)), k3(static_cast<size_t>(B));
   int64_t count = 0;

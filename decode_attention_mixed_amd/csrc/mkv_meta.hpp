@@ -97,6 +97,9 @@ struct WorkItem {
 // Upper bound on WorkItem::npages: the partial kernel stages a work item's
 // page-table entries in a fixed LDS array of this length.
 constexpr int32_t kMaxChunkPages = 240;
+// Pages per chunk below which the split-K floor does not apply (shorter
+// batches are cut for one round of the resident waves instead).
+constexpr int32_t kFloorChunkPages = 16;
 // Waves per partial-kernel workgroup; a workgroup takes one work item and
 // heads_per_wave kv-heads of it, its waves splitting the item's tiles.
 constexpr int32_t kWavesPerWorkgroup = 4;
@@ -116,13 +119,15 @@ inline int32_t heads_per_wave(int32_t d, int32_t Hkv, int32_t G) {
 // ceil(Hkv / kWavesPerWorkgroup) workgroups); an FP8 page counts
 // fp8_page_cost TQ3 pages (by default the kv-heads one wave covers, since
 // FP8 tiles hold one kv-head and TQ3 tiles that many).  min_items raises that count (a split-K floor:
-// more, shorter chunks) as far as min_chunk_pages allows.  A
+// more, shorter chunks) for batches of at least min_items * kFloorChunkPages
+// pages, as far as min_chunk_pages allows.  A
 // nonzero fixed_chunk_pages cuts every list into chunks of exactly that many
 // pages instead (the last one shorter).  Chunks grow when a batch would need
 // more than max_chunks of them; no chunk exceeds kMaxChunkPages.
 struct SchedPolicy {
   int32_t target_waves = 2048;   // resident partial-kernel waves on the device
-  int32_t min_items = 256;       // split-K floor: at least this many items when the pages allow
+  int32_t min_items = 256;       // split-K floor: at least this many items for batches of
+                                 // min_items * kFloorChunkPages pages or more
   int32_t min_chunk_pages = 4;   // smallest balanced chunk (shorter lists stay whole)
   int32_t fixed_chunk_pages = 0; // 0: balanced chunks
   int32_t heads_per_wave = 0;    // kv-heads per partial-kernel workgroup; 0: heads_per_wave()

@@ -284,6 +284,22 @@ def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
     h.close()
 
 
+def test_split_k_floor_only_for_long_batches(lib):
+    # 4 sequences of 64-token pages, 769 pages in all (the d = 256 sweep
+    # shape): fewer than 256 * 16 pages, so no floor; one kv-head per wave and
+    # Hkv = 4 make an item four 4-wave workgroups, and 2048 resident waves
+    # give 128 items
+    h = _host(lib, num_kv_heads=4, head_dim=256, page_size=64, max_seqs=4, max_pages_per_seq=256,
+              max_batch=4, max_q_heads=16, fp8_pages=1024, tq3_pages=1024)
+    for s_, L in enumerate((16384, 16384, 16361, 1)):
+        assert h.append(s_, L)[0] == OK
+    st, sc = h.schedule([0, 1, 2, 3], 16, target_waves=2048)
+    assert st == OK
+    assert 120 <= sc["n_chunks"] <= 136
+    _check_coverage(h, [0, 1, 2, 3], sc, 64)
+    h.close()
+
+
 def test_schedule_respects_chunk_capacity(lib):
     # chunks hold at most 240 pages: 4 * (2 + ceil(512 / 240)) = 20 is the
     # smallest max_chunks this descriptor accepts

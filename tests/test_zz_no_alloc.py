@@ -48,9 +48,10 @@ def test_static_workspace_decode_matches_pool_decode():
 
 
 def test_static_workspace_rejects_an_oversized_batch():
-    # d = 256, Hq = 64 and 256 chunks need 256 * 64 * 258 * 4 bytes of partial
-    # states: more than the 16 MiB workspace.
-    Hkv, Hq, d, P, L, B = 4, 64, 256, 16, 4096, 4
+    # d = 256, Hq = 64 and 256 chunks (the split-K floor of a 4096-page batch)
+    # need 256 * 64 * 258 * 4 bytes of partial states: more than the 16 MiB
+    # workspace.
+    Hkv, Hq, d, P, L, B = 4, 64, 256, 16, 16384, 4
     desc = mkv.make_desc(num_kv_heads=Hkv, head_dim=d, page_size=P, max_seqs=B,
                          max_pages_per_seq=L // P, max_batch=B, max_q_heads=Hq,
                          fp8_pages=B * L // P, tq3_pages=16)
