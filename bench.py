@@ -167,29 +167,109 @@ def _pmc_means(csv_path: str, name_part: str, counter: str):
     return sum(vals) / len(vals), len(vals)
 
 
-def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, wl_name):
+def _req_bytes(rd_csv, wr_csv, name_part):
+    """HBM bytes per dispatch of the kernels matching name_part from the
+    L2-to-memory request counters: reads 32/64/128 B per request by size
+    class, writes 64 B (TCC_EA0_WRREQ_64B) or 32 B (the rest of
+    TCC_EA0_WRREQ)."""
+    n32, nd = _pmc_means(rd_csv, name_part, "TCC_EA0_RDREQ_32B_sum")
+    n64, _ = _pmc_means(rd_csv, name_part, "TCC_EA0_RDREQ_64B_sum")
+    n128, _ = _pmc_means(rd_csv, name_part, "TCC_EA0_RDREQ_128B_sum")
+    nrd, _ = _pmc_means(rd_csv, name_part, "TCC_EA0_RDREQ_sum")
+    w64, nw = _pmc_means(wr_csv, name_part, "TCC_EA0_WRREQ_64B_sum")
+    wall, _ = _pmc_means(wr_csv, name_part, "TCC_EA0_WRREQ_sum")
+    rd = 32 * n32 + 64 * n64 + 128 * n128
+    wr = 64 * w64 + 32 * (wall - w64)
+    return {"read_bytes": rd, "write_bytes": wr, "read_requests": nrd,
+            "read_requests_by_size": [n32, n64, n128], "unsized_read_requests": nrd - n32 - n64 - n128,
+            "write_requests": wall, "write_requests_64B": w64, "dispatches": [nd, nw]}
+
+
+def write_traffic(rd_csv, wr_csv, copy_rd_csv, copy_wr_csv, copy_bytes, wl_name, commands=None):
     """HBM bytes per launch of the partial kernel from two rocprofv3 --pmc
-    passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what
-    the same counter reads for a plain copy of copy_bytes (read and written
-    once).  Writes profiles/traffic_partial_<workload>.json."""
-    fetch, nf = _pmc_means(fetch_csv, "partial_mixed", "FETCH_SIZE")
-    write, nw = _pmc_means(write_csv, "partial_mixed", "WRITE_SIZE")
-    cfetch, _ = _pmc_means(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
-    cwrite, _ = _pmc_means(copy_write_csv, "copyBuffer", "WRITE_SIZE")
-    kib = copy_bytes / 1024.0
-    ffac, wfac = kib / cfetch, kib / cwrite
-    total = (fetch * ffac + write * wfac) * 1024.0
+    passes (read-request counters by size, write-request counters), checked on
+    a plain copy of copy_bytes bytes (read and written once), whose counted
+    bytes are reported beside the true ones rather than used as a scale.
+    Writes profiles/traffic_partial_<workload>.json."""
+    k = _req_bytes(rd_csv, wr_csv, "partial_mixed")
+    c = _req_bytes(copy_rd_csv, copy_wr_csv, "copyBuffer")
     out = {
         "kernel": "partial", "workload": wl_name, "kernel_src_sha": kernel_src_hash(),
-        "bytes_per_launch": round(total), "fetch_kib_per_dispatch": round(fetch, 1),
-        "write_kib_per_dispatch": round(write, 1), "dispatches": [nf, nw],
-        "copy_bytes": copy_bytes, "copy_fetch_kib": round(cfetch, 1), "copy_write_kib": round(cwrite, 1),
-        "fetch_scale": round(ffac, 4), "write_scale": round(wfac, 4),
+        "bytes_per_launch": round(k["read_bytes"] + k["write_bytes"]),
+        "read_bytes_per_launch": round(k["read_bytes"]), "write_bytes_per_launch": round(k["write_bytes"]),
+        "read_requests_32_64_128B": [round(x) for x in k["read_requests_by_size"]],
+        "unsized_read_requests": round(k["unsized_read_requests"]),
+        "write_requests": round(k["write_requests"]), "write_requests_64B": round(k["write_requests_64B"]),
+        "dispatches": k["dispatches"],
+        "copy_check": {"bytes": copy_bytes, "counted_read_bytes": round(c["read_bytes"]),
+                       "counted_write_bytes": round(c["write_bytes"]),
+                       "read_ratio": round(c["read_bytes"] / copy_bytes, 4),
+                       "write_ratio": round(c["write_bytes"] / copy_bytes, 4)},
+        "commands": list(commands or []),
     }
     path = os.path.join(ROOT, "profiles", f"traffic_partial_{wl_name}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def kernel_stats(trace_csv, wl_name, steps, commands=None):
+    """Per-dispatch durations of the partial and merge kernels from a
+    rocprofv3 --kernel-trace CSV of a bench run (the last `steps` dispatches
+    of each, i.e. the timed steps): mean and percentiles, and the same for
+    their sum per step.  Writes profiles/kernel_durations_<workload>.json."""
+    import csv
+    import numpy as np
+    rows = list(csv.DictReader(open(trace_csv)))
+    def durs(part):
+        d = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+             for r in rows if part in r["Kernel_Name"]]
+        d.sort()
+        return np.array([x[1] for x in d[-steps:]], dtype=np.float64) / 1e3
+    part, merge = durs("partial_mixed"), durs("merge")
+    n = min(len(part), len(merge))
+    step = part[-n:] + merge[-n:]
+    def summ(x):
+        return {"mean": round(float(x.mean()), 3),
+                **{f"p{k}": round(float(np.percentile(x, k)), 3) for k in (10, 50, 90, 99)}}
+    out = {"workload": wl_name, "kernel_src_sha": kernel_src_hash(), "dispatches": int(n),
+           "partial_us": summ(part[-n:]), "merge_us": summ(merge[-n:]), "partial_plus_merge_us": summ(step),
+           "commands": list(commands or [])}
+    path = os.path.join(ROOT, "profiles", f"kernel_durations_{wl_name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def load_kernel_stats(wl_name):
+    path = os.path.join(ROOT, "profiles", f"kernel_durations_{wl_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t if t.get("kernel_src_sha") == kernel_src_hash() else None
+
+
+def read_ceiling(mkv, torch, nbytes=4 * 2**30, reps=10):
+    """Read ceiling of the device: the library's read-only calibration kernel
+    over nbytes (16-byte loads), GB/s."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        mkv.debug_read_bandwidth(src, sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mkv.debug_read_bandwidth(src, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, sink
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -232,10 +312,17 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps "
                          "times (reference for the HBM byte counters)")
-    ap.add_argument("--write-traffic", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
-                                                          "COPY_WRITE_CSV", "COPY_BYTES"),
-                    help="only turn rocprofv3 --pmc counter files into the partial kernel's "
-                         "HBM traffic record under profiles/ (no GPU needed)")
+    ap.add_argument("--write-traffic", nargs=5, metavar=("RDREQ_CSV", "WRREQ_CSV", "COPY_RDREQ_CSV",
+                                                          "COPY_WRREQ_CSV", "COPY_BYTES"),
+                    help="only turn rocprofv3 --pmc request-counter files (TCC_EA0_RDREQ{,_32B,_64B,"
+                         "_128B}_sum; TCC_EA0_WRREQ{,_64B}_sum) into the partial kernel's HBM "
+                         "traffic record under profiles/ (no GPU needed)")
+    ap.add_argument("--kernel-stats", metavar="KERNEL_TRACE_CSV",
+                    help="only turn a rocprofv3 --kernel-trace CSV of a bench run into per-dispatch "
+                         "duration percentiles under profiles/ (no GPU needed; --steps = the run's)")
+    ap.add_argument("--profile-command", action="append", default=[], metavar="TEXT",
+                    help="with --kernel-stats / --write-traffic: the profiler command that made "
+                         "each input file, recorded in the summary (repeatable, in input order)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this library "
@@ -246,7 +333,10 @@ def main():
         return
     if args.write_traffic:
         f1, f2, f3, f4, nb = args.write_traffic
-        write_traffic(f1, f2, f3, f4, int(nb), args.workload)
+        write_traffic(f1, f2, f3, f4, int(nb), args.workload, args.profile_command)
+        return
+    if args.kernel_stats:
+        kernel_stats(args.kernel_stats, args.workload, args.steps, args.profile_command)
         return
 
     import numpy as np
@@ -339,17 +429,6 @@ def main():
         for k2, v2 in mkv.profile_read(p.handle).items():
             prof[k2] = prof.get(k2, 0) + v2
         mkv.profile_enable(p.handle, False)
-    # Timed region 3 (library events off again): one event pair around every
-    # step, for the per-step distribution.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record()
-    for i in range(args.steps):
-        mkv.decode(pools[i % R].handle, batch, q, tau, out, lse)
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
-    pct = {f"p{k}": round(float(np.percentile(per_step, k)), 3) for k in (10, 50, 90)}
     log(f"step {ms * 1e3:.2f} us (host {host_s * 1e6:.1f} us per call; {ms_ev * 1e3:.2f} us with "
         f"kernel events); kernel profile {prof}")
     multi = None
@@ -491,6 +570,7 @@ def main():
     copy_ceiling = 2.0 * 2**30 * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
+    read_ceil = read_ceiling(mkv, torch)
 
     kernel_ms = {"partial": prof["ms_partial"] / max(1, prof["n_partial"]),
                  "merge": prof["ms_merge"] / max(1, prof["n_merge"])}
@@ -513,7 +593,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3+tq3 codes, f32 compute",
+        "dtype": "f16 MFMA operands (exact FP8/TQ3 codes and hi/lo probabilities), f32 accumulation and softmax",
         "data": "synthetic: seeded N(0,1) fp32 K/V (outlier channels x8), bf16 N(0,1) query",
         "config": {
             "workload": describe(wl),
@@ -528,9 +608,11 @@ def main():
             "kernel_us": {k: round(v * 1e3, 3) for k, v in kernel_ms.items()},
             "host_us_per_call": round(host_s * 1e6, 2),
             "us_per_step_with_kernel_events": round(ms_ev * 1e3, 3),
-            "us_per_step_percentiles": pct,
+            "kernel_durations_rocprof": load_kernel_stats(wl.name),
             "copy_ceiling_gbs": round(copy_ceiling, 1),
             "pct_of_copy_ceiling": round(100.0 * value / copy_ceiling, 2) if copy_ceiling else None,
+            "read_ceiling_gbs": round(read_ceil, 1),
+            "pct_of_read_ceiling": round(100.0 * value / read_ceil, 2) if read_ceil else None,
         },
         "roofline": {
             "kernel": dom,

@@ -102,7 +102,7 @@ EXPORTED = [
     "mkv_pool_bytes", "mkv_record_bytes", "mkv_pool_create", "mkv_pool_destroy",
     "mkv_seq_reset", "mkv_append", "mkv_append_step", "mkv_demote", "mkv_materialize",
     "mkv_decode", "mkv_decode_static", "mkv_seq_info",
-    "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_debug_schedule", "mkv_profile_enable",
+    "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_debug_schedule", "mkv_debug_read_bandwidth", "mkv_profile_enable",
     "mkv_profile_read", "mkv_status_string", "mkv_last_error",
 ]
 
@@ -136,6 +136,7 @@ def _load():
         "mkv_pool_stats": (I32, [P, ctypes.POINTER(Stats)]),
         "mkv_debug_gather": (I32, [P, I32, I32, I32, P, P]),
         "mkv_debug_schedule": (I32, [P, ctypes.POINTER(ScheduleInfo), P, I32, P, I32, P, I32]),
+        "mkv_debug_read_bandwidth": (I32, [P, SZ, P, P]),
         "mkv_profile_enable": (I32, [P, I32]),
         "mkv_profile_read": (I32, [P, ctypes.POINTER(Profile)]),
         "mkv_status_string": (ctypes.c_char_p, [I32]),
@@ -347,6 +348,14 @@ def debug_schedule(pool, arrays: bool = True):
                                       base.ctypes.data_as(ctypes.c_void_p), base.size))
         out.update(items=items[:info.n_items], entries=ent[:info.n_list], chunk_base=base)
     return out
+
+
+def debug_read_bandwidth(src, sink, stream=None) -> None:
+    """Read every byte of the device tensor src once (read-ceiling calibration);
+    sink: int32/uint32 device tensor of 256 elements."""
+    nbytes = src.numel() * src.element_size()
+    _check(_load().mkv_debug_read_bandwidth(_dev_ptr(src, name="src"), nbytes,
+                                            _dev_ptr(sink, name="sink"), _stream(stream)))
 
 
 def profile_enable(pool, on: bool) -> None:

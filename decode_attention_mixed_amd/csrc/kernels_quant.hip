@@ -318,6 +318,38 @@ hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_p
   return hipGetLastError();
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Read-bandwidth calibration: every byte of src read once with 16-byte
+// nontemporal loads, four in flight per lane, grid-strided; an XOR of the data
+// is stored to sink only if it equals a value no caller arranges (so the loads
+// cannot be dropped).  bytes must be a multiple of 16.
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ p, int64_t n_vec,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t tid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int64_t i = tid;
+  for (; i + 3 * stride < n_vec; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc ^= v[k];
+  }
+  for (; i < n_vec; i += stride) acc ^= p[i];
+  const uint32_t r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (r == 0x9E3779B9u) sink[tid & 255] = r;
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s) {
+  if (bytes <= 0 || bytes % 16) return hipErrorInvalidValue;
+  // 8 workgroups of 256 lanes per CU of the largest part (256 CUs)
+  hipLaunchKernelGGL(stream_read_kernel, dim3(2048), dim3(256), 0, s, static_cast<const u32x4*>(src),
+                     bytes / 16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
                          uint8_t* dst, int64_t slot_bytes, hipStream_t s) {
   if (n <= 0) return hipSuccess;

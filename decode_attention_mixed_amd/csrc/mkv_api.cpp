@@ -796,6 +796,14 @@ mkv_status mkv_debug_gather(mkv_pool* p, int32_t seq, int32_t first, int32_t n, 
   return MKV_OK;
 }
 
+mkv_status mkv_debug_read_bandwidth(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  if (!src || !sink) return set_err(MKV_EINVAL, "null argument");
+  if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return set_err(MKV_EINVAL, "src must be 16-byte aligned and bytes a nonzero multiple of 16");
+  MKV_HIP(mkv::launch_stream_read(src, int64_t(bytes), sink, s));
+  return MKV_OK;
+}
+
 mkv_status mkv_debug_schedule(mkv_pool* p, mkv_schedule_info* info, int32_t* items_host,
                               int32_t items_cap, int32_t* entries_host, int32_t entries_cap,
                               int32_t* chunk_base_host, int32_t base_cap) {

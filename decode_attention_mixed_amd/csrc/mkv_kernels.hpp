@@ -81,6 +81,8 @@ hipError_t launch_append_inline(const PoolView& pv, const InlinePlan& plan, int3
                                 const float* k, const float* v, hipStream_t s);
 hipError_t launch_gather(const PoolView& pv, int32_t seq, int32_t first, int32_t n,
                          uint8_t* dst, int64_t slot_bytes, hipStream_t s);
+// Read-bandwidth calibration: reads bytes (a multiple of 16) of src once.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 // Partial kernel of the pool's kind (mixed FP8/TQ3 or BF16 control).
 hipError_t launch_partial(const DecodeArgs& a, hipStream_t s);
 // Waves of the partial kernel (head dim d, nh kv-heads per wave, pool kind)

@@ -260,6 +260,16 @@ mkv_status mkv_pool_stats(mkv_pool* pool, mkv_stats* out);
 mkv_status mkv_debug_gather(mkv_pool* pool, int32_t seq, int32_t first, int32_t n, void* dst,
                             hipStream_t stream);
 
+/* Read-bandwidth calibration (not part of the decode path): one kernel reads
+ * every byte of src (device, `bytes` a multiple of 16, 16-byte aligned) once
+ * with 16-byte loads, the access the partial kernel's record loads use.  A
+ * lane writes to sink (device, 256 uint32, caller-owned) only when the XOR of
+ * the data it read equals one fixed constant, which keeps the loads live;
+ * timing the call gives the device's read ceiling for the roofline.
+ * MKV_EINVAL for a null pointer, a misaligned src or a size not a multiple of
+ * 16. */
+mkv_status mkv_debug_read_bandwidth(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* The decode schedule the device holds: the one the pool's last mkv_decode
  * used, with the edits later mkv_append_step and mkv_demote calls made to it.
  * Synchronous (waits for the device, then copies).  `info` receives the
