@@ -593,10 +593,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA operands (exact FP8/TQ3 codes and hi/lo probabilities), f32 accumulation and softmax",
+        "dtype": "f16",
         "data": "synthetic: seeded N(0,1) fp32 K/V (outlier channels x8), bf16 N(0,1) query",
         "config": {
             "workload": describe(wl),
+            "arithmetic": "f16 MFMA operands (exact FP8/TQ3 codes, hi/lo split probabilities), "
+                          "f32 accumulation and softmax",
             "kv_bytes_per_step": step_bytes,
             "kv_bytes_fp8": fp8_b,
             "kv_bytes_tq3": tq3_b,
