@@ -304,8 +304,8 @@ def main():
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the BF16-control and all-FP8 comparison runs")
     ap.add_argument("--serve", type=int, default=0, metavar="N",
-                    help="also run N decode steps that each append one token to every sequence "
-                         "(mkv_append_step), demote the pages an anchor policy releases and decode")
+                    help="also run N mkv_decode_step calls: each appends one token to every "
+                         "sequence, converts the pages the library's anchor policy releases and decodes")
     ap.add_argument("--layer-calls", type=int, default=0, metavar="N",
                     help="also time the batch as N calls over consecutive entries (a multi-layer "
                          "workload decoded layer by layer instead of in one call)")
@@ -489,40 +489,33 @@ def main():
     if args.serve > 0:
         # Decode-step loop: the recent window is the workload's FP8 tail; anchors
         # older than it stay protected (FP8) for good.
+        # The library applies the anchor policy (mkv_set_anchor_window, with the
+        # workload's older anchors protected) inside each mkv_decode_step call.
         window = {"long": 4096, "throughput": 1024, "ragged": 512}.get(wl.name, 1024)
-        protected, demoted = [], []
-        for b in range(wl.B):
-            L = int(wl.lengths[b])
-            protected.append([a for a in wl.anchors[b] if (a + 1) * wl.P <= L - window])
-            demoted.append(wl.demote_pages(b))
-        policies = [H.AnchorPolicy(wl.P, window, protected, demoted) for _ in range(R)]
-        lens = [[int(x) for x in wl.lengths] for _ in range(R)]
+        for p in pools:
+            mkv.set_anchor_window(p.handle, window)
+            for b in range(wl.B):
+                L = int(wl.lengths[b])
+                mkv.protect_pages(p.handle, b, [a for a in wl.anchors[b] if (a + 1) * wl.P <= L - window])
+        tq3_before = sum(mkv.pool_stats(p.handle)["tq3_pages_live"] for p in pools)
         gen = torch.Generator(device="cuda").manual_seed(7)
         rows_k = torch.randn(16, wl.B, wl.Hkv, wl.d, device="cuda", generator=gen)
         rows_v = torch.randn(16, wl.B, wl.Hkv, wl.d, device="cuda", generator=gen)
-        n_dem = 0
         torch.cuda.synchronize()
         ev0.record()
         t0 = time.perf_counter()
         for i in range(args.serve):
-            r = i % R
-            h = pools[r].handle
-            mkv.append_step(h, batch, rows_k[i % 16], rows_v[i % 16])
-            for b in batch:
-                lens[r][b] += 1
-                pages = policies[r].step(b, lens[r][b])
-                if pages:
-                    mkv.demote(h, b, np.asarray(pages, np.int32))
-                    n_dem += len(pages)
-            mkv.decode(h, batch, q, tau, out, lse)
+            mkv.decode_step(pools[i % R].handle, batch, rows_k[i % 16], rows_v[i % 16], q, tau, out, lse)
         host = (time.perf_counter() - t0) / args.serve
         ev1.record()
         torch.cuda.synchronize()
         ms_serve = ev0.elapsed_time(ev1) / args.serve
+        n_dem = sum(mkv.pool_stats(p.handle)["tq3_pages_live"] for p in pools) - tq3_before
         serve = {"steps": args.serve, "window_tokens": window,
                  "us_per_step": round(ms_serve * 1e3, 3),
                  "host_us_per_step": round(host * 1e6, 2),
                  "decode_only_us_per_step": round(ms * 1e3, 3),
+                 "ratio_to_decode_only": round(ms_serve / ms, 3),
                  "pages_demoted": n_dem}
         log(f"serve: {serve}")
     for p in pools:

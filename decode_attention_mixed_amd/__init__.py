@@ -101,7 +101,8 @@ class ScheduleInfo(ctypes.Structure):
 EXPORTED = [
     "mkv_pool_bytes", "mkv_record_bytes", "mkv_pool_create", "mkv_pool_destroy",
     "mkv_seq_reset", "mkv_append", "mkv_append_step", "mkv_demote", "mkv_materialize",
-    "mkv_decode", "mkv_decode_static", "mkv_seq_info",
+    "mkv_decode", "mkv_decode_static", "mkv_decode_step", "mkv_set_anchor_window", "mkv_protect_pages",
+    "mkv_seq_info",
     "mkv_page_table", "mkv_pool_stats", "mkv_debug_gather", "mkv_debug_schedule", "mkv_debug_read_bandwidth", "mkv_profile_enable",
     "mkv_profile_read", "mkv_status_string", "mkv_last_error",
 ]
@@ -131,6 +132,9 @@ def _load():
         "mkv_append_step": (I32, [P, P, I32, P, P, P]),
         "mkv_decode": (I32, [P, P, I32, P, I32, F32, P, P, P]),
         "mkv_decode_static": (I32, [P, P, I32, P, I32, F32, P, P, P]),
+        "mkv_decode_step": (I32, [P, P, I32, P, P, P, I32, F32, P, P, P]),
+        "mkv_set_anchor_window": (I32, [P, I32]),
+        "mkv_protect_pages": (I32, [P, I32, P, I32, I32]),
         "mkv_seq_info": (I32, [P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "mkv_page_table": (I32, [P, I32, P, I32]),
         "mkv_pool_stats": (I32, [P, ctypes.POINTER(Stats)]),
@@ -295,6 +299,37 @@ def _decode(fn, pool, seq_ids, q, softmax_scale, out, lse, stream):
 def decode(pool, seq_ids, q, softmax_scale: float, out, lse, stream=None) -> None:
     """q: bf16 [B][Hq][d]; out: fp32 [B][Hq][d]; lse: fp32 [B][Hq] (all device)."""
     _decode(_load().mkv_decode, pool, seq_ids, q, softmax_scale, out, lse, stream)
+
+
+def decode_step(pool, seq_ids, k, v, q, softmax_scale: float, out, lse, stream=None) -> None:
+    """One decode-loop step: append k, v (fp32 device [B][Hkv][d], row b to
+    seq_ids[b]), apply the anchor policy (set_anchor_window), decode q into
+    out, lse (as decode)."""
+    import torch
+    ids, B = _i32_array(seq_ids)
+    _check_rows("k", k, B, pool)
+    d = _geom(pool)[1]
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != d:
+        raise ValueError(f"q must be [B][Hq][{d}] with B = len(seq_ids) = {B}, got {tuple(q.shape)}")
+    _check(_load().mkv_decode_step(pool, ids, B, _dev_ptr(k, torch.float32, name="k"),
+                                   _dev_ptr(v, torch.float32, tuple(k.shape), name="v"),
+                                   _dev_ptr(q, torch.bfloat16, name="q"), q.shape[1],
+                                   ctypes.c_float(softmax_scale),
+                                   _dev_ptr(out, torch.float32, tuple(q.shape), name="out"),
+                                   _dev_ptr(lse, torch.float32, tuple(q.shape[:2]), name="lse"),
+                                   _stream(stream)))
+
+
+def set_anchor_window(pool, window_tokens: int) -> None:
+    """Anchor policy of decode_step: pages wholly older than the last
+    window_tokens tokens and not protected are converted to TQ3 (< 0: off)."""
+    _check(_load().mkv_set_anchor_window(pool, int(window_tokens)))
+
+
+def protect_pages(pool, seq: int, lps, on: bool = True) -> None:
+    """Mark (on) or clear logical pages of seq as protected from the anchor policy."""
+    arr, n = _i32_array(lps)
+    _check(_load().mkv_protect_pages(pool, seq, arr, n, 1 if on else 0))
 
 
 def decode_static(pool, seq_ids, q, softmax_scale: float, out, lse, stream=None) -> None:

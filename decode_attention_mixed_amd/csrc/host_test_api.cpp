@@ -69,6 +69,22 @@ int mkvh_demote(mkvh* h, int32_t seq, const int32_t* lps, int32_t n, int32_t* pl
 
 int mkvh_reset(mkvh* h, int32_t seq) { return h->meta.reset(seq, &g_herr); }
 
+int mkvh_protect(mkvh* h, int32_t seq, const int32_t* lps, int32_t n, int32_t on) {
+  return h->meta.protect(seq, lps, n, on != 0, &g_herr);
+}
+
+// Anchor policy query of seq at its current length: the pages it converts
+// (up to cap into lps_out, the count into *n) and the cursor it would store.
+void mkvh_policy_pages(mkvh* h, int32_t seq, int32_t window, int32_t* lps_out, int32_t cap, int32_t* n,
+                       int32_t* next) {
+  std::vector<int32_t> lps;
+  h->meta.policy_pages(seq, window, &lps, next);
+  *n = int32_t(lps.size());
+  if (int32_t(lps.size()) <= cap) std::memcpy(lps_out, lps.data(), lps.size() * 4);
+}
+
+void mkvh_set_policy_next(mkvh* h, int32_t seq, int32_t next) { h->meta.set_policy_next(seq, next); }
+
 int32_t mkvh_seq_len(mkvh* h, int32_t seq) { return h->meta.seq(seq).len; }
 
 int32_t mkvh_page_table(mkvh* h, int32_t seq, int32_t* out, int32_t cap) {

@@ -92,10 +92,7 @@ append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float*
 // clamped to 65504; c = #{b in -3..3 : x >= b*s} (4 when s == 0); the 32 codes
 // form a 96-bit little-endian stream, code j at bit 3j.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads)
-demote_tq3_kernel(PoolView pv, const DemotePage* __restrict__ plan) {
-  const DemotePage dp = plan[blockIdx.x / pv.Hkv];
-  const int h = blockIdx.x % pv.Hkv;
+__device__ __forceinline__ void demote_block(const PoolView& pv, const DemotePage& dp, int h) {
   const int d = pv.d, ng = d / 32, row_bytes = 3 * d / 8;
   const uint8_t* src = pv.fp8 + int64_t(dp.src_phys) * pv.fp8_stride;
   uint8_t* dst = pv.tq3 + int64_t(dp.dst_phys) * pv.tq3_stride;
@@ -137,6 +134,11 @@ demote_tq3_kernel(PoolView pv, const DemotePage* __restrict__ plan) {
     reinterpret_cast<uint16_t*>(dst + tq3_scale_off(pv, h, kv))[t * ng + g] =
         __builtin_bit_cast(uint16_t, s16);
   }
+}
+
+__global__ void __launch_bounds__(kThreads)
+demote_tq3_kernel(PoolView pv, const DemotePage* __restrict__ plan) {
+  demote_block(pv, plan[blockIdx.x / pv.Hkv], blockIdx.x % pv.Hkv);
 }
 
 // ---------------------------------------------------------------------------
@@ -204,6 +206,33 @@ append_inline_kernel(PoolView pv, InlinePlan plan, const float* __restrict__ k,
     append_bf16_block(pv, ap, k, v);
   else
     append_fp8_block(pv, ap, k, v);
+}
+
+// A decode step's cache writes (StepPlan): blocks [0, 2 Hkv n_append) append
+// as append_inline_kernel, the next Hkv n_conv blocks convert one (page,
+// kv-head) each as demote_tq3_kernel, and the first block of each converted
+// page writes its page-table entry; block 0 applies the schedule patches.
+template <bool kBf16>
+__global__ void __launch_bounds__(kThreads)
+step_kernel(PoolView pv, StepPlan plan, const float* __restrict__ k, const float* __restrict__ v) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < plan.n_patch; i += kThreads) plan.patch_base[plan.patch_off[i]] = plan.patch_val[i];
+  const int n_app = plan.n_append * pv.Hkv * 2;
+  if (int(blockIdx.x) < n_app) {
+    const AppendPage ap = plan.pages[blockIdx.x / (pv.Hkv * 2)];
+    if constexpr (kBf16)
+      append_bf16_block(pv, ap, k, v);
+    else
+      append_fp8_block(pv, ap, k, v);
+    return;
+  }
+  if constexpr (!kBf16) {
+    const int c = (int(blockIdx.x) - n_app) / pv.Hkv, h = (int(blockIdx.x) - n_app) % pv.Hkv;
+    if (c >= plan.n_conv) return;              // the lone block of a patch-only launch
+    const DemotePage dp = plan.conv[c];
+    if (h == 0 && threadIdx.x == 0) const_cast<int32_t*>(pv.pt)[dp.pad0] = dp.pad1;
+    demote_block(pv, dp, h);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -307,6 +336,21 @@ hipError_t launch_append_inline(const PoolView& pv, const InlinePlan& plan, int3
     hipLaunchKernelGGL(append_inline_kernel<true>, grid, dim3(kThreads), 0, s, pv, plan, k, v);
   else
     hipLaunchKernelGGL(append_inline_kernel<false>, grid, dim3(kThreads), 0, s, pv, plan, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const PoolView& pv, const StepPlan& plan, const float* k, const float* v,
+                       hipStream_t s) {
+  if (plan.n_append < 0 || plan.n_append > kInlinePages || plan.n_conv < 0 || plan.n_conv > kStepConv ||
+      plan.n_patch < 0 || plan.n_patch > kStepPatches || (pv.kind == kKindBf16 && plan.n_conv > 0))
+    return hipErrorInvalidValue;
+  const int blocks = plan.n_append * pv.Hkv * 2 + plan.n_conv * pv.Hkv;
+  if (blocks == 0 && plan.n_patch == 0) return hipSuccess;
+  const dim3 grid(unsigned(blocks > 0 ? blocks : 1));
+  if (pv.kind == kKindBf16)
+    hipLaunchKernelGGL(step_kernel<true>, grid, dim3(kThreads), 0, s, pv, plan, k, v);
+  else
+    hipLaunchKernelGGL(step_kernel<false>, grid, dim3(kThreads), 0, s, pv, plan, k, v);
   return hipGetLastError();
 }
 

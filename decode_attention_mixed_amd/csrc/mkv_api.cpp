@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdlib>
 #include <cstring>
@@ -138,6 +139,7 @@ struct mkv_pool {
   int32_t target_waves[2] = {2048, 1024};   // resident partial-kernel waves, 1 or 2 heads per wave
   int32_t merge_narrow_max = 16;            // per-lane merge up to this many chunks per entry
   bool pace = true;                         // progress-paced wave priorities (one-round launches)
+  int32_t anchor_window = -1;               // mkv_decode_step's anchor policy window (-1: off)
   void* static_ws = nullptr;                // the device's fixed workspace (mkv_decode_static)
   // profiling
   bool prof = false;
@@ -192,6 +194,36 @@ mkv_status flush_uploads(mkv_pool* p, const std::vector<Upload>& ups, hipStream_
   MKV_HIP(mkv::launch_upload(u, s));
   MKV_HIP(hipEventRecord(p->staging_ev[p->staging_slot], s));
   p->staging_pending[p->staging_slot] = true;
+  return MKV_OK;
+}
+
+// Host bytes bound for a device offset of the pool (whole 32-bit words).
+struct Piece {
+  size_t dst_off;
+  const void* src;
+  size_t bytes;
+};
+
+// Uploads the pieces in order with as few upload launches as the segment
+// count and the staging slot size allow.
+mkv_status upload_pieces(mkv_pool* p, const std::vector<Piece>& pieces, hipStream_t s) {
+  size_t i = 0;
+  while (i < pieces.size()) {
+    mkv_status r = p->wait_staging();
+    if (r) return r;
+    std::vector<Upload> ups;
+    size_t off = 0;
+    while (i < pieces.size() && ups.size() < size_t(mkv::kUploadSegs) &&
+           off + pieces[i].bytes <= p->staging_bytes) {
+      if (pieces[i].bytes) std::memcpy(p->staging + off, pieces[i].src, pieces[i].bytes);
+      ups.push_back(Upload{pieces[i].dst_off, pieces[i].bytes});
+      off += pieces[i].bytes;
+      ++i;
+    }
+    if (ups.empty()) return set_err(MKV_EINVAL, "upload larger than a staging slot");
+    r = flush_uploads(p, ups, s);
+    if (r) return r;
+  }
   return MKV_OK;
 }
 
@@ -409,34 +441,45 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
 
 namespace {
 
-// Uploads an edited copy of the cached schedule (the items, and the page list
-// from word `from` on) and makes it the cached one.  On failure the cached
-// schedule is dropped, so the next decode rebuilds it.
-mkv_status commit_schedule(mkv_pool* p, mkv::Schedule&& sc, size_t from, hipStream_t s) {
+size_t list_cap(const mkv_pool* p) {
+  return size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
+}
+
+// Pieces that bring the device copy of the cached schedule up to date after
+// in-place edits: all item records and the list words the edits rewrote
+// (sorted, runs closer than 64 words merged).
+void schedule_pieces(const mkv_pool* p, mkv::ListEdits& ed, std::vector<Piece>* out) {
+  const mkv::Schedule& sc = p->sched;
+  const size_t n8 = sc.items[0].size(), n3 = sc.items[1].size();
+  const size_t base = p->lay.sched + p->lay.items_off;
+  out->push_back(Piece{base, sc.items[0].data(), n8 * sizeof(mkv::WorkItem)});
+  out->push_back(Piece{base + n8 * sizeof(mkv::WorkItem), sc.items[1].data(), n3 * sizeof(mkv::WorkItem)});
+  auto& r = ed.ranges;
+  std::sort(r.begin(), r.end());
+  std::vector<std::pair<size_t, size_t>> runs;
+  for (const auto& x : r) {
+    if (!runs.empty() && x.first <= runs.back().second + 64)
+      runs.back().second = std::max(runs.back().second, x.second);
+    else
+      runs.push_back(x);
+  }
+  const size_t eoff = p->lay.sched + entries_off(p->lay, n8 + n3);
+  for (const auto& x : runs)
+    out->push_back(Piece{eoff + x.first * 4, sc.entries.data() + x.first, (x.second - x.first) * 4});
+}
+
+// Uploads what in-place edits changed and marks the cached schedule current;
+// on failure it is dropped (the next decode rebuilds it).
+mkv_status commit_edits(mkv_pool* p, mkv::ListEdits& ed, hipStream_t s) {
   p->sched_valid = false;
-  mkv_status err = p->wait_staging();
-  if (err) return err;
-  size_t off = 0;
-  for (const auto& list : sc.items)
-    for (const mkv::WorkItem& it : list) {
-      std::memcpy(p->staging + off, &it, sizeof(it));
-      off += sizeof(it);
-    }
-  const size_t n_items = sc.items[0].size() + sc.items[1].size();
-  const size_t tail = (sc.entries.size() - from) * 4;
-  std::memcpy(p->staging + off, sc.entries.data() + from, tail);
-  err = flush_uploads(p, {{p->lay.sched + p->lay.items_off, off},
-                          {p->lay.sched + entries_off(p->lay, n_items) + from * 4, tail}}, s);
-  if (err) return err;
-  p->sched = std::move(sc);
+  std::vector<Piece> pieces;
+  schedule_pieces(p, ed, &pieces);
+  mkv_status r = upload_pieces(p, pieces, s);
+  if (r) return r;
   p->sched_version = p->meta.version();
   p->sched_layout = p->meta.layout_version();
   p->sched_valid = true;
   return MKV_OK;
-}
-
-size_t list_cap(const mkv_pool* p) {
-  return size_t(p->desc.max_batch) * size_t(p->desc.max_pages_per_seq);
 }
 
 }  // namespace
@@ -522,21 +565,20 @@ mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
   if (lists_current && p->meta.layout_version() != p->sched_layout) {
     // pages opened: extend the cached schedule where it applies; otherwise
     // (or if its upload fails) the next decode rebuilds it
-    mkv::Schedule sc = p->sched;
-    if (mkv::schedule_extend(p->meta, p->sched_ids, seq_ids, plan, list_cap(p), &sc)) {
-      const size_t from = p->sched.entries.size();
-      (void)commit_schedule(p, std::move(sc), from, s);
-    } else {
+    mkv::ListEdits ed;
+    if (mkv::schedule_extend(p->meta, p->sched_ids, seq_ids, plan, list_cap(p), &p->sched, &ed))
+      (void)commit_edits(p, ed, s);
+    else
       p->sched_valid = false;
-    }
   }
   return MKV_OK;
 }
 
 
-mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, hipStream_t s) {
-  if (!p) return set_err(MKV_EINVAL, "null pool");
-  DeviceGuard guard(p->device);
+namespace {
+
+// mkv_demote on a pool whose device is current.
+mkv_status demote_impl(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, hipStream_t s) {
   std::vector<mkv::DemotePage> plan;
   std::string err;
   const bool lists_current = p->sched_valid && p->sched_layout == p->meta.layout_version();
@@ -557,13 +599,36 @@ mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, h
   // keep the cached schedule current where the moved pages fit it; otherwise
   // (or if its upload fails) the next decode rebuilds it
   if (lists_current) {
-    mkv::Schedule sc = p->sched;
-    if (mkv::schedule_demote(p->meta, p->sched_ids, seq, plan, list_cap(p), &sc))
-      (void)commit_schedule(p, std::move(sc), 0, s);
+    mkv::ListEdits ed;
+    if (mkv::schedule_demote(p->meta, p->sched_ids, seq, plan, list_cap(p), &p->sched, &ed))
+      (void)commit_edits(p, ed, s);
     else
       p->sched_valid = false;
   }
   return MKV_OK;
+}
+
+}  // namespace
+
+mkv_status mkv_demote(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, hipStream_t s) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  DeviceGuard guard(p->device);
+  return demote_impl(p, seq, lps, n, s);
+}
+
+mkv_status mkv_set_anchor_window(mkv_pool* p, int32_t window_tokens) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  if (window_tokens >= 0 && p->meta.geom().kind == mkv::kKindBf16)
+    return set_err(MKV_ESTATE, "a BF16 control pool holds one format; pages are never converted");
+  p->anchor_window = window_tokens < 0 ? -1 : window_tokens;
+  return MKV_OK;
+}
+
+mkv_status mkv_protect_pages(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, int32_t protect) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  std::string err;
+  const int st = p->meta.protect(seq, lps, n, protect != 0, &err);
+  return st ? set_err(mkv_status(st), err) : MKV_OK;
 }
 
 namespace {
@@ -699,6 +764,240 @@ mkv_status decode_impl(mkv_pool* p, const int32_t* seq_ids, int32_t B, const voi
 mkv_status mkv_decode(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void* q, int32_t Hq,
                       float softmax_scale, float* out, float* lse, hipStream_t s) {
   return decode_impl(p, seq_ids, B, q, Hq, softmax_scale, out, lse, s, StateHome::kPool);
+}
+
+mkv_status mkv_decode_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const float* k, const float* v,
+                           const void* q, int32_t Hq, float softmax_scale, float* out, float* lse,
+                           hipStream_t s) {
+  if (!p) return set_err(MKV_EINVAL, "null pool");
+  if (B < 1 || !seq_ids || !k || !v || !q || !out || !lse) return set_err(MKV_EINVAL, "null argument");
+  if (B > p->desc.max_batch) return set_err(MKV_ERANGE, "B exceeds max_batch");
+  // the decode's argument checks come first: once the append is enqueued the
+  // step can only fail on the device side
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return set_err(MKV_EINVAL, "q must be 16-byte aligned");
+  const int32_t Hkv = p->meta.geom().Hkv;
+  if (Hq < 1 || Hq % Hkv) return set_err(MKV_EINVAL, "Hq must be a positive multiple of Hkv");
+  if (Hq > p->desc.max_q_heads) return set_err(MKV_ERANGE, "Hq exceeds max_q_heads");
+  if (Hq / Hkv > 16) return set_err(MKV_EINVAL, "Hq / Hkv must be at most 16");
+  DeviceGuard guard(p->device);
+  std::vector<mkv::AppendPage> plan;
+  std::string err;
+  const bool lists_current = p->sched_valid && p->sched_layout == p->meta.layout_version();
+  mkv::Undo undo;
+  int st = p->meta.append_step(seq_ids, B, p->desc.max_pages_per_seq, &plan, &err, &undo);
+  if (st) return set_err(mkv_status(st), err);
+
+  // The anchor policy's conversions at the new lengths, checked against the
+  // TQ3 slab, then applied to the metadata (each with its undo record).
+  struct Conv {
+    int32_t seq, next;
+    std::vector<mkv::DemotePage> plan;
+    mkv::Undo undo;
+  };
+  std::vector<Conv> conv;
+  auto take_back = [&]() {
+    for (size_t i = conv.size(); i-- > 0;) p->meta.rollback(conv[i].undo);
+    p->meta.rollback(undo);
+  };
+  size_t n_conv = 0;
+  if (p->anchor_window >= 0) {
+    std::vector<int32_t> lps;
+    std::vector<std::vector<int32_t>> todo(static_cast<size_t>(B));
+    std::vector<int32_t> nexts(static_cast<size_t>(B));
+    for (int32_t b = 0; b < B; ++b) {
+      p->meta.policy_pages(seq_ids[b], p->anchor_window, &todo[size_t(b)], &nexts[size_t(b)]);
+      n_conv += todo[size_t(b)].size();
+    }
+    if (int64_t(n_conv) > p->meta.tq3_free()) {
+      p->meta.rollback(undo);
+      return set_err(MKV_ENOMEM, "TQ3 slab has too few free pages for the anchor policy's conversions");
+    }
+    for (int32_t b = 0; b < B; ++b) {
+      conv.push_back(Conv{seq_ids[b], nexts[size_t(b)], {}, {}});
+      const auto& t = todo[size_t(b)];
+      if (t.empty()) continue;
+      st = p->meta.demote(seq_ids[b], t.data(), int32_t(t.size()), &conv.back().plan, &err, &conv.back().undo);
+      if (st) {
+        conv.pop_back();
+        take_back();
+        return set_err(mkv_status(st), err);
+      }
+    }
+  }
+  auto finish = [&]() {
+    for (const Conv& c : conv) p->meta.set_policy_next(c.seq, c.next);
+    return decode_impl(p, seq_ids, B, q, Hq, softmax_scale, out, lse, s, StateHome::kPool);
+  };
+
+  // One launch when it fits the kernel arguments: the appended pages, the
+  // conversions (each writing its page-table entry) and the cached
+  // schedule's edits as word patches.  The appended and converted FP8 pages
+  // must differ (a window of 0 can convert the page this step filled).
+  bool fused = plan.size() <= size_t(mkv::kInlinePages) && n_conv <= size_t(mkv::kStepConv);
+  for (const Conv& c : conv)
+    for (const mkv::DemotePage& dp : c.plan)
+      for (const mkv::AppendPage& ap : plan) fused = fused && ap.phys != dp.src_phys;
+  if (fused) {
+    mkv::StepPlan sp{};
+    sp.patch_base = reinterpret_cast<int32_t*>(p->mem + p->lay.sched + p->lay.items_off);
+    sp.n_append = int32_t(plan.size());
+    std::memcpy(sp.pages, plan.data(), plan.size() * sizeof(plan[0]));
+    for (const Conv& c : conv)
+      for (const mkv::DemotePage& dp : c.plan) {
+        mkv::DemotePage x = dp;
+        x.pad0 = c.seq * p->desc.max_pages_per_seq + dp.lp;
+        x.pad1 = p->meta.seq(c.seq).pt[size_t(dp.lp)];
+        sp.conv[sp.n_conv++] = x;
+      }
+    // schedule edits in place; their changed words become patches (or, past
+    // the patch capacity, an upload before the launch)
+    bool edited = false;
+    mkv::ListEdits ed;
+    if (lists_current) {
+      const std::vector<mkv::WorkItem> before[2] = {p->sched.items[0], p->sched.items[1]};
+      edited = mkv::schedule_extend(p->meta, p->sched_ids, seq_ids, plan, list_cap(p), &p->sched, &ed);
+      for (const Conv& c : conv)
+        if (edited && !c.plan.empty())
+          edited = mkv::schedule_demote(p->meta, p->sched_ids, c.seq, c.plan, list_cap(p), &p->sched, &ed);
+      if (edited) {
+        const size_t words = sizeof(mkv::WorkItem) / 4;
+        const size_t n8 = p->sched.items[0].size();
+        const int32_t eword = int32_t((entries_off(p->lay, n8 + p->sched.items[1].size()) - p->lay.items_off) / 4);
+        bool fits = true;
+        auto patch = [&](int32_t off, int32_t val) {
+          if (sp.n_patch == mkv::kStepPatches) {
+            fits = false;
+            return;
+          }
+          sp.patch_off[sp.n_patch] = off;
+          sp.patch_val[sp.n_patch++] = val;
+        };
+        for (int f = 0; f < 2 && fits; ++f)
+          for (size_t i = 0; i < before[f].size() && fits; ++i) {
+            const int32_t* a = reinterpret_cast<const int32_t*>(&before[f][i]);
+            const int32_t* b = reinterpret_cast<const int32_t*>(&p->sched.items[f][i]);
+            for (size_t w = 0; w < words; ++w)
+              if (a[w] != b[w]) patch(int32_t(((f ? n8 : 0) + i) * words + w), b[w]);
+          }
+        for (const auto& x : ed.ranges)
+          for (size_t w = x.first; w < x.second && fits; ++w) patch(eword + int32_t(w), p->sched.entries[w]);
+        if (!fits) {
+          sp.n_patch = 0;
+          p->sched_valid = false;
+          std::vector<Piece> pieces;
+          schedule_pieces(p, ed, &pieces);
+          mkv_status r = upload_pieces(p, pieces, s);
+          if (r) {
+            take_back();
+            return r;
+          }
+        }
+      }
+    }
+    p->sched_valid = false;
+    const hipError_t e = mkv::launch_step(p->view(), sp, k, v, s);
+    if (e != hipSuccess) {
+      take_back();
+      return set_err(MKV_EHIP, std::string("step launch: ") + hipGetErrorString(e));
+    }
+    if (edited) {
+      p->sched_version = p->meta.version();
+      p->sched_layout = p->meta.layout_version();
+      p->sched_valid = true;
+    }
+    return finish();
+  }
+
+  // Otherwise batched uploads: the append plan (unless it travels in the
+  // kernel arguments), the conversions' plan and the cached schedule's edits,
+  // then the append; the converted sequences' page-table rows, then one
+  // conversion launch (so that a failed append leaves the device page table
+  // as the metadata it rolls back to).
+  const bool inline_plan = plan.size() <= size_t(mkv::kInlinePages);
+  const size_t a_bytes = inline_plan ? 0 : plan.size() * sizeof(plan[0]);
+  std::vector<mkv::DemotePage> dplan;
+  for (const Conv& c : conv) dplan.insert(dplan.end(), c.plan.begin(), c.plan.end());
+  const size_t d_bytes = dplan.size() * sizeof(mkv::DemotePage);
+  if (a_bytes + d_bytes > p->lay.plan_bytes) {
+    // too large for one plan region: the calls one after another
+    mkv_status r = append_step_device(p, seq_ids, B, plan, k, v, s);
+    if (r) {
+      take_back();
+      return r;
+    }
+    p->sched_valid = false;
+    for (const Conv& c : conv) {
+      if (c.plan.empty()) continue;
+      r = upload_pt_row_and_plan(p, c.seq, c.plan.data(), c.plan.size() * sizeof(c.plan[0]), s);
+      if (r == MKV_OK) {
+        const hipError_t e = mkv::launch_demote(
+            p->view(), reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan), int32_t(c.plan.size()), s);
+        if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("demote launch: ") + hipGetErrorString(e));
+      }
+      if (r) return r;
+    }
+    return finish();
+  }
+  std::vector<Piece> pieces, rows;
+  if (a_bytes) pieces.push_back(Piece{p->lay.plan, plan.data(), a_bytes});
+  if (d_bytes) pieces.push_back(Piece{p->lay.plan + a_bytes, dplan.data(), d_bytes});
+  for (const Conv& c : conv) {
+    if (c.plan.empty()) continue;
+    const std::vector<int32_t>& pt = p->meta.seq(c.seq).pt;
+    rows.push_back(Piece{p->lay.pt + size_t(c.seq) * size_t(p->desc.max_pages_per_seq) * 4, pt.data(),
+                         pt.size() * 4});
+  }
+  mkv::ListEdits ed;
+  bool edited = false;
+  if (lists_current) {
+    edited = mkv::schedule_extend(p->meta, p->sched_ids, seq_ids, plan, list_cap(p), &p->sched, &ed);
+    for (const Conv& c : conv)
+      if (edited && !c.plan.empty())
+        edited = mkv::schedule_demote(p->meta, p->sched_ids, c.seq, c.plan, list_cap(p), &p->sched, &ed);
+    if (edited) schedule_pieces(p, ed, &pieces);
+  }
+  p->sched_valid = false;
+  mkv_status r = upload_pieces(p, pieces, s);
+  if (r == MKV_OK) {
+    if (inline_plan) {
+      mkv::InlinePlan ip{};
+      std::memcpy(ip.pages, plan.data(), plan.size() * sizeof(plan[0]));
+      ip.patch_base = reinterpret_cast<int32_t*>(p->mem + p->lay.sched + p->lay.items_off);
+      const hipError_t e = mkv::launch_append_inline(p->view(), ip, int32_t(plan.size()), k, v, s);
+      if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("append launch: ") + hipGetErrorString(e));
+    } else {
+      const auto* ap = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
+      const hipError_t e = p->meta.geom().kind == mkv::kKindBf16
+                               ? mkv::launch_append_bf16(p->view(), ap, int32_t(plan.size()), k, v, s)
+                               : mkv::launch_append(p->view(), ap, int32_t(plan.size()), k, v, s);
+      if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("append launch: ") + hipGetErrorString(e));
+    }
+  }
+  if (r) {
+    take_back();
+    return r;
+  }
+  if (!dplan.empty()) {
+    r = upload_pieces(p, rows, s);
+    if (r == MKV_OK) {
+      const hipError_t e = mkv::launch_demote(
+          p->view(), reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan + a_bytes),
+          int32_t(dplan.size()), s);
+      if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("demote launch: ") + hipGetErrorString(e));
+    }
+    if (r) {
+      // the append stays; the conversions are taken back (their cursors do
+      // not move, so the next step retries them)
+      for (size_t i = conv.size(); i-- > 0;) p->meta.rollback(conv[i].undo);
+      return r;
+    }
+  }
+  if (edited) {
+    p->sched_version = p->meta.version();
+    p->sched_layout = p->meta.layout_version();
+    p->sched_valid = true;
+  }
+  return finish();
 }
 
 mkv_status mkv_decode_static(mkv_pool* p, const int32_t* seq_ids, int32_t B, const void* q, int32_t Hq,

@@ -63,11 +63,32 @@ struct InlinePlan {
   int32_t patch_off[kInlinePages];
   int32_t patch_val[kInlinePages];
 };
+// One decode step's cache writes in one launch, everything in the kernel
+// arguments: the appended pages (as InlinePlan), the pages the anchor policy
+// converts (DemotePage with pad0 = page-table slot, pad1 = its new entry,
+// written by the kernel), and word patches of the cached schedule region
+// (offsets in 32-bit words from patch_base).  The appended and the converted
+// FP8 pages must be distinct.
+constexpr int kStepConv = 16;
+constexpr int kStepPatches = 128;
+struct StepPlan {
+  int32_t* patch_base;
+  int32_t n_append, n_conv, n_patch, pad0;
+  AppendPage pages[kInlinePages];
+  DemotePage conv[kStepConv];
+  int32_t patch_off[kStepPatches];
+  int32_t patch_val[kStepPatches];
+};
+static_assert(sizeof(StepPlan) + sizeof(PoolView) + 2 * sizeof(void*) <= 4096,
+              "the step kernel's arguments fit the 4 KB kernel-argument limit");
+hipError_t launch_step(const PoolView& pv, const StepPlan& plan, const float* k, const float* v,
+                       hipStream_t s);
+
 // Metadata upload: up to kUploadSegs runs of 32-bit words copied from a
 // device-mapped, coherent pinned host buffer (src, word offsets src_word) to
 // device memory, in one launch (a copy-engine transfer of the same bytes adds
 // more latency to the stream than this kernel takes).
-constexpr int kUploadSegs = 4;
+constexpr int kUploadSegs = 16;
 struct UploadSet {
   const uint32_t* src;
   int32_t nseg, pad0;

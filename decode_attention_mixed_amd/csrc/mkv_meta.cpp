@@ -272,9 +272,44 @@ int Meta::reset(int32_t s, std::string* err) {
   for (int32_t e : q.pt) free_[pt_is_tq3(e) ? 1 : 0].push(pt_index(e));
   q.pt.clear();
   q.len = 0;
+  q.prot.clear();
+  q.policy_next = 0;
   ++version_;
   ++layout_version_;
   return MKV_S_OK;
+}
+
+int Meta::protect(int32_t s, const int32_t* lps, int32_t n, bool on, std::string* err) {
+  int st = check_seq(s, err);
+  if (st) return st;
+  if (n < 0 || (n > 0 && !lps)) return fail(err, MKV_S_EINVAL, "bad page list");
+  for (int32_t i = 0; i < n; ++i)
+    if (lps[i] < 0 || lps[i] >= d_.max_pages_per_seq)
+      return fail(err, MKV_S_EINVAL, "logical page out of range");
+  Seq& q = seqs_[size_t(s)];
+  for (int32_t i = 0; i < n; ++i) {
+    const size_t lp = size_t(lps[i]);
+    if (lp >= q.prot.size()) {
+      if (!on) continue;
+      q.prot.resize(lp + 1, 0);
+    }
+    q.prot[lp] = on ? 1 : 0;
+  }
+  return MKV_S_OK;
+}
+
+void Meta::policy_pages(int32_t s, int32_t window, std::vector<int32_t>* lps, int32_t* next) const {
+  lps->clear();
+  const Seq& q = seqs_[size_t(s)];
+  *next = q.policy_next;
+  if (window < 0) return;
+  // pages wholly before the window: tokens [lp P, (lp + 1) P) all below len - window
+  const int32_t full = std::max(0, (q.len - window) / g_.P);
+  for (int32_t lp = q.policy_next; lp < full; ++lp) {
+    const bool marked = size_t(lp) < q.prot.size() && q.prot[size_t(lp)];
+    if (!marked && !pt_is_tq3(q.pt[size_t(lp)])) lps->push_back(lp);
+  }
+  *next = std::max(q.policy_next, full);
 }
 
 int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedPolicy& pol,
@@ -381,11 +416,18 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
   }
   out->items[0].clear();
   out->items[1].clear();
+  out->cap[0].clear();
+  out->cap[1].clear();
   out->pages.clear();
   out->pages.reserve(size_t(total_pages));
   out->entries.clear();
   out->entries.reserve(size_t(total_pages));
   out->chunk_base.assign(size_t(B) + 1, 0);
+  // spare room after each entry's last FP8 and TQ3 item, as far as the list
+  // capacity allows
+  const int64_t list_cap = int64_t(d_.max_batch) * int64_t(d_.max_pages_per_seq);
+  const int32_t slack = int32_t(std::max<int64_t>(
+      0, std::min<int64_t>(kGrowSlack, (list_cap - total_pages) / std::max<int64_t>(1, 2 * int64_t(B)))));
   int32_t nc = 0, largest = 0;
   for (int32_t b = 0; b < B; ++b) {
     out->chunk_base[size_t(b)] = nc;
@@ -404,6 +446,7 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
           ++chunk_idx;
           left = small + (chunk_idx < extra ? 1 : 0);
           items.push_back(WorkItem{b, ids[b], int32_t(out->pages.size()), 0, 0, nc++, fmt, 0});
+          out->cap[fmt].push_back(left);
         }
         out->pages.push_back(lp);
         out->entries.push_back(q.pt[size_t(lp)]);
@@ -412,6 +455,13 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
         items.back().last_lp = lp;
         largest = std::max(largest, items.back().npages);
         --left;
+      }
+      // the list's last item (its pages end the arrays) gets the spare room
+      const int32_t room = std::min(slack, kMaxChunkPages - items.back().npages);
+      if (room > 0) {
+        out->pages.insert(out->pages.end(), size_t(room), -1);
+        out->entries.insert(out->entries.end(), size_t(room), 0);
+        out->cap[fmt].back() += room;
       }
     }
   }
@@ -471,49 +521,70 @@ void schedule_refresh_tokens(const Meta& m, Schedule* sc) {
 
 namespace {
 
-// Copies item `it`'s page list to the end of the list arrays, one page longer
-// (the new last page is (lp, entry)).
-void grow_item(Schedule& sc, WorkItem& it, int32_t lp, int32_t entry) {
-  const int32_t off = int32_t(sc.entries.size());
-  for (int32_t i = 0; i < it.npages; ++i) {
-    const int32_t e = sc.entries[size_t(it.list_off + i)], p = sc.pages[size_t(it.list_off + i)];
-    sc.entries.push_back(e);
-    sc.pages.push_back(p);
+// Item idx of list f takes (lp, entry) as its new last page: in its spare
+// room, or with its list copied to the end of the list arrays with up to
+// kGrowSlack spare pages (false when the arrays would exceed list_cap).
+bool grow_item(Schedule& sc, int f, size_t idx, int32_t lp, int32_t entry, size_t list_cap,
+               ListEdits* edits) {
+  WorkItem& it = sc.items[f][idx];
+  int32_t& cap = sc.cap[f][idx];
+  if (it.npages >= cap) {
+    const int32_t room = std::max(0, std::min(kGrowSlack, kMaxChunkPages - it.npages - 1));
+    const size_t off = sc.entries.size();
+    if (off + size_t(it.npages) + 1 + size_t(room) > list_cap) return false;
+    for (int32_t i = 0; i < it.npages; ++i) {
+      const int32_t e = sc.entries[size_t(it.list_off + i)], p = sc.pages[size_t(it.list_off + i)];
+      sc.entries.push_back(e);
+      sc.pages.push_back(p);
+    }
+    sc.entries.insert(sc.entries.end(), size_t(1 + room), 0);
+    sc.pages.insert(sc.pages.end(), size_t(1 + room), -1);
+    if (edits) edits->add(off, off + size_t(it.npages));
+    it.list_off = int32_t(off);
+    cap = it.npages + 1 + room;
   }
-  sc.entries.push_back(entry);
-  sc.pages.push_back(lp);
-  it.list_off = off;
+  const size_t at = size_t(it.list_off + it.npages);
+  sc.entries[at] = entry;
+  sc.pages[at] = lp;
+  if (edits) edits->add(at, at + 1);
   it.npages += 1;
   it.last_lp = lp;
   sc.chunk_pages = std::max(sc.chunk_pages, it.npages);
+  return true;
+}
+
+// Index of entry b's last item of list f (highest last page), or -1.
+int64_t last_item(const Schedule& sc, int f, int32_t b) {
+  int64_t best = -1;
+  for (size_t i = 0; i < sc.items[f].size(); ++i) {
+    const WorkItem& it = sc.items[f][i];
+    if (it.b == b && (best < 0 || it.last_lp > sc.items[f][size_t(best)].last_lp)) best = int64_t(i);
+  }
+  return best;
 }
 
 }  // namespace
 
 bool schedule_extend(const Meta& m, const std::vector<int32_t>& ids, const int32_t* ids_of_rows,
-                     const std::vector<AppendPage>& plan, size_t list_cap, Schedule* out) {
-  Schedule sc = *out;
+                     const std::vector<AppendPage>& plan, size_t list_cap, Schedule* sc,
+                     ListEdits* edits) {
   for (const AppendPage& ap : plan) {
     if (ap.pt_slot < 0) continue;
     const int32_t seq = ids_of_rows[ap.src_row];
     for (size_t b = 0; b < ids.size(); ++b) {
       if (ids[b] != seq) continue;
-      WorkItem* last = nullptr;
-      for (WorkItem& it : sc.items[0])
-        if (it.b == int32_t(b) && (!last || it.last_lp > last->last_lp)) last = &it;
-      if (!last || last->npages >= kMaxChunkPages || sc.entries.size() + size_t(last->npages) + 1 > list_cap)
-        return false;
-      grow_item(sc, *last, ap.lp, ap.pt_entry);
+      const int64_t last = last_item(*sc, 0, int32_t(b));
+      if (last < 0 || sc->items[0][size_t(last)].npages >= kMaxChunkPages) return false;
+      if (!grow_item(*sc, 0, size_t(last), ap.lp, ap.pt_entry, list_cap, edits)) return false;
     }
   }
-  schedule_refresh_tokens(m, &sc);
-  *out = std::move(sc);
+  schedule_refresh_tokens(m, sc);
   return true;
 }
 
 bool schedule_demote(const Meta& m, const std::vector<int32_t>& ids, int32_t seq,
-                     const std::vector<DemotePage>& plan, size_t list_cap, Schedule* out) {
-  Schedule sc = *out;
+                     const std::vector<DemotePage>& plan, size_t list_cap, Schedule* sc,
+                     ListEdits* edits) {
   const Seq& q = m.seq(seq);
   const int32_t P = m.geom().P;
   for (size_t b = 0; b < ids.size(); ++b) {
@@ -521,33 +592,38 @@ bool schedule_demote(const Meta& m, const std::vector<int32_t>& ids, int32_t seq
     for (const DemotePage& dp : plan) {
       WorkItem* src = nullptr;
       int32_t at = -1;
-      for (WorkItem& it : sc.items[0]) {
+      for (WorkItem& it : sc->items[0]) {
         if (it.b != int32_t(b)) continue;
         for (int32_t i = 0; i < it.npages && at < 0; ++i)
-          if (sc.pages[size_t(it.list_off + i)] == dp.lp) at = i;
+          if (sc->pages[size_t(it.list_off + i)] == dp.lp) at = i;
         if (at >= 0) {
           src = &it;
           break;
         }
       }
       if (!src || src->npages < 2) return false;
-      for (int32_t i = at; i + 1 < src->npages; ++i) {
-        sc.entries[size_t(src->list_off + i)] = sc.entries[size_t(src->list_off + i + 1)];
-        sc.pages[size_t(src->list_off + i)] = sc.pages[size_t(src->list_off + i + 1)];
+      if (at == 0) {
+        // the item's first page (the oldest page of a recency window): the
+        // list starts one word later, no word moves
+        src->list_off += 1;
+        sc->cap[0][size_t(src - sc->items[0].data())] -= 1;
+      } else {
+        for (int32_t i = at; i + 1 < src->npages; ++i) {
+          sc->entries[size_t(src->list_off + i)] = sc->entries[size_t(src->list_off + i + 1)];
+          sc->pages[size_t(src->list_off + i)] = sc->pages[size_t(src->list_off + i + 1)];
+        }
+        if (edits) edits->add(size_t(src->list_off + at), size_t(src->list_off + src->npages - 1));
       }
       --src->npages;
-      src->last_lp = sc.pages[size_t(src->list_off + src->npages - 1)];
-      WorkItem* dst = nullptr;
-      for (WorkItem& it : sc.items[1])
-        if (it.b == int32_t(b) && (!dst || it.last_lp > dst->last_lp)) dst = &it;
-      if (!dst || dst->npages >= kMaxChunkPages || page_tokens(q.len, P, dst->last_lp) != P ||
-          sc.entries.size() + size_t(dst->npages) + 1 > list_cap)
+      src->last_lp = sc->pages[size_t(src->list_off + src->npages - 1)];
+      const int64_t dst = last_item(*sc, 1, int32_t(b));
+      if (dst < 0 || sc->items[1][size_t(dst)].npages >= kMaxChunkPages ||
+          page_tokens(q.len, P, sc->items[1][size_t(dst)].last_lp) != P)
         return false;
-      grow_item(sc, *dst, dp.lp, q.pt[size_t(dp.lp)]);
+      if (!grow_item(*sc, 1, size_t(dst), dp.lp, q.pt[size_t(dp.lp)], list_cap, edits)) return false;
     }
   }
-  schedule_refresh_tokens(m, &sc);
-  *out = std::move(sc);
+  schedule_refresh_tokens(m, sc);
   return true;
 }
 

@@ -67,7 +67,9 @@ class FreeList {
 
 struct Seq {
   int32_t len = 0;
-  std::vector<int32_t> pt;  // one entry per logical page
+  std::vector<int32_t> pt;      // one entry per logical page
+  std::vector<uint8_t> prot;    // nonzero: logical page protected from the anchor policy
+  int32_t policy_next = 0;      // pages below this were passed by the anchor policy
 };
 
 // One page an append touches: rows row0 .. row0+nrows-1 of page `phys`
@@ -136,7 +138,8 @@ struct SchedPolicy {
 
 struct Schedule {
   std::vector<WorkItem> items[2];   // per format (FP8, TQ3)
-  std::vector<int32_t> pages;       // logical page ids referenced by the items
+  std::vector<int32_t> cap[2];      // list capacity of each item (room to grow in place)
+  std::vector<int32_t> pages;       // logical page ids referenced by the items (-1: spare room)
   std::vector<int32_t> entries;     // their page-table entries (what the device reads)
   std::vector<int32_t> chunk_base;  // [B + 1] prefix sums of chunks per batch entry
   int32_t heads_per_wave = 1;       // kv-heads per partial-kernel workgroup
@@ -196,6 +199,20 @@ class Meta {
   int reset(int32_t seq, std::string* err);
   void rollback(const Undo& u);
 
+  // Anchor policy (recent and protected pages stay FP8, older ones are
+  // converted).  protect() marks (on) or clears logical pages of seq, which
+  // may lie past its current end (below max_pages_per_seq); the policy never
+  // demotes a marked page.  policy_pages() lists, without changing anything,
+  // the pages the policy converts at seq's current length: the FP8 pages,
+  // not marked, whose tokens all lie before the last `window` tokens and that
+  // the policy has not passed yet, in logical order; *next receives the new
+  // cursor, which set_policy_next() stores once the conversion is done (a
+  // page passed while marked keeps its format from then on).  reset() clears
+  // a sequence's marks and cursor.
+  int protect(int32_t seq, const int32_t* lps, int32_t n, bool on, std::string* err);
+  void policy_pages(int32_t seq, int32_t window, std::vector<int32_t>* lps, int32_t* next) const;
+  void set_policy_next(int32_t seq, int32_t next) { seqs_[size_t(seq)].policy_next = next; }
+
   int build_schedule(const int32_t* seq_ids, int32_t B, int32_t Hq, const SchedPolicy& pol,
                      Schedule* out, std::string* err) const;
 
@@ -235,23 +252,42 @@ inline int32_t page_tokens(int32_t len, int32_t P, int32_t lp) {
 // Every item's last-page token count from the sequences' current lengths.
 void schedule_refresh_tokens(const Meta& m, Schedule* sc);
 
+// Spare list room the schedule builder leaves after the last item of each
+// (batch entry, format) list, the items that decode steps grow: pages opened
+// by appends join the last FP8 item, converted pages the last TQ3 item.
+constexpr int32_t kGrowSlack = 32;
+
+// The page-list ranges [first, last) an in-place schedule edit rewrote (for
+// the upload of the changed words only).
+struct ListEdits {
+  std::vector<std::pair<size_t, size_t>> ranges;
+  void add(size_t a, size_t b) { if (b > a) ranges.emplace_back(a, b); }
+};
+
+// Both edits below change *sc in place and record the list words they
+// rewrote in *edits (if given).  An item grows in its list's spare room, or,
+// without room, its list moves to the end of the list arrays with
+// kGrowSlack spare pages.  They return false when the edit does not apply;
+// *sc is then left partly edited and must be rebuilt.
+//
 // Pages were opened by an append step (plan rows src_row -> ids_of_rows):
 // for each batch entry of a sequence that got a page, its last FP8 item (the
-// one ending at the highest logical page) takes the page; its list is copied,
-// one longer, to the end of the list array.  Does not apply to an entry with
-// no FP8 item, a full chunk, or no room left.
+// one ending at the highest logical page) takes the page.  Does not apply to
+// an entry with no FP8 item, a full chunk, or no room left.
 bool schedule_extend(const Meta& m, const std::vector<int32_t>& ids, const int32_t* ids_of_rows,
-                     const std::vector<AppendPage>& plan, size_t list_cap, Schedule* sc);
+                     const std::vector<AppendPage>& plan, size_t list_cap, Schedule* sc,
+                     ListEdits* edits = nullptr);
 
 // Pages of sequence seq were demoted: in each batch entry of the sequence the
-// FP8 item listing a page drops it in place, and the entry's last TQ3 item
-// (highest last page) takes it, its list copied one longer to the end of the
-// list array.  That TQ3 item's previous last page must be full (only an
-// item's last page may hold fewer tokens).  Does not apply when an FP8 item
-// would become empty, an entry has no TQ3 item, a chunk is full or there is no
-// room.
+// FP8 item listing a page drops it in place (its first page by starting its
+// list one word later), and the entry's last TQ3 item
+// (highest last page) takes it.  That TQ3 item's previous last page must be
+// full (only an item's last page may hold fewer tokens).  Does not apply when
+// an FP8 item would become empty, an entry has no TQ3 item, a chunk is full
+// or there is no room.
 bool schedule_demote(const Meta& m, const std::vector<int32_t>& ids, int32_t seq,
-                     const std::vector<DemotePage>& plan, size_t list_cap, Schedule* sc);
+                     const std::vector<DemotePage>& plan, size_t list_cap, Schedule* sc,
+                     ListEdits* edits = nullptr);
 
 // Checks that sc is a valid decode schedule of batch ids for the current
 // metadata: chunk_base partitions the partial-state slots by batch entry;

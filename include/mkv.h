@@ -192,6 +192,44 @@ mkv_status mkv_append_step(mkv_pool* pool, const int32_t* seq_ids, int32_t B, co
 mkv_status mkv_demote(mkv_pool* pool, int32_t seq, const int32_t* logical_pages, int32_t n,
                       hipStream_t stream);
 
+/* Anchor policy of mkv_decode_step ("Ancoras em FP8, arquivo em TQ3": recent
+ * and protected pages stay FP8, older ones are converted).  window_tokens >= 0
+ * turns it on: after each step's append, every FP8 page of a stepped sequence
+ * whose tokens all lie before the sequence's last window_tokens tokens, that
+ * is not protected and that the policy has not passed before, is converted to
+ * TQ3 (as mkv_demote).  Each sequence keeps a cursor: pages below it were
+ * passed, and a page passed while protected keeps its format for good.
+ * window_tokens < 0 turns the policy off (the default).  MKV_ESTATE for a
+ * control pool with window_tokens >= 0. */
+mkv_status mkv_set_anchor_window(mkv_pool* pool, int32_t window_tokens);
+
+/* Marks (protect != 0) or clears the listed logical pages of `seq` as
+ * protected from the anchor policy (attention sinks, pages the caller pins).
+ * lps: host int32 [n], each in [0, max_pages_per_seq) (pages may lie past the
+ * sequence's current end).  mkv_seq_reset clears a sequence's marks and its
+ * policy cursor.  MKV_EINVAL for a bad id or page. */
+mkv_status mkv_protect_pages(mkv_pool* pool, int32_t seq, const int32_t* lps, int32_t n, int32_t protect);
+
+/* One step of a decode loop: mkv_append_step(seq_ids, B, k, v), then the
+ * anchor policy's conversions for the stepped sequences (mkv_set_anchor_window),
+ * then mkv_decode(seq_ids, B, q, Hq, softmax_scale, out, lse), all on
+ * `stream` in that order, from one call.  k, v: device fp32 [B][Hkv][d]
+ * (row b to seq_ids[b]); q, out, lse as in mkv_decode.  Arguments, the
+ * append's metadata and the TQ3 capacity for the conversions are checked
+ * before anything is enqueued: any error there (MKV_EINVAL, MKV_ERANGE,
+ * MKV_ESTATE, MKV_ENOMEM as in the three calls) leaves the pool unchanged.
+ * Past that point only device-side failures remain: MKV_EHIP from the
+ * append leaves the pool unchanged; MKV_EHIP from the conversions keeps the
+ * append and takes every conversion back (the policy's cursors do not move,
+ * so the next step retries them); MKV_EHIP, or MKV_ERANGE for a batch over
+ * max_chunks chunks, from the decode keeps the append and the conversions.
+ * A step that opens no page and converts nothing (with B <= 32) uploads
+ * nothing; otherwise its metadata goes up in batched upload launches and the
+ * conversions in one launch. */
+mkv_status mkv_decode_step(mkv_pool* pool, const int32_t* seq_ids, int32_t B, const float* k,
+                           const float* v, const void* q, int32_t Hq, float softmax_scale, float* out,
+                           float* lse, hipStream_t stream);
+
 /* Decode attention for one query token per sequence ("Como os resultados
  * parciais sao combinados").  seq_ids: host int32 [B] of non-empty sequences.
  * q: device bf16 [B][Hq][d], 16-byte aligned; query head h reads kv-head

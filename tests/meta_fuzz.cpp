@@ -5,9 +5,13 @@
 //  * every schedule the builder returns passes check_schedule: each live page
 //    of each batch entry is listed once, with its current page-table entry;
 //  * a cached schedule kept current by the edit functions passes as well,
-//    after append steps that open pages and after demotions.
+//    after append steps that open pages and after demotions;
+//  * a copy of the page-list words updated only where the edits say they
+//    wrote (what the device receives) agrees with the schedule on every
+//    listed word.
 // It also takes random calls back with their undo record and compares the
 // whole state with a copy taken before the call.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <random>
@@ -48,6 +52,8 @@ int main() {
   std::vector<int32_t> cached_ids;
   Schedule cached;
   bool cached_ok = false;
+  std::vector<int32_t> dev(list_cap, -7);   // the device's copy of the list words
+  ListEdits edits;
   int edits_applied = 0, rollbacks = 0;
   for (int step = 0; step < 100000; ++step) {
     const int op = int(rng() % 12);
@@ -71,7 +77,8 @@ int main() {
       std::vector<AppendPage> plan;
       st = m.append_step(ids.data(), int32_t(ids.size()), d.max_pages_per_seq, &plan, &err, &undo);
       if (st == 0 && cached_ok && m.layout_version() != lay0) {
-        cached_ok = schedule_extend(m, cached_ids, ids.data(), plan, list_cap, &cached);
+        edits.ranges.clear();
+        cached_ok = schedule_extend(m, cached_ids, ids.data(), plan, list_cap, &cached, &edits);
         edits_applied += cached_ok;
       } else if (st == 0 && cached_ok) {
         schedule_refresh_tokens(m, &cached);
@@ -86,7 +93,8 @@ int main() {
       std::vector<DemotePage> plan;
       st = m.demote(s, lps.data(), int32_t(lps.size()), &plan, &err, &undo);
       if (st == 0 && cached_ok && !plan.empty()) {
-        cached_ok = schedule_demote(m, cached_ids, s, plan, list_cap, &cached);
+        edits.ranges.clear();
+        cached_ok = schedule_demote(m, cached_ids, s, plan, list_cap, &cached, &edits);
         edits_applied += cached_ok;
       }
     } else if (op == 9) {
@@ -107,6 +115,9 @@ int main() {
         cached_ids = ids;
         cached = sc;
         cached_ok = true;
+        if (cached.entries.size() > list_cap) die("schedule exceeds the list capacity");
+        std::copy(cached.entries.begin(), cached.entries.end(), dev.begin());   // full upload
+        edits.ranges.clear();
       }
       continue;
     }
@@ -119,6 +130,21 @@ int main() {
     if (cached_ok &&
         check_schedule(m, cached_ids.data(), int32_t(cached_ids.size()), cached, &err))
       die("edited schedule", err);
+    if (cached_ok) {
+      if (cached.entries.size() > list_cap || cached.pages.size() != cached.entries.size())
+        die("edited schedule exceeds the list capacity");
+      for (const auto& r : edits.ranges) {
+        if (r.second > cached.entries.size()) die("edit range past the list");
+        std::copy(cached.entries.begin() + std::ptrdiff_t(r.first), cached.entries.begin() + std::ptrdiff_t(r.second),
+                  dev.begin() + std::ptrdiff_t(r.first));
+      }
+      edits.ranges.clear();
+      for (int f = 0; f < 2; ++f)
+        for (const WorkItem& it : cached.items[f])
+          for (int32_t i = 0; i < it.npages; ++i)
+            if (dev[size_t(it.list_off + i)] != cached.entries[size_t(it.list_off + i)])
+              die("an edit changed a listed word outside its recorded ranges");
+    }
     // ownership invariant
     std::vector<int> own8(size_t(d.fp8_pages), 0), own3(size_t(d.tq3_pages), 0);
     for (int q = 0; q < d.max_seqs; ++q)

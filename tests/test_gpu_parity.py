@@ -7,6 +7,7 @@
 Pool memory is poisoned with 0x7F before use, so unwritten slots hold NaN
 patterns and any unmasked read shows up in the outputs.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -454,6 +455,103 @@ def test_decode_steps_with_appends_and_demotions():
             bad = np.nonzero((recs[lp, :ref.size] != ref) & mask)[0]
             assert bad.size == 0, f"seq {b} page {lp}: {bad.size} bytes differ"
     pool.close()
+
+
+@pytest.mark.parametrize("case", ["window40", "window0", "batch36"])
+def test_decode_step_appends_converts_and_decodes_in_one_call(case):
+    """mkv_decode_step over 40 steps (one token per sequence, the anchor
+    policy's conversions with the older anchors protected, the decode): each
+    step's output against the oracle replaying the same appends and the
+    reference policy's conversions, then every record and format.  window40
+    takes the one-launch path; window0 converts, in the step that fills it,
+    the page the step appended to (the path with separate launches); batch36
+    has more pages than one launch's arguments hold (batched uploads).  A call
+    with a bad Hq, and one whose conversions do not fit the TQ3 slab, change
+    nothing."""
+    window = {"window40": 40, "window0": 0, "batch36": 16}[case]
+    if case == "batch36":
+        lens = tuple(int(x) for x in np.random.default_rng(55).integers(20, 120, 36))
+        wl = W.small(seed=56, B=36, Hq=4, Hkv=2, d=64, P=16, lengths=lens)
+    else:
+        wl = W.small(seed=51, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(100, 37, 250),
+                     outliers={"k": (3, 8.0)})
+    pool = H.DevicePool(H.pool_desc(wl, max_pages_per_seq=32))
+    H.load_cache(pool, wl)
+    models = [OS.seq_model(wl, b) for b in range(wl.B)]
+    protected = [[a for a in wl.anchors[b] if (a + 1) * wl.P <= int(wl.lengths[b]) - window]
+                 for b in range(wl.B)]
+    policy = H.AnchorPolicy(wl.P, window, protected=protected,
+                            demoted=[wl.demote_pages(b) for b in range(wl.B)])
+    mkv.set_anchor_window(pool.handle, window)
+    for b in range(wl.B):
+        mkv.protect_pages(pool.handle, b, protected[b])
+    rng = np.random.default_rng(53)
+    ids = list(range(wl.B))
+    lengths = [int(x) for x in wl.lengths]
+    q = H.q_tensor(wl)
+    out = torch.full((wl.B, wl.Hq, wl.d), float("nan"), device="cuda")
+    lse = torch.full((wl.B, wl.Hq), float("nan"), device="cuda")
+    n_demoted = 0
+    for step in range(40):
+        k = rng.standard_normal((wl.B, wl.Hkv, wl.d)).astype(np.float32)
+        v = (rng.standard_normal((wl.B, wl.Hkv, wl.d)) * (1.0 + step % 3)).astype(np.float32)
+        mkv.decode_step(pool.handle, ids, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), q,
+                        float(wl.tau), out, lse)
+        torch.cuda.synchronize()
+        for b in ids:
+            models[b].append(k[b:b + 1], v[b:b + 1])
+            lengths[b] += 1
+            for lp in policy.step(b, lengths[b]):
+                models[b].demote(lp)
+                n_demoted += 1
+        if step < 6 or step % 5 == 4:
+            _check(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+                   *OS.decode_all(wl, models), f"decode_step {step}")
+    assert n_demoted >= 3
+    for b in ids:
+        pt = mkv.page_table(pool.handle, b)
+        recs = H.gather_records(pool, b, len(models[b].pages))
+        for lp, page in enumerate(models[b].pages):
+            assert (pt[lp] < 0) == (page.fmt == 1), (b, lp)
+            ref, mask = models[b].record(lp), models[b].valid_mask(lp)
+            bad = np.nonzero((recs[lp, :ref.size] != ref) & mask)[0]
+            assert bad.size == 0, f"seq {b} page {lp}: {bad.size} bytes differ"
+    if case != "window40":
+        pool.close()
+        return
+    # a bad Hq is refused before the append
+    kz = torch.zeros(wl.B, wl.Hkv, wl.d, device="cuda")
+    ids_arr = (ctypes.c_int32 * wl.B)(*ids)
+    st = mkv._load().mkv_decode_step(pool.handle, ids_arr, wl.B, ctypes.c_void_p(kz.data_ptr()),
+                                     ctypes.c_void_p(kz.data_ptr()), ctypes.c_void_p(q.data_ptr()), 3,
+                                     ctypes.c_float(1.0), ctypes.c_void_p(out.data_ptr()),
+                                     ctypes.c_void_p(lse.data_ptr()), None)
+    assert st == mkv.EINVAL
+    assert [mkv.seq_info(pool.handle, b)[0] for b in ids] == lengths
+    pool.close()
+    # conversions that do not fit the TQ3 slab: ENOMEM, and the append is taken back
+    wl2 = W.small(seed=54, B=1, Hq=4, Hkv=2, d=64, P=16, lengths=(80,))
+    n_tq3 = wl2.n_pages(0) - len(wl2.anchors[0])
+    pool2 = H.DevicePool(H.pool_desc(wl2, tq3_pages=n_tq3, fp8_pages=wl2.n_pages(0) + 4,
+                                     max_pages_per_seq=wl2.n_pages(0) + 4))
+    H.load_cache(pool2, wl2)
+    mkv.set_anchor_window(pool2.handle, 0)
+    L0 = mkv.seq_info(pool2.handle, 0)[0]
+    fp8_before = mkv.pool_stats(pool2.handle)["fp8_pages_live"]
+    k1 = torch.zeros(1, wl2.Hkv, wl2.d, device="cuda")
+    q2 = H.q_tensor(wl2)
+    o2 = torch.empty(1, wl2.Hq, wl2.d, device="cuda")
+    l2 = torch.empty(1, wl2.Hq, device="cuda")
+    with pytest.raises(mkv.MkvError) as e:
+        mkv.decode_step(pool2.handle, [0], k1, k1, q2, float(wl2.tau), o2, l2)
+    assert e.value.status == mkv.ENOMEM
+    assert mkv.seq_info(pool2.handle, 0)[0] == L0
+    assert mkv.pool_stats(pool2.handle)["fp8_pages_live"] == fp8_before
+    mkv.set_anchor_window(pool2.handle, -1)           # off: the same step goes through
+    mkv.decode_step(pool2.handle, [0], k1, k1, q2, float(wl2.tau), o2, l2)
+    torch.cuda.synchronize()
+    assert mkv.seq_info(pool2.handle, 0)[0] == L0 + 1
+    pool2.close()
 
 
 @pytest.mark.parametrize("B", [3, 40])

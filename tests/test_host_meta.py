@@ -40,6 +40,11 @@ def lib():
     L.mkvh_append_rollback.argtypes = [P, I32, I32]
     L.mkvh_demote_rollback.argtypes = [P, I32, P, I32]
     L.mkvh_append_step_rollback.argtypes = [P, P, I32, I32]
+    L.mkvh_protect.argtypes = [P, I32, P, I32, I32]
+    L.mkvh_policy_pages.argtypes = [P, I32, I32, P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+    L.mkvh_policy_pages.restype = None
+    L.mkvh_set_policy_next.argtypes = [P, I32, I32]
+    L.mkvh_set_policy_next.restype = None
     L.mkvh_last_error.restype = ctypes.c_char_p
     return L
 
@@ -77,6 +82,17 @@ class Host:
         st = self.L.mkvh_demote(self.h, seq, arr.ctypes.data, arr.size, buf.ctypes.data, 4096,
                                 ctypes.byref(cnt))
         return st, buf[:cnt.value]
+
+    def protect(self, seq, lps, on=True):
+        arr = np.asarray(lps, np.int32)
+        return self.L.mkvh_protect(self.h, seq, arr.ctypes.data, arr.size, 1 if on else 0)
+
+    def policy_pages(self, seq, window):
+        buf = np.zeros(4096, np.int32)
+        n, nxt = ctypes.c_int32(), ctypes.c_int32()
+        self.L.mkvh_policy_pages(self.h, seq, window, buf.ctypes.data, buf.size, ctypes.byref(n),
+                                 ctypes.byref(nxt))
+        return buf[:n.value].tolist(), nxt.value
 
     def pt(self, seq):
         buf = np.zeros(1 << 16, np.int32)
@@ -363,7 +379,7 @@ def test_bf16_control_pool_metadata(lib):
     assert h.L.mkvh_version(h.h) == v0 and not any(is_tq3(e) for e in h.pt(0))
     st, sch = h.schedule([0], Hq=8)
     assert st == 0 and sch["n3"] == 0 and sch["n8"] >= 1
-    assert sorted(sch["pages"].tolist()) == list(range(7))
+    assert sorted(p for p in sch["pages"].tolist() if p >= 0) == list(range(7))   # -1: spare room
     h.close()
 
 
@@ -478,3 +494,59 @@ def test_rolled_back_calls_leave_no_trace(lib):
     assert state(a) == state(b)
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("window", [0, 5, 16, 40])
+def test_anchor_policy_matches_the_reference_policy(lib, window):
+    """The library's anchor policy (what mkv_decode_step applies after each
+    append: policy_pages, the conversion, then the cursor) decides exactly as
+    the harness's reference policy over random one-token steps, with pages
+    marked before and after they exist, marks cleared, and a sequence reset."""
+    from decode_attention_mixed_amd.harness import AnchorPolicy
+    rng = np.random.default_rng(100 + window)
+    P, S = 16, 4
+    h = _host(lib, max_seqs=S, max_pages_per_seq=64, max_batch=S, fp8_pages=256, tq3_pages=256)
+    ref = AnchorPolicy(P, window, protected=[[] for _ in range(S)], demoted=[[] for _ in range(S)])
+    lens = [0] * S
+    for s_ in range(S):
+        n = int(rng.integers(1, 90))
+        assert h.append(s_, n)[0] == OK
+        lens[s_] = n
+    assert h.protect(0, [0, 3]) == OK and h.protect(2, [7, 40]) == OK
+    ref.protected[0].update([0, 3])
+    ref.protected[2].update([7, 40])
+    converted = 0
+    for step in range(300):
+        if step == 120:                                  # unmark one, mark a passed page
+            assert h.protect(2, [7], on=False) == OK
+            ref.protected[2].discard(7)
+            assert h.protect(1, [0]) == OK
+            ref.protected[1].add(0)
+        if step == 200:                                  # a sequence starts over
+            assert lib.mkvh_reset(h.h, 3) == OK
+            ref.protected[3].clear()
+            ref.demoted[3].clear()
+            ref.seen[3] = 0
+            lens[3] = 0
+        ids = sorted(rng.choice(S, size=int(rng.integers(1, S + 1)), replace=False).tolist())
+        st, _ = h.append_step(ids)
+        assert st == OK, (step, lib.mkvh_last_error())
+        for s_ in ids:
+            lens[s_] += 1
+            got, nxt = h.policy_pages(s_, window)
+            want = ref.step(s_, lens[s_])
+            assert got == want, (step, s_, got, want)
+            if got:
+                assert h.demote(s_, got)[0] == OK
+                converted += len(got)
+            lib.mkvh_set_policy_next(h.h, s_, nxt)
+            assert nxt == max(0, (lens[s_] - window) // P)        # lengths only grow between resets
+    assert converted > 0
+    for s_ in range(S):
+        pt = h.pt(s_)
+        full = max(0, (lens[s_] - window) // P)
+        for lp in range(full):
+            assert is_tq3(pt[lp]) == (lp in ref.demoted[s_]), (s_, lp)
+    # marks outside the page-table range, and on a bad sequence, are refused
+    assert h.protect(0, [64]) == EINVAL and h.protect(0, [-1]) == EINVAL and h.protect(9, [0]) == EINVAL
+    h.close()
