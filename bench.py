@@ -367,6 +367,8 @@ def main():
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
 
+    build_rates = {}
+
     def build(kind):
         """R pools of one kind: "mixed" (anchors FP8, the rest demoted to TQ3),
         "bf16" (control pool) or "fp8" (mixed pool, nothing demoted)."""
@@ -387,13 +389,58 @@ def main():
                 desc = H.pool_desc(wl, kind=kind, fp8_pages=all_pages + 16,
                                    placement_seed=wl.placement_seed + r)
             pools.append(H.DevicePool(desc))
+        # replica 0 of the mixed cache is built with events around each
+        # sequence's append and conversion (the cache-write kernels' rates)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        t_app = t_dem = 0.0
+        n_dem = 0
+        if kind == "mixed":
+            mkv.profile_enable(pools[0].handle, True)
         for b in range(wl.B):
             kv = kvs[b] if kvs is not None else wl.kv(b)
             for r in range(R):
-                H.load_sequence(pools[r], wl, b, kv=kv, demote=(kind == "mixed"))
+                if kind == "mixed" and r == 0:
+                    kd = torch.from_numpy(kv[0]).cuda().contiguous()
+                    vd = torch.from_numpy(kv[1]).cuda().contiguous()
+                    dem = wl.demote_pages(b)
+                    torch.cuda.synchronize()
+                    ev[0].record()
+                    mkv.append(pools[0].handle, b, kd, vd)
+                    ev[1].record()
+                    if dem.size:
+                        mkv.demote(pools[0].handle, b, dem)
+                    ev[2].record()
+                    torch.cuda.synchronize()
+                    t_app += ev[0].elapsed_time(ev[1])
+                    t_dem += ev[1].elapsed_time(ev[2])
+                    n_dem += int(dem.size)
+                    del kd, vd
+                else:
+                    H.load_sequence(pools[r], wl, b, kv=kv, demote=(kind == "mixed"))
         torch.cuda.synchronize()
         st = mkv.pool_stats(pools[0].handle)
         log(f"{kind} cache built in {time.perf_counter() - t0:.1f} s: {st}")
+        if kind == "mixed":
+            kprof = mkv.profile_read(pools[0].handle)
+            mkv.profile_enable(pools[0].handle, False)
+            toks = int(sum(int(x) for x in wl.lengths))
+            app_bytes = toks * wl.Hkv * wl.d * (2 * 4 + 2)        # fp32 K, V read; FP8 codes written
+            dem_bytes = n_dem * (2 * wl.Hkv * wl.P * wl.d + 2 * wl.Hkv * wl.P * (wl.d // 32) * 14)
+            ka, kd = kprof["ms_append"], kprof["ms_demote"]
+            build_rates.update({
+                "what": "replica 0 of the cache: kernel time from the library's events around the "
+                        "append and conversion launches; call time from events around each mkv_append "
+                        "and mkv_demote call (host metadata and uploads included)",
+                "append_kernel_us": round(ka * 1e3, 1),
+                "append_kernel_gbs": round(app_bytes / (ka * 1e-3) / 1e9, 1) if ka else None,
+                "append_kernel_frac": round(app_bytes / (ka * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if ka else None,
+                "append_call_us": round(t_app * 1e3, 1),
+                "demote_pages": n_dem,
+                "demote_kernel_us": round(kd * 1e3, 1),
+                "demote_kernel_gbs": round(dem_bytes / (kd * 1e-3) / 1e9, 1) if kd else None,
+                "demote_kernel_frac": round(dem_bytes / (kd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if kd else None,
+                "demote_call_us": round(t_dem * 1e3, 1),
+                "bytes": {"append": app_bytes, "demote": dem_bytes}})
         return pools, st
 
     def timed_steps(pools):
@@ -608,6 +655,7 @@ def main():
             "pct_of_copy_ceiling": round(100.0 * value / copy_ceiling, 2) if copy_ceiling else None,
             "read_ceiling_gbs": round(read_ceil, 1),
             "pct_of_read_ceiling": round(100.0 * value / read_ceil, 2) if read_ceil else None,
+            "cache_build": build_rates,
         },
         "roofline": {
             "kernel": dom,

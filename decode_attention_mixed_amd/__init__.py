@@ -76,6 +76,10 @@ class Profile(ctypes.Structure):
         ("ms_merge", ctypes.c_double),
         ("n_partial", ctypes.c_int64),
         ("n_merge", ctypes.c_int64),
+        ("ms_append", ctypes.c_double),
+        ("ms_demote", ctypes.c_double),
+        ("n_append", ctypes.c_int64),
+        ("n_demote", ctypes.c_int64),
     ]
 
     def as_dict(self):

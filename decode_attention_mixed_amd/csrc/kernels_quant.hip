@@ -48,31 +48,60 @@ __device__ __forceinline__ void append_fp8_block(const PoolView& pv, const Appen
 
   if (ap.pt_slot >= 0 && h == 0 && kv == 0 && threadIdx.x == 0)
     const_cast<int32_t*>(pv.pt)[ap.pt_slot] = ap.pt_entry;   // a page the step opened
-  const int n_new = ap.nrows * d;
-  float local = 0.0f;
-  for (int i = threadIdx.x; i < n_new; i += kThreads) {
-    const int r = i / d, j = i % d;
-    local = fmaxf(local, fabsf(src[(int64_t(ap.src_row + r) * pv.Hkv + h) * d + j]));
-  }
-  const float new_amax = block_max(local, red);
+  // the page's scale and amax so far, loaded while the new rows arrive
   const float old_amax = ap.row0 > 0 ? *amax_p : 0.0f;
   const float old_sigma = ap.row0 > 0 ? *scale_p : 1.0f;
+  // new rows as 16-byte vectors (d is a multiple of 32, rows 16-byte aligned),
+  // kept in registers from the amax pass to the encoding
+  constexpr int kVec = 4;
+  const int n4 = ap.nrows * d / 4;
+  auto row_vec = [&](int i) {
+    const int e = 4 * i, r = e / d, j = e % d;
+    return *reinterpret_cast<const float4*>(src + (int64_t(ap.src_row + r) * pv.Hkv + h) * d + j);
+  };
+  float4 val[kVec];
+  float local = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    const int i = int(threadIdx.x) + u * kThreads;
+    if (i < n4) {
+      val[u] = row_vec(i);
+      local = fmaxf(local, fmaxf(fmaxf(fabsf(val[u].x), fabsf(val[u].y)), fmaxf(fabsf(val[u].z), fabsf(val[u].w))));
+    }
+  }
+  for (int i = int(threadIdx.x) + kVec * kThreads; i < n4; i += kThreads) {   // pages past kVec vectors a lane
+    const float4 x = row_vec(i);
+    local = fmaxf(local, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+  }
+  const float new_amax = block_max(local, red);
   const bool grown = new_amax > old_amax;
   const float amax = grown ? new_amax : old_amax;
   const float sigma = amax == 0.0f ? 1.0f : amax / 448.0f;
-  __syncthreads();  // everyone has read the old scale and amax
 
+  auto enc4 = [&](const float4 x) {
+    return uint32_t(f32_to_e4m3(x.x / sigma)) | (uint32_t(f32_to_e4m3(x.y / sigma)) << 8) |
+           (uint32_t(f32_to_e4m3(x.z / sigma)) << 16) | (uint32_t(f32_to_e4m3(x.w / sigma)) << 24);
+  };
   if (grown && ap.row0 > 0) {
-    for (int i = threadIdx.x; i < ap.row0 * d; i += kThreads) {
-      const float x = e4m3_to_f32(codes[i]) * old_sigma;
-      codes[i] = uint8_t(f32_to_e4m3(x / sigma));
+    // earlier rows re-encoded from their dequantised values, four codes a word
+    uint32_t* old = reinterpret_cast<uint32_t*>(codes);
+    for (int i = threadIdx.x; i < ap.row0 * d / 4; i += kThreads) {
+      const uint32_t w = old[i];
+      float4 x;
+      x.x = e4m3_to_f32(uint8_t(w)) * old_sigma;
+      x.y = e4m3_to_f32(uint8_t(w >> 8)) * old_sigma;
+      x.z = e4m3_to_f32(uint8_t(w >> 16)) * old_sigma;
+      x.w = e4m3_to_f32(uint8_t(w >> 24)) * old_sigma;
+      old[i] = enc4(x);
     }
   }
-  for (int i = threadIdx.x; i < n_new; i += kThreads) {
-    const int r = i / d, j = i % d;
-    const float x = src[(int64_t(ap.src_row + r) * pv.Hkv + h) * d + j];
-    codes[int64_t(ap.row0) * d + i] = uint8_t(f32_to_e4m3(x / sigma));
+  uint32_t* out = reinterpret_cast<uint32_t*>(codes + int64_t(ap.row0) * d);
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    const int i = int(threadIdx.x) + u * kThreads;
+    if (i < n4) out[i] = enc4(val[u]);
   }
+  for (int i = int(threadIdx.x) + kVec * kThreads; i < n4; i += kThreads) out[i] = enc4(row_vec(i));
   if (threadIdx.x == 0) {
     *scale_p = sigma;
     *amax_p = amax;
@@ -86,59 +115,88 @@ append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float*
 }
 
 // ---------------------------------------------------------------------------
-// Demote: one block per (page, kv-head); each thread encodes 32-element groups.
+// Demote: one thread per 32-element group of a converted page.
 // Minima-KV summary, "Ancoras em FP8, arquivo em TQ3": older non-anchor pages
 // are converted to packed TQ3.  x = fp32(e4m3(c) * sigma); s = fp16(fp32(a/3.5))
 // clamped to 65504; c = #{b in -3..3 : x >= b*s} (4 when s == 0); the 32 codes
 // form a 96-bit little-endian stream, code j at bit 3j.
+// Threads of a page walk its groups with the group fastest, then the token,
+// then (kv-head, K or V), so consecutive lanes read consecutive 32-byte runs
+// of codes and write consecutive 12-byte runs and fp16 scales.  The count of
+// thresholds at or below x is floor(x / s) + 4 clamped to 0..7 in exact
+// arithmetic; it is formed from x * (1 / s) (far less than one step off) and
+// settled by comparing x with the exact products b * s on each side, so the
+// codes equal those of the seven comparisons.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void demote_block(const PoolView& pv, const DemotePage& dp, int h) {
-  const int d = pv.d, ng = d / 32, row_bytes = 3 * d / 8;
+__device__ __forceinline__ int demote_groups(const PoolView& pv) { return pv.Hkv * 2 * pv.P * (pv.d / 32); }
+
+// NG groups a row and PP tokens a page when known at compile time (0: the
+// pool's values), so that the lane's (kv-head, K or V, token, group) comes
+// from shifts and constant divisions.
+template <int NG = 0, int PP = 0>
+__device__ __forceinline__ void demote_group(const PoolView& pv, const DemotePage& dp, int rem) {
+  const int ng = NG ? NG : pv.d / 32, P = PP ? PP : pv.P, d = 32 * ng, row_bytes = 12 * ng;
+  const int g = rem % ng, t = (rem / ng) % P, hk = rem / (ng * P);
+  const int h = hk >> 1, kv = hk & 1;
+  if (t >= dp.ntok) return;
   const uint8_t* src = pv.fp8 + int64_t(dp.src_phys) * pv.fp8_stride;
   uint8_t* dst = pv.tq3 + int64_t(dp.dst_phys) * pv.tq3_stride;
-  const int tasks = 2 * dp.ntok * ng;
-  for (int task = threadIdx.x; task < tasks; task += kThreads) {
-    const int kv = task / (dp.ntok * ng);
-    const int rem = task % (dp.ntok * ng);
-    const int t = rem / ng, g = rem % ng;
-    const float sigma = *reinterpret_cast<const float*>(src + fp8_scale_off(pv, h, kv));
-    const uint8_t* c8 = src + fp8_codes_off(pv, h, kv) + int64_t(t) * d + 32 * g;
-    float x[32];
-    float a = 0.0f;
+  const uint4* c8 = reinterpret_cast<const uint4*>(src + fp8_codes_off(pv, h, kv) + int64_t(t) * d + 32 * g);
+  const uint4 w0 = c8[0], w1 = c8[1];
+  const float sigma = *reinterpret_cast<const float*>(src + fp8_scale_off(pv, h, kv));
+  const uint32_t cw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float x[32];
+  float a = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      x[j] = e4m3_to_f32(c8[j]) * sigma;
-      a = fmaxf(a, fabsf(x[j]));
-    }
-    const float q = fminf(a / 3.5f, 65504.0f);
-    const _Float16 s16 = _Float16(q);          // round to nearest even
-    const float s = float(s16);
-    uint32_t w[3] = {0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      uint32_t c = 4u;
-      if (s != 0.0f) {
-        c = 0u;
-#pragma unroll
-        for (int b = -3; b <= 3; ++b) c += (x[j] >= float(b) * s) ? 1u : 0u;
-      }
-      const int bit = 3 * j;
-      w[bit >> 5] |= c << (bit & 31);
-      if ((bit & 31) > 29) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-    }
-    uint32_t* out = reinterpret_cast<uint32_t*>(dst + tq3_codes_off(pv, h, kv) +
-                                                int64_t(t) * row_bytes + 12 * g);
-    out[0] = w[0];
-    out[1] = w[1];
-    out[2] = w[2];
-    reinterpret_cast<uint16_t*>(dst + tq3_scale_off(pv, h, kv))[t * ng + g] =
-        __builtin_bit_cast(uint16_t, s16);
+  for (int i = 0; i < 8; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(cw[i], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(cw[i], true);
+    x[4 * i + 0] = lo[0] * sigma;
+    x[4 * i + 1] = lo[1] * sigma;
+    x[4 * i + 2] = hi[0] * sigma;
+    x[4 * i + 3] = hi[1] * sigma;
   }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(x[j]));
+  const float q = fminf(a / 3.5f, 65504.0f);
+  const _Float16 s16 = _Float16(q);            // round to nearest even
+  const float s = float(s16);
+  const float rs = __builtin_amdgcn_rcpf(s);    // s == 0 is settled below
+  uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    // floor(x / s) clamped to -4..3, without branches: the estimate f from
+    // x * (1 / s) is at most one off, and the exact products (f + 1) * s
+    // (fma(f, s, s) forms it exactly) and f * s tell which way, both judged
+    // against the same f, before the final clamp
+    const float f = __builtin_amdgcn_fmed3f(floorf(x[j] * rs), -4.0f, 3.0f);
+    const int up = x[j] >= __builtin_fmaf(f, s, s) ? 1 : 0;
+    const int dn = x[j] < f * s ? 1 : 0;
+    const int fi = min(max(int(f) + up - dn, -4), 3);
+    // code fi + 4: the low three bits of fi, with bit 2 flipped for all codes at once below
+    const uint32_t c = uint32_t(fi) & 7u;
+    const int bit = 3 * j;
+    w[bit >> 5] |= c << (bit & 31);
+    if ((bit & 31) > 29) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+  }
+  // +4 in every 3-bit field (0b100 at bit 3j + 2), or all codes 4 when s == 0
+  constexpr uint32_t kFour[3] = {0x24924924u, 0x49249249u, 0x92492492u};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) w[i] = s != 0.0f ? (w[i] ^ kFour[i]) : kFour[i];
+  uint32_t* out = reinterpret_cast<uint32_t*>(dst + tq3_codes_off(pv, h, kv) + int64_t(t) * row_bytes + 12 * g);
+  out[0] = w[0];
+  out[1] = w[1];
+  out[2] = w[2];
+  reinterpret_cast<uint16_t*>(dst + tq3_scale_off(pv, h, kv))[t * ng + g] = __builtin_bit_cast(uint16_t, s16);
 }
 
+// Grid (page, block of the page's groups).
+template <int NG, int PP>
 __global__ void __launch_bounds__(kThreads)
 demote_tq3_kernel(PoolView pv, const DemotePage* __restrict__ plan) {
-  demote_block(pv, plan[blockIdx.x / pv.Hkv], blockIdx.x % pv.Hkv);
+  const int rem = int(blockIdx.y) * kThreads + int(threadIdx.x);
+  if (rem >= pv.Hkv * 2 * (PP ? PP : pv.P) * (NG ? NG : pv.d / 32)) return;
+  demote_group<NG, PP>(pv, plan[blockIdx.x], rem);
 }
 
 // ---------------------------------------------------------------------------
@@ -209,9 +267,10 @@ append_inline_kernel(PoolView pv, InlinePlan plan, const float* __restrict__ k,
 }
 
 // A decode step's cache writes (StepPlan): blocks [0, 2 Hkv n_append) append
-// as append_inline_kernel, the next Hkv n_conv blocks convert one (page,
-// kv-head) each as demote_tq3_kernel, and the first block of each converted
-// page writes its page-table entry; block 0 applies the schedule patches.
+// as append_inline_kernel, the blocks after them convert the n_conv pages as
+// demote_tq3_kernel (one thread per group), the first thread of each
+// converted page writing its page-table entry; block 0 applies the schedule
+// patches.
 template <bool kBf16>
 __global__ void __launch_bounds__(kThreads)
 step_kernel(PoolView pv, StepPlan plan, const float* __restrict__ k, const float* __restrict__ v) {
@@ -227,11 +286,13 @@ step_kernel(PoolView pv, StepPlan plan, const float* __restrict__ k, const float
     return;
   }
   if constexpr (!kBf16) {
-    const int c = (int(blockIdx.x) - n_app) / pv.Hkv, h = (int(blockIdx.x) - n_app) % pv.Hkv;
-    if (c >= plan.n_conv) return;              // the lone block of a patch-only launch
+    const int per = demote_groups(pv);
+    const int task = (int(blockIdx.x) - n_app) * kThreads + int(threadIdx.x);
+    const int c = task / per, rem = task % per;
+    if (c >= plan.n_conv) return;              // past the last page (or a patch-only launch)
     const DemotePage dp = plan.conv[c];
-    if (h == 0 && threadIdx.x == 0) const_cast<int32_t*>(pv.pt)[dp.pad0] = dp.pad1;
-    demote_block(pv, dp, h);
+    if (rem == 0) const_cast<int32_t*>(pv.pt)[dp.pad0] = dp.pad1;
+    demote_group(pv, dp, rem);
   }
 }
 
@@ -344,7 +405,8 @@ hipError_t launch_step(const PoolView& pv, const StepPlan& plan, const float* k,
   if (plan.n_append < 0 || plan.n_append > kInlinePages || plan.n_conv < 0 || plan.n_conv > kStepConv ||
       plan.n_patch < 0 || plan.n_patch > kStepPatches || (pv.kind == kKindBf16 && plan.n_conv > 0))
     return hipErrorInvalidValue;
-  const int blocks = plan.n_append * pv.Hkv * 2 + plan.n_conv * pv.Hkv;
+  const int per = pv.Hkv * 2 * pv.P * (pv.d / 32);
+  const int blocks = plan.n_append * pv.Hkv * 2 + (plan.n_conv * per + kThreads - 1) / kThreads;
   if (blocks == 0 && plan.n_patch == 0) return hipSuccess;
   const dim3 grid(unsigned(blocks > 0 ? blocks : 1));
   if (pv.kind == kKindBf16)
@@ -357,8 +419,21 @@ hipError_t launch_step(const PoolView& pv, const StepPlan& plan, const float* k,
 hipError_t launch_demote(const PoolView& pv, const DemotePage* plan, int32_t n_pages,
                          hipStream_t s) {
   if (n_pages <= 0) return hipSuccess;
-  hipLaunchKernelGGL(demote_tq3_kernel, dim3(unsigned(n_pages * pv.Hkv)), dim3(kThreads), 0, s,
-                     pv, plan);
+  const int per = pv.Hkv * 2 * pv.P * (pv.d / 32);
+  const dim3 grid(unsigned(n_pages), unsigned((per + kThreads - 1) / kThreads));
+  const int ng = pv.d / 32;
+  if (ng == 4 && pv.P == 16)
+    hipLaunchKernelGGL((demote_tq3_kernel<4, 16>), grid, dim3(kThreads), 0, s, pv, plan);
+  else if (ng == 8 && pv.P == 64)
+    hipLaunchKernelGGL((demote_tq3_kernel<8, 64>), grid, dim3(kThreads), 0, s, pv, plan);
+  else if (ng == 8 && pv.P == 16)
+    hipLaunchKernelGGL((demote_tq3_kernel<8, 16>), grid, dim3(kThreads), 0, s, pv, plan);
+  else if (ng == 4 && pv.P == 64)
+    hipLaunchKernelGGL((demote_tq3_kernel<4, 64>), grid, dim3(kThreads), 0, s, pv, plan);
+  else if (ng == 2 && pv.P == 16)
+    hipLaunchKernelGGL((demote_tq3_kernel<2, 16>), grid, dim3(kThreads), 0, s, pv, plan);
+  else
+    hipLaunchKernelGGL((demote_tq3_kernel<0, 0>), grid, dim3(kThreads), 0, s, pv, plan);
   return hipGetLastError();
 }
 

@@ -145,8 +145,8 @@ struct mkv_pool {
   bool prof = false;
   std::vector<ProfEvent> prof_events;
   std::vector<ProfEvent> prof_free;
-  double prof_ms[2] = {0, 0};    // partial, merge
-  int64_t prof_n[2] = {0, 0};
+  double prof_ms[4] = {0, 0, 0, 0};    // partial, merge, append, demote
+  int64_t prof_n[4] = {0, 0, 0, 0};
 
   mkv::PoolView view() const {
     const mkv::Geom& g = meta.geom();
@@ -168,6 +168,11 @@ struct mkv_pool {
 };
 
 namespace {
+
+// K/V rows are read as 16-byte vectors.
+bool rows_aligned(const float* k, const float* v) {
+  return reinterpret_cast<uintptr_t>(k) % 16 == 0 && reinterpret_cast<uintptr_t>(v) % 16 == 0;
+}
 
 struct Upload {
   size_t dst_off;  // offset in the pool's device block
@@ -241,24 +246,33 @@ mkv_status upload_pt_row_and_plan(mkv_pool* p, int32_t seq, const void* plan, si
   return flush_uploads(p, ups, s);
 }
 
-ProfEvent* prof_begin(mkv_pool* p, int kind, hipStream_t s) {
-  if (!p->prof) return nullptr;
-  ProfEvent e{kind, nullptr, nullptr};
-  if (!p->prof_free.empty()) {
-    e = p->prof_free.back();
-    p->prof_free.pop_back();
-    e.kind = kind;
-  } else if (hipEventCreate(&e.a) != hipSuccess || hipEventCreate(&e.b) != hipSuccess) {
-    return nullptr;
+// Brackets the launches of its scope with a pair of profiling events of one
+// kind (0 partial, 1 merge, 2 append, 3 demote) while profiling is on.
+struct ProfScope {
+  mkv_pool* p;
+  hipStream_t s;
+  size_t idx = SIZE_MAX;
+  ProfScope(mkv_pool* pool, int kind, hipStream_t stream, bool on = true) : p(pool), s(stream) {
+    if (!on || !p->prof) return;
+    ProfEvent e{kind, nullptr, nullptr};
+    if (!p->prof_free.empty()) {
+      e = p->prof_free.back();
+      p->prof_free.pop_back();
+      e.kind = kind;
+    } else if (hipEventCreate(&e.a) != hipSuccess || hipEventCreate(&e.b) != hipSuccess) {
+      return;
+    }
+    if (hipEventRecord(e.a, s) != hipSuccess) {
+      p->prof_free.push_back(e);
+      return;
+    }
+    idx = p->prof_events.size();
+    p->prof_events.push_back(e);
   }
-  if (hipEventRecord(e.a, s) != hipSuccess) return nullptr;
-  p->prof_events.push_back(e);
-  return &p->prof_events.back();
-}
-
-void prof_end(mkv_pool*, ProfEvent* e, hipStream_t s) {
-  if (e) (void)hipEventRecord(e->b, s);
-}
+  ~ProfScope() {
+    if (idx != SIZE_MAX) (void)hipEventRecord(p->prof_events[idx].b, s);
+  }
+};
 
 mkv_status prof_collect(mkv_pool* p) {
   for (ProfEvent& e : p->prof_events) {
@@ -420,6 +434,7 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
                       hipStream_t s) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
   if (n > 0 && (!k || !v)) return set_err(MKV_EINVAL, "null K or V");
+  if (n > 0 && !rows_aligned(k, v)) return set_err(MKV_EINVAL, "K and V must be 16-byte aligned");
   DeviceGuard guard(p->device);
   std::vector<mkv::AppendPage> plan;
   std::string err;
@@ -430,6 +445,7 @@ mkv_status mkv_append(mkv_pool* p, int32_t seq, int32_t n, const float* k, const
   mkv_status r = upload_pt_row_and_plan(p, seq, plan.data(), plan.size() * sizeof(plan[0]), s);
   if (r == MKV_OK) {
     const auto* dplan = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
+    ProfScope ps(p, 2, s);
     const hipError_t e = p->meta.geom().kind == mkv::kKindBf16
                              ? mkv::launch_append_bf16(p->view(), dplan, int32_t(plan.size()), k, v, s)
                              : mkv::launch_append(p->view(), dplan, int32_t(plan.size()), k, v, s);
@@ -521,7 +537,10 @@ mkv_status append_step_device(mkv_pool* p, const int32_t*, int32_t B,
     }
     if (!patch) ip.n_patch = 0;
     ip.patch_base = reinterpret_cast<int32_t*>(p->mem + p->lay.sched + p->lay.items_off);
-    MKV_HIP(mkv::launch_append_inline(p->view(), ip, int32_t(plan.size()), k, v, s));
+    {
+      ProfScope ps(p, 2, s);
+      MKV_HIP(mkv::launch_append_inline(p->view(), ip, int32_t(plan.size()), k, v, s));
+    }
     if (patch) {
       for (auto& f : fixes) f.first->last_ntok = f.second;
       p->sched_version = p->meta.version();
@@ -535,6 +554,7 @@ mkv_status append_step_device(mkv_pool* p, const int32_t*, int32_t B,
   r = flush_uploads(p, {{p->lay.plan, bytes}}, s);
   if (r) return r;
   const auto* dplan = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
+  ProfScope ps(p, 2, s);
   if (p->meta.geom().kind == mkv::kKindBf16)
     MKV_HIP(mkv::launch_append_bf16(p->view(), dplan, B, k, v, s));
   else
@@ -548,6 +568,7 @@ mkv_status mkv_append_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
                            const float* v, hipStream_t s) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
   if (B < 0 || (B > 0 && (!seq_ids || !k || !v))) return set_err(MKV_EINVAL, "null argument");
+  if (B > 0 && !rows_aligned(k, v)) return set_err(MKV_EINVAL, "K and V must be 16-byte aligned");
   if (B > p->desc.max_batch) return set_err(MKV_ERANGE, "B exceeds max_batch");
   if (B == 0) return MKV_OK;
   DeviceGuard guard(p->device);
@@ -588,6 +609,7 @@ mkv_status demote_impl(mkv_pool* p, int32_t seq, const int32_t* lps, int32_t n, 
   if (plan.empty()) return MKV_OK;
   mkv_status r = upload_pt_row_and_plan(p, seq, plan.data(), plan.size() * sizeof(plan[0]), s);
   if (r == MKV_OK) {
+    ProfScope ps(p, 3, s);
     const hipError_t e = mkv::launch_demote(
         p->view(), reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan), int32_t(plan.size()), s);
     if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("demote launch: ") + hipGetErrorString(e));
@@ -749,13 +771,13 @@ mkv_status decode_impl(mkv_pool* p, const int32_t* seq_ids, int32_t B, const voi
   // (profiling events are taken only on the pool-workspace path)
   const bool prof = home == StateHome::kPool;
   {
-    ProfEvent* e = prof ? prof_begin(p, 0, s) : nullptr;
+    ProfScope ps(p, 0, s, prof);
     MKV_HIP(mkv::launch_partial(a, s));
-    if (prof) prof_end(p, e, s);
   }
-  ProfEvent* e = prof ? prof_begin(p, 1, s) : nullptr;
-  MKV_HIP(mkv::launch_merge(a, p->merge_narrow_max, s));
-  if (prof) prof_end(p, e, s);
+  {
+    ProfScope ps(p, 1, s, prof);
+    MKV_HIP(mkv::launch_merge(a, p->merge_narrow_max, s));
+  }
   return MKV_OK;
 }
 
@@ -771,6 +793,7 @@ mkv_status mkv_decode_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
                            hipStream_t s) {
   if (!p) return set_err(MKV_EINVAL, "null pool");
   if (B < 1 || !seq_ids || !k || !v || !q || !out || !lse) return set_err(MKV_EINVAL, "null argument");
+  if (!rows_aligned(k, v)) return set_err(MKV_EINVAL, "K and V must be 16-byte aligned");
   if (B > p->desc.max_batch) return set_err(MKV_ERANGE, "B exceeds max_batch");
   // the decode's argument checks come first: once the append is enqueued the
   // step can only fail on the device side
@@ -895,6 +918,7 @@ mkv_status mkv_decode_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
       }
     }
     p->sched_valid = false;
+    ProfScope ps(p, 2, s);
     const hipError_t e = mkv::launch_step(p->view(), sp, k, v, s);
     if (e != hipSuccess) {
       take_back();
@@ -930,6 +954,7 @@ mkv_status mkv_decode_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
       if (c.plan.empty()) continue;
       r = upload_pt_row_and_plan(p, c.seq, c.plan.data(), c.plan.size() * sizeof(c.plan[0]), s);
       if (r == MKV_OK) {
+        ProfScope ps(p, 3, s);
         const hipError_t e = mkv::launch_demote(
             p->view(), reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan), int32_t(c.plan.size()), s);
         if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("demote launch: ") + hipGetErrorString(e));
@@ -963,10 +988,12 @@ mkv_status mkv_decode_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
       mkv::InlinePlan ip{};
       std::memcpy(ip.pages, plan.data(), plan.size() * sizeof(plan[0]));
       ip.patch_base = reinterpret_cast<int32_t*>(p->mem + p->lay.sched + p->lay.items_off);
+      ProfScope ps(p, 2, s);
       const hipError_t e = mkv::launch_append_inline(p->view(), ip, int32_t(plan.size()), k, v, s);
       if (e != hipSuccess) r = set_err(MKV_EHIP, std::string("append launch: ") + hipGetErrorString(e));
     } else {
       const auto* ap = reinterpret_cast<const mkv::AppendPage*>(p->mem + p->lay.plan);
+      ProfScope ps(p, 2, s);
       const hipError_t e = p->meta.geom().kind == mkv::kKindBf16
                                ? mkv::launch_append_bf16(p->view(), ap, int32_t(plan.size()), k, v, s)
                                : mkv::launch_append(p->view(), ap, int32_t(plan.size()), k, v, s);
@@ -980,6 +1007,7 @@ mkv_status mkv_decode_step(mkv_pool* p, const int32_t* seq_ids, int32_t B, const
   if (!dplan.empty()) {
     r = upload_pieces(p, rows, s);
     if (r == MKV_OK) {
+      ProfScope ps(p, 3, s);
       const hipError_t e = mkv::launch_demote(
           p->view(), reinterpret_cast<const mkv::DemotePage*>(p->mem + p->lay.plan + a_bytes),
           int32_t(dplan.size()), s);
@@ -1151,7 +1179,11 @@ mkv_status mkv_profile_read(mkv_pool* p, mkv_profile* o) {
   o->ms_merge = p->prof_ms[1];
   o->n_partial = p->prof_n[0];
   o->n_merge = p->prof_n[1];
-  for (int i = 0; i < 2; ++i) {
+  o->ms_append = p->prof_ms[2];
+  o->ms_demote = p->prof_ms[3];
+  o->n_append = p->prof_n[2];
+  o->n_demote = p->prof_n[3];
+  for (int i = 0; i < 4; ++i) {
     p->prof_ms[i] = 0;
     p->prof_n[i] = 0;
   }

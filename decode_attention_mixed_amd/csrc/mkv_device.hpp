@@ -53,27 +53,22 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 // Round a finite fp32 value to E4M3: nearest, ties to even code, saturating at
 // +-448.  Works on the fp32 bit pattern so the result does not depend on the
-// hardware conversion's rounding or saturation mode.
+// hardware conversion's rounding or saturation mode.  Both ranges are formed
+// and one is selected (no branches):
+//  * |x| < 2^-6: the subnormal grid m * 2^-9; |x| * 512 is exact and rint
+//    rounds half to even (a result of 8 is the smallest normal code);
+//  * otherwise the top 3 mantissa bits rounded to nearest even on the bit
+//    pattern (adding 0x7FFFF plus the kept part's lowest bit carries into it
+//    exactly when the dropped 20 bits are above half, or at half with an odd
+//    kept part, and a carry moves into the exponent), rebased from the fp32
+//    exponent bias to E4M3's (120 << 3), then saturated at 0x7E (448).
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   const uint32_t bits = __float_as_uint(x);
   const uint32_t sign = (bits >> 24) & 0x80u;
   const uint32_t a = bits & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E00000u) {                  // |x| >= 448
-    code = 0x7Eu;
-  } else if (a < 0x3C800000u) {            // |x| < 2^-6: subnormal grid m * 2^-9
-    // |x| * 512 is exact; rint rounds half to even.
-    code = uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));
-  } else {
-    const uint32_t exp = (a >> 23) - 120u; // E4M3 exponent field (1..15)
-    const uint32_t man = a & 0x7FFFFFu;
-    uint32_t r = man >> 20;                // 3 kept mantissa bits
-    const uint32_t rest = man & 0xFFFFFu;
-    if (rest > 0x80000u || (rest == 0x80000u && (r & 1u))) r += 1u;
-    code = (exp << 3) + r;                 // a carry moves into the exponent
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return sign | code;
+  const uint32_t sub = uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  const uint32_t nrm = min(((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - 960u, 0x7Eu);
+  return sign | (a < 0x3C800000u ? sub : nrm);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

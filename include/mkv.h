@@ -121,10 +121,15 @@ typedef struct {
 } mkv_stats;
 
 /* Per-kernel device time accumulated while profiling is on (milliseconds):
- * the partial kernel (both formats, one launch per decode) and the merge. */
+ * the partial kernel (both formats, one launch per decode), the merge, the
+ * cache-write launches that append (mkv_append, mkv_append_step, and the one
+ * launch of an mkv_decode_step, which may convert pages too) and the
+ * conversion launches (mkv_demote, and mkv_decode_step's separate ones). */
 typedef struct {
   double ms_partial, ms_merge;
   int64_t n_partial, n_merge;
+  double ms_append, ms_demote;
+  int64_t n_append, n_demote;
 } mkv_profile;
 
 /* Device bytes a pool with this descriptor needs (slabs, page tables,
@@ -153,7 +158,7 @@ mkv_status mkv_seq_reset(mkv_pool* pool, int32_t seq, hipStream_t stream);
 /* Append n tokens to sequence `seq` as FP8 ("Ancoras em FP8": new pages start
  * FP8; in a control pool, as bf16 rows rounded to nearest even, with none of
  * the scale handling below).  k, v: device fp32 [n][Hkv][d], row-major,
- * finite values.  New pages
+ * finite values, 16-byte aligned (MKV_EINVAL otherwise).  New pages
  * come from the FP8 free list.  The FP8 scale of a page-head is recomputed when
  * new rows raise its running amax and the page's earlier rows are re-encoded
  * against it, so a page filled by one call equals one-shot quantisation.
@@ -163,8 +168,8 @@ mkv_status mkv_append(mkv_pool* pool, int32_t seq, int32_t n, const float* k, co
                       hipStream_t stream);
 
 /* One decode step's new rows: append one token to each of B distinct
- * sequences, row b of k and v (device fp32 [B][Hkv][d]) to seq_ids[b] (host
- * int32 [B]), with one kernel launch; otherwise as mkv_append (FP8 rows with
+ * sequences, row b of k and v (device fp32 [B][Hkv][d], 16-byte aligned) to
+ * seq_ids[b] (host int32 [B]), with one kernel launch; otherwise as mkv_append (FP8 rows with
  * rescale-on-grow, or bf16 rows in a control pool).  A sequence whose last
  * page is full gets a new FP8 page.  All sequences are validated before any
  * changes (MKV_EINVAL for a repeated or bad id, MKV_ESTATE for a frozen TQ3
@@ -333,7 +338,7 @@ mkv_status mkv_debug_schedule(mkv_pool* pool, mkv_schedule_info* info, int32_t* 
                               int32_t items_cap, int32_t* entries_host, int32_t entries_cap,
                               int32_t* chunk_base_host, int32_t base_cap);
 
-/* Profiling: when enabled, decode brackets each kernel with HIP events;
+/* Profiling: when enabled, the calls bracket each kernel with HIP events;
  * mkv_profile_read waits for the device and returns the accumulated times
  * (then clears them). */
 mkv_status mkv_profile_enable(mkv_pool* pool, int32_t on);
