@@ -46,7 +46,9 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   const int bh = blockIdx.x / nslices;
   const int slice = blockIdx.x % nslices;
   const int b = bh / a.Hq, h = bh % a.Hq;
-  const int c0 = a.chunk_base[b], c1 = a.chunk_base[b + 1];
+  // one batch entry: its chunks are 0 .. max_seq_chunks - 1 (no dependent load)
+  const int c0 = a.B == 1 ? 0 : a.chunk_base[b];
+  const int c1 = a.B == 1 ? a.max_seq_chunks : a.chunk_base[b + 1];
   const int t = threadIdx.x;
   const int j = t % kVecLanes, k = t / kVecLanes;
 
@@ -111,7 +113,8 @@ __global__ void __launch_bounds__(64) merge_narrow_kernel(DecodeArgs a) {
   const int j = lane % lanes_per_head;
   if (row >= a.B * a.Hq) return;
   const int b = row / a.Hq, h = row % a.Hq;
-  const int c0 = a.chunk_base[b], c1 = a.chunk_base[b + 1];
+  const int c0 = a.B == 1 ? 0 : a.chunk_base[b];
+  const int c1 = a.B == 1 ? a.max_seq_chunks : a.chunk_base[b + 1];
   float M = -INFINITY;
   float L = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);

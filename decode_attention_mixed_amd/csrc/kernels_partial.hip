@@ -424,6 +424,9 @@ __device__ __forceinline__ int q_shift(float amax) {
 // the item's page `page` (pages hold P = 16 * tpp tokens); tiles are numbered
 // page * tpp + sub.  The four waves of a workgroup take consecutive quarters
 // of the item's tiles.  Cursors are wave-uniform and advance without division.
+// (When the tiles do not divide by four the later quarters hold one more.
+// Rotating which wave takes which quarter per workgroup measured about 1 us
+// slower on the long-context launch.)
 struct Cursor {
   int page = 0, sub = 0;
 };

@@ -227,6 +227,43 @@ def test_both_merge_kernels(monkeypatch, narrow_max):
     pool.close()
 
 
+def test_graph_replays_of_the_decode(monkeypatch):
+    """A decode captured in a graph (partial kernel and merge; the schedule
+    cached by an eager call first, so capture records no upload) replays to
+    the eager result bit for bit, replay after replay, with eager decodes of
+    another pool in between."""
+    monkeypatch.setenv("MKV_MERGE_NARROW_MAX", "0")
+    wl = W.small(seed=65, B=3, Hq=8, Hkv=2, d=128, P=16, lengths=(900, 45, 333))
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    q = H.q_tensor(wl)
+    ids = list(range(wl.B))
+    out = torch.zeros((wl.B, wl.Hq, wl.d), device="cuda")
+    lse = torch.zeros((wl.B, wl.Hq), device="cuda")
+    mkv.decode(pool.handle, ids, q, float(wl.tau), out, lse)
+    torch.cuda.synchronize()
+    want = (out.clone(), lse.clone())
+    other = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(other, wl)
+    o2 = torch.zeros_like(out)
+    l2 = torch.zeros_like(lse)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mkv.decode(pool.handle, ids, q, float(wl.tau), out, lse)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want[0]) and torch.equal(lse, want[1]), f"replay {rep}"
+        mkv.decode(other.handle, ids, q, float(wl.tau), o2, l2)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, want[0]) and torch.equal(l2, want[1]), f"eager after replay {rep}"
+    del g
+    other.close()
+    pool.close()
+
+
 def test_paced_priorities_change_no_bits(monkeypatch):
     """Progress-paced wave priorities (on for launches whose workgroups are all
     resident at once, as here) only reorder instruction issue: the results are
