@@ -569,65 +569,72 @@ struct SoftState {
 
 // LDS image for combining the four waves' states of one work item: per wave
 // the reference max and denominator of the 16 columns and the accumulator
-// rows of the live columns in true units (row stride padded); then per wave
-// and column the weight 2^(m_w - M) of that wave's state.
+// rows of the live columns in true units (row stride padded).
 template <int D>
 struct MergeLds {
   static constexpr int ROW = D + 4;
   float m[kWaves][16];
   float l[kWaves][16];
-  float f[kWaves][16];
   float acc[kWaves][16 * ROW];
 };
 
 // Combine the waves' states in M and write the item's partial state of the
 // ncol query heads starting at hq0 (all threads of the workgroup call this,
-// with M.m, M.l and M.acc written and visible).
+// with M.m, M.l and M.acc written and visible; nothing may follow it that
+// needs every thread).  Thread (c, s) takes column c and the 16-byte slices
+// of dims 4s + 64k: it forms the column's wave weights 2^(m_w - M) itself
+// (the 16 threads of a column the same way), so the combine needs no further
+// barrier, and its LDS reads and global stores are 16-byte vectors, eight
+// consecutive lanes on consecutive slices.
 template <int D>
 __device__ __forceinline__ void merge_waves_and_store(MergeLds<D>& M, const DecodeArgs& a, int chunk,
                                                       int hq0, int ncol) {
-  const int64_t base = int64_t(chunk) * a.Hq + hq0;
-  float mx = -INFINITY, lsum = 0.0f;
-  if (threadIdx.x < 16) {
-    // per column: the common reference max and the waves' weights
-    const int c = threadIdx.x;
+  const int c = int(threadIdx.x) >> 4, s = int(threadIdx.x) & 15;
+  if (c >= ncol) return;
+  float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (M.l[w][c] > 0.0f) mx = fmaxf(mx, M.m[w][c]);
+  for (int w = 0; w < kWaves; ++w)
+    if (M.l[w][c] > 0.0f) mx = fmaxf(mx, M.m[w][c]);
+  float f[kWaves];
+  float lsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = M.l[w][c] > 0.0f ? exp2f(M.m[w][c] - mx) : 0.0f;
-      M.f[w][c] = f;
-      lsum += M.l[w][c] * f;
-    }
+  for (int w = 0; w < kWaves; ++w) {
+    f[w] = M.l[w][c] > 0.0f ? exp2f(M.m[w][c] - mx) : 0.0f;
+    lsum += M.l[w][c] * f[w];
   }
-  // (the global stores come after the barrier: a barrier's release fence
-  // would otherwise wait for them to reach memory)
-  __syncthreads();
-  if (int(threadIdx.x) < ncol) {
-    a.pm[base + threadIdx.x] = mx;
-    a.pl[base + threadIdx.x] = lsum;
+  const int64_t row = int64_t(chunk) * a.Hq + hq0 + c;
+  if (s == 0) {
+    a.pm[row] = mx;
+    a.pl[row] = lsum;
   }
   // (a wave without tiles has weight 0 and a zero accumulator, so every wave
-  // enters the sum; the loop has its maximum trip count so that all LDS
-  // reads can be issued together)
-  constexpr int kIter = (16 * D + kThreads - 1) / kThreads;
+  // enters the sum, in wave order)
+  if constexpr (D >= 64) {
 #pragma unroll
-  for (int k = 0; k < kIter; ++k) {
-    const int idx = threadIdx.x + kThreads * k;
-    const int c = idx / D, dim = idx % D;
-    if (c < ncol) {
-      float o = 0.0f;
+    for (int k = 0; k < D / 64; ++k) {
+      const int dim = 4 * s + 64 * k;
+      f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) o = __builtin_fmaf(M.acc[w][c * MergeLds<D>::ROW + dim], M.f[w][c], o);
-      a.pacc[(base + c) * D + dim] = o;
+      for (int w = 0; w < kWaves; ++w) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&M.acc[w][c * MergeLds<D>::ROW + dim]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(v[e], f[w], o[e]);
+      }
+      *reinterpret_cast<f32x4*>(a.pacc + row * D + dim) = o;
     }
+  } else {
+    const int dim = (D / 16) * s;
+    f32x2 o = {0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(&M.acc[w][c * MergeLds<D>::ROW + dim]);
+      o[0] = __builtin_fmaf(v[0], f[w], o[0]);
+      o[1] = __builtin_fmaf(v[1], f[w], o[1]);
+    }
+    *reinterpret_cast<f32x2*>(a.pacc + row * D + dim) = o;
   }
 }
 
-// Softmax step of one tile for the lane's column: scores s (fp32, already
-// multiplied by the column's score factor and masked) -> probabilities p;
-// rescales the accumulators when the reference max must rise.
 template <int NACC>
 __device__ __forceinline__ void softmax_step(SoftState& st, float s[4], float p[4],
                                              f32x4 (&acc)[NACC], float* corr_lds, int col, int quad) {
