@@ -1654,11 +1654,15 @@ __device__ __forceinline__ void bf16_item(const DecodeArgs& a, const WorkItem& i
 // Four waves per SIMD at head dim <= 128 (at most 128 VGPRs and 10 KB of LDS
 // per wave); two at head dim 256.
 // ---------------------------------------------------------------------------
+//
+// The work items' address comes first among the arguments, so the kernel can
+// receive it preloaded in scalar registers (built with a kernel-argument
+// preload count of 2): the item load then waits for no argument load.
 template <int NG, int NH>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NG < 8 ? 4 : 2)))
-partial_mixed(DecodeArgs a) {
+partial_mixed(const WorkItem* __restrict__ items, DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Mix<NG, NH>::SMEM];
-  const WorkItem it = a.items[blockIdx.x];
+  const WorkItem it = items[blockIdx.x];
   if (it.fmt == 0)
     fp8_item<NG, NH>(a, it, smem);
   else
@@ -1668,10 +1672,10 @@ partial_mixed(DecodeArgs a) {
 // Control pools: every work item is BF16.  Two waves per SIMD; one tile in
 // flight (a BF16 tile row share is 4x the TQ3 one).
 template <int NG, int NH>
-__global__ void __launch_bounds__(kThreads, 2) partial_bf16(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, 2) partial_bf16(const WorkItem* __restrict__ items, DecodeArgs a) {
   constexpr size_t kSmem = Mix<NG, NH>::cmax(sizeof(Fp8Lds<NG, NH>), sizeof(MergeLds<32 * NG>));
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-  const WorkItem it = a.items[blockIdx.x];
+  const WorkItem it = items[blockIdx.x];
   bf16_item<NG, NH, 1>(a, it, smem);
 }
 
@@ -1724,7 +1728,7 @@ hipError_t launch_partial(const DecodeArgs& a, hipStream_t s) {
   const int nh = a.nh;
   const dim3 grid(unsigned(a.n_items), unsigned((a.pv.Hkv + nh - 1) / nh));
   auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, a.items, a);
     return hipGetLastError();
   };
   return a.pv.kind == kKindBf16 ? with_bf16_kernel(a.pv.d, nh, launch) : with_kernel(a.pv.d, nh, launch);
