@@ -1138,10 +1138,14 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     const int vr = 4 * quad + (col >> 2);
     const uint32_t va0 = lds_addr(vt) + uint32_t(vr * VROWB + 32 * vseg<VROWB>(vr, 0) + ((8 * (col & 3)) ^ vhalf<VROWB>(vr)));
     const uint32_t va1 = va0 ^ 32u;
-    // value unpack: lane -> (token ut, head uj, group ug of the pass); spare
-    // lanes repeat a real one's work
+    // value unpack: lane -> (group ug of the pass, token ut, head uj), the
+    // group fastest: a half-wave's raw reads (three dwords per lane at
+    // 12 ut + 3 ug, one head) then spread over more banks than with the
+    // token fastest, and eight consecutive lanes still write eight distinct
+    // 16-byte bank groups of the swizzled value tile; spare lanes repeat a
+    // real one's work
     const int ci = lane % (16 * NH * PASS);
-    const int ut = ci & 15, uj = (ci >> 4) % NH, ug = ci / (16 * NH);
+    const int ug = ci % PASS, ut = (ci / PASS) & 15, uj = ci / (16 * PASS);
 
     Cursor pc = tg.first;
     int ks = 0;                                  // slot of this tile's key half
