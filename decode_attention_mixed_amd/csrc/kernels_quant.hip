@@ -124,9 +124,12 @@ append_fp8_kernel(PoolView pv, const AppendPage* __restrict__ plan, const float*
 // then (kv-head, K or V), so consecutive lanes read consecutive 32-byte runs
 // of codes and write consecutive 12-byte runs and fp16 scales.  The count of
 // thresholds at or below x is floor(x / s) + 4 clamped to 0..7 in exact
-// arithmetic; it is formed from x * (1 / s) (far less than one step off) and
-// settled by comparing x with the exact products b * s on each side, so the
-// codes equal those of the seven comparisons.
+// arithmetic.  t = x * (1 / s) is far less than one step from x / s, so with
+// k = rint(t), x / s lies in (k - 1, k + 1) and floor(x / s) is k when
+// x >= k * s and k - 1 otherwise: one comparison with an exact product
+// (k * s is exact in fp32 for the small integers k), and the codes equal
+// those of the seven comparisons.  The +4 rides along: k' = rint(x / s + 4)
+// from one fma, compared with k' * s - 4 s (also exact).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int demote_groups(const PoolView& pv) { return pv.Hkv * 2 * pv.P * (pv.d / 32); }
 
@@ -162,27 +165,22 @@ __device__ __forceinline__ void demote_group(const PoolView& pv, const DemotePag
   const _Float16 s16 = _Float16(q);            // round to nearest even
   const float s = float(s16);
   const float rs = __builtin_amdgcn_rcpf(s);    // s == 0 is settled below
+  const float s4 = -4.0f * s;
   uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    // floor(x / s) clamped to -4..3, without branches: the estimate f from
-    // x * (1 / s) is at most one off, and the exact products (f + 1) * s
-    // (fma(f, s, s) forms it exactly) and f * s tell which way, both judged
-    // against the same f, before the final clamp
-    const float f = __builtin_amdgcn_fmed3f(floorf(x[j] * rs), -4.0f, 3.0f);
-    const int up = x[j] >= __builtin_fmaf(f, s, s) ? 1 : 0;
-    const int dn = x[j] < f * s ? 1 : 0;
-    const int fi = min(max(int(f) + up - dn, -4), 3);
-    // code fi + 4: the low three bits of fi, with bit 2 flipped for all codes at once below
-    const uint32_t c = uint32_t(fi) & 7u;
+    // code = floor(x / s) + 4 clamped to 0..7, without branches
+    const float k = __builtin_rintf(__builtin_fmaf(x[j], rs, 4.0f));
+    const float f = x[j] < __builtin_fmaf(k, s, s4) ? k - 1.0f : k;
+    const uint32_t c = uint32_t(__builtin_amdgcn_fmed3f(f, 0.0f, 7.0f));
     const int bit = 3 * j;
     w[bit >> 5] |= c << (bit & 31);
     if ((bit & 31) > 29) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
   }
-  // +4 in every 3-bit field (0b100 at bit 3j + 2), or all codes 4 when s == 0
+  // all codes 4 when s == 0 (0b100 in every 3-bit field)
   constexpr uint32_t kFour[3] = {0x24924924u, 0x49249249u, 0x92492492u};
 #pragma unroll
-  for (int i = 0; i < 3; ++i) w[i] = s != 0.0f ? (w[i] ^ kFour[i]) : kFour[i];
+  for (int i = 0; i < 3; ++i) w[i] = s != 0.0f ? w[i] : kFour[i];
   uint32_t* out = reinterpret_cast<uint32_t*>(dst + tq3_codes_off(pv, h, kv) + int64_t(t) * row_bytes + 12 * g);
   out[0] = w[0];
   out[1] = w[1];
