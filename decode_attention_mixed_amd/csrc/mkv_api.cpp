@@ -137,6 +137,7 @@ struct mkv_pool {
   std::vector<int32_t> sched_ids;
   mkv::Schedule sched;
   int32_t target_waves[2] = {2048, 1024};   // resident partial-kernel waves, 1 or 2 heads per wave
+  int32_t sched_waves[2] = {2048, 1024};    // waves a schedule below the split-K floor fills
   int32_t merge_narrow_max = 16;            // per-lane merge up to this many chunks per entry
   bool pace = true;                         // progress-paced wave priorities (one-round launches)
   int32_t anchor_window = -1;               // mkv_decode_step's anchor policy window (-1: off)
@@ -302,7 +303,7 @@ mkv::SchedPolicy pool_policy(const mkv_pool* p, int32_t Hq) {
     const int nh = std::atoi(e);
     if (nh == 1 || (nh == 2 && g.d <= 128 && g.Hkv % 2 == 0 && 2 * (Hq / g.Hkv) <= 16)) pol.heads_per_wave = nh;
   }
-  pol.target_waves = p->target_waves[pol.heads_per_wave - 1];
+  pol.target_waves = p->sched_waves[pol.heads_per_wave - 1];
   if (const char* e = std::getenv("MKV_CHUNK_PAGES")) pol.fixed_chunk_pages = std::max(0, std::atoi(e));
   if (const char* e = std::getenv("MKV_TARGET_WAVES")) pol.target_waves = std::max(1, std::atoi(e));
   if (const char* e = std::getenv("MKV_FP8_PAGE_COST")) pol.fp8_page_cost = float(std::atof(e));
@@ -356,12 +357,23 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, void* device_mem, size_t b
   if (e != hipSuccess) return cleanup(MKV_EHIP, hipGetErrorString(e));
   e = mkv::static_workspace(p->device, &p->static_ws);
   if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("static workspace: ") + hipGetErrorString(e));
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("device attribute: ") + hipGetErrorString(e));
   for (int nh = 1; nh <= 2; ++nh) {
     if (nh == 2 && desc->head_dim > 128) break;
     int waves = 0;
     e = mkv::partial_resident_waves(desc->head_dim, nh, desc->kv_kind, &waves);
     if (e != hipSuccess) return cleanup(MKV_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
-    if (waves > 0) p->target_waves[nh - 1] = waves;
+    if (waves > 0) {
+      p->target_waves[nh - 1] = waves;
+      // Where four waves fit a SIMD, schedules below the split-K floor fill
+      // three of them: fewer, longer items pay the per-workgroup set-up and
+      // combine less often, and three waves still hide the tile loop's
+      // latencies (measured on the ragged batch: 25.4 against 26.7 us per
+      // step); with two waves per SIMD every slot is needed.
+      p->sched_waves[nh - 1] = cus > 0 && waves >= 16 * cus ? waves / 4 * 3 : waves;
+    }
   }
   if (const char* ev = std::getenv("MKV_MERGE_NARROW_MAX")) p->merge_narrow_max = std::max(0, std::atoi(ev));
   if (const char* ev = std::getenv("MKV_PACE")) p->pace = std::atoi(ev) != 0;

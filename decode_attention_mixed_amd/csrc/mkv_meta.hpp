@@ -128,7 +128,8 @@ inline int32_t heads_per_wave(int32_t d, int32_t Hkv, int32_t G) {
 // pages instead (the last one shorter).  Chunks grow when a batch would need
 // more than max_chunks of them; no chunk exceeds kMaxChunkPages.
 struct SchedPolicy {
-  int32_t target_waves = 2048;   // resident partial-kernel waves on the device
+  int32_t target_waves = 2048;   // partial-kernel waves a schedule fills (the library passes the
+                                 // resident waves, or three quarters of them where four fit a SIMD)
   int32_t min_items = 256;       // split-K floor: at least this many items for batches of
                                  // min_items * kFloorChunkPages pages or more
   int32_t min_chunk_pages = 4;   // smallest balanced chunk (shorter lists stay whole)
