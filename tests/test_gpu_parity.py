@@ -773,6 +773,57 @@ def test_schedule_export_matches_page_tables():
     pool.close()
 
 
+def test_demote_codes_at_exact_thresholds():
+    """TQ3 codes of values on and beside the thresholds b * s: every 32-dim
+    group holds +-448 times the page's factor, so the page-head scale is that
+    factor exactly (amax / 448) and the group scale is 128 times it; the
+    other entries are E4M3 values equal to b * s (b = +-1, +-2, +-3) and their
+    E4M3 neighbours.  Four pages at factors 1, 1/2, 2^-10 and 3; all pages
+    converted, records bit for bit against the oracle, then the decode with
+    the queries scaled by 2^-12 (exactly, in bf16): keys of magnitude up to
+    1344 would otherwise put the log-sum-exp in the hundreds, where fp32
+    cannot hold it to the absolute tolerance."""
+    wl = W.small(seed=47, B=1, Hq=8, Hkv=2, d=128, P=16, lengths=(64,), anchor_frac=0.0)
+    wl.anchors = [np.zeros(0, np.int64)]
+    base = np.array([448, 384, 352, 416, 256, 240, 288, 128, 120, 144, 0, 64, 8, 192, 320, 448], np.float32)
+    vals = np.concatenate([base, -base])                  # 32 values, +-448 included
+    rng = np.random.default_rng(9)
+    rows = np.empty((64, 2, 2, 128), np.float32)          # token, K/V, kv-head, dim
+    for t in range(64):
+        for kv in range(2):
+            for h in range(2):
+                rows[t, kv, h] = np.concatenate([rng.permutation(vals) for _ in range(4)])
+    factor = np.repeat(np.array([1.0, 0.5, 2.0 ** -10, 3.0], np.float32), 16)[:, None, None, None]
+    rows = rows * factor
+    # values at 1/64 of the keys' size (a power of two: their codes sit on
+    # the thresholds all the same) keep the outputs small enough for the
+    # absolute tolerance
+    k, v = rows[:, 0].copy(), rows[:, 1] * np.float32(1.0 / 64.0)
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_sequence(pool, wl, 0, kv=(k, v))
+    model = OS.seq_model(wl, 0, kv=(k, v))
+    assert all(p.fmt == 1 for p in model.pages)
+    _check_records(pool, wl, [model])
+    # the exact-tie values reach the packer: group scales 128 x the page factor
+    # (keys) and 2 x it (values)
+    for kvi, unit in ((0, 128.0), (1, 2.0)):
+        scales = np.unique(np.concatenate([p.tscale[kvi, :, :p.ntok].astype(np.float64).ravel()
+                                           for p in model.pages]))
+        assert set(scales.tolist()) == {unit * f for f in (1.0, 0.5, 2.0 ** -10, 3.0)}
+    from oracle import codecs as CD
+    from oracle import attention as OA
+    qb = CD.bf16_encode(CD.bf16_bits_to_value(wl.q_bits).astype(np.float32) * np.float32(2.0 ** -12))
+    q = torch.from_numpy(qb.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    out = torch.empty(1, wl.Hq, wl.d, device="cuda")
+    lse = torch.empty(1, wl.Hq, device="cuda")
+    mkv.decode(pool.handle, [0], q, float(wl.tau), out, lse)
+    torch.cuda.synchronize()
+    O, L = OA.decode_seq(model, qb[0], wl.tau)
+    _check(out[0].cpu().numpy().astype(np.float64), lse[0].cpu().numpy().astype(np.float64), O, L,
+           "threshold values")
+    pool.close()
+
+
 def test_edge_values_records_and_decode():
     """Edge values through append, demote and decode: a kv-head whose rows are
     zero on whole pages (FP8 scale 1, TQ3 scale 0), zero groups, groups so small
