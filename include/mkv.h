@@ -331,7 +331,9 @@ typedef struct {
   int32_t n_chunks;        /* partial-state slots */
   int32_t max_seq_chunks;  /* most slots of one batch entry */
   int32_t heads_per_wave;  /* kv-heads per partial-kernel workgroup */
-  int32_t resident_waves;  /* partial-kernel waves the device holds at once (the schedule's target) */
+  int32_t resident_waves;  /* partial-kernel waves the device holds at once (a schedule below the
+                              split-K floor fills three quarters of them where four fit a SIMD,
+                              all of them otherwise) */
   int32_t pad0;
 } mkv_schedule_info;
 mkv_status mkv_debug_schedule(mkv_pool* pool, mkv_schedule_info* info, int32_t* items_host,
