@@ -36,7 +36,7 @@ LIB_SOURCES = [
     ("mkv_api.cpp", []),
     ("kernels_quant.hip", ["-ffp-contract=off"]),
     ("kernels_partial.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=2"]),
-    ("kernels_merge.hip", []),
+    ("kernels_merge.hip", ["-mllvm", "-amdgpu-kernarg-preload-count=12"]),
     ("workspace.hip", []),
 ]
 

@@ -39,9 +39,26 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// The arguments the first state loads need come first, so the kernel can
+// receive them preloaded in scalar registers (built with a kernel-argument
+// preload count of 12): pm, pl, pacc, chunk_base, Hq, d, B, the largest
+// chunk count per entry.
+struct MergeArgs {
+  const float* pm;
+  const float* pl;
+  const float* pacc;
+  const int32_t* chunk_base;
+  int32_t Hq, d, B, max_seq_chunks;
+  float* out;
+  float* lse;
+};
+
 template <int U>
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
-  const int d = a.pv.d;
+__global__ void __launch_bounds__(kMergeThreads)
+merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl, const float* __restrict__ pacc,
+             const int32_t* __restrict__ chunk_base, int32_t Hq, int32_t d, int32_t B, int32_t max_seq_chunks,
+             float* __restrict__ out, float* __restrict__ lse) {
+  const MergeArgs a{pm, pl, pacc, chunk_base, Hq, d, B, max_seq_chunks, out, lse};
   const int nslices = d / kSlice;
   const int bh = blockIdx.x / nslices;
   const int slice = blockIdx.x % nslices;
@@ -105,8 +122,11 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(64) merge_narrow_kernel(DecodeArgs a) {
-  const int d = a.pv.d;
+__global__ void __launch_bounds__(64)
+merge_narrow_kernel(const float* __restrict__ pm, const float* __restrict__ pl, const float* __restrict__ pacc,
+                    const int32_t* __restrict__ chunk_base, int32_t Hq, int32_t d, int32_t B,
+                    int32_t max_seq_chunks, float* __restrict__ out, float* __restrict__ lse) {
+  const MergeArgs a{pm, pl, pacc, chunk_base, Hq, d, B, max_seq_chunks, out, lse};
   const int lanes_per_head = d / 4;                // 8 .. 64
   const int lane = threadIdx.x;
   const int row = blockIdx.x * (64 / lanes_per_head) + lane / lanes_per_head;   // b * Hq + h
@@ -163,19 +183,23 @@ __global__ void __launch_bounds__(64) merge_narrow_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_merge(const DecodeArgs& a, int narrow_max, hipStream_t s) {
+  const MergeArgs M{a.pm, a.pl, a.pacc, a.chunk_base, a.Hq, a.pv.d, a.B, a.max_seq_chunks, a.out, a.lse};
   if (a.max_seq_chunks <= narrow_max) {
     const int heads_per_wave = 256 / a.pv.d;
     const int rows = a.B * a.Hq;
     hipLaunchKernelGGL(merge_narrow_kernel, dim3(unsigned((rows + heads_per_wave - 1) / heads_per_wave)),
-                       dim3(64), 0, s, a);
+                       dim3(64), 0, s, M.pm, M.pl, M.pacc, M.chunk_base, M.Hq, M.d, M.B, M.max_seq_chunks, M.out,
+                       M.lse);
     return hipGetLastError();
   }
   const int nslices = a.pv.d / kSlice;
   const dim3 grid(unsigned(a.B * a.Hq * nslices));
   if (a.max_seq_chunks > kChunkLanes * 8)
-    hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(kMergeThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<16>, grid, dim3(kMergeThreads), 0, s, M.pm, M.pl, M.pacc, M.chunk_base, M.Hq,
+                       M.d, M.B, M.max_seq_chunks, M.out, M.lse);
   else
-    hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(kMergeThreads), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<8>, grid, dim3(kMergeThreads), 0, s, M.pm, M.pl, M.pacc, M.chunk_base, M.Hq,
+                       M.d, M.B, M.max_seq_chunks, M.out, M.lse);
   return hipGetLastError();
 }
 
