@@ -46,17 +46,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "mixed FP8/TQ3 paged decode: µs/step and achieved KV HBM GB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["kernels_partial.hip", "kernels_merge.hip", "mkv_device.hpp",
-                  "mkv_kernels.hpp"]
+# Sources of the decode kernels: the partial kernel's own (its HBM traffic
+# record is keyed to these) and, with the merge, those of a whole decode step
+# (the per-dispatch duration records).
+PARTIAL_SOURCES = ["kernels_partial.hip", "mkv_device.hpp", "mkv_kernels.hpp"]
+KERNEL_SOURCES = PARTIAL_SOURCES + ["kernels_merge.hip"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_src_hash() -> str:
+def kernel_src_hash(names=None) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "decode_attention_mixed_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -151,7 +154,7 @@ def load_traffic(kernel: str, wl_name: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_src_sha") != kernel_src_hash():
+    if t.get("kernel_src_sha") != kernel_src_hash(PARTIAL_SOURCES):
         return None
     return t.get("bytes_per_launch")
 
@@ -194,7 +197,7 @@ def write_traffic(rd_csv, wr_csv, copy_rd_csv, copy_wr_csv, copy_bytes, wl_name,
     k = _req_bytes(rd_csv, wr_csv, "partial_mixed")
     c = _req_bytes(copy_rd_csv, copy_wr_csv, "copyBuffer")
     out = {
-        "kernel": "partial", "workload": wl_name, "kernel_src_sha": kernel_src_hash(),
+        "kernel": "partial", "workload": wl_name, "kernel_src_sha": kernel_src_hash(PARTIAL_SOURCES),
         "bytes_per_launch": round(k["read_bytes"] + k["write_bytes"]),
         "read_bytes_per_launch": round(k["read_bytes"]), "write_bytes_per_launch": round(k["write_bytes"]),
         "read_requests_32_64_128B": [round(x) for x in k["read_requests_by_size"]],
