@@ -299,27 +299,17 @@ __device__ __forceinline__ float fma_mix_f32(float p, uint32_t w, float c) {
 
 // Value scales of pass ps for the lane's 4 tokens, from the slot's scale rows
 // sp (token t: NG f16): NG >= 2: sw[i] = the scales of groups 2ps, 2ps + 1 of
-// token i; NG = 1: sw[0], sw[1] = tokens (0, 1) and (2, 3).  Tokens i >= nv
-// get 0.
+// token i; NG = 1: sw[0], sw[1] = tokens (0, 1) and (2, 3).  (Rows past the
+// valid tokens of a tile hold 0 by then: the tile loop clears them.)
 template <int NG>
-__device__ __forceinline__ void tq3_pass_scales(const uint32_t* sp, int ps, int nv, uint32_t (&sw)[4]) {
+__device__ __forceinline__ void tq3_pass_scales(const uint32_t* sp, int ps, uint32_t (&sw)[4]) {
   if constexpr (NG >= 2) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sw[i] = sp[i * (NG / 2) + ps];
-    if (nv < 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i >= nv) sw[i] = 0u;
-    }
   } else {
     sw[0] = sp[0];
     sw[1] = sp[1];
     sw[2] = sw[3] = 0u;
-    if (nv < 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i >= nv) sw[i >> 1] &= (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-    }
   }
 }
 
@@ -845,11 +835,12 @@ __device__ __forceinline__ int vhalf(int r) {
 }
 
 // p with address bit 4 flipped (an asm statement: the result is formed where
-// it is used instead of being kept live).
+// it is used instead of being kept live; one instruction, no copy of p).
 __device__ __forceinline__ uint8_t* flip16(uint8_t* p) {
-  uint32_t a = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(p)));
-  asm volatile("v_xor_b32 %0, 16, %0" : "+v"(a));
-  return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t(a));
+  const uint32_t a = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(p)));
+  uint32_t r;
+  asm volatile("v_xor_b32 %0, 16, %1" : "=v"(r) : "v"(a));
+  return (uint8_t*)(__attribute__((address_space(3))) uint8_t*)(uintptr_t(r));
 }
 
 // LDS byte address of a pointer into this workgroup's LDS.
@@ -974,6 +965,37 @@ __device__ __forceinline__ void softmax_live(SoftState& st, float s[4], float p[
   }
 }
 
+// The same for a live column whose scores still take a wave-uniform factor
+// fs >= 0: the maximum is taken over the raw scores (a non-negative factor
+// keeps their order, so max(s) * fs is the maximum of the products exactly)
+// and each weight is 2^(fs * s - m) from one fma.  Scores of -inf need
+// fs > 0.
+template <int NACC, typename OnRescale>
+__device__ __forceinline__ void softmax_scaled(SoftState& st, const float s[4], float fs, float p[4],
+                                               f32x4 (&acc)[NACC], int quad, OnRescale on_rescale) {
+  float tmax = vmax(vmax(s[0], s[1]), vmax(s[2], s[3]));
+  tmax = quad_max2(tmax) * fs;
+  if (__any(tmax > st.m)) {
+    const bool rise = tmax > st.m;
+    const float m_new = rise ? tmax + kHeadroom : st.m;
+    const float corr = rise ? exp2f(st.m - m_new) : 1.0f;   // 0 on the column's first tile
+    st.m = m_new;
+    st.l *= corr;
+    on_rescale(corr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float c = __shfl(corr, 4 * quad + i, 64);
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) acc[j][i] *= c;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], fs, -st.m));
+    st.l += p[i];
+  }
+}
+
 // Page-table entries of a wave's pages, one per lane (a wave's tiles span at
 // most 64 pages), read per tile with readlane.
 struct WavePages {
@@ -1090,7 +1112,10 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
     float amax = __uint_as_float(max(mbits & 0xFFFFu, mbits >> 16) << 16);
     amax = qlive ? quad_max(amax) : 0.0f;
     const int E = q_shift(amax);
-    F = a.scale * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 17 - E);
+    // the sign of the softmax scale goes to the query operands (exact), so
+    // the score factor F is never negative
+    const float qsign = a.scale < 0.0f ? -1.0f : 1.0f;
+    F = __builtin_fabsf(a.scale) * kLog2e * __builtin_amdgcn_ldexpf(1.0f, 17 - E);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g % kWaves != wave) continue;
@@ -1099,7 +1124,7 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) {
         const int e = kSlotCode[sl];
-        const float x = qlive ? bf16_to_f32(uint16_t(qraw[g][e >> 1] >> (16 * (e & 1)))) : 0.0f;
+        const float x = qlive ? qsign * bf16_to_f32(uint16_t(qraw[g][e >> 1] >> (16 * (e & 1)))) : 0.0f;
         qh[sl] = _Float16(__builtin_amdgcn_ldexpf(x, E + 7 - kSlotShift[sl]));
         part = __builtin_fmaf(float(qh[sl]), __builtin_amdgcn_ldexpf(1.0f, kSlotShift[sl] - 24), part);
       }
@@ -1177,15 +1202,17 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       }
       wait_lds();                                // the key half is consumed: its slot takes
       issue(true);                               // the next tile's value half
+      // score factor F enters the softmax's exponent fma; a partial tile
+      // scales its scores first and masks the rows past the valid tokens
+      const bool partial = nvalid < 16;
+      float fs = F;
+      if (partial) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] *= F;
-      if (nvalid < 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * quad + i >= nvalid) s[i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) s[i] = 4 * quad + i >= nvalid ? -INFINITY : s[i] * F;
+        fs = 1.0f;
       }
       float p[4];
-      softmax_live(st, s, p, acc, quad, true, [&](float c) {
+      softmax_scaled(st, s, fs, p, acc, quad, [&](float c) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) vmass[g] *= c;
       });
@@ -1193,14 +1220,21 @@ __device__ __forceinline__ void tq3_item(const DecodeArgs& a, const WorkItem& it
       // ---- values: per pass of PASS groups, unpack into the value tile, then
       // P' = p * value scale (hi/lo f16) and acc += P' * V
       wait_vm<2 * TNI>();                        // this tile's value half has landed
+      if (partial) {
+        // rows past the valid tokens: their value scales (unwritten memory,
+        // possibly NaN, and p = 0 times NaN is NaN) become 0; the scale rows
+        // of the slot are [head][token][group] f16
+        uint16_t* vsc = reinterpret_cast<uint16_t*>(wl + vs * C::SLOT + C::SCOFF);
+        for (int x = lane; x < NH * 16 * NG; x += 64)
+          if ((x / NG) % 16 >= nvalid) vsc[x] = 0;
+        wave_lds_sync();
+      }
       const uint32_t* vsp = reinterpret_cast<const uint32_t*>(vb + C::SCOFF + jcol * 16 * C::SCB + 8 * NG * quad);
 #pragma unroll
       for (int ps = 0; ps < C::NPASS; ++ps) {
-        // value scales of the pass for the lane's 4 tokens (an unwritten
-        // row's scale may be NaN, and p = 0 times NaN is NaN: invalid rows
-        // get 0)
+        // value scales of the pass for the lane's 4 tokens
         uint32_t sw[4];
-        tq3_pass_scales<NG>(vsp, ps, nvalid - 4 * quad, sw);
+        tq3_pass_scales<NG>(vsp, ps, sw);
         {
           const uint32_t* src = reinterpret_cast<const uint32_t*>(vb + uj * 16 * ROWB + ut * ROWB + 12 * (ps * PASS + ug));
           const uint32_t w[3] = {src[0], src[1], src[2]};

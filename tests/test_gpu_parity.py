@@ -872,3 +872,28 @@ def test_edge_values_records_and_decode():
         _check(out[b].cpu().numpy().astype(np.float64), lse[b].cpu().numpy().astype(np.float64), Ob, Lb,
                f"edge values [{b}]")
     pool.close()
+
+
+@pytest.mark.parametrize("tau_factor", [-1.0, 0.0, -4.0])
+def test_negative_and_zero_softmax_scale(tau_factor):
+    """The softmax scale is the caller's fp32 factor on <q, k>, any sign: a
+    negative scale reverses the order of the scores (the partial kernels fold
+    its sign into the query operands) and a zero scale gives uniform weights
+    (O = mean of the values, LSE = log of the token count).  Mixed pools with
+    partial last tiles on both formats and a one-token sequence."""
+    wl = W.small(seed=47, B=3, Hq=12, Hkv=2, d=128, P=16, lengths=(203, 1, 77), anchor_frac=0.3,
+                 outliers={"k": (3, 8.0)})
+    pool = H.DevicePool(H.pool_desc(wl))
+    H.load_cache(pool, wl)
+    tau = float(np.float32(wl.tau * tau_factor))
+    q = H.q_tensor(wl)
+    out = torch.empty(wl.B, wl.Hq, wl.d, device="cuda")
+    lse = torch.empty(wl.B, wl.Hq, device="cuda")
+    mkv.decode(pool.handle, list(range(wl.B)), q, tau, out, lse)
+    torch.cuda.synchronize()
+    for b in range(wl.B):
+        model = OS.seq_model(wl, b)
+        O, L = A.decode_seq(model, wl.q_bits[b], tau)
+        _check(out[b].cpu().numpy().astype(np.float64), lse[b].cpu().numpy().astype(np.float64), O, L,
+               f"softmax scale x{tau_factor} [{b}]")
+    pool.close()
