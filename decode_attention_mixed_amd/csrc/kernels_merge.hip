@@ -34,9 +34,54 @@ constexpr int kVecLanes = kSlice / 4;              // lanes per chunk (float4 ea
 constexpr int kChunkLanes = kMergeThreads / kVecLanes;
 constexpr int kUnroll = 8;
 
+// Cross-lane steps without the LDS permute unit (each ds_bpermute is a round
+// trip through the LDS pipeline; these are ALU operations): DPP moves within a
+// row of 16 lanes and the row swaps of permlane16/32.
+constexpr int kDppXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppRor4 = 0x124;     // row_ror:4
+constexpr int kDppRor8 = 0x128;     // row_ror:8
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// permlane16_swap (permlane32_swap) of a register with itself leaves, in the
+// two results, the even and the odd row of each pair of 16-lane rows (the
+// lower and the upper 32 lanes): combining the two gives every lane the
+// combination of its row (half) and the partner row (half), the same bits in
+// both.
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum over the 64 lanes.
 __device__ __forceinline__ float wave_max(float x) {
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppRor4>(x));
+  x = fmaxf(x, dpp<kDppRor8>(x));
+  return pair32_max(pair16_max(x));
+}
+
+// Sum over the 16 lanes of the wave with the same lane index mod 4 (the
+// rotations by 4 and 8 within a row reach the row's lanes of that residue).
+__device__ __forceinline__ float sum_mod4(float x) {
+  x += dpp<kDppRor4>(x);
+  x += dpp<kDppRor8>(x);
+  return pair32_sum(pair16_sum(x));
 }
 
 // The arguments the first state loads need come first, so the kernel can
@@ -111,9 +156,9 @@ merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl, const f
   }
   // sum over the chunk lanes (lanes j + 4k')
   float r5[5] = {acc.x, acc.y, acc.z, acc.w, L};
+  static_assert(kVecLanes == 4, "chunk lanes are the lanes of one residue mod 4");
 #pragma unroll
-  for (int e = 0; e < 5; ++e)
-    for (int off = kVecLanes; off < 64; off <<= 1) r5[e] += __shfl_xor(r5[e], off, 64);
+  for (int e = 0; e < 5; ++e) r5[e] = sum_mod4(r5[e]);
   if (t < kVecLanes) {
     const float inv = 1.0f / r5[4];
     *reinterpret_cast<float4*>(a.out + (int64_t(b) * a.Hq + h) * d + slice * kSlice + 4 * t) =
