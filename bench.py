@@ -58,10 +58,18 @@ def log(*a):
 
 
 def kernel_src_hash(names=None) -> str:
+    """Hash of the kernel sources with comments and blank lines left out, so a
+    record made with the kernels stays keyed to them when only their comments
+    change."""
+    import re
     h = hashlib.sha256()
     for name in names or KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "decode_attention_mixed_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "decode_attention_mixed_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

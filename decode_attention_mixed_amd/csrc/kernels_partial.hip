@@ -10,12 +10,14 @@
 //   acc = sum 2^(s2 - m) * v.
 //
 // Work decomposition.  One launch covers both formats: one workgroup (4
-// wave64) per (work item = chunk of at most 256 pages of one format of one
-// sequence, block of NH kv-heads).  The workgroup first copies the chunk's
-// page-table entries to LDS; each wave then walks its quarter of the chunk's
-// 16-token tiles for the NH kv-heads, with the raw bytes of the next R tiles
-// in flight (a ring of register buffers).  The four waves' softmax states are
-// combined through LDS and one partial state per query head is written.
+// wave64) per (work item = chunk of at most 240 pages of one format of one
+// sequence, block of NH kv-heads).  Each wave walks its quarter of the
+// chunk's 16-token tiles for the NH kv-heads (its pages' page-table entries
+// held one per lane, or staged in LDS for the workgroup), with the next tiles'
+// bytes in flight: copied by 16-byte loads straight into a ring of LDS
+// half-slots in the mixed kernel, held in registers in the BF16 control
+// kernel.  The four waves' softmax states are combined through LDS and one
+// partial state per query head is written.
 //
 // Tile computation (16 tokens x up to 16 query-head columns; column c is
 // query head hk*G + c of kv-head hk, columns c >= G are zero):
