@@ -1359,9 +1359,18 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
     for (int g = 0; g < NG; ++g) qraw[g] = *reinterpret_cast<const u32x4*>(qrow + 32 * g + 8 * quad);
 
     // a one-head half is 16 consecutive token rows of that head's key (or
-    // value) block: vector v of the slot is bytes 16v.. of it
+    // value) block.  Rows are D bytes apart, a multiple of the LDS bank width,
+    // so the 16 rows of a tile read at one column would share banks; at D >=
+    // 128 the load therefore swizzles each row's 16-byte chunks: slot chunk
+    // (t, c) holds record chunk (t, c ^ sw(t)) with sw(t) = t mod (rows per
+    // load instruction), which keeps each lane's record offset constant
     const int PD = pv.P * D;
-    const uint32_t voff_c = 16u * uint32_t(lane);
+    constexpr int CPR = D / 16;                   // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                 // rows per load instruction
+    constexpr bool SWZ = D >= 128;
+    static_assert(!SWZ || RPI <= CPR, "the swizzle stays within a row");
+    const uint32_t voff_c = SWZ ? 16u * uint32_t((lane / CPR) * CPR + ((lane % CPR) ^ (lane / CPR)))
+                                : 16u * uint32_t(lane);
     Cursor lc = tg.first;
     int lj = 0;                                  // head of the next one-head tile to load
     int ls = 0;
@@ -1428,7 +1437,9 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
         f32x4 dsum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int r = 0; r < NG; ++r) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(kb + col * D + 32 * r + 8 * quad);
+          // logical bytes 32 r + 8 quad of row col: chunk 2 r + quad / 2
+          const int chunk = SWZ ? (2 * r + (quad >> 1)) ^ (col % RPI) : 2 * r + (quad >> 1);
+          const u32x2 w = *reinterpret_cast<const u32x2*>(kb + col * D + 16 * chunk + 8 * (quad & 1));
           const u32x2 k0 = fp8x4_to_f16_s(w[0]);
           const u32x2 k1 = fp8x4_to_f16_s(w[1]);
           const u32x4 ku = {k0[0], k0[1], k1[0], k1[1]};
@@ -1451,7 +1462,8 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, const WorkItem& it
             // token ut's dims 32 PASS ps + 8 PASS uq .. +8 PASS, widened to f16
             // (rows past the valid tokens are zeroed: an unwritten byte may be NaN)
             constexpr int NB = 8 * PASS;                     // bytes (dims) per lane
-            const uint8_t* src = vb + ut * D + 32 * PASS * ps + NB * uq;
+            const int vbyte = 32 * PASS * ps + NB * uq;      // logical bytes of row ut
+            const uint8_t* src = vb + ut * D + (SWZ ? 16 * ((vbyte >> 4) ^ (ut % RPI)) + (vbyte & 15) : vbyte);
             uint32_t o[NB / 2];
             if constexpr (NB == 16) {
               const u32x4 w = *reinterpret_cast<const u32x4*>(src);
