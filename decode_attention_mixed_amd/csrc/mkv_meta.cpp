@@ -329,12 +329,13 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
     return fail(err, MKV_S_EINVAL, "unsupported kv-heads per wave");
   // Per-format page counts of each batch entry.  A wave walks an FP8 page one
   // kv-head at a time and a TQ3 page heads_per_block kv-heads at a time; the
-  // default cost of an FP8 page in TQ3 pages is the measured ratio of their
-  // tile-loop times (1.25 with one kv-head per workgroup, 1.75 with two).
+  // default cost of an FP8 page in TQ3 pages is the one that gave the
+  // shortest partial kernels in a sweep of the cost (0.85 with one kv-head per
+  // workgroup, 1.2 with two).
   std::vector<int32_t> n8(size_t(B), 0), n3(size_t(B), 0);
   int64_t total_pages = 0;
   double total_cost = 0.0;
-  const double c8 = pol.fp8_page_cost > 0.0f ? double(pol.fp8_page_cost) : (heads_per_block == 2 ? 1.75 : 1.25);
+  const double c8 = pol.fp8_page_cost > 0.0f ? double(pol.fp8_page_cost) : (heads_per_block == 2 ? 1.2 : 0.85);
   for (int32_t b = 0; b < B; ++b) {
     for (int32_t e : seqs_[size_t(ids[b])].pt) (pt_is_tq3(e) ? n3 : n8)[size_t(b)]++;
     total_pages += int64_t(seqs_[size_t(ids[b])].pt.size());

@@ -280,8 +280,8 @@ def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
     # so an item takes four 4-wave workgroups for its 8 kv-heads.  The split-K
     # floor keeps at least 256 chunks even where the resident waves (2048
     # here) would give 128; 4096 resident waves (four per SIMD) give 256 too.
-    # An FP8 page costs 1.75 TQ3 pages (a wave walks it one kv-head at a time;
-    # 1.75 is the measured ratio of the two formats' tile-loop times).
+    # An FP8 page costs 1.2 TQ3 pages (a wave walks it one kv-head at a time;
+    # 1.2 gave the shortest partial kernels in a sweep of the cost).
     h = _host(lib, num_kv_heads=8, max_seqs=1, max_pages_per_seq=8192, max_batch=1,
               max_q_heads=48, fp8_pages=8192, tq3_pages=8192, placement_seed=5)
     assert h.append(0, 131072)[0] == OK
@@ -291,8 +291,8 @@ def test_long_context_schedule_is_balanced_for_the_resident_waves(lib):
         assert st == OK
         assert 256 <= sc["n_chunks"] <= 264 and sc["n8"] >= 1 and sc["n3"] >= 1
         _check_coverage(h, [0], sc, 16)
-        cost = np.array([float(it[3]) * (1.75 if i < sc["n8"] else 1) for i, it in enumerate(sc["items"])])
-        assert cost.max() <= 1.15 * (7936 + 1.75 * 256) / 256
+        cost = np.array([float(it[3]) * (1.2 if i < sc["n8"] else 1) for i, it in enumerate(sc["items"])])
+        assert cost.max() <= 1.15 * (7936 + 1.2 * 256) / 256
     sizes3 = sc["items"][sc["n8"]:, 3]
     assert sizes3.max() - sizes3.min() <= 1
     # algorithmic bytes: 126976 TQ3 tokens * 896 B + 4096 FP8 tokens * 2048 B + 256 pages * 64 B
