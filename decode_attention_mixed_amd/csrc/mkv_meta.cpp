@@ -330,12 +330,12 @@ int Meta::build_schedule(const int32_t* ids, int32_t B, int32_t Hq, const SchedP
   // Per-format page counts of each batch entry.  A wave walks an FP8 page one
   // kv-head at a time and a TQ3 page heads_per_block kv-heads at a time; the
   // default cost of an FP8 page in TQ3 pages is the one that gave the
-  // shortest partial kernels in a sweep of the cost (0.85 with one kv-head per
+  // shortest partial kernels in a sweep of the cost (0.6 with one kv-head per
   // workgroup, 1.2 with two).
   std::vector<int32_t> n8(size_t(B), 0), n3(size_t(B), 0);
   int64_t total_pages = 0;
   double total_cost = 0.0;
-  const double c8 = pol.fp8_page_cost > 0.0f ? double(pol.fp8_page_cost) : (heads_per_block == 2 ? 1.2 : 0.85);
+  const double c8 = pol.fp8_page_cost > 0.0f ? double(pol.fp8_page_cost) : (heads_per_block == 2 ? 1.2 : 0.6);
   for (int32_t b = 0; b < B; ++b) {
     for (int32_t e : seqs_[size_t(ids[b])].pt) (pt_is_tq3(e) ? n3 : n8)[size_t(b)]++;
     total_pages += int64_t(seqs_[size_t(ids[b])].pt.size());

@@ -120,7 +120,7 @@ inline int32_t heads_per_wave(int32_t d, int32_t Hkv, int32_t G) {
 // together they fill the partial kernel's resident waves once (an item takes
 // ceil(Hkv / kWavesPerWorkgroup) workgroups); an FP8 page counts
 // fp8_page_cost TQ3 pages (by default the cost that gave the shortest partial
-// kernels in a measured sweep: 0.85 with one kv-head per wave, 1.2 with two,
+// kernels in a measured sweep: 0.6 with one kv-head per wave, 1.2 with two,
 // since FP8 tiles hold one kv-head and TQ3 tiles that many).  min_items raises that count (a split-K floor:
 // more, shorter chunks) for batches of at least min_items * kFloorChunkPages
 // pages, as far as min_chunk_pages allows.  A
@@ -135,7 +135,7 @@ struct SchedPolicy {
   int32_t min_chunk_pages = 4;   // smallest balanced chunk (shorter lists stay whole)
   int32_t fixed_chunk_pages = 0; // 0: balanced chunks
   int32_t heads_per_wave = 0;    // kv-heads per partial-kernel workgroup; 0: heads_per_wave()
-  float fp8_page_cost = 0.0f;    // cost of an FP8 page relative to a TQ3 page; 0: 0.85 or 1.2
+  float fp8_page_cost = 0.0f;    // cost of an FP8 page relative to a TQ3 page; 0: 0.6 or 1.2
 };
 
 struct Schedule {
